@@ -1,0 +1,299 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (runs without a GPU).
+
+Each decode rule is checked against hand-decoded blocks stored under tests/golden/ (each file
+cites its page and section); the multiply loop is checked against closed forms (one-hot and zero
+activations, row permutations) and against numpy's fp64 matmul of the oracle's decoded matrix.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_quantized_decode_amd import inputs as I
+from weight_quantized_decode_amd import metrics as MX
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    out = {}
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+def f16(v):
+    return int(np.float16(v).view(np.uint16))
+
+
+def le16(h):
+    return [h & 0xFF, h >> 8]
+
+
+# ----------------------------------------------------------------------------- fp16 decode
+
+
+def test_half_to_double_matches_ieee_binary16_everywhere():
+    # numpy's float16 is an IEEE binary16 implementation: every one of the 65536 bit patterns must
+    # decode to the same value (NaNs compared as NaN), subnormals included.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    assert oracle.half_to_double(0x0001) == 2.0 ** -24
+    assert oracle.half_to_double(0x7BFF) == 65504.0
+
+
+# ----------------------------------------------------------------------------- byte budgets
+
+
+def test_q4_0_is_18_bytes_per_32_weights_4_5_bpw():
+    # blog.localai.hex7.com, ladder table: Q4_0 = 4 stored bits, 4.5 effective bits per weight,
+    # block-32 with one fp16 scale; "Anatomy of a block": 16-bit scale per 32 weights = 0.5 bpw.
+    assert oracle.canonical_bytes(1, 1, 32) == 18
+    assert MX.bits_per_weight(oracle.canonical_bytes(1, 4096, 4096), 4096 * 4096) == 4.5
+    assert MX.bits_per_weight(2, 32) == 0.5
+    assert oracle.canonical_bytes(1, 4096, 4096) == 9_437_184
+
+
+def test_tq2_is_34_bytes_per_128_weights_and_row_shape():
+    # vLLM ternary page, "Anatomy of a PQ2_0 block": 34 bytes per 128 weights = 2.125 bpw, and a
+    # weight matrix is a uint8 tensor of shape (N, K/128 * 34).
+    assert oracle.canonical_bytes(4, 1, 128) == 34
+    assert MX.bits_per_weight(34, 128) == 2.125
+    N, K = 17408, 5120
+    assert oracle.canonical_bytes(4, N, K) == N * (K // 128 * 34) == 23_674_880
+
+
+def test_aq2x8_code_bytes_at_4096_square():
+    # trapetum "Additive vector-quantization GEMV": at 2 bits (M=2, K=256, D=8), 4.2 MB of codes
+    # against 33.6 MB of fp16 weight at 4096x4096.
+    N = K = 4096
+    codes = oracle.canonical_bytes(5, N, K) - 8192 - 2 * N
+    assert codes == 4_194_304 and round(codes / 1e6, 1) == 4.2
+    assert round(N * K * 2 / 1e6, 1) == 33.6
+    assert MX.bits_per_weight(codes, N * K) == 2.0
+
+
+def test_byte_counts_of_the_workloads():
+    total = sum(oracle.canonical_bytes(p.fmt, p.N, p.K) for p in I.config_projections(3))
+    assert total == 3_369_082_368
+    assert sum(oracle.canonical_bytes(p.fmt, p.N, p.K) for p in I.config_projections(2)) == 101_187_808
+    assert [oracle.canonical_bytes(p.fmt, p.N, p.K) for p in I.config_projections(5)] == [
+        58_785_792, 58_785_792, 58_744_832]
+    for p in I.config_projections(4):
+        assert oracle.canonical_bytes(p.fmt, p.N, p.K) == 23_674_880
+
+
+def test_bad_shapes_are_rejected():
+    assert oracle.canonical_bytes(1, 4, 48) == -1   # K not a multiple of 32
+    assert oracle.canonical_bytes(4, 4, 64) == -1   # K not a multiple of 128
+    assert oracle.canonical_bytes(5, 4, 12) == -1   # K not a multiple of 8
+    assert oracle.canonical_bytes(2, 4, 3) == -1    # odd K
+    assert oracle.canonical_bytes(9, 4, 8) == -1
+
+
+# ----------------------------------------------------------------------------- byte-model formulas
+
+
+def test_bandwidth_floor_and_ceiling_of_the_ternary_page():
+    # "A rough speed limit": 6.80 GB / 1008 GB/s is about 6.75 ms per token, reciprocal 148 tok/s.
+    assert round(MX.floor_seconds(6.80e9, 1008) * 1e3, 2) == 6.75
+    assert round(MX.ceiling_tok_s(6.80e9, 1008)) == 148
+    # 25 tok/s * 6.80 GB/token = about 170 GB/s, 17% of the card.
+    assert round(MX.effective_gbps(25, 6.80e9)) == 170
+    assert round(MX.fraction_of_peak(MX.effective_gbps(25, 6.80e9), 1008) * 100) == 17
+
+
+def test_effective_bandwidth_of_the_70b_2x8_decode():
+    # trapetum Llama-2-70B 2x8: about 17.4 GB per token at 38.4 tok/s, so about 670 GB/s,
+    # two thirds of 1,008 GB/s.
+    g = MX.effective_gbps(38.4, 17.4e9)
+    assert abs(g - 670) < 5
+    assert abs(MX.fraction_of_peak(g, 1008) - 2 / 3) < 0.01
+
+
+# ----------------------------------------------------------------------------- hand-decoded blocks
+
+
+def test_tq2_worked_byte_0x64():
+    g = read_golden("tq2_byte_0x64.txt")
+    d = int(g["scale_f16"][0], 16)
+    byte = int(g["byte"][0], 16)
+    qs = [byte] + [0x55] * 31  # remaining codes 1 -> weight 0
+    canon = np.array(le16(d) + qs, dtype=np.uint8)
+    w = oracle.decode_f64(4, 1, 128, canon)[0]
+    assert list(w[:4]) == [float(v) for v in g["weights"]]
+    assert np.all(w[4:] == 0.0)
+    # code 3 would decode to +2 * d
+    canon3 = np.array(le16(d) + [0x03] + [0x55] * 31, dtype=np.uint8)
+    assert oracle.decode_f64(4, 1, 128, canon3)[0][0] == float(g["code3_weight"][0])
+
+
+def test_q4_0_hand_block():
+    g = read_golden("q4_0_block.txt")
+    d = int(g["scale_f16"][0], 16)
+    qs = [int(b, 16) for b in g["qs"]]
+    canon = np.array(le16(d) + qs, dtype=np.uint8)
+    w = oracle.decode_f64(1, 1, 32, canon)[0]
+    assert list(w) == [float(v) for v in g["weights"]]
+
+
+def test_q4_0_scale_belongs_to_its_own_block():
+    # two blocks with different scales: the second block's weights use the second scale
+    canon = np.array(le16(f16(1.0)) + [0x99] * 16 + le16(f16(-0.5)) + [0x99] * 16, dtype=np.uint8)
+    w = oracle.decode_f64(1, 1, 64, canon)[0]
+    assert np.all(w[:32] == 1.0) and np.all(w[32:] == -0.5)
+
+
+def test_cb4_hand_row():
+    g = read_golden("cb4_row.txt")
+    cb = [f16(float(v)) for v in g["codebook"]]
+    codes = [int(b, 16) for b in g["codes"]]
+    canon = np.array(sum((le16(h) for h in cb), []) + codes, dtype=np.uint8)
+    w = oracle.decode_f64(2, 1, 2 * len(codes), canon)[0]
+    assert list(w) == [float(v) for v in g["weights"]]
+
+
+def test_cb8_hand_row():
+    g = read_golden("cb8_row.txt")
+    cb = [f16((i - 128) / 4) for i in range(256)]
+    codes = [int(b, 16) for b in g["codes"]]
+    canon = np.array(sum((le16(h) for h in cb), []) + codes, dtype=np.uint8)
+    w = oracle.decode_f64(3, 1, len(codes), canon)[0]
+    assert list(w) == [float(v) for v in g["weights"]]
+
+
+def _aq_canon_from_golden(g):
+    C0 = [[f16(8 * c + j) for j in range(8)] for c in range(256)]
+    C1 = [[f16(-c) for _ in range(8)] for c in range(256)]
+    cbk = sum((le16(h) for row in C0 + C1 for h in row), [])
+    sc = sum((le16(f16(float(v))) for v in g["scales"]), [])
+    codes = [int(v) for v in g["codes_row0"]] + [int(v) for v in g["codes_row1"]]
+    return np.array(cbk + sc + codes, dtype=np.uint8)
+
+
+def test_aq2x8_hand_rows():
+    g = read_golden("aq2x8_rows.txt")
+    canon = _aq_canon_from_golden(g)
+    w = oracle.decode_f64(5, 2, 8, canon)
+    assert list(w[0]) == [float(v) for v in g["weights_row0"]]
+    assert list(w[1]) == [float(v) for v in g["weights_row1"]]
+
+
+def test_aq2x8_fp32_dequant_rounds_sum_then_product():
+    # fp32 reading of the decode: round the codebook sum to fp32 (nearest even), then the product.
+    # C0 = 1, C1 = 2^-24 (an fp16 subnormal): the fp32 sum 1 + 2^-24 is a tie and rounds to 1.
+    C = np.zeros((2, 256, 8), dtype=np.uint16)
+    C[0, 0, :] = f16(1.0)
+    C[1, 0, :] = 0x0001
+    s = f16(0.75)
+    canon = np.concatenate([C.astype("<u2").view(np.uint8).reshape(-1),
+                            np.array(le16(s), dtype=np.uint8), np.zeros(2, dtype=np.uint8)])
+    w64 = oracle.decode_f64(5, 1, 8, canon)[0]
+    w32 = oracle.dequant_f32(5, 1, 8, canon)[0]
+    assert np.all(w64 == 0.75 * (1 + 2.0 ** -24))
+    assert np.all(w32 == np.float32(0.75))
+
+
+def test_subnormal_scales_are_kept():
+    # an fp16 subnormal scale (2^-24) is kept, not flushed: Q4_0 code 15 -> 7 * 2^-24
+    canon = np.array(le16(0x0001) + [0xFF] * 16, dtype=np.uint8)
+    w = oracle.decode_f64(1, 1, 32, canon)[0]
+    assert np.all(w == 7 * 2.0 ** -24)
+    assert np.all(oracle.dequant_f32(1, 1, 32, canon)[0] == np.float32(7 * 2.0 ** -24))
+
+
+# ----------------------------------------------------------------------------- the multiply
+
+
+SHAPES = [(1, 5, 96), (2, 7, 256), (3, 3, 128), (4, 6, 384), (5, 4, 40)]
+
+
+@pytest.mark.parametrize("fmt,N,K", SHAPES)
+def test_one_hot_activation_returns_a_weight_column(fmt, N, K):
+    canon = I.gen_weight(fmt, N, K, (77, fmt))
+    W = oracle.decode_f64(fmt, N, K, canon)
+    for k in (0, K // 3, K - 1):
+        x = np.zeros((1, K), dtype=np.uint16)
+        x[0, k] = f16(1.0)
+        y, a = oracle.gemm_f64(fmt, N, K, canon, x)
+        assert np.array_equal(y[0], W[:, k])
+        assert np.array_equal(a[0], np.abs(W[:, k]))
+
+
+@pytest.mark.parametrize("fmt,N,K", SHAPES)
+def test_zero_activation_gives_zero(fmt, N, K):
+    canon = I.gen_weight(fmt, N, K, (78, fmt))
+    y, a = oracle.gemm_f64(fmt, N, K, canon, np.zeros((2, K), dtype=np.uint16))
+    assert np.all(y == 0) and np.all(a == 0)
+
+
+@pytest.mark.parametrize("fmt,N,K", SHAPES)
+def test_gemm_matches_numpy_matmul_of_decoded_matrix(fmt, N, K):
+    canon = I.gen_weight(fmt, N, K, (79, fmt))
+    x = I.gen_x(3, K, (79, fmt))
+    W = oracle.decode_f64(fmt, N, K, canon)
+    X = x.view(np.float16).astype(np.float64)
+    y, a = oracle.gemm_f64(fmt, N, K, canon, x)
+    ref = X @ W.T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+    assert np.allclose(a, np.abs(X) @ np.abs(W).T, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("fmt,N,K", SHAPES)
+def test_row_subset_equals_full_rows(fmt, N, K):
+    canon = I.gen_weight(fmt, N, K, (80, fmt))
+    x = I.gen_x(2, K, (80, fmt))
+    y, _ = oracle.gemm_f64(fmt, N, K, canon, x)
+    rows = np.array([N - 1, 0, N // 2], dtype=np.int64)
+    ys, _ = oracle.gemm_f64(fmt, N, K, canon, x, rows=rows)
+    assert np.array_equal(ys, y[:, rows])
+
+
+def test_gemm_exact_on_dyadic_tiny_case():
+    # Brute force with exact rationals: a 2x64 Q4_0 matrix with power-of-two scales and
+    # integer activations has an exactly representable product.
+    qs0 = [0x1F, 0x2E, 0x3D, 0x4C] * 4
+    qs1 = [0x80, 0x08, 0xFF, 0x00] * 4
+    canon = np.array(le16(f16(0.5)) + qs0 + le16(f16(2.0)) + qs1
+                     + le16(f16(0.25)) + qs1 + le16(f16(4.0)) + qs0, dtype=np.uint8)
+    xs = [((k * 7) % 11) - 5 for k in range(64)]
+    x = np.array([[f16(v) for v in xs]], dtype=np.uint16)
+    y, _ = oracle.gemm_f64(1, 2, 64, canon, x)
+
+    def lo(b):
+        return b & 15
+
+    def hi(b):
+        return b >> 4
+
+    def row_weights(blocks):
+        w = []
+        for d, qs in blocks:
+            w += [Fraction(lo(b) - 8) * d for b in qs] + [Fraction(hi(b) - 8) * d for b in qs]
+        return w
+
+    r0 = row_weights([(Fraction(1, 2), qs0), (Fraction(2), qs1)])
+    r1 = row_weights([(Fraction(1, 4), qs1), (Fraction(4), qs0)])
+    exact = [sum(Fraction(a) * b for a, b in zip(xs, r)) for r in (r0, r1)]
+    assert [Fraction(v) for v in y[0]] == exact
+
+
+def test_dequant_f32_is_the_rounded_exact_value_for_exact_formats():
+    for fmt in (1, 2, 3, 4):
+        canon = I.gen_weight(fmt, 4, 256, (81, fmt))
+        w64 = oracle.decode_f64(fmt, 4, 256, canon)
+        w32 = oracle.dequant_f32(fmt, 4, 256, canon)
+        assert np.array_equal(w32.astype(np.float64), w64)  # exact in fp32
