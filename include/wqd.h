@@ -1,0 +1,149 @@
+/* wqd.h -- C ABI of the MI355X (gfx950) weight-quantized decode library (libwqd.so).
+ *
+ * The library computes the projection of batch-1 and small-batch LLM decode,
+ *
+ *     y[m][n] = sum_k x[m][k] * dequant(Wq)[n][k]       (0 <= m < M <= 8, 0 <= n < N, 0 <= k < K)
+ *
+ * with packed low-bit weights streamed from HBM once, decoded in registers and multiplied by a
+ * short fp16 activation row, accumulating in fp32.  The operation and the formats are those of:
+ *   - trapetum "Benchmarks" (trapetum.neuralboot.com), "Kernel microbenchmarks" (4-bit and 8-bit
+ *     codebook GEMV), "Additive vector-quantization GEMV (AQLM-style, 2-bit)", and the November
+ *     update's fused, graphed decode step;
+ *   - "Making a ternary reasoning model fast in vLLM", "Anatomy of a PQ2_0 block" and "The ideal
+ *     kernel, as a checklist" (the 2-bit ternary block and the batch-1 projection y = x W^T with
+ *     M input rows, N outputs and K inputs);
+ *   - "Model quantization, read carefully" (blog.localai.hex7.com), "The ladder" table (Q4_0).
+ *
+ * Conventions
+ *   - Every pointer is a device pointer unless its name ends in _host.  The caller owns every
+ *     buffer; the library allocates no device memory and never synchronizes the stream except in
+ *     wqd_stack_setup and wqd_stream_check.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Kernels are enqueued
+ *     on it asynchronously; calls are stream-ordered and reentrant.
+ *   - Functions return a wqd_status.  Argument errors are detected before any HIP call.  A launch
+ *     failure returns WQD_EHIP (see wqd_last_hip_error); a fault inside a kernel surfaces later,
+ *     through wqd_stream_check.
+ *   - x is fp16 (IEEE binary16 bit patterns), row-major with leading dimension ldx (elements).
+ *     y is fp32, row-major with leading dimension ldy (elements).
+ *
+ * Formats (fmt) and their canonical (interchange) bytes, all little-endian:
+ *   WQD_Q4_0  per row, K/32 blocks of 18 B: fp16 scale d, then 16 bytes of 4-bit codes; byte j
+ *             holds weight j (low nibble) and weight j+16 (high nibble); weight = (code - 8) * d.
+ *   WQD_CB4   16 fp16 centroids (32 B), then codes [N][K/2]: low nibble = even k; weight = cb[code].
+ *   WQD_CB8   256 fp16 centroids (512 B), then codes [N][K]; weight = cb[code].
+ *   WQD_TQ2   per row, K/128 blocks of 34 B: fp16 scale d, then 32 bytes of 2-bit codes, weight j
+ *             of the block at bits 2*(j%4) of byte j/4; weight = (code - 1) * d (code 3 -> +2d).
+ *   WQD_AQ2X8 codebooks C[2][256][8] fp16 (8192 B), row scales s[N] fp16, codes [N][K/8][2]
+ *             (codebook 0 first); weight k of row n = s[n] * (C[0][c0][k%8] + C[1][c1][k%8]) with
+ *             (c0, c1) the codes of group k/8.
+ *   K must be a multiple of 32 (Q4_0), 2 (CB4), 1 (CB8), 128 (TQ2) or 8 (AQ2X8).
+ *
+ * Prepared (device) layout: the same bytes re-laid once at load time into planes ("prepared
+ * weights": a contiguous code plane, then the scale plane, then codebooks), built by
+ * wqd_prepare_host and uploaded by the caller.  Its size is wqd_prepared_bytes(); it must be
+ * 16-byte aligned on the device.
+ */
+#ifndef WQD_H
+#define WQD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQD_API __attribute__((visibility("default")))
+
+typedef enum { WQD_Q4_0 = 1, WQD_CB4 = 2, WQD_CB8 = 3, WQD_TQ2 = 4, WQD_AQ2X8 = 5 } wqd_format;
+
+typedef enum {
+    WQD_OK = 0,
+    WQD_EINVAL = -1, /* null pointer, unknown format or mode */
+    WQD_ESHAPE = -2, /* N < 1, K not a whole number of blocks/groups, M outside 1..8, ld too small */
+    WQD_EALIGN = -3, /* weight not 16-byte aligned, x or y not 4-byte aligned, odd ldx */
+    WQD_ESPACE = -4, /* a capacity or workspace argument is smaller than required */
+    WQD_EHIP = -5    /* a HIP call failed; wqd_last_hip_error() gives its hipError_t */
+} wqd_status;
+
+enum { WQD_MAX_M = 8 };
+
+/* ---------------------------------------------------------------- layout (host only, no HIP) */
+
+/* Bytes of the canonical encoding of an N x K matrix, or a negative wqd_status. */
+WQD_API int64_t wqd_canonical_bytes(int fmt, int64_t N, int64_t K);
+
+/* Bytes of the prepared (device) layout, or a negative wqd_status. */
+WQD_API int64_t wqd_prepared_bytes(int fmt, int64_t N, int64_t K);
+
+/* Re-lay canonical bytes (host memory) into the prepared layout (host memory).  Pure host code:
+ * canonical_bytes and prepared_bytes are the capacities of the two buffers; they must be at least
+ * wqd_canonical_bytes() and wqd_prepared_bytes().  Padding bytes are written as zero. */
+WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonical_host,
+                             int64_t canonical_bytes, void *prepared_host, int64_t prepared_bytes);
+
+/* ---------------------------------------------------------------- one projection */
+
+/* Device workspace wqd_gemm needs for this shape (split-K partial sums), in bytes (0 = none). */
+WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
+
+/* y[m*ldy + n] = sum_k x[m*ldx + k] * W[n][k] for 1 <= M <= 8, enqueued on `stream`.
+ * w: prepared weights (wqd_prepared_bytes(fmt, N, K) bytes, 16-byte aligned).
+ * x: M rows of K fp16 values, ldx >= K and even, 4-byte aligned.  y: M rows of N fp32, ldy >= N.
+ * workspace: at least wqd_gemm_workspace_bytes(fmt, N, K, M) bytes of device memory (may be NULL
+ * when that is 0); it is scratch, overwritten by the call.  Results are the same bits from run
+ * to run (fixed-order reductions, no atomics). */
+WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
+                     int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+
+/* Debug decode: out[n*K + k] = dequantized weight in fp32, bit-exact: the exact value for Q4_0,
+ * CB4, CB8 and TQ2 (all representable in fp32); for AQ2X8 fp32(fp32(C0 + C1) * s) with
+ * round-to-nearest-even after the add and after the product. */
+WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream);
+
+/* ---------------------------------------------------------------- layer / stack */
+
+typedef struct {
+    int32_t fmt;
+    int32_t reserved; /* must be 0 */
+    int64_t N, K;
+    const void *w;    /* prepared weights */
+    const void *x;    /* fp16 activations, M rows of ldx */
+    int64_t ldx;
+    float *y;         /* fp32 outputs, M rows of ldy */
+    int64_t ldy;
+} wqd_proj;
+
+enum {
+    WQD_ORDERED = 0,   /* projections one after another, each its own launches */
+    WQD_PERSISTENT = 1 /* all projections of a format in one persistent launch, then one launch
+                          for the fixed-order split-K reduction of every projection; valid when
+                          no projection's x is another projection's y */
+};
+
+/* Device workspace bytes for wqd_run_projections over this list (descriptor table + partials). */
+WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
+
+/* Write the descriptor table of this projection list into the workspace (a blocking copy).
+ * Must be called once before wqd_run_projections in WQD_PERSISTENT mode, and again whenever a
+ * pointer or shape in the list changes. */
+WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, void *workspace,
+                            int64_t workspace_bytes, void *stream);
+
+/* Run every projection of the list (same semantics as wqd_gemm for each).  `mode` is
+ * WQD_ORDERED or WQD_PERSISTENT. */
+WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
+                                void *workspace, int64_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- errors */
+
+/* Synchronize `stream` and map any pending asynchronous error to WQD_EHIP. */
+WQD_API int wqd_stream_check(void *stream);
+/* hipError_t of the last WQD_EHIP returned on this thread (0 if none). */
+WQD_API int wqd_last_hip_error(void);
+WQD_API const char *wqd_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WQD_H */

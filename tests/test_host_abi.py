@@ -1,0 +1,147 @@
+"""Host-side checks of libwqd (no GPU needed): exported symbols, byte counts, the prepared
+layout's re-lay of the canonical bytes, and argument validation before any HIP call."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from weight_quantized_decode_amd import _lib as W
+from weight_quantized_decode_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FMTS = [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8]
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "wqd.h")).read()
+    return sorted(set(re.findall(r"WQD_API\s+[\w\s\*]+?\b(wqd_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    L = W.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(W.EXPORTED) == syms
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_canonical_bytes_agree_with_oracle(fmt):
+    for N, K in [(1, 256), (64, 1024), (4096, 4096), (11008, 4096), (5120, 17408), (8192, 28672)]:
+        assert W.wqd_canonical_bytes(fmt, N, K) == oracle.canonical_bytes(fmt, N, K)
+
+
+def test_prepared_sizes_are_canonical_plus_padding_only():
+    # at the workload shapes (N multiple of 64, rows a whole number of 16-byte chunks) the
+    # prepared planes hold exactly the canonical bytes, plus plane alignment (<= 3 x 255 bytes)
+    for cfg in (1, 2, 4, 5):
+        for p in I.config_projections(cfg):
+            c = W.wqd_canonical_bytes(p.fmt, p.N, p.K)
+            q = W.wqd_prepared_bytes(p.fmt, p.N, p.K)
+            assert c <= q <= c + 3 * 256, (p, c, q)
+
+
+def _tile_rows(prep, fmt, N, K):
+    """Code plane back to [N][C*16] row order (inverse of the 64-row tiling)."""
+    L = W.wqd_prepared_bytes(fmt, N, K)
+    row_bytes = {I.Q4_0: K // 2, I.CB4: K // 2, I.CB8: K, I.TQ2: K // 4, I.AQ2X8: K // 4}[fmt]
+    C = (row_bytes + 15) // 16
+    RG = (N + 63) // 64
+    codes = prep[:RG * C * 64 * 16].reshape(RG, C, 64, 16).transpose(0, 2, 1, 3).reshape(RG * 64, C * 16)
+    return codes[:N], row_bytes, C, RG
+
+
+@pytest.mark.parametrize("fmt,N,K", [(I.CB4, 70, 1002), (I.CB8, 70, 1001), (I.AQ2X8, 70, 1000)])
+def test_prepare_keeps_canonical_byte_order_for_byte_formats(fmt, N, K):
+    canon = I.gen_weight(fmt, N, K, (5, fmt))
+    prep = W.wqd_prepare_host(fmt, N, K, canon)
+    rows, row_bytes, C, RG = _tile_rows(prep, fmt, N, K)
+    head = {I.CB4: 32, I.CB8: 512, I.AQ2X8: 8192 + 2 * N}[fmt]
+    assert np.array_equal(rows[:, :row_bytes], canon[head:].reshape(N, row_bytes))
+    assert np.all(rows[:, row_bytes:] == 0)  # tail padding is zero
+    full = prep[:RG * C * 1024].reshape(RG, C, 64, 16)
+    assert np.all(full[:, :, (N - (RG - 1) * 64):, :][-1] == 0)  # padded rows are zero
+
+
+@pytest.mark.parametrize("fmt,N,K", [(I.Q4_0, 70, 256), (I.TQ2, 70, 512)])
+def test_prepare_permutes_codes_within_rows_only(fmt, N, K):
+    # the block formats' code bits are permuted inside each row: every row keeps its multiset of
+    # codes, and its scales
+    canon = I.gen_weight(fmt, N, K, (6, fmt))
+    prep = W.wqd_prepare_host(fmt, N, K, canon)
+    rows, row_bytes, C, RG = _tile_rows(prep, fmt, N, K)
+    bits = 4 if fmt == I.Q4_0 else 2
+    bsz = 18 if fmt == I.Q4_0 else 34
+    nb = K // (32 if fmt == I.Q4_0 else 128)
+    blk = canon.reshape(N, nb, bsz)
+
+    def hist(b):
+        vals = np.stack([(b >> s) & ((1 << bits) - 1) for s in range(0, 8, bits)], -1)
+        return np.bincount(vals.reshape(-1), minlength=1 << bits)
+
+    for n in range(N):
+        assert np.array_equal(hist(rows[n]), hist(blk[n, :, 2:]))
+    scales_canon = np.sort(blk[:, :, 0:2].copy().view(np.uint16).reshape(-1))
+    off = ((RG * C * 1024 + 255) // 256) * 256
+    Q = (nb + 3) // 4
+    sc = prep[off:off + RG * Q * 64 * 8].view(np.uint16).reshape(RG, Q, 64, 4)
+    sc = sc.transpose(0, 2, 1, 3).reshape(RG * 64, Q * 4)[:N, :nb]
+    assert np.array_equal(np.sort(sc.reshape(-1)), scales_canon)
+    assert np.array_equal(sc, blk[:, :, 0:2].copy().view(np.uint16).reshape(N, nb))
+
+
+def test_prepare_rejects_bad_arguments():
+    canon = np.zeros(64, dtype=np.uint8)
+    out = np.zeros(4096, dtype=np.uint8)
+    L = W.lib()
+    assert L.wqd_prepare_host(9, 1, 32, canon.ctypes.data, 64, out.ctypes.data, 4096) == W.WQD_EINVAL
+    assert L.wqd_prepare_host(1, 1, 48, canon.ctypes.data, 64, out.ctypes.data, 4096) == W.WQD_ESHAPE
+    assert L.wqd_prepare_host(1, 2, 32, canon.ctypes.data, 20, out.ctypes.data, 4096) == W.WQD_ESPACE
+    assert L.wqd_prepare_host(1, 1, 32, None, 64, out.ctypes.data, 4096) == W.WQD_EINVAL
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((9, 64, 64, FAKE, FAKE, 1, 64, FAKE, 64), W.WQD_EINVAL),          # unknown format
+    ((1, 64, 48, FAKE, FAKE, 1, 64, FAKE, 64), W.WQD_ESHAPE),          # K not whole blocks
+    ((1, 64, 64, FAKE, FAKE, 0, 64, FAKE, 64), W.WQD_ESHAPE),          # M = 0
+    ((1, 64, 64, FAKE, FAKE, 9, 64, FAKE, 64), W.WQD_ESHAPE),          # M = 9
+    ((1, 64, 64, FAKE, FAKE, 1, 32, FAKE, 64), W.WQD_ESHAPE),          # ldx < K
+    ((1, 64, 64, FAKE, FAKE, 1, 64, FAKE, 10), W.WQD_ESHAPE),          # ldy < N
+    ((1, 64, 64, FAKE + 8, FAKE, 1, 64, FAKE, 64), W.WQD_EALIGN),      # w not 16-byte aligned
+    ((1, 64, 64, FAKE, FAKE + 2, 1, 64, FAKE, 64), W.WQD_EALIGN),      # x not 4-byte aligned
+    ((1, 64, 64, FAKE, FAKE, 1, 65, FAKE, 64), W.WQD_EALIGN),          # odd ldx
+    ((1, 64, 64, None, FAKE, 1, 64, FAKE, 64), W.WQD_EINVAL),          # null weight
+])
+def test_gemm_argument_errors_before_any_launch(args, status):
+    fmt, N, K, w, x, M, ldx, y, ldy = args
+    assert W.lib().wqd_gemm(fmt, N, K, w, x, M, ldx, y, ldy, None, 0, None) == status
+
+
+def test_gemm_workspace_too_small_is_reported():
+    need = W.wqd_gemm_workspace_bytes(I.Q4_0, 4096, 4096, 1)
+    assert need > 0
+    assert W.lib().wqd_gemm(I.Q4_0, 4096, 4096, FAKE, FAKE, 1, 4096, FAKE, 4096, FAKE, need - 4,
+                            None) == W.WQD_ESPACE
+
+
+def test_run_projections_rejects_bad_mode_and_lists():
+    arr = (W.wqd_proj * 1)()
+    arr[0].fmt, arr[0].N, arr[0].K = I.CB4, 64, 64
+    arr[0].w, arr[0].x, arr[0].y, arr[0].ldx, arr[0].ldy = FAKE, FAKE, FAKE, 64, 64
+    L = W.lib()
+    assert L.wqd_run_projections(arr, 1, 1, 7, FAKE, 1 << 20, None) == W.WQD_EINVAL
+    assert L.wqd_run_projections(arr, 1, 0, 0, FAKE, 1 << 20, None) == W.WQD_ESHAPE
+    arr[0].reserved = 1
+    assert L.wqd_run_projections(arr, 1, 1, 0, FAKE, 1 << 20, None) == W.WQD_EINVAL
+    assert L.wqd_stack_workspace_bytes(arr, 1, 1) == W.WQD_EINVAL
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert W.wqd_status_str(s)

@@ -1,0 +1,174 @@
+"""Thin ctypes binding of libwqd.so (include/wqd.h): argument marshalling only.
+
+Every function keeps the name of the C entry point it wraps.  Device buffers are torch tensors
+(used for memory and streams only); host buffers are numpy arrays.  A non-zero status raises
+WqdError.  There is no fallback: if libwqd.so is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SO_PATH = os.path.join(_HERE, "libwqd.so")
+
+WQD_Q4_0, WQD_CB4, WQD_CB8, WQD_TQ2, WQD_AQ2X8 = 1, 2, 3, 4, 5
+WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP = 0, -1, -2, -3, -4, -5
+WQD_ORDERED, WQD_PERSISTENT = 0, 1
+WQD_MAX_M = 8
+
+EXPORTED = [
+    "wqd_canonical_bytes", "wqd_prepared_bytes", "wqd_prepare_host", "wqd_gemm_workspace_bytes",
+    "wqd_gemm", "wqd_dequant_f32", "wqd_stack_workspace_bytes", "wqd_stack_setup",
+    "wqd_run_projections", "wqd_stream_check", "wqd_last_hip_error", "wqd_status_str",
+]
+
+
+class WqdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().wqd_status_str(status).decode()
+        if status == WQD_EHIP:
+            msg += f" (hipError_t {lib().wqd_last_hip_error()})"
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+class wqd_proj(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("w", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwqd.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO_PATH):
+            raise OSError(f"{SO_PATH} is missing: build it with weight_quantized_decode_amd.build.build()")
+        L = ctypes.CDLL(SO_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        sig = {
+            "wqd_canonical_bytes": (i64, [ctypes.c_int, i64, i64]),
+            "wqd_prepared_bytes": (i64, [ctypes.c_int, i64, i64]),
+            "wqd_prepare_host": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, i64, vp, i64]),
+            "wqd_gemm_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
+            "wqd_gemm": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
+            "wqd_dequant_f32": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp]),
+            "wqd_stack_workspace_bytes": (i64, [ctypes.POINTER(wqd_proj), i32, i64]),
+            "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, vp, i64, vp]),
+            "wqd_run_projections": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
+            "wqd_stream_check": (ctypes.c_int, [vp]),
+            "wqd_last_hip_error": (ctypes.c_int, []),
+            "wqd_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> int:
+    if status < 0:
+        raise WqdError(fn, status)
+    return status
+
+
+def _dptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (None passes NULL)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------------- layout (host only)
+
+def wqd_canonical_bytes(fmt: int, N: int, K: int) -> int:
+    return _check("wqd_canonical_bytes", lib().wqd_canonical_bytes(fmt, N, K))
+
+
+def wqd_prepared_bytes(fmt: int, N: int, K: int) -> int:
+    return _check("wqd_prepared_bytes", lib().wqd_prepared_bytes(fmt, N, K))
+
+
+def wqd_prepare_host(fmt: int, N: int, K: int, canonical: np.ndarray) -> np.ndarray:
+    canonical = np.ascontiguousarray(canonical, dtype=np.uint8)
+    out = np.empty(wqd_prepared_bytes(fmt, N, K), dtype=np.uint8)
+    _check("wqd_prepare_host", lib().wqd_prepare_host(fmt, N, K, canonical.ctypes.data, canonical.nbytes,
+                                                      out.ctypes.data, out.nbytes))
+    return out
+
+
+# ------------------------------------------------------------------------- one projection
+
+def wqd_gemm_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
+    return _check("wqd_gemm_workspace_bytes", lib().wqd_gemm_workspace_bytes(fmt, N, K, M))
+
+
+def wqd_gemm(fmt: int, N: int, K: int, w, x, y, workspace=None, stream=None) -> None:
+    """y[M, N] (fp32) = x[M, K] (fp16) times the dequantized W[N, K]; x and y may have row strides."""
+    M = x.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("wqd_gemm", lib().wqd_gemm(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
+                                      _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wqd_dequant_f32(fmt: int, N: int, K: int, w, out, stream=None) -> None:
+    _check("wqd_dequant_f32", lib().wqd_dequant_f32(fmt, N, K, _dptr(w), _dptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------------- layer / stack
+
+def make_proj_array(projs: Sequence[dict]):
+    """projs: dicts with fmt, N, K, w, x, y (torch tensors); returns a ctypes array of wqd_proj."""
+    arr = (wqd_proj * len(projs))()
+    for i, p in enumerate(projs):
+        arr[i].fmt = p["fmt"]
+        arr[i].reserved = 0
+        arr[i].N = p["N"]
+        arr[i].K = p["K"]
+        arr[i].w = p["w"].data_ptr()
+        arr[i].x = p["x"].data_ptr()
+        arr[i].ldx = p["x"].stride(0)
+        arr[i].y = p["y"].data_ptr()
+        arr[i].ldy = p["y"].stride(0)
+    return arr
+
+
+def wqd_stack_workspace_bytes(arr, M: int) -> int:
+    return _check("wqd_stack_workspace_bytes", lib().wqd_stack_workspace_bytes(arr, len(arr), M))
+
+
+def wqd_stack_setup(arr, M: int, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("wqd_stack_setup", lib().wqd_stack_setup(arr, len(arr), M, _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wqd_run_projections(arr, M: int, mode: int, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("wqd_run_projections", lib().wqd_run_projections(arr, len(arr), M, mode, _dptr(workspace), ws_bytes,
+                                                            _stream(stream)))
+
+
+def wqd_stream_check(stream=None) -> None:
+    _check("wqd_stream_check", lib().wqd_stream_check(_stream(stream)))
+
+
+def wqd_status_str(status: int) -> str:
+    return lib().wqd_status_str(status).decode()

@@ -1,0 +1,6 @@
+// AQ2X8 instances of the dequantize-and-multiply kernel (see gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace wqd {
+GemvFn gemv_fn_aq2x8(int M) { return gemv_fn<AQ2X8>(M); }
+}  // namespace wqd

@@ -1,0 +1,6 @@
+// CB8 instances of the dequantize-and-multiply kernel (see gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace wqd {
+GemvFn gemv_fn_cb8(int M) { return gemv_fn<CB8>(M); }
+}  // namespace wqd

@@ -1,0 +1,435 @@
+// HIP kernels (gfx950) and the C entry points of libwqd that launch them.
+//
+// Design (one projection y = x W^T, M <= 8 activation rows):
+//   * One wavefront lane per weight row: a wave covers a group of 64 rows, and every load
+//     instruction reads chunk c of those 64 rows, 1 KiB of contiguous prepared code bytes
+//     (layout.h).  Each row's dot product stays inside its lane, so no cross-lane reduction.
+//   * The activations are the same for all 64 lanes, so they are read with scalar loads into
+//     SGPRs and fed to v_dot2 (two fp16 products accumulated in fp32 per instruction).
+//   * Work unit of a wave = (row group, K-slice).  K is split only as far as needed to give the
+//     GPU enough waves; slices write fp32 partial sums and a second kernel adds them in a fixed
+//     order, so results are the same bits from run to run (no atomics).
+//   * Codebook formats decode through tables in LDS replicated per lane slot (one copy per bank),
+//     indexed with one v_perm per byte; the block formats decode with AND masks that leave the
+//     codes as fp16 subnormals (code * 2^-24 * 4^j) and apply the -8 / -1 offset through the
+//     per-block sum of the activations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace wqd {
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+__device__ __forceinline__ cu32p scalar_ptr(const void *p) {
+    return (cu32p)(uintptr_t)p;
+}
+// Descriptor read with scalar loads, so its fields live in SGPRs and count as wave-uniform.
+__device__ __forceinline__ Desc load_desc(const Desc *p) {
+    static_assert(sizeof(Desc) % 4 == 0, "descriptor must be whole dwords");
+    uint32_t w[sizeof(Desc) / 4];
+    cu32p s = scalar_ptr(p);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(Desc) / 4; i++) w[i] = s[i];
+    Desc D;
+    __builtin_memcpy(&D, w, sizeof(Desc));
+    return D;
+}
+__device__ __forceinline__ int load_wgu_begin(const Desc *p) {
+    return (int)scalar_ptr(&p->wgu_begin)[0];
+}
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// LDS dword at a byte offset (the offset is already a multiple of 4).
+__device__ __forceinline__ uint32_t lds_word(const uint32_t *lds, uint32_t byte_off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds) + byte_off);
+}
+
+// Loads through the global address space (global_load_*, counted by vmcnt only; a generic
+// pointer would compile to flat loads, which also hold up LDS waits).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T gld(const void *p) {
+    return *(const T __attribute__((address_space(1))) *)(uintptr_t)p;
+}
+__device__ __forceinline__ uint4 ld16(const uint8_t *p) {
+    const u32x4 v = gld<u32x4>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8(const uint8_t *p) {
+    const u32x2 v = gld<u32x2>(p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld16(const uint4 *p) { return ld16(reinterpret_cast<const uint8_t *>(p)); }
+__device__ __forceinline__ void gst(float *p, float v) {
+    *(float __attribute__((address_space(1))) *)(uintptr_t)p = v;
+}
+
+// Uniform read of NW consecutive x dwords (2*NW fp16 values starting at element k) of one row.
+// FULL: the whole range lies inside K (scalar loads).  Otherwise elements at or beyond K read as
+// zero (only a partial last chunk takes that path).
+template <bool FULL, int NW>
+__device__ __forceinline__ void load_x(uint32_t (&xs)[NW], const uint16_t *xrow, int k, int K) {
+    if constexpr (FULL) {
+        cu32p p = scalar_ptr(xrow + k);
+#pragma unroll
+        for (int i = 0; i < NW; i++) xs[i] = p[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            uint32_t lo = (k + 2 * i < K) ? gld<uint16_t>(xrow + k + 2 * i) : 0u;
+            uint32_t hi = (k + 2 * i + 1 < K) ? gld<uint16_t>(xrow + k + 2 * i + 1) : 0u;
+            xs[i] = lo | (hi << 16);
+        }
+    }
+}
+
+template <bool B>
+struct FullTag {
+    static constexpr bool value = B;
+};
+
+template <int FMT>
+struct LdsSize {
+    static constexpr int dwords = (FMT == CB4 || FMT == CB8) ? 256 * kTableCopies
+                                  : (FMT == AQ2X8)          ? 2048
+                                                            : 1;
+};
+
+// Build the per-workgroup LDS table of a projection.
+template <int FMT>
+__device__ void build_table(uint32_t *lds, const Desc &D) {
+    const int t = threadIdx.x;
+    if constexpr (FMT == CB4 || FMT == CB8) {
+        // entry e, copy j at dword e*64 + j: lane slot j reads bank j for any entry.
+        for (int e = t; e < 256; e += kThreads) {
+            uint32_t v;
+            if constexpr (FMT == CB4) v = uint32_t(gld<uint16_t>(D.cbk + (e & 15))) | (uint32_t(gld<uint16_t>(D.cbk + (e >> 4))) << 16);
+            else v = uint32_t(gld<uint16_t>(D.cbk + e));
+            uint4 q = make_uint4(v, v, v, v);
+            for (int j = 0; j < kTableCopies / 4; j++) {
+                int jj = (j + e) % (kTableCopies / 4);
+                reinterpret_cast<uint4 *>(lds)[e * (kTableCopies / 4) + jj] = q;
+            }
+        }
+    } else if constexpr (FMT == AQ2X8) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(D.cbk);
+        for (int i = t; i < 512; i += kThreads) reinterpret_cast<uint4 *>(lds)[i] = ld16(src + i);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// One wave unit: rows 64g..64g+63 (one per lane) times chunks [cb, ce).
+// ------------------------------------------------------------------------------------------
+template <int FMT, int M>
+__device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const uint32_t *lds) {
+    const int g = wu / D.S;
+    const int s = wu - g * D.S;
+    const int cb = s * D.CS;
+    const int ce = min(D.C, cb + D.CS);
+    const int row = g * 64 + lane;
+    const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
+    const uint16_t *xrow[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) xrow[m] = D.x + (int64_t)m * D.ldx;
+
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) acc[m] = 0.f;
+
+    // Per-block activation sums for the block formats: lane l holds the sum of block b0 + l.
+    float bsum[M];
+    int b0 = 0;
+    constexpr int WPB = (FMT == Q4_0) ? 32 : 128;   // weights per scale block
+    if constexpr (FMT == Q4_0 || FMT == TQ2) {
+        b0 = (FMT == Q4_0) ? cb : cb / 2;
+        const int b1 = (FMT == Q4_0) ? ce : ce / 2;
+        const int blk = b0 + lane;
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            float sacc = 0.f;
+            if (blk < b1) {
+                const uint32_t *xp = reinterpret_cast<const uint32_t *>(xrow[m] + (int64_t)blk * WPB);
+                constexpr uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in fp16
+#pragma unroll 8
+                for (int i = 0; i < WPB / 2; i++) sacc = dot2(gld<uint32_t>(xp + i), ones, sacc);
+            }
+            bsum[m] = sacc;
+        }
+    }
+
+    const uint32_t loff = uint32_t(lane) * 4u;  // lane slot byte offset inside a table entry
+    // TQ2 per-block partial accumulators (weights scaled by 4^j * 2^-24)
+    float ta[M][5];
+
+    auto process = [&](auto full_tag, const uint4 &v, int c, uint2 sq) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (FMT == CB4) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                uint32_t e[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    uint32_t a = __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(i) << 8));
+                    e[i] = lds_word(lds, a);
+                }
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    uint32_t xs[4];
+                    load_x<FULL, 4>(xs, xrow[m], c * 32 + t * 8, D.K);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[m] = dot2(e[i], xs[i], acc[m]);
+                }
+            }
+        } else if constexpr (FMT == CB8) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                uint32_t pr[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    uint32_t a0 = __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(2 * i) << 8));
+                    uint32_t a1 = __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(2 * i + 1) << 8));
+                    uint32_t e0 = lds_word(lds, a0), e1 = lds_word(lds, a1);
+                    pr[i] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                }
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    uint32_t xs[2];
+                    load_x<FULL, 2>(xs, xrow[m], c * 16 + t * 4, D.K);
+                    acc[m] = dot2(pr[0], xs[0], acc[m]);
+                    acc[m] = dot2(pr[1], xs[1], acc[m]);
+                }
+            }
+        } else if constexpr (FMT == Q4_0) {
+            uint32_t q[4][4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                uint32_t w = w4[t], w8 = w4[t] >> 8;
+                q[t][0] = w & 0x000F000Fu;
+                q[t][1] = w & 0x00F000F0u;
+                q[t][2] = w8 & 0x000F000Fu;
+                q[t][3] = w8 & 0x00F000F0u;
+            }
+            const int bq = c & 3;
+            const uint32_t dbits = (bq < 2 ? sq.x : sq.y) >> ((bq & 1) * 16);
+            const float d = half_bits_to_float(dbits & 0xFFFFu);
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                uint32_t xs[16];
+                load_x<FULL, 16>(xs, xrow[m], c * 32, D.K);
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    a0 = dot2(q[t][0], xs[4 * t + 0], a0);
+                    a1 = dot2(q[t][1], xs[4 * t + 1], a1);
+                    a0 = dot2(q[t][2], xs[4 * t + 2], a0);
+                    a1 = dot2(q[t][3], xs[4 * t + 3], a1);
+                }
+                const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsum[m]), c - b0));
+                const float p = fmaf(a1, 0.0625f, a0);               // 2^-24 * sum code*x
+                const float blk = fmaf(p, 16777216.0f, -8.0f * sb);  // sum (code-8)*x
+                acc[m] = fmaf(d, blk, acc[m]);
+            }
+        } else if constexpr (FMT == TQ2) {
+            const bool first = (c & 1) == 0;
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                if (first) {
+#pragma unroll
+                    for (int j = 0; j < 5; j++) ta[m][j] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t w = w4[t], w10 = w4[t] >> 10;
+                uint32_t q[8];
+                q[0] = w & 0x00030003u;
+                q[1] = w & 0x000C000Cu;
+                q[2] = w & 0x00300030u;
+                q[3] = w & 0x00C000C0u;
+                q[4] = w & 0x03000300u;
+                q[5] = w10 & 0x00030003u;
+                q[6] = w10 & 0x000C000Cu;
+                q[7] = w10 & 0x00300030u;
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    uint32_t xs[8];
+                    load_x<FULL, 8>(xs, xrow[m], c * 64 + t * 16, D.K);
+                    ta[m][0] = dot2(q[0], xs[0], ta[m][0]);
+                    ta[m][1] = dot2(q[1], xs[1], ta[m][1]);
+                    ta[m][2] = dot2(q[2], xs[2], ta[m][2]);
+                    ta[m][3] = dot2(q[3], xs[3], ta[m][3]);
+                    ta[m][4] = dot2(q[4], xs[4], ta[m][4]);
+                    ta[m][0] = dot2(q[5], xs[5], ta[m][0]);
+                    ta[m][1] = dot2(q[6], xs[6], ta[m][1]);
+                    ta[m][2] = dot2(q[7], xs[7], ta[m][2]);
+                }
+            }
+            if (!first) {
+                const int b = c >> 1;
+                const int bq = b & 3;
+                const uint32_t dbits = (bq < 2 ? sq.x : sq.y) >> ((bq & 1) * 16);
+                const float d = half_bits_to_float(dbits & 0xFFFFu);
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    float p = fmaf(ta[m][4], 0.00390625f, ta[m][3] * 0.015625f);
+                    p = fmaf(ta[m][2], 0.0625f, p);
+                    p = fmaf(ta[m][1], 0.25f, p);
+                    p += ta[m][0];                                   // 2^-24 * sum code*x
+                    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsum[m]), b - b0));
+                    const float blk = fmaf(p, 16777216.0f, -sb);     // sum (code-1)*x
+                    acc[m] = fmaf(d, blk, acc[m]);
+                }
+            }
+        } else if constexpr (FMT == AQ2X8) {
+            const uint4 *cbv = reinterpret_cast<const uint4 *>(lds);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t c0 = (w4[t] >> (16 * h)) & 0xFFu;
+                    const uint32_t c1 = (w4[t] >> (16 * h + 8)) & 0xFFu;
+                    const uint4 A = cbv[c0], B = cbv[256 + c1];
+                    uint32_t wv[4];
+                    const uint32_t a4[4] = {A.x, A.y, A.z, A.w}, b4[4] = {B.x, B.y, B.z, B.w};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        h2 sum = as_h2(a4[i]) + as_h2(b4[i]);
+                        wv[i] = __builtin_bit_cast(uint32_t, sum);
+                    }
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        uint32_t xs[4];
+                        load_x<FULL, 4>(xs, xrow[m], c * 64 + (2 * t + h) * 8, D.K);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[m] = dot2(wv[i], xs[i], acc[m]);
+                    }
+                }
+            }
+        }
+    };
+
+    // Scale quad of the chunk group starting at c (block formats only).
+    auto load_sq = [&](int c) -> uint2 {
+        if constexpr (FMT == Q4_0 || FMT == TQ2) {
+            const int q = (FMT == Q4_0) ? (c >> 2) : (c >> 3);
+            return ld8(D.scales + (((int64_t)g * D.Q + q) * 64 + lane) * 8);
+        } else {
+            return make_uint2(0, 0);
+        }
+    };
+    auto load_group = [&](uint4 (&buf)[kU], int c) {
+#pragma unroll
+        for (int j = 0; j < kU; j++) {
+            const int cc = min(c + j, ce - 1);
+            buf[j] = ld16(cptr + (int64_t)cc * 1024);
+        }
+    };
+    auto proc_group = [&](const uint4 (&buf)[kU], int c, uint2 sq) {
+#pragma unroll
+        for (int j = 0; j < kU; j++) {
+            if (c + j < ce) {
+                if constexpr (FMT == Q4_0 || FMT == TQ2) {
+                    process(FullTag<true>{}, buf[j], c + j, sq);  // K is a whole number of chunks
+                } else {
+                    if (c + j < D.C_full) process(FullTag<true>{}, buf[j], c + j, sq);
+                    else process(FullTag<false>{}, buf[j], c + j, sq);
+                }
+            }
+        }
+    };
+
+    uint4 A[kU], B[kU];
+    uint2 sqA = load_sq(cb), sqB = make_uint2(0, 0);
+    load_group(A, cb);
+    for (int c = cb; c < ce; c += 2 * kU) {
+        if (c + kU < ce) {
+            load_group(B, c + kU);
+            sqB = load_sq(c + kU);
+        }
+        proc_group(A, c, sqA);
+        if (c + kU >= ce) break;
+        if (c + 2 * kU < ce) {
+            load_group(A, c + 2 * kU);
+            sqA = load_sq(c + 2 * kU);
+        }
+        proc_group(B, c + kU, sqB);
+    }
+
+    if constexpr (FMT == AQ2X8) {
+        const float sr = half_bits_to_float(gld<uint16_t>(D.scales + 2 * (int64_t)row));
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[m] *= sr;
+    }
+    if (D.S == 1) {
+        if (row < D.N) {
+#pragma unroll
+            for (int m = 0; m < M; m++) gst(D.y + (int64_t)m * D.ldy + row, acc[m]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; m++) gst(D.part + ((int64_t)m * D.S + s) * D.Npad + row, acc[m]);
+    }
+}
+
+template <int FMT, int M>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
+    __shared__ uint32_t lds[LdsSize<FMT>::dwords];
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int total = P.total_wgu;
+    const int per = total / (int)gridDim.x, rem = total % (int)gridDim.x;
+    const int b = blockIdx.x;
+    const int u0 = b * per + min(b, rem);
+    const int u1 = u0 + per + (b < rem ? 1 : 0);
+    int cur = -1;
+    Desc D = P.d0;
+    for (int u = u0; u < u1; u++) {
+        int p = 0;
+        if (P.descs) {
+            // last descriptor whose first workgroup-unit is <= u (uniform binary search)
+            int lo = 0, hi = P.ndesc - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (load_wgu_begin(P.descs + mid) <= u) lo = mid; else hi = mid - 1;
+            }
+            p = lo;
+        }
+        if (p != cur) {
+            if (P.descs) D = load_desc(P.descs + p);
+            if constexpr (LdsSize<FMT>::dwords > 1) {
+                __syncthreads();
+                build_table<FMT>(lds, D);
+                __syncthreads();
+            }
+            cur = p;
+        }
+        const int wu = (u - D.wgu_begin) * kWaves + wid;
+        if (wu < D.wu_count) run_unit<FMT, M>(D, wu, lane, lds);
+    }
+}
+
+
+template <int FMT>
+GemvFn gemv_fn(int M) {
+    switch (M) {
+    case 1: return gemv_kernel<FMT, 1>;
+    case 2: return gemv_kernel<FMT, 2>;
+    case 3: return gemv_kernel<FMT, 3>;
+    case 4: return gemv_kernel<FMT, 4>;
+    case 5: return gemv_kernel<FMT, 5>;
+    case 6: return gemv_kernel<FMT, 6>;
+    case 7: return gemv_kernel<FMT, 7>;
+    case 8: return gemv_kernel<FMT, 8>;
+    }
+    return nullptr;
+}
+
+}  // namespace wqd

@@ -1,0 +1,6 @@
+// Q4_0 instances of the dequantize-and-multiply kernel (see gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace wqd {
+GemvFn gemv_fn_q4_0(int M) { return gemv_fn<Q4_0>(M); }
+}  // namespace wqd

@@ -1,0 +1,6 @@
+// TQ2 instances of the dequantize-and-multiply kernel (see gemv_impl.h).
+#include "gemv_impl.h"
+
+namespace wqd {
+GemvFn gemv_fn_tq2(int M) { return gemv_fn<TQ2>(M); }
+}  // namespace wqd

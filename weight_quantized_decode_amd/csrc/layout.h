@@ -1,0 +1,115 @@
+// Prepared (device) layout of the packed weights, shared by the host re-layout code and the
+// kernels of libwqd.
+//
+// Rows are grouped in tiles of 64 (one wavefront lane per row).  Each row's code bytes are cut
+// into 16-byte chunks; the code plane stores, for row group g, chunk c and lane r, the 16 bytes
+// of row 64g+r at ((g*C + c)*64 + r)*16.  One wavefront load instruction therefore reads 1 KiB
+// of contiguous memory: chunk c of 64 consecutive rows.  This is the "re-lay the misaligned
+// blocks into planes at load time" step of the ternary vLLM page ("Anatomy of a PQ2_0 block",
+// prepared weights: a code plane, then a scale plane, rows 16-byte aligned), applied to all five
+// formats.  Within a chunk the codes are permuted so that the decoder can extract two weights
+// with one AND (see the per-format notes below).  Byte counts per weight are unchanged; only
+// the zero padding of the last row group (N up to a multiple of 64) and of a last partial chunk
+// is added.
+//
+// Planes, each starting at a 256-byte aligned offset from the weight base pointer:
+//   codes   : RG*C*64*16 bytes
+//   scales  : Q4_0 / TQ2: per row group g, per quad q of blocks, per lane r: 4 fp16 scales of
+//             blocks 4q..4q+3 (8 bytes), at ((g*Q + q)*64 + r)*8.  AQ2X8: s[Npad] fp16.
+//   codebook: CB4 16 fp16, CB8 256 fp16, AQ2X8 C[2][256][8] fp16.
+//
+// Intra-chunk code order (w = one 32-bit word of the chunk, t = its index 0..3):
+//   Q4_0  chunk = one block of 32 weights.  Word t holds weights 8t..8t+7; weight 8t+i sits in
+//         nibble p = i/2 + 4*(i%2), so masks 0x000F000F / 0x00F000F0 of w and of w>>8 each give a
+//         pair of consecutive weights (the second mask scaled by 16).
+//   TQ2   chunk = half a block, 64 weights.  Word t holds weights 16t..16t+15; weight 16t+i sits in
+//         the 2-bit field p = i/2 + 8*(i%2), so masks (0x00030003 << 2j) of w (j < 5) and of
+//         w>>10 (j < 3) each give a pair of consecutive weights scaled by 4^j.
+//   CB4   chunk = 32 weights in canonical order: byte b holds weights 2b (low) and 2b+1 (high).
+//   CB8   chunk = 16 weights, byte b = weight b.
+//   AQ2X8 chunk = 8 groups: bytes (c0, c1) of group 8c+0, then group 8c+1, ...
+#pragma once
+#include <stdint.h>
+
+namespace wqd {
+
+constexpr int kRowsPerGroup = 64;
+constexpr int kChunkBytes = 16;
+constexpr int64_t kPlaneAlign = 256;
+
+enum Fmt : int { Q4_0 = 1, CB4 = 2, CB8 = 3, TQ2 = 4, AQ2X8 = 5 };
+
+struct Layout {
+    int fmt = 0;
+    int64_t N = 0, K = 0;
+    int64_t RG = 0;           // row groups (ceil(N / 64))
+    int64_t Npad = 0;         // RG * 64
+    int64_t row_code_bytes = 0;
+    int64_t C = 0;            // 16-byte chunks per row
+    int64_t C_full = 0;       // chunks entirely inside K (the rest is a partial tail chunk)
+    int64_t weights_per_chunk = 0;
+    int64_t blocks = 0;       // scale blocks per row (Q4_0, TQ2)
+    int64_t Q = 0;            // quads of blocks per row (Q4_0, TQ2)
+    int64_t off_scales = 0, off_cbk = 0, total = 0;
+    bool ok = false;
+};
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+inline int k_multiple(int fmt) {
+    switch (fmt) {
+    case Q4_0: return 32;
+    case CB4: return 2;
+    case CB8: return 1;
+    case TQ2: return 128;
+    case AQ2X8: return 8;
+    default: return 0;
+    }
+}
+
+inline Layout make_layout(int fmt, int64_t N, int64_t K) {
+    Layout L;
+    L.fmt = fmt;
+    L.N = N;
+    L.K = K;
+    int km = k_multiple(fmt);
+    if (km == 0 || N < 1 || K < 1 || K % km != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
+        return L;
+    L.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
+    L.Npad = L.RG * kRowsPerGroup;
+    switch (fmt) {
+    case Q4_0: L.row_code_bytes = K / 2; L.weights_per_chunk = 32; L.blocks = K / 32; break;
+    case CB4: L.row_code_bytes = K / 2; L.weights_per_chunk = 32; break;
+    case CB8: L.row_code_bytes = K; L.weights_per_chunk = 16; break;
+    case TQ2: L.row_code_bytes = K / 4; L.weights_per_chunk = 64; L.blocks = K / 128; break;
+    case AQ2X8: L.row_code_bytes = K / 4; L.weights_per_chunk = 64; break;
+    }
+    L.C = (L.row_code_bytes + kChunkBytes - 1) / kChunkBytes;
+    L.C_full = K / L.weights_per_chunk;
+    L.Q = (L.blocks + 3) / 4;
+    int64_t codes = L.RG * L.C * kRowsPerGroup * kChunkBytes;
+    int64_t scales = 0, cbk = 0;
+    if (fmt == Q4_0 || fmt == TQ2) scales = L.RG * L.Q * kRowsPerGroup * 8;
+    if (fmt == AQ2X8) scales = L.Npad * 2;
+    if (fmt == CB4) cbk = 32;
+    if (fmt == CB8) cbk = 512;
+    if (fmt == AQ2X8) cbk = 8192;
+    L.off_scales = align_up(codes, kPlaneAlign);
+    L.off_cbk = align_up(L.off_scales + scales, kPlaneAlign);
+    L.total = align_up(L.off_cbk + cbk, kPlaneAlign);
+    L.ok = true;
+    return L;
+}
+
+inline int64_t canonical_bytes(int fmt, int64_t N, int64_t K) {
+    switch (fmt) {
+    case Q4_0: return N * (K / 32) * 18;
+    case CB4: return 32 + N * (K / 2);
+    case CB8: return 512 + N * K;
+    case TQ2: return N * (K / 128) * 34;
+    case AQ2X8: return 8192 + 2 * N + N * (K / 8) * 2;
+    default: return -1;
+    }
+}
+
+}  // namespace wqd
