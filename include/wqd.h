@@ -135,6 +135,18 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M
 WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
+/* Profiling variant: the same work as wqd_run_projections in WQD_PERSISTENT mode, with hipEvent_t
+ * events[2i] recorded on the stream just before the i-th kernel launch of the call and
+ * events[2i+1] just after it.  Launch order: one dequantize-and-multiply launch per format present
+ * (ascending format id), then one split-K reduction launch if any projection is split.
+ * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
+WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
+                                      int32_t mode, void *workspace, int64_t workspace_bytes,
+                                      void *stream, void *const *events, int32_t n_events);
+
+/* Number of kernel launches one WQD_PERSISTENT call issues for this list (or a negative status). */
+WQD_API int wqd_stack_launches(const wqd_proj *projs_host, int32_t count, int64_t M);
+
 /* ---------------------------------------------------------------- errors */
 
 /* Synchronize `stream` and map any pending asynchronous error to WQD_EHIP. */

@@ -23,7 +23,8 @@ WQD_MAX_M = 8
 EXPORTED = [
     "wqd_canonical_bytes", "wqd_prepared_bytes", "wqd_prepare_host", "wqd_gemm_workspace_bytes",
     "wqd_gemm", "wqd_dequant_f32", "wqd_stack_workspace_bytes", "wqd_stack_setup",
-    "wqd_run_projections", "wqd_stream_check", "wqd_last_hip_error", "wqd_status_str",
+    "wqd_run_projections", "wqd_run_projections_timed", "wqd_stack_launches", "wqd_stream_check",
+    "wqd_last_hip_error", "wqd_status_str",
 ]
 
 
@@ -63,6 +64,9 @@ def lib() -> ctypes.CDLL:
             "wqd_stack_workspace_bytes": (i64, [ctypes.POINTER(wqd_proj), i32, i64]),
             "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, vp, i64, vp]),
             "wqd_run_projections": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
+            "wqd_run_projections_timed": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp,
+                                                         ctypes.POINTER(ctypes.c_void_p), i32]),
+            "wqd_stack_launches": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64]),
             "wqd_stream_check": (ctypes.c_int, [vp]),
             "wqd_last_hip_error": (ctypes.c_int, []),
             "wqd_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -164,6 +168,18 @@ def wqd_run_projections(arr, M: int, mode: int, workspace, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("wqd_run_projections", lib().wqd_run_projections(arr, len(arr), M, mode, _dptr(workspace), ws_bytes,
                                                             _stream(stream)))
+
+
+def wqd_stack_launches(arr, M: int) -> int:
+    return _check("wqd_stack_launches", lib().wqd_stack_launches(arr, len(arr), M))
+
+
+def wqd_run_projections_timed(arr, M: int, mode: int, workspace, events, stream=None) -> None:
+    """events: sequence of raw hipEvent_t handles (ints), 2 per kernel launch."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ev = (ctypes.c_void_p * len(events))(*events)
+    _check("wqd_run_projections_timed", lib().wqd_run_projections_timed(
+        arr, len(arr), M, mode, _dptr(workspace), ws_bytes, _stream(stream), ev, len(events)))
 
 
 def wqd_stream_check(stream=None) -> None:

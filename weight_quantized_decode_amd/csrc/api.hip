@@ -15,20 +15,29 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// y[m][n] = sum_s part[m][s][n], s ascending.
+// y[m][n] = sum_s part[m][s][n], s ascending.  Every projection's (m, n) range starts at a
+// multiple of 256 in the flattened index space, so one workgroup never straddles two
+// projections and its descriptor is found with scalar loads.
 __global__ __launch_bounds__(256) void reduce_kernel(RedParams P) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= P.total) return;
+    const int64_t base = (int64_t)blockIdx.x * 256;
     RedDesc D = P.d0;
     if (P.descs) {
+        typedef const int64_t __attribute__((address_space(4))) *ci64p;
         int lo = 0, hi = P.ndesc - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (P.descs[mid].begin <= i) lo = mid; else hi = mid - 1;
+            const int64_t b = ((ci64p)(uintptr_t)&P.descs[mid].begin)[0];
+            if (b <= base) lo = mid; else hi = mid - 1;
         }
-        D = P.descs[lo];
+        typedef const uint32_t __attribute__((address_space(4))) *cu32;
+        uint32_t w[sizeof(RedDesc) / 4];
+        cu32 src = (cu32)(uintptr_t)(P.descs + lo);
+#pragma unroll
+        for (unsigned k = 0; k < sizeof(RedDesc) / 4; k++) w[k] = src[k];
+        __builtin_memcpy(&D, w, sizeof(RedDesc));
     }
-    const int64_t j = i - D.begin;
+    const int64_t j = base + threadIdx.x - D.begin;
+    if (j >= (int64_t)D.M * D.N) return;
     const int m = (int)(j / D.N);
     const int n = (int)(j - (int64_t)m * D.N);
     const float *p = D.part + (int64_t)m * D.S * D.Npad + n;
@@ -121,19 +130,19 @@ static int device_cus() {
     return cached_cus;
 }
 
-static bool has_table(int fmt) { return fmt == CB4 || fmt == CB8 || fmt == AQ2X8; }
-
-// Chunks per split for a single projection: enough wave units to cover the GPU.
-static int64_t choose_cs(const Layout &L, int64_t target_units, int64_t min_cs) {
-    int64_t splits = target_units / L.RG;
-    if (splits < 1) splits = 1;
+// Chunks per K-slice.  `splits_wanted` slices per row are asked for (at least min_cs chunks
+// each); the slices are then made as equal as the format's alignment allows.
+static int64_t choose_cs(const Layout &L, int64_t splits_wanted, int64_t min_cs) {
+    int64_t mult = (L.fmt == TQ2) ? 8 : (L.fmt == Q4_0) ? 4 : 1;
+    int64_t cap = (L.fmt == Q4_0) ? 64 : (L.fmt == TQ2) ? 128 : (int64_t(1) << 30);
+    int64_t splits = splits_wanted < 1 ? 1 : splits_wanted;
     int64_t cs = (L.C + splits - 1) / splits;
     if (cs < min_cs) cs = min_cs;
-    int64_t mult = (L.fmt == TQ2) ? 8 : 4;
-    cs = align_up(cs, mult);
-    int64_t cap = (L.fmt == Q4_0) ? 64 : (L.fmt == TQ2) ? 128 : (int64_t(1) << 30);
     if (cs > cap) cs = cap;
-    if (cs >= L.C) cs = L.C;  // one split: the whole row
+    if (cs >= L.C) return L.C;  // one slice: the whole row
+    const int64_t S = (L.C + cs - 1) / cs;
+    cs = align_up((L.C + S - 1) / S, mult);  // equalize the slices
+    if (cs > cap) cs = cap;
     return cs;
 }
 
@@ -143,24 +152,30 @@ struct Plan {
     int64_t part_bytes = 0;  // M * S * Npad * 4 when S > 1
 };
 
-static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
-    Plan P;
-    P.L = make_layout(fmt, N, K);
-    if (!P.L.ok) return P;
-    P.CS = choose_cs(P.L, int64_t(cus) * 16, 8);
+static Plan finish_plan(Plan P, int64_t M) {
     P.S = (P.L.C + P.CS - 1) / P.CS;
     P.part_bytes = (P.S > 1) ? M * P.S * P.L.Npad * 4 : 0;
     return P;
 }
 
+// One projection alone: split K until the wave units cover the GPU about 4 times.
+static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
+    Plan P;
+    P.L = make_layout(fmt, N, K);
+    if (!P.L.ok) return P;
+    P.CS = choose_cs(P.L, int64_t(cus) * 16 / P.L.RG, 8);
+    return finish_plan(P, M);
+}
+
+// A projection inside a persistent stack launch: K-slices of about WQD_STACK_MIN_CS chunks.
 static Plan plan_stack(int fmt, int64_t N, int64_t K, int64_t M) {
     Plan P;
     P.L = make_layout(fmt, N, K);
     if (!P.L.ok) return P;
-    P.CS = choose_cs(P.L, 1, 32);  // about 32 KiB of codes per wave unit
-    P.S = (P.L.C + P.CS - 1) / P.CS;
-    P.part_bytes = (P.S > 1) ? M * P.S * P.L.Npad * 4 : 0;
-    return P;
+    int64_t target = WQD_STACK_MIN_CS;
+    int64_t splits = (P.L.C + target / 2) / target;
+    P.CS = choose_cs(P.L, splits, 1);
+    return finish_plan(P, M);
 }
 
 static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
@@ -187,31 +202,46 @@ static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, 
     D.Npad = int32_t(P.L.Npad);
     D.wu_count = int32_t(P.L.RG * P.S);
     D.wgu_begin = 0;
+    D.fmt = P.L.fmt;
     return D;
 }
 
-static GemvFn pick_gemv(int fmt, int M) {
-    switch (fmt) {
-    case Q4_0: return gemv_fn_q4_0(M);
-    case CB4: return gemv_fn_cb4(M);
-    case CB8: return gemv_fn_cb8(M);
-    case TQ2: return gemv_fn_tq2(M);
-    case AQ2X8: return gemv_fn_aq2x8(M);
+static GemvFn pick_gemv(int mask, int M) {
+    switch (mask) {
+    case 1 << Q4_0: return gemv_fn_q4_0(M);
+    case 1 << CB4: return gemv_fn_cb4(M);
+    case 1 << CB8: return gemv_fn_cb8(M);
+    case 1 << TQ2: return gemv_fn_tq2(M);
+    case 1 << AQ2X8: return gemv_fn_aq2x8(M);
+    case kMaskCB48: return gemv_fn_cb48(M);
     }
     return nullptr;
 }
 
-static int grid_for(int fmt, int64_t total_wgu, int cus) {
-    int64_t per_cu = has_table(fmt) ? (fmt == AQ2X8 ? 4 : 2) : 4;
-    int64_t g = int64_t(cus) * per_cu;
-    if (g > total_wgu) g = total_wgu;
-    return int(g < 1 ? 1 : g);
+// Resident workgroups per CU of a kernel (queried once per kernel and device).  The persistent
+// grid never exceeds what is resident at once, so every workgroup starts immediately.
+static int resident_per_cu(GemvFn fn) {
+    struct Entry { GemvFn fn; int dev; int n; };
+    static thread_local std::vector<Entry> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    for (const Entry &e : cache)
+        if (e.fn == fn && e.dev == dev) return e.n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(fn), kThreads, 0) !=
+            hipSuccess || n < 1)
+        n = 1;
+    cache.push_back({fn, dev, n});
+    return n;
 }
 
-static int launch_gemv(int fmt, int M, const GemvParams &GP, int grid, hipStream_t st) {
-    GemvFn fn = pick_gemv(fmt, M);
+static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus) {
+    GemvFn fn = pick_gemv(mask, M);
     if (!fn) return WQD_EINVAL;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, st, GP);
+    int64_t grid = int64_t(cus) * resident_per_cu(fn);
+    if (grid > GP.total_wgu) grid = GP.total_wgu;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(fn, dim3(unsigned(grid)), dim3(kThreads), 0, st, GP);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
@@ -247,7 +277,7 @@ static int gemm_one(int fmt, int64_t N, int64_t K, const void *w, const void *x,
     GP.descs = nullptr;
     GP.ndesc = 1;
     GP.total_wgu = int32_t((GP.d0.wu_count + kWaves - 1) / kWaves);
-    int rc = launch_gemv(fmt, int(M), GP, grid_for(fmt, GP.total_wgu, cus), st);
+    int rc = launch_gemv(fmt_bit(fmt), int(M), GP, st, cus);
     if (rc != WQD_OK || P.S == 1) return rc;
     RedParams RP;
     memset(&RP, 0, sizeof(RP));
@@ -265,11 +295,19 @@ static int gemm_one(int fmt, int64_t N, int64_t K, const void *w, const void *x,
     return launch_reduce(RP, st);
 }
 
-// Stack workspace: [Desc table][RedDesc table][partials...], each 256-byte aligned.
+// Stack workspace: [Desc table][RedDesc table][partials...], each 256-byte aligned.  The
+// projections are grouped into launches: all CB4/CB8 projections together when both appear,
+// otherwise one launch per format; within a launch, descriptors are in format order.
+struct LaunchGroup {
+    int mask = 0;
+    int first = 0, count = 0;  // range in StackPlan::descs
+    int total_wgu = 0;
+};
+
 struct StackPlan {
-    std::vector<Desc> descs;       // grouped by format, in format order
-    std::vector<int> fmt_begin;    // index into descs of each format group (size 6)
-    std::vector<int> wgu_total;    // per format
+    int64_t off_ctr = 0;           // 2 ints per launch group (dynamic-tail counters)
+    std::vector<Desc> descs;
+    std::vector<LaunchGroup> groups;
     std::vector<RedDesc> reds;
     int64_t red_total = 0;
     int64_t off_descs = 0, off_reds = 0, off_part = 0, total = 0;
@@ -278,51 +316,65 @@ struct StackPlan {
 
 static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *ws, StackPlan &SP, int cus) {
     if (!p || count < 1) return WQD_EINVAL;
+    int present = 0;
     for (int i = 0; i < count; i++) {
         if (p[i].reserved != 0) return WQD_EINVAL;
         int rc = check_proj(p[i].fmt, p[i].N, p[i].K, p[i].w, p[i].x, M, p[i].ldx, p[i].y, p[i].ldy);
         if (rc != WQD_OK) return rc;
+        present |= fmt_bit(p[i].fmt);
     }
+    std::vector<int> masks;
+    if ((present & kMaskCB48) == kMaskCB48) {
+        masks.push_back(kMaskCB48);
+        present &= ~kMaskCB48;
+    }
+    for (int fmt = 1; fmt <= 5; fmt++)
+        if (present & fmt_bit(fmt)) masks.push_back(fmt_bit(fmt));
     SP.off_descs = 0;
-    SP.off_reds = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_ctr = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_reds = SP.off_ctr + 256;
     SP.off_part = SP.off_reds + align_up(int64_t(sizeof(RedDesc)) * count, 256);
     int64_t part_off = SP.off_part;
     uint8_t *base = static_cast<uint8_t *>(ws);
-    SP.fmt_begin.assign(7, 0);
-    SP.wgu_total.assign(7, 0);
-    for (int fmt = 1; fmt <= 5; fmt++) {
-        SP.fmt_begin[fmt] = int(SP.descs.size());
+    for (int mask : masks) {
+        LaunchGroup G;
+        G.mask = mask;
+        G.first = int(SP.descs.size());
         int wgu = 0;
-        for (int i = 0; i < count; i++) {
-            if (p[i].fmt != fmt) continue;
-            Plan P = plan_stack(fmt, p[i].N, p[i].K, M);
-            float *part = nullptr;
-            if (P.part_bytes > 0) {
-                part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
-                RedDesc R;
-                memset(&R, 0, sizeof(R));
-                R.part = part;
-                R.y = p[i].y;
-                R.ldy = p[i].ldy;
-                R.N = int32_t(p[i].N);
-                R.Npad = int32_t(P.L.Npad);
-                R.S = int32_t(P.S);
-                R.M = int32_t(M);
-                R.begin = SP.red_total;
-                SP.red_total += M * p[i].N;
-                SP.reds.push_back(R);
-                part_off += align_up(P.part_bytes, 256);
+        for (int fmt = 1; fmt <= 5; fmt++) {
+            if (!(mask & fmt_bit(fmt))) continue;
+            for (int i = 0; i < count; i++) {
+                if (p[i].fmt != fmt) continue;
+                Plan P = plan_stack(fmt, p[i].N, p[i].K, M);
+                float *part = nullptr;
+                if (P.part_bytes > 0) {
+                    part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
+                    RedDesc R;
+                    memset(&R, 0, sizeof(R));
+                    R.part = part;
+                    R.y = p[i].y;
+                    R.ldy = p[i].ldy;
+                    R.N = int32_t(p[i].N);
+                    R.Npad = int32_t(P.L.Npad);
+                    R.S = int32_t(P.S);
+                    R.M = int32_t(M);
+                    R.begin = SP.red_total;
+                    SP.red_total += align_up(M * p[i].N, 256);
+                    SP.reds.push_back(R);
+                    part_off += align_up(P.part_bytes, 256);
+                }
+                Desc D = make_desc(P, p[i].w, p[i].x, p[i].ldx, p[i].y, p[i].ldy, part);
+                D.wgu_begin = wgu;
+                wgu += (D.wu_count + kWaves - 1) / kWaves;
+                SP.descs.push_back(D);
+                Plan Q = plan_single(p[i].fmt, p[i].N, p[i].K, M, cus);
+                if (Q.part_bytes > SP.max_single_part) SP.max_single_part = Q.part_bytes;
             }
-            Desc D = make_desc(P, p[i].w, p[i].x, p[i].ldx, p[i].y, p[i].ldy, part);
-            D.wgu_begin = wgu;
-            wgu += (D.wu_count + kWaves - 1) / kWaves;
-            SP.descs.push_back(D);
-            Plan Q = plan_single(p[i].fmt, p[i].N, p[i].K, M, cus);
-            if (Q.part_bytes > SP.max_single_part) SP.max_single_part = Q.part_bytes;
         }
-        SP.wgu_total[fmt] = wgu;
+        G.count = int(SP.descs.size()) - G.first;
+        G.total_wgu = wgu;
+        SP.groups.push_back(G);
     }
-    SP.fmt_begin[6] = int(SP.descs.size());
     SP.total = part_off;
     if (SP.max_single_part > SP.total) SP.total = SP.max_single_part;
     return WQD_OK;
@@ -393,18 +445,22 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, voi
     if (e == hipSuccess && !SP.reds.empty())
         e = hipMemcpyAsync(base + SP.off_reds, SP.reds.data(), sizeof(RedDesc) * SP.reds.size(),
                            hipMemcpyHostToDevice, st);
+    static const int zeros[64] = {0};  // dynamic-tail counters start at 0 (each launch resets them)
+    if (e == hipSuccess) e = hipMemcpyAsync(base + SP.off_ctr, zeros, sizeof(zeros), hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
 
-WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
-                                void *workspace, int64_t workspace_bytes, void *stream) {
+static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
+                                void *workspace, int64_t workspace_bytes, hipStream_t st,
+                                void *const *events, int32_t n_events) {
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT) return WQD_EINVAL;
+    if (n_events < 0 || (n_events > 0 && !events)) return WQD_EINVAL;
     const int cus = device_cus();
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (mode == WQD_ORDERED) {
         if (!projs || count < 1) return WQD_EINVAL;
+        if (n_events != 0) return WQD_EINVAL;
         for (int i = 0; i < count; i++) {
             const wqd_proj &q = projs[i];
             if (q.reserved != 0) return WQD_EINVAL;
@@ -420,19 +476,32 @@ WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M,
     int rc = build_stack_plan(projs, count, M, workspace, SP, cus);
     if (rc != WQD_OK) return rc;
     if (workspace_bytes < SP.total) return WQD_ESPACE;
+    const int launches = int(SP.groups.size()) + (SP.reds.empty() ? 0 : 1);
+    if (n_events != 0 && n_events != 2 * launches) return WQD_ESPACE;
+    int li = 0;
+    auto mark = [&](int which) -> int {
+        if (n_events == 0) return WQD_OK;
+        hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * li + which]), st);
+        return e == hipSuccess ? WQD_OK : hip_fail(e);
+    };
     const uint8_t *base = static_cast<const uint8_t *>(workspace);
     const Desc *dtab = reinterpret_cast<const Desc *>(base + SP.off_descs);
-    for (int fmt = 1; fmt <= 5; fmt++) {
-        const int nd = SP.fmt_begin[fmt + 1] - SP.fmt_begin[fmt];
-        if (nd == 0) continue;
+    for (const LaunchGroup &G : SP.groups) {
         GemvParams GP;
         memset(&GP, 0, sizeof(GP));
-        GP.d0 = SP.descs[SP.fmt_begin[fmt]];
-        GP.descs = dtab + SP.fmt_begin[fmt];
-        GP.ndesc = nd;
-        GP.total_wgu = SP.wgu_total[fmt];
-        rc = launch_gemv(fmt, int(M), GP, grid_for(fmt, GP.total_wgu, cus), st);
+        GP.d0 = SP.descs[G.first];
+        GP.descs = dtab + G.first;
+        GP.ndesc = G.count;
+        GP.total_wgu = G.total_wgu;
+        if (WQD_POOL_PERCENT > 0) {
+            GP.ctr = reinterpret_cast<int *>(const_cast<uint8_t *>(base) + SP.off_ctr) + 2 * (&G - SP.groups.data());
+            GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
+        }
+        if ((rc = mark(0)) != WQD_OK) return rc;
+        rc = launch_gemv(G.mask, int(M), GP, st, cus);
         if (rc != WQD_OK) return rc;
+        if ((rc = mark(1)) != WQD_OK) return rc;
+        li++;
     }
     if (!SP.reds.empty()) {
         RedParams RP;
@@ -441,9 +510,34 @@ WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M,
         RP.descs = reinterpret_cast<const RedDesc *>(base + SP.off_reds);
         RP.ndesc = int32_t(SP.reds.size());
         RP.total = SP.red_total;
+        if ((rc = mark(0)) != WQD_OK) return rc;
         rc = launch_reduce(RP, st);
+        if (rc != WQD_OK) return rc;
+        if ((rc = mark(1)) != WQD_OK) return rc;
+        li++;
     }
     return rc;
+}
+
+WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
+                                void *workspace, int64_t workspace_bytes, void *stream) {
+    return run_projections_impl(projs, count, M, mode, workspace, workspace_bytes,
+                                static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+WQD_API int wqd_stack_launches(const wqd_proj *projs, int32_t count, int64_t M) {
+    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+    StackPlan SP;
+    int rc = build_stack_plan(projs, count, M, nullptr, SP, device_cus());
+    if (rc != WQD_OK) return rc;
+    return int(SP.groups.size()) + (SP.reds.empty() ? 0 : 1);
+}
+
+WQD_API int wqd_run_projections_timed(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
+                                      void *workspace, int64_t workspace_bytes, void *stream,
+                                      void *const *events, int32_t n_events) {
+    return run_projections_impl(projs, count, M, mode, workspace, workspace_bytes,
+                                static_cast<hipStream_t>(stream), events, n_events);
 }
 
 WQD_API int wqd_stream_check(void *stream) {

@@ -10,10 +10,34 @@ namespace wqd {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-loadable pointer
 
-constexpr int kWaves = 4;                 // waves per workgroup
+#ifndef WQD_WAVES
+#define WQD_WAVES 8
+#endif
+#ifndef WQD_U
+#define WQD_U 4
+#endif
+#ifndef WQD_TABLE_COPIES
+#define WQD_TABLE_COPIES 64
+#endif
+#ifndef WQD_STACK_MIN_CS
+#define WQD_STACK_MIN_CS 32
+#endif
+#ifndef WQD_STACK_UNITS
+#define WQD_STACK_UNITS 1
+#endif
+#ifndef WQD_NT_CODES
+#define WQD_NT_CODES 1
+#endif
+#ifndef WQD_POOL_PERCENT
+#define WQD_POOL_PERCENT 0
+#endif
+#ifndef WQD_WG_PER_CU
+#define WQD_WG_PER_CU 2
+#endif
+constexpr int kWaves = WQD_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int kU = 4;                     // chunks per load group (double buffered)
-constexpr int kTableCopies = 64;          // LDS table copies (one per lane slot)
+constexpr int kU = WQD_U;                 // chunks per load group (double buffered)
+constexpr int kTableCopies = WQD_TABLE_COPIES;  // LDS table copies (one per lane slot)
 
 struct Desc {
     const uint8_t *codes;
@@ -26,7 +50,7 @@ struct Desc {
     int32_t N, K, C, C_full, S, CS, Q, RG, Npad;
     int32_t wgu_begin;  // first workgroup-unit of this projection
     int32_t wu_count;   // wave units = RG * S
-    int32_t pad_;
+    int32_t fmt;        // wqd format id of this projection
 };
 
 struct GemvParams {
@@ -34,6 +58,12 @@ struct GemvParams {
     const Desc *descs;   // device array (stack)
     int32_t ndesc;
     int32_t total_wgu;
+    // Dynamic tail: workgroup units [pool_begin, total_wgu) are taken one at a time from the
+    // counter ctr[0] (ctr[1] counts finished workgroups; the last one resets both to 0).
+    // ctr == nullptr: static assignment of every unit.
+    int *ctr;
+    int32_t pool_begin;
+    int32_t pad_;
 };
 
 struct RedDesc {
@@ -53,11 +83,17 @@ struct RedParams {
 
 typedef void (*GemvFn)(GemvParams);
 
-// Kernel instances of one format for M = 1..8 (each defined in its own translation unit).
+// Format sets a kernel instance handles (bit 1 << fmt per format).
+constexpr int fmt_bit(int fmt) { return 1 << fmt; }
+constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
+
+// Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
+// 8-bit head), each defined in its own translation unit.
 GemvFn gemv_fn_q4_0(int M);
 GemvFn gemv_fn_cb4(int M);
 GemvFn gemv_fn_cb8(int M);
 GemvFn gemv_fn_tq2(int M);
 GemvFn gemv_fn_aq2x8(int M);
+GemvFn gemv_fn_cb48(int M);
 
 }  // namespace wqd

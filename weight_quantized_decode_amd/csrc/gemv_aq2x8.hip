@@ -2,5 +2,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_aq2x8(int M) { return gemv_fn<AQ2X8>(M); }
+GemvFn gemv_fn_aq2x8(int M) { return gemv_fn<fmt_bit(AQ2X8)>(M); }
 }  // namespace wqd

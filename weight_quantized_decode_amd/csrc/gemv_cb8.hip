@@ -2,5 +2,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_cb8(int M) { return gemv_fn<CB8>(M); }
+GemvFn gemv_fn_cb8(int M) { return gemv_fn<fmt_bit(CB8)>(M); }
 }  // namespace wqd

@@ -62,6 +62,16 @@ __device__ __forceinline__ uint4 ld16(const uint8_t *p) {
     const u32x4 v = gld<u32x4>(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Streaming read of packed codes: each byte is used once, so the load is marked nontemporal
+// (it then does not displace reused data such as activations and tables in the caches).
+__device__ __forceinline__ uint4 ld16_stream(const uint8_t *p) {
+#if WQD_NT_CODES
+    const u32x4 v = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)p);
+#else
+    const u32x4 v = gld<u32x4>(p);
+#endif
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint2 ld8(const uint8_t *p) {
     const u32x2 v = gld<u32x2>(p);
     return make_uint2(v.x, v.y);
@@ -100,6 +110,14 @@ struct LdsSize {
     static constexpr int dwords = (FMT == CB4 || FMT == CB8) ? 256 * kTableCopies
                                   : (FMT == AQ2X8)          ? 2048
                                                             : 1;
+};
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+template <int MASK>
+struct LdsSizeMask {
+    static constexpr int dwords = cmax(cmax(cmax((MASK & (1 << CB4)) ? LdsSize<CB4>::dwords : 1,
+                                                 (MASK & (1 << CB8)) ? LdsSize<CB8>::dwords : 1),
+                                            (MASK & (1 << AQ2X8)) ? LdsSize<AQ2X8>::dwords : 1),
+                                       1);
 };
 
 // Build the per-workgroup LDS table of a projection.
@@ -325,42 +343,56 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
             return make_uint2(0, 0);
         }
     };
+    // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
+    // row, if this unit owns it, is handled after the pipelined loop.
+    const int cfe = min(ce, D.C_full);
     auto load_group = [&](uint4 (&buf)[kU], int c) {
 #pragma unroll
         for (int j = 0; j < kU; j++) {
-            const int cc = min(c + j, ce - 1);
-            buf[j] = ld16(cptr + (int64_t)cc * 1024);
+            const int cc = min(c + j, cfe - 1);
+            buf[j] = ld16_stream(cptr + (int64_t)cc * 1024);
         }
     };
     auto proc_group = [&](const uint4 (&buf)[kU], int c, uint2 sq) {
 #pragma unroll
-        for (int j = 0; j < kU; j++) {
-            if (c + j < ce) {
-                if constexpr (FMT == Q4_0 || FMT == TQ2) {
-                    process(FullTag<true>{}, buf[j], c + j, sq);  // K is a whole number of chunks
-                } else {
-                    if (c + j < D.C_full) process(FullTag<true>{}, buf[j], c + j, sq);
-                    else process(FullTag<false>{}, buf[j], c + j, sq);
-                }
-            }
-        }
+        for (int j = 0; j < kU; j++)
+            if (c + j < cfe) process(FullTag<true>{}, buf[j], c + j, sq);
     };
 
-    uint4 A[kU], B[kU];
-    uint2 sqA = load_sq(cb), sqB = make_uint2(0, 0);
-    load_group(A, cb);
-    for (int c = cb; c < ce; c += 2 * kU) {
-        if (c + kU < ce) {
-            load_group(B, c + kU);
+    // Double-buffered pipeline: the loads of group g+1 are in flight while group g is decoded.
+    // Each branch below is straight-line code, so the compiler can wait for exactly the older
+    // group (vmcnt = kU) instead of draining every load.
+    if (cb < cfe) {
+        const int ng = (cfe - cb + kU - 1) / kU;
+        uint4 A[kU], B[kU];
+        uint2 sqA = load_sq(cb), sqB = make_uint2(0, 0);
+        load_group(A, cb);
+        int gi = 0;
+        while (true) {
+            const int c = cb + gi * kU;
+            if (gi + 1 >= ng) {
+                proc_group(A, c, sqA);
+                break;
+            }
             sqB = load_sq(c + kU);
-        }
-        proc_group(A, c, sqA);
-        if (c + kU >= ce) break;
-        if (c + 2 * kU < ce) {
-            load_group(A, c + 2 * kU);
+            load_group(B, c + kU);
+            proc_group(A, c, sqA);
+            gi++;
+            if (gi + 1 >= ng) {
+                proc_group(B, c + kU, sqB);
+                break;
+            }
             sqA = load_sq(c + 2 * kU);
+            load_group(A, c + 2 * kU);
+            proc_group(B, c + kU, sqB);
+            gi++;
         }
-        proc_group(B, c + kU, sqB);
+    }
+    if constexpr (FMT != Q4_0 && FMT != TQ2) {
+        for (int c = max(cb, cfe); c < ce; c++) {
+            const uint4 v = ld16(cptr + (int64_t)c * 1024);
+            process(FullTag<false>{}, v, c, make_uint2(0, 0));
+        }
     }
 
     if constexpr (FMT == AQ2X8) {
@@ -379,55 +411,97 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
     }
 }
 
-template <int FMT, int M>
+// Index of the projection owning workgroup unit u (uniform binary search over the descriptors).
+__device__ __forceinline__ int find_proj(const GemvParams &P, int u) {
+    if (!P.descs) return 0;
+    int lo = 0, hi = P.ndesc - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (load_wgu_begin(P.descs + mid) <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// One workgroup unit: kWaves wave units of one projection, one per wave.  The LDS table is
+// rebuilt (between two barriers, so all waves of the workgroup take part) when the projection
+// changes.
+template <int MASK, int M>
+__device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, int wid,
+                                        int lane) {
+    const int p = find_proj(P, u);
+    if (p != cur) {
+        if (P.descs) D = load_desc(P.descs + p);
+        if constexpr (LdsSizeMask<MASK>::dwords > 1) {
+            __syncthreads();
+            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) build_table<CB4>(lds, D);
+            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) build_table<CB8>(lds, D);
+            if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) build_table<AQ2X8>(lds, D);
+            __syncthreads();
+        }
+        cur = p;
+    }
+    const int wu = (u - D.wgu_begin) * kWaves + wid;
+    if (wu < D.wu_count) {
+        if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds);
+        if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds);
+        if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds);
+        if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds);
+        if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) run_unit<AQ2X8, M>(D, wu, lane, lds);
+    }
+}
+
+// Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
+// [0, pool_begin) are split into equal contiguous ranges, one per workgroup; the rest are handed
+// out one by one from a device-wide counter to whichever workgroup is free, which evens out the
+// finish times (workgroups on different XCDs stream at different speeds).
+template <int MASK, int M>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
-    __shared__ uint32_t lds[LdsSize<FMT>::dwords];
+    __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
+    __shared__ int next_u;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int total = P.total_wgu;
-    const int per = total / (int)gridDim.x, rem = total % (int)gridDim.x;
+    const int nstatic = P.ctr ? P.pool_begin : total;
+    const int per = nstatic / (int)gridDim.x, rem = nstatic % (int)gridDim.x;
     const int b = blockIdx.x;
     const int u0 = b * per + min(b, rem);
     const int u1 = u0 + per + (b < rem ? 1 : 0);
     int cur = -1;
     Desc D = P.d0;
-    for (int u = u0; u < u1; u++) {
-        int p = 0;
-        if (P.descs) {
-            // last descriptor whose first workgroup-unit is <= u (uniform binary search)
-            int lo = 0, hi = P.ndesc - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (load_wgu_begin(P.descs + mid) <= u) lo = mid; else hi = mid - 1;
-            }
-            p = lo;
+    for (int u = u0; u < u1; u++) run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
+    if (P.ctr) {
+        while (true) {
+            __syncthreads();
+            if (threadIdx.x == 0)
+                next_u = nstatic + __hip_atomic_fetch_add(P.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int u = __builtin_amdgcn_readfirstlane(next_u);
+            if (u >= total) break;
+            run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
         }
-        if (p != cur) {
-            if (P.descs) D = load_desc(P.descs + p);
-            if constexpr (LdsSize<FMT>::dwords > 1) {
-                __syncthreads();
-                build_table<FMT>(lds, D);
-                __syncthreads();
+        // Every workgroup has taken its last index once it reaches here; the last one to arrive
+        // resets the counters for the next launch on this workspace.
+        if (threadIdx.x == 0) {
+            if (__hip_atomic_fetch_add(P.ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (int)gridDim.x - 1) {
+                __hip_atomic_store(P.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(P.ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            cur = p;
         }
-        const int wu = (u - D.wgu_begin) * kWaves + wid;
-        if (wu < D.wu_count) run_unit<FMT, M>(D, wu, lane, lds);
     }
 }
 
-
-template <int FMT>
+template <int MASK>
 GemvFn gemv_fn(int M) {
     switch (M) {
-    case 1: return gemv_kernel<FMT, 1>;
-    case 2: return gemv_kernel<FMT, 2>;
-    case 3: return gemv_kernel<FMT, 3>;
-    case 4: return gemv_kernel<FMT, 4>;
-    case 5: return gemv_kernel<FMT, 5>;
-    case 6: return gemv_kernel<FMT, 6>;
-    case 7: return gemv_kernel<FMT, 7>;
-    case 8: return gemv_kernel<FMT, 8>;
+    case 1: return gemv_kernel<MASK, 1>;
+    case 2: return gemv_kernel<MASK, 2>;
+    case 3: return gemv_kernel<MASK, 3>;
+    case 4: return gemv_kernel<MASK, 4>;
+    case 5: return gemv_kernel<MASK, 5>;
+    case 6: return gemv_kernel<MASK, 6>;
+    case 7: return gemv_kernel<MASK, 7>;
+    case 8: return gemv_kernel<MASK, 8>;
     }
     return nullptr;
 }
