@@ -83,15 +83,19 @@ WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonica
 
 /* ---------------------------------------------------------------- one projection */
 
-/* Device workspace wqd_gemm needs for this shape (split-K partial sums), in bytes (0 = none). */
+/* Device workspace wqd_gemm needs for this shape, in bytes (0 = none): one counter per 64-row
+ * group and the split-K partial sums. */
 WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
 
 /* y[m*ldy + n] = sum_k x[m*ldx + k] * W[n][k] for 1 <= M <= 8, enqueued on `stream`.
  * w: prepared weights (wqd_prepared_bytes(fmt, N, K) bytes, 16-byte aligned).
  * x: M rows of K fp16 values, ldx >= K and even, 4-byte aligned.  y: M rows of N fp32, ldy >= N.
  * workspace: at least wqd_gemm_workspace_bytes(fmt, N, K, M) bytes of device memory (may be NULL
- * when that is 0); it is scratch, overwritten by the call.  Results are the same bits from run
- * to run (fixed-order reductions, no atomics). */
+ * when that is 0).  It must be zero-filled before its first use; every call leaves its counters
+ * at zero again, so it can be reused by later calls on the same stream (calls that overlap in
+ * time must not share a workspace).  When K is split, the wave that finishes the last K-slice of
+ * a 64-row group adds the slices' partial sums in ascending order, so results are the same bits
+ * from run to run. */
 WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
                      int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
@@ -116,15 +120,17 @@ typedef struct {
 
 enum {
     WQD_ORDERED = 0,   /* projections one after another, each its own launches */
-    WQD_PERSISTENT = 1 /* all projections of a format in one persistent launch, then one launch
-                          for the fixed-order split-K reduction of every projection; valid when
+    WQD_PERSISTENT = 1 /* one persistent launch per format set (CB4 and CB8 together); valid when
                           no projection's x is another projection's y */
 };
 
-/* Device workspace bytes for wqd_run_projections over this list (descriptor table + partials). */
+/* Device workspace bytes for wqd_run_projections over this list (descriptor table, counters and
+ * partial sums).  In WQD_ORDERED mode the workspace is used like wqd_gemm's (zero-filled before
+ * its first use); in WQD_PERSISTENT mode wqd_stack_setup initialises it. */
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
 
-/* Write the descriptor table of this projection list into the workspace (a blocking copy).
+/* Write the descriptor table of this projection list into the workspace and zero its counters
+ * (blocking copies).
  * Must be called once before wqd_run_projections in WQD_PERSISTENT mode, and again whenever a
  * pointer or shape in the list changes. */
 WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, void *workspace,
@@ -137,8 +143,8 @@ WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64
 
 /* Profiling variant: the same work as wqd_run_projections in WQD_PERSISTENT mode, with hipEvent_t
  * events[2i] recorded on the stream just before the i-th kernel launch of the call and
- * events[2i+1] just after it.  Launch order: one dequantize-and-multiply launch per format present
- * (ascending format id), then one split-K reduction launch if any projection is split.
+ * events[2i+1] just after it.  Launch order: the CB4+CB8 launch if both formats are present, then
+ * one launch per remaining format (ascending format id).
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,

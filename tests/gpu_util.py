@@ -41,8 +41,9 @@ def new_y(M, N, ldy=None, fill=float("nan")):
 
 
 def workspace(nbytes):
+    """Device workspace, zero-filled before first use as the library requires."""
     import torch
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device="cuda")
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device="cuda")
 
 
 def run_gemm(fmt, N, K, w, x_dev, M, y=None, stream=None):

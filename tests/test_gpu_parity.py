@@ -124,3 +124,25 @@ def test_gemm_one_hot_and_zero_activations(fmt):
     assert np.all(y[1] == 0.0)
     rtol = 2.0 ** -11 + 2.0 ** -23 if fmt == I.AQ2X8 else 1e-7
     assert np.all(np.abs(y[0] - W64[:, k]) <= rtol * np.abs(W64[:, k]))
+
+
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8])
+def test_workspace_reuse_leaves_counters_zero(fmt):
+    # The split-K slice counters in the workspace must be back at zero after every call, so one
+    # workspace serves many calls (and differently shaped ones) in a row.
+    import torch
+    note(f"workspace reuse fmt={fmt}")
+    shapes = [(300, 2048, 2), (130, 1024, 1), (300, 2048, 3)]
+    need = max(W.wqd_gemm_workspace_bytes(fmt, N, K, M) for N, K, M in shapes)
+    ws = workspace(need)
+    for i, (N, K, M) in enumerate(shapes):
+        canon = I.gen_weight(fmt, N, K, (18, fmt, i))
+        x = I.gen_x(M, K, (18, fmt, i))
+        w = upload_weight(fmt, N, K, canon)
+        y = new_y(M, N)
+        W.wqd_gemm(fmt, N, K, w, upload_x(x), y, ws)
+        W.wqd_stream_check()
+        yref, aref = oracle.gemm_f64(fmt, N, K, canon, x)
+        check_parity(y.cpu().numpy(), yref, aref, f"reuse fmt={fmt} call {i}")
+        rg = (N + 63) // 64
+        assert int(ws[: 4 * rg].view(torch.int32).abs().sum().item()) == 0

@@ -1,5 +1,5 @@
-// Host launch code and C entry points of libwqd, plus the split-K reduction and the debug
-// dequantize kernels.  The dequantize-and-multiply kernels live in gemv_<format>.hip.
+// Host launch code and C entry points of libwqd, plus the debug dequantize kernel.  The
+// dequantize-and-multiply kernels live in gemv_<format>.hip (instances of gemv_impl.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -13,37 +13,6 @@ namespace wqd {
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// y[m][n] = sum_s part[m][s][n], s ascending.  Every projection's (m, n) range starts at a
-// multiple of 256 in the flattened index space, so one workgroup never straddles two
-// projections and its descriptor is found with scalar loads.
-__global__ __launch_bounds__(256) void reduce_kernel(RedParams P) {
-    const int64_t base = (int64_t)blockIdx.x * 256;
-    RedDesc D = P.d0;
-    if (P.descs) {
-        typedef const int64_t __attribute__((address_space(4))) *ci64p;
-        int lo = 0, hi = P.ndesc - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            const int64_t b = ((ci64p)(uintptr_t)&P.descs[mid].begin)[0];
-            if (b <= base) lo = mid; else hi = mid - 1;
-        }
-        typedef const uint32_t __attribute__((address_space(4))) *cu32;
-        uint32_t w[sizeof(RedDesc) / 4];
-        cu32 src = (cu32)(uintptr_t)(P.descs + lo);
-#pragma unroll
-        for (unsigned k = 0; k < sizeof(RedDesc) / 4; k++) w[k] = src[k];
-        __builtin_memcpy(&D, w, sizeof(RedDesc));
-    }
-    const int64_t j = base + threadIdx.x - D.begin;
-    if (j >= (int64_t)D.M * D.N) return;
-    const int m = (int)(j / D.N);
-    const int n = (int)(j - (int64_t)m * D.N);
-    const float *p = D.part + (int64_t)m * D.S * D.Npad + n;
-    float s = 0.f;
-    for (int k = 0; k < D.S; k++) s += p[(int64_t)k * D.Npad];
-    D.y[(int64_t)m * D.ldy + n] = s;
 }
 
 // Debug decode of the prepared layout to dense fp32, one thread per (row, chunk).
@@ -130,82 +99,6 @@ static int device_cus() {
     return cached_cus;
 }
 
-// Chunks per K-slice.  `splits_wanted` slices per row are asked for (at least min_cs chunks
-// each); the slices are then made as equal as the format's alignment allows.
-static int64_t choose_cs(const Layout &L, int64_t splits_wanted, int64_t min_cs) {
-    int64_t mult = (L.fmt == TQ2) ? 8 : (L.fmt == Q4_0) ? 4 : 1;
-    int64_t cap = (L.fmt == Q4_0) ? 64 : (L.fmt == TQ2) ? 128 : (int64_t(1) << 30);
-    int64_t splits = splits_wanted < 1 ? 1 : splits_wanted;
-    int64_t cs = (L.C + splits - 1) / splits;
-    if (cs < min_cs) cs = min_cs;
-    if (cs > cap) cs = cap;
-    if (cs >= L.C) return L.C;  // one slice: the whole row
-    const int64_t S = (L.C + cs - 1) / cs;
-    cs = align_up((L.C + S - 1) / S, mult);  // equalize the slices
-    if (cs > cap) cs = cap;
-    return cs;
-}
-
-struct Plan {
-    Layout L;
-    int64_t CS = 0, S = 1;
-    int64_t part_bytes = 0;  // M * S * Npad * 4 when S > 1
-};
-
-static Plan finish_plan(Plan P, int64_t M) {
-    P.S = (P.L.C + P.CS - 1) / P.CS;
-    P.part_bytes = (P.S > 1) ? M * P.S * P.L.Npad * 4 : 0;
-    return P;
-}
-
-// One projection alone: split K until the wave units cover the GPU about 4 times.
-static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
-    Plan P;
-    P.L = make_layout(fmt, N, K);
-    if (!P.L.ok) return P;
-    P.CS = choose_cs(P.L, int64_t(cus) * 16 / P.L.RG, 8);
-    return finish_plan(P, M);
-}
-
-// A projection inside a persistent stack launch: K-slices of about WQD_STACK_MIN_CS chunks.
-static Plan plan_stack(int fmt, int64_t N, int64_t K, int64_t M) {
-    Plan P;
-    P.L = make_layout(fmt, N, K);
-    if (!P.L.ok) return P;
-    int64_t target = WQD_STACK_MIN_CS;
-    int64_t splits = (P.L.C + target / 2) / target;
-    P.CS = choose_cs(P.L, splits, 1);
-    return finish_plan(P, M);
-}
-
-static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
-                      float *part) {
-    Desc D;
-    memset(&D, 0, sizeof(D));
-    const uint8_t *base = static_cast<const uint8_t *>(w);
-    D.codes = base;
-    D.scales = base + P.L.off_scales;
-    D.cbk = reinterpret_cast<const uint16_t *>(base + P.L.off_cbk);
-    D.x = static_cast<const uint16_t *>(x);
-    D.y = y;
-    D.part = part;
-    D.ldx = ldx;
-    D.ldy = ldy;
-    D.N = int32_t(P.L.N);
-    D.K = int32_t(P.L.K);
-    D.C = int32_t(P.L.C);
-    D.C_full = int32_t(P.L.C_full);
-    D.S = int32_t(P.S);
-    D.CS = int32_t(P.CS);
-    D.Q = int32_t(P.L.Q);
-    D.RG = int32_t(P.L.RG);
-    D.Npad = int32_t(P.L.Npad);
-    D.wu_count = int32_t(P.L.RG * P.S);
-    D.wgu_begin = 0;
-    D.fmt = P.L.fmt;
-    return D;
-}
-
 static GemvFn pick_gemv(int mask, int M) {
     switch (mask) {
     case 1 << Q4_0: return gemv_fn_q4_0(M);
@@ -235,6 +128,110 @@ static int resident_per_cu(GemvFn fn) {
     return n;
 }
 
+// Wave slots resident at once for a kernel instance (the persistent grid's capacity).
+static int64_t resident_waves(int mask, int64_t M, int cus) {
+    GemvFn fn = pick_gemv(mask, int(M));
+    return int64_t(cus) * (fn ? resident_per_cu(fn) : 1) * kWaves;
+}
+
+// Chunks per wave unit for a launch covering `total_cc` chunk-columns (one 1 KiB wave load
+// each): about WQD_UNITS_PER_WAVE units per resident wave, between 8 and WQD_STACK_MIN_CS chunks.
+static int64_t target_cs(int64_t total_cc, int64_t waves) {
+    int64_t cs = total_cc / (waves * WQD_UNITS_PER_WAVE);
+    if (cs < 8) cs = 8;
+    if (cs > WQD_STACK_MIN_CS) cs = WQD_STACK_MIN_CS;
+    return cs;
+}
+
+// Chunks per K-slice.  `splits_wanted` slices per row are asked for (at least min_cs chunks
+// each); the slices are then made as equal as the format's alignment allows.
+static int64_t choose_cs(const Layout &L, int64_t splits_wanted, int64_t min_cs) {
+    int64_t mult = (L.fmt == TQ2) ? 8 : (L.fmt == Q4_0) ? 4 : 1;
+    int64_t cap = (L.fmt == Q4_0) ? 64 : (L.fmt == TQ2) ? 128 : (int64_t(1) << 30);
+    int64_t splits = splits_wanted < 1 ? 1 : splits_wanted;
+    int64_t cs = (L.C + splits - 1) / splits;
+    if (cs < min_cs) cs = min_cs;
+    if (cs > cap) cs = cap;
+    if (cs >= L.C) return L.C;  // one slice: the whole row
+    const int64_t S = (L.C + cs - 1) / cs;
+    cs = align_up((L.C + S - 1) / S, mult);  // equalize the slices
+    if (cs > cap) cs = cap;
+    return cs;
+}
+
+// Slice counters live in a region of their own that partial sums never overlap, so a
+// workspace stays valid across calls of different shapes: the first kCntRegion bytes of a
+// wqd_gemm workspace, or the counter region of a stack workspace.
+constexpr int64_t kCntRegion = 65536;
+constexpr int64_t kMaxSplitRG = kCntRegion / 4;  // row groups one split call can count
+
+struct Plan {
+    Layout L;
+    int64_t CS = 0, S = 1;
+    int64_t cnt_bytes = 0;   // one int per row group when S > 1 (256-byte aligned)
+    int64_t part_bytes = 0;  // M * S * Npad * 4 when S > 1 (256-byte aligned)
+    // wqd_gemm workspace: [kCntRegion bytes of counters][partials]
+    int64_t ws_bytes() const { return S > 1 ? kCntRegion + part_bytes : 0; }
+};
+
+static Plan finish_plan(Plan P, int64_t M) {
+    if (P.L.RG > kMaxSplitRG) P.CS = P.L.C;  // too many row groups to count: no split
+    P.S = (P.L.C + P.CS - 1) / P.CS;
+    P.cnt_bytes = (P.S > 1) ? align_up(P.L.RG * 4, 256) : 0;
+    P.part_bytes = (P.S > 1) ? align_up(M * P.S * P.L.Npad * 4, 256) : 0;
+    return P;
+}
+
+// A projection split into K-slices of about `cs_target` chunks (equal slices).
+static Plan plan_cs(int fmt, int64_t N, int64_t K, int64_t M, int64_t cs_target) {
+    Plan P;
+    P.L = make_layout(fmt, N, K);
+    if (!P.L.ok) return P;
+    int64_t splits = (P.L.C + cs_target / 2) / cs_target;
+    P.CS = choose_cs(P.L, splits, 1);
+    return finish_plan(P, M);
+}
+
+// One projection alone.
+static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
+    Layout L = make_layout(fmt, N, K);
+    if (!L.ok) {
+        Plan P;
+        P.L = L;
+        return P;
+    }
+    return plan_cs(fmt, N, K, M, target_cs(L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus)));
+}
+
+static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
+                      float *part, int *cnt) {
+    Desc D;
+    memset(&D, 0, sizeof(D));
+    const uint8_t *base = static_cast<const uint8_t *>(w);
+    D.codes = base;
+    D.scales = base + P.L.off_scales;
+    D.cbk = reinterpret_cast<const uint16_t *>(base + P.L.off_cbk);
+    D.x = static_cast<const uint16_t *>(x);
+    D.y = y;
+    D.part = P.S > 1 ? part : nullptr;
+    D.cnt = P.S > 1 ? cnt : nullptr;
+    D.ldx = ldx;
+    D.ldy = ldy;
+    D.N = int32_t(P.L.N);
+    D.K = int32_t(P.L.K);
+    D.C = int32_t(P.L.C);
+    D.C_full = int32_t(P.L.C_full);
+    D.S = int32_t(P.S);
+    D.CS = int32_t(P.CS);
+    D.Q = int32_t(P.L.Q);
+    D.RG = int32_t(P.L.RG);
+    D.Npad = int32_t(P.L.Npad);
+    D.wu_count = int32_t(P.L.RG * P.S);
+    D.wgu_begin = 0;
+    D.fmt = P.L.fmt;
+    return D;
+}
+
 static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus) {
     GemvFn fn = pick_gemv(mask, M);
     if (!fn) return WQD_EINVAL;
@@ -242,14 +239,6 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
     if (grid > GP.total_wgu) grid = GP.total_wgu;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(fn, dim3(unsigned(grid)), dim3(kThreads), 0, st, GP);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? WQD_OK : hip_fail(e);
-}
-
-static int launch_reduce(const RedParams &RP, hipStream_t st) {
-    if (RP.total <= 0) return WQD_OK;
-    const int64_t blocks = (RP.total + 255) / 256;
-    hipLaunchKernelGGL(reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, RP);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
@@ -265,39 +254,24 @@ static int check_proj(int fmt, int64_t N, int64_t K, const void *w, const void *
     return WQD_OK;
 }
 
-// One projection onto the stream (validated arguments).
-static int gemm_one(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
-                    float *y, int64_t ldy, void *ws, int64_t ws_bytes, hipStream_t st, int cus) {
-    Plan P = plan_single(fmt, N, K, M, cus);
-    if (P.part_bytes > 0 && (!ws || ws_bytes < P.part_bytes)) return WQD_ESPACE;
-    float *part = P.part_bytes > 0 ? static_cast<float *>(ws) : nullptr;
+// One projection onto the stream, with its slice counters and partials.
+static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, int64_t ldx, float *y,
+                       int64_t ldy, int *cnt, float *part, hipStream_t st, int cus) {
     GemvParams GP;
     memset(&GP, 0, sizeof(GP));
-    GP.d0 = make_desc(P, w, x, ldx, y, ldy, part);
+    GP.d0 = make_desc(P, w, x, ldx, y, ldy, part, cnt);
     GP.descs = nullptr;
     GP.ndesc = 1;
     GP.total_wgu = int32_t((GP.d0.wu_count + kWaves - 1) / kWaves);
-    int rc = launch_gemv(fmt_bit(fmt), int(M), GP, st, cus);
-    if (rc != WQD_OK || P.S == 1) return rc;
-    RedParams RP;
-    memset(&RP, 0, sizeof(RP));
-    RP.d0.part = part;
-    RP.d0.y = y;
-    RP.d0.ldy = ldy;
-    RP.d0.N = int32_t(N);
-    RP.d0.Npad = int32_t(P.L.Npad);
-    RP.d0.S = int32_t(P.S);
-    RP.d0.M = int32_t(M);
-    RP.d0.begin = 0;
-    RP.descs = nullptr;
-    RP.ndesc = 1;
-    RP.total = M * N;
-    return launch_reduce(RP, st);
+    return launch_gemv(fmt_bit(P.L.fmt), int(M), GP, st, cus);
 }
 
-// Stack workspace: [Desc table][RedDesc table][partials...], each 256-byte aligned.  The
-// projections are grouped into launches: all CB4/CB8 projections together when both appear,
-// otherwise one launch per format; within a launch, descriptors are in format order.
+// Stack workspace: [Desc table][launch-group counters, 256 B][slice counters][partials], each
+// region 256-byte aligned.  The slice-counter region is at least kCntRegion bytes and the
+// partial region at least what the largest projection needs alone, so WQD_ORDERED mode uses
+// the same two regions.  Projections are grouped into launches: all CB4/CB8 projections
+// together when both appear, otherwise one launch per format; within a launch, descriptors
+// are in format order.
 struct LaunchGroup {
     int mask = 0;
     int first = 0, count = 0;  // range in StackPlan::descs
@@ -305,13 +279,9 @@ struct LaunchGroup {
 };
 
 struct StackPlan {
-    int64_t off_ctr = 0;           // 2 ints per launch group (dynamic-tail counters)
     std::vector<Desc> descs;
     std::vector<LaunchGroup> groups;
-    std::vector<RedDesc> reds;
-    int64_t red_total = 0;
-    int64_t off_descs = 0, off_reds = 0, off_part = 0, total = 0;
-    int64_t max_single_part = 0;   // for ORDERED mode
+    int64_t off_descs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0, total = 0;
 };
 
 static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *ws, StackPlan &SP, int cus) {
@@ -330,53 +300,65 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
     }
     for (int fmt = 1; fmt <= 5; fmt++)
         if (present & fmt_bit(fmt)) masks.push_back(fmt_bit(fmt));
-    SP.off_descs = 0;
-    SP.off_ctr = align_up(int64_t(sizeof(Desc)) * count, 256);
-    SP.off_reds = SP.off_ctr + 256;
-    SP.off_part = SP.off_reds + align_up(int64_t(sizeof(RedDesc)) * count, 256);
-    int64_t part_off = SP.off_part;
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    for (int mask : masks) {
-        LaunchGroup G;
-        G.mask = mask;
-        G.first = int(SP.descs.size());
-        int wgu = 0;
+
+    // plans: the K-slice size of a launch group follows its total work
+    std::vector<Plan> plans(count);
+    std::vector<int> order, group_of;
+    int64_t cnt_total = 0, part_total = 0, single_part = 0;
+    for (size_t gi = 0; gi < masks.size(); gi++) {
+        const int mask = masks[gi];
+        int64_t total_cc = 0;
+        for (int i = 0; i < count; i++) {
+            if (!(mask & fmt_bit(p[i].fmt))) continue;
+            Layout L = make_layout(p[i].fmt, p[i].N, p[i].K);
+            total_cc += L.RG * L.C;
+        }
+        const int64_t cs_target = target_cs(total_cc, resident_waves(mask, M, cus));
         for (int fmt = 1; fmt <= 5; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = 0; i < count; i++) {
                 if (p[i].fmt != fmt) continue;
-                Plan P = plan_stack(fmt, p[i].N, p[i].K, M);
-                float *part = nullptr;
-                if (P.part_bytes > 0) {
-                    part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
-                    RedDesc R;
-                    memset(&R, 0, sizeof(R));
-                    R.part = part;
-                    R.y = p[i].y;
-                    R.ldy = p[i].ldy;
-                    R.N = int32_t(p[i].N);
-                    R.Npad = int32_t(P.L.Npad);
-                    R.S = int32_t(P.S);
-                    R.M = int32_t(M);
-                    R.begin = SP.red_total;
-                    SP.red_total += align_up(M * p[i].N, 256);
-                    SP.reds.push_back(R);
-                    part_off += align_up(P.part_bytes, 256);
-                }
-                Desc D = make_desc(P, p[i].w, p[i].x, p[i].ldx, p[i].y, p[i].ldy, part);
-                D.wgu_begin = wgu;
-                wgu += (D.wu_count + kWaves - 1) / kWaves;
-                SP.descs.push_back(D);
-                Plan Q = plan_single(p[i].fmt, p[i].N, p[i].K, M, cus);
-                if (Q.part_bytes > SP.max_single_part) SP.max_single_part = Q.part_bytes;
+                plans[i] = plan_cs(fmt, p[i].N, p[i].K, M, cs_target);
+                cnt_total += plans[i].cnt_bytes;
+                part_total += plans[i].part_bytes;
+                Plan Q = plan_single(fmt, p[i].N, p[i].K, M, cus);
+                if (Q.part_bytes > single_part) single_part = Q.part_bytes;
+                order.push_back(i);
+                group_of.push_back(int(gi));
             }
+        }
+    }
+    SP.off_descs = 0;
+    SP.off_ctr = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_cnt = SP.off_ctr + 256;
+    SP.cnt_bytes = cnt_total > kCntRegion ? cnt_total : kCntRegion;
+    SP.off_part = SP.off_cnt + SP.cnt_bytes;
+    SP.total = SP.off_part + (part_total > single_part ? part_total : single_part);
+
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int64_t cnt_off = SP.off_cnt, part_off = SP.off_part;
+    size_t oi = 0;
+    for (size_t gi = 0; gi < masks.size(); gi++) {
+        LaunchGroup G;
+        G.mask = masks[gi];
+        G.first = int(SP.descs.size());
+        int wgu = 0;
+        for (; oi < order.size() && group_of[oi] == int(gi); oi++) {
+            const int i = order[oi];
+            const Plan &P = plans[i];
+            int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
+            float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
+            cnt_off += P.cnt_bytes;
+            part_off += P.part_bytes;
+            Desc D = make_desc(P, p[i].w, p[i].x, p[i].ldx, p[i].y, p[i].ldy, part, cnt);
+            D.wgu_begin = wgu;
+            wgu += (D.wu_count + kWaves - 1) / kWaves;
+            SP.descs.push_back(D);
         }
         G.count = int(SP.descs.size()) - G.first;
         G.total_wgu = wgu;
         SP.groups.push_back(G);
     }
-    SP.total = part_off;
-    if (SP.max_single_part > SP.total) SP.total = SP.max_single_part;
     return WQD_OK;
 }
 
@@ -391,15 +373,20 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     Plan P = plan_single(fmt, N, K, M, device_cus());
     if (!P.L.ok) return WQD_ESHAPE;
-    return P.part_bytes;
+    return P.ws_bytes();
 }
 
 WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
                      float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
     int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
     if (rc != WQD_OK) return rc;
-    return gemm_one(fmt, N, K, w, x, M, ldx, y, ldy, workspace, workspace_bytes,
-                    static_cast<hipStream_t>(stream), device_cus());
+    const int cus = device_cus();
+    Plan P = plan_single(fmt, N, K, M, cus);
+    if (P.ws_bytes() > 0 && (!workspace || workspace_bytes < P.ws_bytes())) return WQD_ESPACE;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    int *cnt = reinterpret_cast<int *>(ws);
+    float *part = ws ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr;
+    return gemm_launch(P, w, x, M, ldx, y, ldy, cnt, part, static_cast<hipStream_t>(stream), cus);
 }
 
 WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream) {
@@ -442,11 +429,10 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, voi
     uint8_t *base = static_cast<uint8_t *>(workspace);
     hipError_t e = hipMemcpyAsync(base + SP.off_descs, SP.descs.data(), sizeof(Desc) * SP.descs.size(),
                                   hipMemcpyHostToDevice, st);
-    if (e == hipSuccess && !SP.reds.empty())
-        e = hipMemcpyAsync(base + SP.off_reds, SP.reds.data(), sizeof(RedDesc) * SP.reds.size(),
-                           hipMemcpyHostToDevice, st);
-    static const int zeros[64] = {0};  // dynamic-tail counters start at 0 (each launch resets them)
-    if (e == hipSuccess) e = hipMemcpyAsync(base + SP.off_ctr, zeros, sizeof(zeros), hipMemcpyHostToDevice, st);
+    // launch-group and slice counters start at 0; every launch leaves them at 0 again
+    std::vector<uint8_t> zeros(size_t(SP.off_part - SP.off_ctr), 0);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(base + SP.off_ctr, zeros.data(), zeros.size(), hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
@@ -458,25 +444,29 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT) return WQD_EINVAL;
     if (n_events < 0 || (n_events > 0 && !events)) return WQD_EINVAL;
     const int cus = device_cus();
+    StackPlan SP;
+    int rc = build_stack_plan(projs, count, M, workspace, SP, cus);
+    if (rc != WQD_OK) return rc;
+    uint8_t *base = static_cast<uint8_t *>(workspace);
     if (mode == WQD_ORDERED) {
-        if (!projs || count < 1) return WQD_EINVAL;
+        // one launch per projection, on the stack workspace's counter and partial regions
         if (n_events != 0) return WQD_EINVAL;
+        bool split = false;
+        for (int i = 0; i < count; i++) split |= plan_single(projs[i].fmt, projs[i].N, projs[i].K, M, cus).S > 1;
+        if (split && (!base || workspace_bytes < SP.total)) return WQD_ESPACE;
+        int *cnt = base ? reinterpret_cast<int *>(base + SP.off_cnt) : nullptr;
+        float *part = base ? reinterpret_cast<float *>(base + SP.off_part) : nullptr;
         for (int i = 0; i < count; i++) {
             const wqd_proj &q = projs[i];
-            if (q.reserved != 0) return WQD_EINVAL;
-            int rc = check_proj(q.fmt, q.N, q.K, q.w, q.x, M, q.ldx, q.y, q.ldy);
-            if (rc != WQD_OK) return rc;
-            rc = gemm_one(q.fmt, q.N, q.K, q.w, q.x, M, q.ldx, q.y, q.ldy, workspace, workspace_bytes, st, cus);
+            Plan P = plan_single(q.fmt, q.N, q.K, M, cus);
+            rc = gemm_launch(P, q.w, q.x, M, q.ldx, q.y, q.ldy, cnt, part, st, cus);
             if (rc != WQD_OK) return rc;
         }
         return WQD_OK;
     }
-    if (!workspace) return WQD_EINVAL;
-    StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, workspace, SP, cus);
-    if (rc != WQD_OK) return rc;
+    if (!base) return WQD_EINVAL;
     if (workspace_bytes < SP.total) return WQD_ESPACE;
-    const int launches = int(SP.groups.size()) + (SP.reds.empty() ? 0 : 1);
+    const int launches = int(SP.groups.size());
     if (n_events != 0 && n_events != 2 * launches) return WQD_ESPACE;
     int li = 0;
     auto mark = [&](int which) -> int {
@@ -484,9 +474,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * li + which]), st);
         return e == hipSuccess ? WQD_OK : hip_fail(e);
     };
-    const uint8_t *base = static_cast<const uint8_t *>(workspace);
     const Desc *dtab = reinterpret_cast<const Desc *>(base + SP.off_descs);
-    for (const LaunchGroup &G : SP.groups) {
+    for (size_t gi = 0; gi < SP.groups.size(); gi++) {
+        const LaunchGroup &G = SP.groups[gi];
         GemvParams GP;
         memset(&GP, 0, sizeof(GP));
         GP.d0 = SP.descs[G.first];
@@ -494,7 +484,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         GP.ndesc = G.count;
         GP.total_wgu = G.total_wgu;
         if (WQD_POOL_PERCENT > 0) {
-            GP.ctr = reinterpret_cast<int *>(const_cast<uint8_t *>(base) + SP.off_ctr) + 2 * (&G - SP.groups.data());
+            GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr) + 2 * gi;
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }
         if ((rc = mark(0)) != WQD_OK) return rc;
@@ -503,20 +493,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         if ((rc = mark(1)) != WQD_OK) return rc;
         li++;
     }
-    if (!SP.reds.empty()) {
-        RedParams RP;
-        memset(&RP, 0, sizeof(RP));
-        RP.d0 = SP.reds[0];
-        RP.descs = reinterpret_cast<const RedDesc *>(base + SP.off_reds);
-        RP.ndesc = int32_t(SP.reds.size());
-        RP.total = SP.red_total;
-        if ((rc = mark(0)) != WQD_OK) return rc;
-        rc = launch_reduce(RP, st);
-        if (rc != WQD_OK) return rc;
-        if ((rc = mark(1)) != WQD_OK) return rc;
-        li++;
-    }
-    return rc;
+    return WQD_OK;
 }
 
 WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
@@ -530,7 +507,7 @@ WQD_API int wqd_stack_launches(const wqd_proj *projs, int32_t count, int64_t M) 
     StackPlan SP;
     int rc = build_stack_plan(projs, count, M, nullptr, SP, device_cus());
     if (rc != WQD_OK) return rc;
-    return int(SP.groups.size()) + (SP.reds.empty() ? 0 : 1);
+    return int(SP.groups.size());
 }
 
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,

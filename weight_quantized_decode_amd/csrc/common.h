@@ -20,7 +20,10 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #define WQD_TABLE_COPIES 64
 #endif
 #ifndef WQD_STACK_MIN_CS
-#define WQD_STACK_MIN_CS 32
+#define WQD_STACK_MIN_CS 64
+#endif
+#ifndef WQD_UNITS_PER_WAVE
+#define WQD_UNITS_PER_WAVE 4
 #endif
 #ifndef WQD_STACK_UNITS
 #define WQD_STACK_UNITS 1
@@ -34,6 +37,7 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #ifndef WQD_WG_PER_CU
 #define WQD_WG_PER_CU 2
 #endif
+constexpr int kMaxM = 8;                  // largest M (activation rows) per call
 constexpr int kWaves = WQD_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kU = WQD_U;                 // chunks per load group (double buffered)
@@ -46,6 +50,7 @@ struct Desc {
     const uint16_t *x;
     float *y;
     float *part;        // split-K partials [M][S][Npad], or null when S == 1
+    int *cnt;           // per row group: K-slices finished (zero between calls), or null
     int64_t ldx, ldy;
     int32_t N, K, C, C_full, S, CS, Q, RG, Npad;
     int32_t wgu_begin;  // first workgroup-unit of this projection
@@ -66,20 +71,6 @@ struct GemvParams {
     int32_t pad_;
 };
 
-struct RedDesc {
-    const float *part;
-    float *y;
-    int64_t ldy;
-    int32_t N, Npad, S, M;
-    int64_t begin;       // first flattened (m, n) element
-};
-
-struct RedParams {
-    RedDesc d0;
-    const RedDesc *descs;
-    int32_t ndesc;
-    int64_t total;
-};
 
 typedef void (*GemvFn)(GemvParams);
 

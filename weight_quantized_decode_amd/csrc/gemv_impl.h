@@ -114,10 +114,11 @@ struct LdsSize {
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <int MASK>
 struct LdsSizeMask {
+    // tables of the codebook formats; per-wave block sums (WQD_MAX_M x 64 floats) of Q4_0 / TQ2
     static constexpr int dwords = cmax(cmax(cmax((MASK & (1 << CB4)) ? LdsSize<CB4>::dwords : 1,
                                                  (MASK & (1 << CB8)) ? LdsSize<CB8>::dwords : 1),
                                             (MASK & (1 << AQ2X8)) ? LdsSize<AQ2X8>::dwords : 1),
-                                       1);
+                                       (MASK & ((1 << Q4_0) | (1 << TQ2))) ? kWaves * kMaxM * 64 : 1);
 };
 
 // Build the per-workgroup LDS table of a projection.
@@ -145,8 +146,10 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
 // ------------------------------------------------------------------------------------------
 // One wave unit: rows 64g..64g+63 (one per lane) times chunks [cb, ce).
 // ------------------------------------------------------------------------------------------
-template <int FMT, int M>
-__device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const uint32_t *lds) {
+// `hook` runs once, right after the first loads of the unit are issued: the workgroup uses it
+// to (re)build its LDS table while those loads are in flight.
+template <int FMT, int M, typename Hook>
+__device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32_t *lds, Hook &&hook) {
     const int g = wu / D.S;
     const int s = wu - g * D.S;
     const int cb = s * D.CS;
@@ -161,24 +164,63 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
 
-    // Per-block activation sums for the block formats: lane l holds the sum of block b0 + l.
-    float bsum[M];
+    // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
+    // row, if this unit owns it, is handled after the pipelined loop.
+    const int cfe = min(ce, D.C_full);
+    auto load_group = [&](uint4 (&buf)[kU], int c) {
+#pragma unroll
+        for (int j = 0; j < kU; j++) {
+            const int cc = min(c + j, cfe - 1);
+            buf[j] = ld16_stream(cptr + (int64_t)cc * 1024);
+        }
+    };
+    // Scale quad of the chunk group starting at c (block formats only).
+    auto load_sq = [&](int c) -> uint2 {
+        if constexpr (FMT == Q4_0 || FMT == TQ2) {
+            const int q = (FMT == Q4_0) ? (c >> 2) : (c >> 3);
+            return ld8(D.scales + (((int64_t)g * D.Q + q) * 64 + lane) * 8);
+        } else {
+            return make_uint2(0, 0);
+        }
+    };
+    uint4 A[kU], B[kU];
+    uint2 sqA = make_uint2(0, 0), sqB = make_uint2(0, 0);
+    if (cb < cfe) {
+        sqA = load_sq(cb);
+        load_group(A, cb);
+    }
+    hook();
+
+    // Per-block activation sums for the block formats (the -8 / -1 code offsets are applied
+    // through them).  All 64 lanes load the unit's slice of x together, SEG lanes per block, and
+    // the sums are parked in this wave's LDS area; the main loop reads them back with a uniform
+    // (broadcast) address.
     int b0 = 0;
     constexpr int WPB = (FMT == Q4_0) ? 32 : 128;   // weights per scale block
+    float *bs = nullptr;
     if constexpr (FMT == Q4_0 || FMT == TQ2) {
+        const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        bs = reinterpret_cast<float *>(lds) + wid * (kMaxM * 64);
         b0 = (FMT == Q4_0) ? cb : cb / 2;
         const int b1 = (FMT == Q4_0) ? ce : ce / 2;
-        const int blk = b0 + lane;
+        constexpr int SEG = WPB / 8;   // lanes per block, 8 activations per lane
+        constexpr int BPR = 64 / SEG;  // blocks per round of the wave
+        const int rounds = (b1 - b0 + BPR - 1) / BPR;
+        constexpr uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in fp16
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            float sacc = 0.f;
-            if (blk < b1) {
-                const uint32_t *xp = reinterpret_cast<const uint32_t *>(xrow[m] + (int64_t)blk * WPB);
-                constexpr uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in fp16
-#pragma unroll 8
-                for (int i = 0; i < WPB / 2; i++) sacc = dot2(gld<uint32_t>(xp + i), ones, sacc);
+            for (int r = 0; r < rounds; r++) {
+                const int blk = b0 + r * BPR + lane / SEG;
+                float sacc = 0.f;
+                if (blk < b1) {
+                    const uint16_t *xp = xrow[m] + (int64_t)blk * WPB + (lane % SEG) * 8;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) sacc = dot2(gld<uint32_t>(xp + 2 * i), ones, sacc);
+                }
+#pragma unroll
+                for (int o = 1; o < SEG; o <<= 1) sacc += __shfl_xor(sacc, o);
+                if ((lane % SEG) == 0 && blk < b1) bs[m * 64 + (blk - b0)] = sacc;
             }
-            bsum[m] = sacc;
         }
     }
 
@@ -250,7 +292,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
                     a0 = dot2(q[t][2], xs[4 * t + 2], a0);
                     a1 = dot2(q[t][3], xs[4 * t + 3], a1);
                 }
-                const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsum[m]), c - b0));
+                const float sb = bs[m * 64 + (c - b0)];
                 const float p = fmaf(a1, 0.0625f, a0);               // 2^-24 * sum code*x
                 const float blk = fmaf(p, 16777216.0f, -8.0f * sb);  // sum (code-8)*x
                 acc[m] = fmaf(d, blk, acc[m]);
@@ -301,7 +343,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
                     p = fmaf(ta[m][2], 0.0625f, p);
                     p = fmaf(ta[m][1], 0.25f, p);
                     p += ta[m][0];                                   // 2^-24 * sum code*x
-                    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bsum[m]), b - b0));
+                    const float sb = bs[m * 64 + (b - b0)];
                     const float blk = fmaf(p, 16777216.0f, -sb);     // sum (code-1)*x
                     acc[m] = fmaf(d, blk, acc[m]);
                 }
@@ -334,25 +376,6 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
         }
     };
 
-    // Scale quad of the chunk group starting at c (block formats only).
-    auto load_sq = [&](int c) -> uint2 {
-        if constexpr (FMT == Q4_0 || FMT == TQ2) {
-            const int q = (FMT == Q4_0) ? (c >> 2) : (c >> 3);
-            return ld8(D.scales + (((int64_t)g * D.Q + q) * 64 + lane) * 8);
-        } else {
-            return make_uint2(0, 0);
-        }
-    };
-    // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
-    // row, if this unit owns it, is handled after the pipelined loop.
-    const int cfe = min(ce, D.C_full);
-    auto load_group = [&](uint4 (&buf)[kU], int c) {
-#pragma unroll
-        for (int j = 0; j < kU; j++) {
-            const int cc = min(c + j, cfe - 1);
-            buf[j] = ld16_stream(cptr + (int64_t)cc * 1024);
-        }
-    };
     auto proc_group = [&](const uint4 (&buf)[kU], int c, uint2 sq) {
 #pragma unroll
         for (int j = 0; j < kU; j++)
@@ -364,9 +387,6 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
     // group (vmcnt = kU) instead of draining every load.
     if (cb < cfe) {
         const int ng = (cfe - cb + kU - 1) / kU;
-        uint4 A[kU], B[kU];
-        uint2 sqA = load_sq(cb), sqB = make_uint2(0, 0);
-        load_group(A, cb);
         int gi = 0;
         while (true) {
             const int c = cb + gi * kU;
@@ -405,9 +425,40 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, const 
 #pragma unroll
             for (int m = 0; m < M; m++) gst(D.y + (int64_t)m * D.ldy + row, acc[m]);
         }
-    } else {
+        return;
+    }
+    // Split K: publish this slice's partial sums, then count the finished slices of the row
+    // group; the wave that finishes the last slice adds all slices in ascending order and writes
+    // y.  The partials are written and read with device-coherent (agent scope) accesses, which
+    // go through to memory instead of a single XCD's L2; the wait below makes the stores
+    // complete before the counter is incremented, so whoever sees the final count sees them.
 #pragma unroll
-        for (int m = 0; m < M; m++) gst(D.part + ((int64_t)m * D.S + s) * D.Npad + row, acc[m]);
+    for (int m = 0; m < M; m++)
+        __hip_atomic_store(D.part + ((int64_t)m * D.S + s) * D.Npad + row, acc[m], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(D.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (done == D.S - 1) {
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float *pm = D.part + (int64_t)m * D.S * D.Npad + row;
+            float sum = 0.f;
+            // 8 loads in flight at a time, added in ascending slice order
+            for (int k0 = 0; k0 < D.S; k0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    v[j] = (k0 + j < D.S) ? __hip_atomic_load(pm + (int64_t)(k0 + j) * D.Npad, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; j++) sum += v[j];
+            }
+            if (row < D.N) gst(D.y + (int64_t)m * D.ldy + row, sum);
+        }
+        if (lane == 0) __hip_atomic_store(D.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -428,25 +479,43 @@ __device__ __forceinline__ int find_proj(const GemvParams &P, int u) {
 template <int MASK, int M>
 __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, int wid,
                                         int lane) {
-    const int p = find_proj(P, u);
+    // Units are visited in increasing order: search only for the first one, then step forward.
+    int p = 0;
+    if (P.descs) {
+        if (cur < 0) {
+            p = find_proj(P, u);
+        } else {
+            p = cur;
+            while (p + 1 < P.ndesc && load_wgu_begin(P.descs + p + 1) <= u) p++;
+        }
+    }
+    bool rebuild = false;
     if (p != cur) {
         if (P.descs) D = load_desc(P.descs + p);
-        if constexpr (LdsSizeMask<MASK>::dwords > 1) {
-            __syncthreads();
-            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) build_table<CB4>(lds, D);
-            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) build_table<CB8>(lds, D);
-            if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) build_table<AQ2X8>(lds, D);
-            __syncthreads();
-        }
+        rebuild = true;
         cur = p;
     }
+    // All waves take part in the table rebuild (two barriers), after issuing their first loads.
+    auto hook = [&]() {
+        if constexpr ((MASK & ((1 << CB4) | (1 << CB8) | (1 << AQ2X8))) != 0) {
+            if (rebuild) {
+                __syncthreads();
+                if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) build_table<CB4>(lds, D);
+                if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) build_table<CB8>(lds, D);
+                if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) build_table<AQ2X8>(lds, D);
+                __syncthreads();
+            }
+        }
+    };
     const int wu = (u - D.wgu_begin) * kWaves + wid;
     if (wu < D.wu_count) {
-        if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds);
-        if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds);
-        if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds);
-        if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds);
-        if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) run_unit<AQ2X8, M>(D, wu, lane, lds);
+        if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds, hook);
+        if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
+        if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds, hook);
+        if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds, hook);
+        if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) run_unit<AQ2X8, M>(D, wu, lane, lds, hook);
+    } else {
+        hook();
     }
 }
 
