@@ -54,7 +54,7 @@ def _tile_rows(prep, fmt, N, K):
     return codes[:N], row_bytes, C, RG
 
 
-@pytest.mark.parametrize("fmt,N,K", [(I.CB4, 70, 1002), (I.CB8, 70, 1001), (I.AQ2X8, 70, 1000)])
+@pytest.mark.parametrize("fmt,N,K", [(I.CB4, 70, 1002), (I.CB8, 70, 1001)])
 def test_prepare_keeps_canonical_byte_order_for_byte_formats(fmt, N, K):
     canon = I.gen_weight(fmt, N, K, (5, fmt))
     prep = W.wqd_prepare_host(fmt, N, K, canon)
@@ -64,6 +64,30 @@ def test_prepare_keeps_canonical_byte_order_for_byte_formats(fmt, N, K):
     assert np.all(rows[:, row_bytes:] == 0)  # tail padding is zero
     full = prep[:RG * C * 1024].reshape(RG, C, 64, 16)
     assert np.all(full[:, :, (N - (RG - 1) * 64):, :][-1] == 0)  # padded rows are zero
+
+
+@pytest.mark.parametrize("N,K", [(70, 1000), (64, 512), (8, 8), (130, 8 * 200)])
+def test_prepare_tiles_aq2x8_codes(N, K):
+    # AQ2X8 codes go to tiles of 8 rows x 64 groups, slice-major: the 16 bytes of lane l in tile
+    # (r8, s) are (c0, c1) of rows 8*r8..8*r8+7 for group 64*s + l.  Rebuild the canonical [N][G][2] code array
+    # from the tiles, and check the padding (rows >= N, groups >= G) is zero; scales and codebooks
+    # are copied verbatim.
+    canon = I.gen_weight(I.AQ2X8, N, K, (5, I.AQ2X8))
+    prep = W.wqd_prepare_host(I.AQ2X8, N, K, canon)
+    G = K // 8
+    KS = (G + 63) // 64
+    RG = (N + 63) // 64
+    Npad = RG * 64
+    tiles = prep[:Npad // 8 * KS * 1024].reshape(KS, Npad // 8, 64, 8, 2)  # [s][r8][lane][row][c]
+    codes = tiles.transpose(1, 3, 0, 2, 4).reshape(Npad, KS * 64, 2)        # [n][g][c]
+    want = canon[8192 + 2 * N:].reshape(N, G, 2)
+    assert np.array_equal(codes[:N, :G], want)
+    assert np.all(codes[N:] == 0) and np.all(codes[:, G:] == 0)
+    off_s = (Npad // 8 * KS * 1024 + 255) // 256 * 256
+    assert np.array_equal(prep[off_s:off_s + 2 * N], canon[8192:8192 + 2 * N])
+    off_c = (off_s + 2 * Npad + 255) // 256 * 256
+    assert np.array_equal(prep[off_c:off_c + 8192], canon[:8192])
+    assert W.wqd_prepared_bytes(I.AQ2X8, N, K) == (off_c + 8192 + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("fmt,N,K", [(I.Q4_0, 70, 256), (I.TQ2, 70, 512)])

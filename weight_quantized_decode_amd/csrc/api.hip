@@ -58,19 +58,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, Layout L
             const int64_t k = c * 16 + b;
             if (k < L.K) orow[k] = half_bits_to_float(cbk[byte]);
         }
-    } else if constexpr (FMT == AQ2X8) {
-        const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
-        for (int gi = 0; gi < 8; gi++) {
-            const int64_t k0 = c * 64 + gi * 8;
-            if (k0 >= L.K) break;
-            const uint32_t c0 = (w4[gi / 2] >> (16 * (gi % 2))) & 0xFF;
-            const uint32_t c1 = (w4[gi / 2] >> (16 * (gi % 2) + 8)) & 0xFF;
-            for (int j = 0; j < 8; j++) {
-                const float e0 = half_bits_to_float(cbk[(0 * 256 + c0) * 8 + j]);
-                const float e1 = half_bits_to_float(cbk[(1 * 256 + c1) * 8 + j]);
-                orow[k0 + j] = __fmul_rn(__fadd_rn(e0, e1), s);
-            }
-        }
+    }
+}
+
+// Debug decode of the AQ2X8 tile layout, one thread per (row, group of 8 weights).
+__global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, Layout L, float *out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= L.N * L.G) return;
+    const int64_t n = i / L.G, g = i - n * L.G;
+    const uint8_t *t = w + ((g / 64 * (L.Npad / 8) + n / 8) * 64 + g % 64) * 16 + 2 * (n % 8);
+    const uint32_t c0 = t[0], c1 = t[1];
+    const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
+    const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
+    float *o = out + n * L.K + g * 8;
+    for (int j = 0; j < 8; j++) {
+        const float e0 = half_bits_to_float(cbk[(0 * 256 + c0) * 8 + j]);
+        const float e1 = half_bits_to_float(cbk[(1 * 256 + c1) * 8 + j]);
+        o[j] = __fmul_rn(__fadd_rn(e0, e1), s);
     }
 }
 
@@ -105,7 +109,6 @@ static GemvFn pick_gemv(int mask, int M) {
     case 1 << CB4: return gemv_fn_cb4(M);
     case 1 << CB8: return gemv_fn_cb8(M);
     case 1 << TQ2: return gemv_fn_tq2(M);
-    case 1 << AQ2X8: return gemv_fn_aq2x8(M);
     case kMaskCB48: return gemv_fn_cb48(M);
     }
     return nullptr;
@@ -113,20 +116,19 @@ static GemvFn pick_gemv(int mask, int M) {
 
 // Resident workgroups per CU of a kernel (queried once per kernel and device).  The persistent
 // grid never exceeds what is resident at once, so every workgroup starts immediately.
-static int resident_per_cu(GemvFn fn) {
-    struct Entry { GemvFn fn; int dev; int n; };
+static int resident_per_cu(const void *fn, int threads) {
+    struct Entry { const void *fn; int dev; int n; };
     static thread_local std::vector<Entry> cache;
     int dev = 0;
     (void)hipGetDevice(&dev);
     for (const Entry &e : cache)
         if (e.fn == fn && e.dev == dev) return e.n;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(fn), kThreads, 0) !=
-            hipSuccess || n < 1)
-        n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 1) n = 1;
     cache.push_back({fn, dev, n});
     return n;
 }
+static int resident_per_cu(GemvFn fn) { return resident_per_cu(reinterpret_cast<const void *>(fn), kThreads); }
 
 // Wave slots resident at once for a kernel instance (the persistent grid's capacity).
 static int64_t resident_waves(int mask, int64_t M, int cus) {
@@ -243,6 +245,109 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
 
+// ------------------------------------------------------------------------------------------
+// AQ2X8 planning.  A projection's RB x KS tiles (8-row blocks x 64-group slices) are cut into
+// a x b pieces (row chunks of nrb <= 16*RW blocks, K-splits of ns slices); every workgroup of the
+// launch takes one piece of each projection (piece j on workgroup (j + off) % nwg).  The cost
+// model per piece, in tile loads (KiB): ns * (nrb + table build) plus a fixed charge for a
+// K-split (its partial round trip); the shape with the cheapest busiest workgroup wins.
+// ------------------------------------------------------------------------------------------
+static int aq_rw_max(int64_t M) { return M == 1 ? 8 : 2; }
+
+static int64_t aq_nwg(int64_t M, int cus) {
+    AqFn fn = aq_fn(int(M), aq_rw_max(M));
+    return int64_t(cus) * (fn ? resident_per_cu(reinterpret_cast<const void *>(fn), aq_waves(int(M)) * 64) : 1);
+}
+
+struct AqPlan {
+    Layout L;
+    int64_t RB = 0, a = 1, b = 1, nrb = 1, ns = 1, RW = 1;
+    int64_t part_bytes = 0;  // M * b * Npad tagged 8-byte slots when b > 1 (256-byte aligned)
+    // wqd_gemm workspace: [kCntRegion bytes, unused by AQ2X8][partials]
+    int64_t ws_bytes() const { return b > 1 ? kCntRegion + part_bytes : 0; }
+};
+
+static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
+    AqPlan A;
+    A.L = make_layout(AQ2X8, N, K);
+    if (!A.L.ok) return A;
+    const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = aq_rw_max(M), W = aq_waves(int(M));
+    const int64_t build = (M == 1) ? 16 : 2, split_charge = 32;
+    if (nwg < 1) nwg = 1;
+    double best = 1e300;
+    for (int64_t b = 1; b <= KS; b++) {
+        const int64_t ns = (KS + b - 1) / b;
+        if ((KS + ns - 1) / ns != b) continue;  // same split as a smaller b
+        int64_t a = nwg / b;
+        if (a > (RB + W - 1) / W) a = (RB + W - 1) / W;    // at least one block per wave...
+        if (a < (RB + W * rwmax - 1) / (W * rwmax)) a = (RB + W * rwmax - 1) / (W * rwmax);  // ...at most RW
+        if (a < 1) a = 1;
+        const int64_t nrb = (RB + a - 1) / a;
+        a = (RB + nrb - 1) / nrb;
+        const int64_t rounds = (a * b + nwg - 1) / nwg;
+        const double cost = double(rounds) * double(ns * (nrb + build) + (b > 1 ? split_charge : 0));
+        if (cost < best) {
+            best = cost;
+            A.a = a;
+            A.b = b;
+            A.nrb = nrb;
+            A.ns = ns;
+        }
+    }
+    A.RB = RB;
+    A.RW = (M == 1) ? 2 : 1;  // M = 1 kernels exist for RW = 2, 4, 8; M > 1 for 1, 2
+    while (A.RW * W < A.nrb) A.RW *= 2;
+    A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 8, 256) : 0;
+    return A;
+}
+
+static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
+                           void *part, int64_t off) {
+    AqDesc D;
+    memset(&D, 0, sizeof(D));
+    const uint8_t *base = static_cast<const uint8_t *>(w);
+    D.codes = base;
+    D.rscale = reinterpret_cast<const uint16_t *>(base + A.L.off_scales);
+    D.cbk = reinterpret_cast<const uint16_t *>(base + A.L.off_cbk);
+    D.x = static_cast<const uint16_t *>(x);
+    D.y = y;
+    D.part = A.b > 1 ? static_cast<uint64_t *>(part) : nullptr;
+    D.ldx = ldx;
+    D.ldy = ldy;
+    D.N = int32_t(A.L.N);
+    D.G = int32_t(A.L.G);
+    D.KS = int32_t(A.L.KS);
+    D.RB = int32_t(A.RB);
+    D.Npad = int32_t(A.L.Npad);
+    D.a = int32_t(A.a);
+    D.b = int32_t(A.b);
+    D.nrb = int32_t(A.nrb);
+    D.ns = int32_t(A.ns);
+    D.npieces = int32_t(A.a * A.b);
+    D.off = int32_t(off);
+    return D;
+}
+
+static int launch_aq(int64_t M, int64_t RW, const AqParams &AP, hipStream_t st) {
+    AqFn fn = aq_fn(int(M), int(RW));
+    if (!fn) return WQD_EINVAL;
+    hipLaunchKernelGGL(fn, dim3(unsigned(AP.nwg)), dim3(aq_waves(int(M)) * 64), 0, st, AP);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? WQD_OK : hip_fail(e);
+}
+
+// One AQ2X8 projection alone, on a workspace whose partial region starts at `part`.
+static int aq_gemm_launch(const AqPlan &A, int64_t nwg, const void *w, const void *x, int64_t M, int64_t ldx,
+                          float *y, int64_t ldy, void *part, hipStream_t st) {
+    AqParams AP;
+    memset(&AP, 0, sizeof(AP));
+    AP.d0 = make_aq_desc(A, w, x, ldx, y, ldy, part, 0);
+    AP.descs = nullptr;
+    AP.ndesc = 1;
+    AP.nwg = int32_t(nwg < A.a * A.b ? nwg : A.a * A.b);
+    return launch_aq(M, A.RW, AP, st);
+}
+
 static int check_proj(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
                       int64_t ldx, const float *y, int64_t ldy) {
     if (k_multiple(fmt) == 0 || !w || !x || !y) return WQD_EINVAL;
@@ -274,14 +379,17 @@ static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, i
 // are in format order.
 struct LaunchGroup {
     int mask = 0;
-    int first = 0, count = 0;  // range in StackPlan::descs
+    int first = 0, count = 0;  // range in StackPlan::descs (or StackPlan::aqdescs)
     int total_wgu = 0;
+    bool aq = false;           // the AQ2X8 launch
+    int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
 };
 
 struct StackPlan {
     std::vector<Desc> descs;
+    std::vector<AqDesc> aqdescs;
     std::vector<LaunchGroup> groups;
-    int64_t off_descs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0, total = 0;
+    int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0, total = 0;
 };
 
 static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *ws, StackPlan &SP, int cus) {
@@ -293,6 +401,8 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
         if (rc != WQD_OK) return rc;
         present |= fmt_bit(p[i].fmt);
     }
+    const bool has_aq = (present & fmt_bit(AQ2X8)) != 0;
+    present &= ~fmt_bit(AQ2X8);
     std::vector<int> masks;
     if ((present & kMaskCB48) == kMaskCB48) {
         masks.push_back(kMaskCB48);
@@ -328,8 +438,24 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
             }
         }
     }
+    // AQ2X8 projections: one launch, every workgroup taking one piece of each
+    std::vector<AqPlan> aqplans;
+    std::vector<int> aqidx;
+    const int64_t aq_wg = has_aq ? aq_nwg(M, cus) : 0;
+    int64_t aq_part_total = 0;
+    for (int i = 0; has_aq && i < count; i++) {
+        if (p[i].fmt != AQ2X8) continue;
+        AqPlan A = plan_aq(p[i].N, p[i].K, M, aq_wg);  // also the plan of a WQD_ORDERED launch
+        aq_part_total += A.part_bytes;
+        if (A.part_bytes > single_part) single_part = A.part_bytes;
+        aqplans.push_back(A);
+        aqidx.push_back(i);
+    }
+    part_total += aq_part_total;
+
     SP.off_descs = 0;
-    SP.off_ctr = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * int64_t(aqplans.size()), 256);
     SP.off_cnt = SP.off_ctr + 256;
     SP.cnt_bytes = cnt_total > kCntRegion ? cnt_total : kCntRegion;
     SP.off_part = SP.off_cnt + SP.cnt_bytes;
@@ -359,6 +485,27 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
         G.total_wgu = wgu;
         SP.groups.push_back(G);
     }
+    if (!aqplans.empty()) {
+        LaunchGroup G;
+        G.mask = fmt_bit(AQ2X8);
+        G.aq = true;
+        G.first = 0;
+        G.count = int(aqplans.size());
+        int64_t total_pieces = 0;
+        for (const AqPlan &A : aqplans) total_pieces += A.a * A.b;
+        G.nwg = total_pieces < aq_wg ? total_pieces : aq_wg;  // no idle workgroups
+        int64_t off = 0;
+        for (size_t k = 0; k < aqplans.size(); k++) {
+            const AqPlan &A = aqplans[k];
+            const wqd_proj &q = p[aqidx[k]];
+            void *part = base ? static_cast<void *>(base + part_off) : nullptr;
+            part_off += A.part_bytes;
+            SP.aqdescs.push_back(make_aq_desc(A, q.w, q.x, q.ldx, q.y, q.ldy, part, off % G.nwg));
+            off += A.a * A.b;
+            if (A.RW > G.rw) G.rw = A.RW;
+        }
+        SP.groups.push_back(G);
+    }
     return WQD_OK;
 }
 
@@ -371,6 +518,11 @@ extern "C" {
 WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M) {
     if (k_multiple(fmt) == 0) return WQD_EINVAL;
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+    if (fmt == AQ2X8) {
+        AqPlan A = plan_aq(N, K, M, aq_nwg(M, device_cus()));
+        if (!A.L.ok) return WQD_ESHAPE;
+        return A.ws_bytes();
+    }
     Plan P = plan_single(fmt, N, K, M, device_cus());
     if (!P.L.ok) return WQD_ESHAPE;
     return P.ws_bytes();
@@ -381,9 +533,16 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
     int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
     if (rc != WQD_OK) return rc;
     const int cus = device_cus();
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    if (fmt == AQ2X8) {
+        const int64_t nwg = aq_nwg(M, cus);
+        AqPlan A = plan_aq(N, K, M, nwg);
+        if (A.ws_bytes() > 0 && (!workspace || workspace_bytes < A.ws_bytes())) return WQD_ESPACE;
+        return aq_gemm_launch(A, nwg, w, x, M, ldx, y, ldy, ws ? ws + kCntRegion : nullptr,
+                              static_cast<hipStream_t>(stream));
+    }
     Plan P = plan_single(fmt, N, K, M, cus);
     if (P.ws_bytes() > 0 && (!workspace || workspace_bytes < P.ws_bytes())) return WQD_ESPACE;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
     int *cnt = reinterpret_cast<int *>(ws);
     float *part = ws ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr;
     return gemm_launch(P, w, x, M, ldx, y, ldy, cnt, part, static_cast<hipStream_t>(stream), cus);
@@ -394,7 +553,7 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
     Layout L = make_layout(fmt, N, K);
     if (!L.ok) return WQD_ESHAPE;
     if (reinterpret_cast<uintptr_t>(w) & 15) return WQD_EALIGN;
-    const int64_t threads = L.N * L.C;
+    const int64_t threads = (fmt == AQ2X8) ? L.N * L.G : L.N * L.C;
     const unsigned blocks = unsigned((threads + 255) / 256);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint8_t *wb = static_cast<const uint8_t *>(w);
@@ -403,7 +562,7 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
     case CB4: hipLaunchKernelGGL(dequant_kernel<CB4>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     case CB8: hipLaunchKernelGGL(dequant_kernel<CB8>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     case TQ2: hipLaunchKernelGGL(dequant_kernel<TQ2>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case AQ2X8: hipLaunchKernelGGL(dequant_kernel<AQ2X8>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
+    case AQ2X8: hipLaunchKernelGGL(dequant_aq2x8_kernel, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     }
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);
@@ -427,8 +586,13 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, voi
     if (workspace_bytes < SP.total) return WQD_ESPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *base = static_cast<uint8_t *>(workspace);
-    hipError_t e = hipMemcpyAsync(base + SP.off_descs, SP.descs.data(), sizeof(Desc) * SP.descs.size(),
-                                  hipMemcpyHostToDevice, st);
+    hipError_t e = hipSuccess;
+    if (!SP.descs.empty())
+        e = hipMemcpyAsync(base + SP.off_descs, SP.descs.data(), sizeof(Desc) * SP.descs.size(),
+                           hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && !SP.aqdescs.empty())
+        e = hipMemcpyAsync(base + SP.off_aqdescs, SP.aqdescs.data(), sizeof(AqDesc) * SP.aqdescs.size(),
+                           hipMemcpyHostToDevice, st);
     // launch-group and slice counters start at 0; every launch leaves them at 0 again
     std::vector<uint8_t> zeros(size_t(SP.off_part - SP.off_ctr), 0);
     if (e == hipSuccess)
@@ -451,15 +615,24 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     if (mode == WQD_ORDERED) {
         // one launch per projection, on the stack workspace's counter and partial regions
         if (n_events != 0) return WQD_EINVAL;
+        const int64_t aq_wg = aq_nwg(M, cus);
         bool split = false;
-        for (int i = 0; i < count; i++) split |= plan_single(projs[i].fmt, projs[i].N, projs[i].K, M, cus).S > 1;
+        for (int i = 0; i < count; i++) {
+            if (projs[i].fmt == AQ2X8) split |= plan_aq(projs[i].N, projs[i].K, M, aq_wg).b > 1;
+            else split |= plan_single(projs[i].fmt, projs[i].N, projs[i].K, M, cus).S > 1;
+        }
         if (split && (!base || workspace_bytes < SP.total)) return WQD_ESPACE;
         int *cnt = base ? reinterpret_cast<int *>(base + SP.off_cnt) : nullptr;
         float *part = base ? reinterpret_cast<float *>(base + SP.off_part) : nullptr;
         for (int i = 0; i < count; i++) {
             const wqd_proj &q = projs[i];
-            Plan P = plan_single(q.fmt, q.N, q.K, M, cus);
-            rc = gemm_launch(P, q.w, q.x, M, q.ldx, q.y, q.ldy, cnt, part, st, cus);
+            if (q.fmt == AQ2X8) {
+                AqPlan A = plan_aq(q.N, q.K, M, aq_wg);
+                rc = aq_gemm_launch(A, aq_wg, q.w, q.x, M, q.ldx, q.y, q.ldy, part, st);
+            } else {
+                Plan P = plan_single(q.fmt, q.N, q.K, M, cus);
+                rc = gemm_launch(P, q.w, q.x, M, q.ldx, q.y, q.ldy, cnt, part, st, cus);
+            }
             if (rc != WQD_OK) return rc;
         }
         return WQD_OK;
@@ -475,8 +648,23 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         return e == hipSuccess ? WQD_OK : hip_fail(e);
     };
     const Desc *dtab = reinterpret_cast<const Desc *>(base + SP.off_descs);
+    const AqDesc *atab = reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs);
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
         const LaunchGroup &G = SP.groups[gi];
+        if (G.aq) {
+            AqParams AP;
+            memset(&AP, 0, sizeof(AP));
+            AP.d0 = SP.aqdescs[G.first];
+            AP.descs = atab + G.first;
+            AP.ndesc = G.count;
+            AP.nwg = int32_t(G.nwg);
+            if ((rc = mark(0)) != WQD_OK) return rc;
+            rc = launch_aq(M, G.rw, AP, st);
+            if (rc != WQD_OK) return rc;
+            if ((rc = mark(1)) != WQD_OK) return rc;
+            li++;
+            continue;
+        }
         GemvParams GP;
         memset(&GP, 0, sizeof(GP));
         GP.d0 = SP.descs[G.first];

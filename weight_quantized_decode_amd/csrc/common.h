@@ -78,13 +78,53 @@ typedef void (*GemvFn)(GemvParams);
 constexpr int fmt_bit(int fmt) { return 1 << fmt; }
 constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 
+// ------------------------------------------------------------------------------------------
+// AQ2X8 (its own kernel, on the transposed tile layout): a projection's (8-row block x K-slice)
+// tiles are cut into a x b rectangular pieces, a row chunks of nrb blocks times b K-splits of ns
+// slices.  Piece j = split * a + chunk runs on workgroup (j + off) % nwg (and j + nwg, ... when
+// there are more pieces than workgroups).  With b > 1 each piece stores one tagged partial per
+// row, and the workgroup running split b-1 of a chunk adds the b partials of its rows at the end
+// of its work.
+// ------------------------------------------------------------------------------------------
+// Waves per AQ2X8 workgroup: 8 for M = 1 (one workgroup per CU, 256 VGPRs per wave for a deep
+// load ring), 16 for M > 1.  A piece has at most waves * RW row blocks.
+__host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? 8 : 16; }
+constexpr uint32_t kAqTag = 0x7FA5A5A5u;     // high word of a written partial slot (an sNaN,
+                                             // which no float arithmetic produces)
+
+struct AqDesc {
+    const uint8_t *codes;     // tile plane
+    const uint16_t *rscale;   // row scales s[Npad], fp16
+    const uint16_t *cbk;      // codebooks C[2][256][8], fp16
+    const uint16_t *x;        // activations, M rows of ldx fp16
+    float *y;                 // output, M rows of ldy fp32
+    uint64_t *part;           // [M][b][Npad] tagged partials when b > 1
+    int64_t ldx, ldy;
+    int32_t N, G, KS, RB;     // rows, groups, K-slices, 8-row blocks holding rows < N
+    int32_t Npad;
+    int32_t a, b, nrb, ns;    // pieces: a row chunks of nrb blocks x b splits of ns slices
+    int32_t npieces, off;     // a * b pieces; piece j runs on workgroup (j + off) % nwg
+    int32_t pad_;
+};
+
+struct AqParams {
+    AqDesc d0;                // the projection when descs == nullptr
+    const AqDesc *descs;      // device array (stack)
+    int32_t ndesc;
+    int32_t nwg;              // workgroups of the launch
+};
+
+typedef void (*AqFn)(AqParams);
+// AQ2X8 kernel for M activation rows with RW 8-row blocks per wave per K-slice (M = 1: 2, 4 or
+// 8; M > 1: 1 or 2).
+AqFn aq_fn(int M, int RW);
+
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit.
 GemvFn gemv_fn_q4_0(int M);
 GemvFn gemv_fn_cb4(int M);
 GemvFn gemv_fn_cb8(int M);
 GemvFn gemv_fn_tq2(int M);
-GemvFn gemv_fn_aq2x8(int M);
 GemvFn gemv_fn_cb48(int M);
 
 }  // namespace wqd

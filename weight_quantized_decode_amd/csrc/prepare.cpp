@@ -76,7 +76,7 @@ void prep_tq2(const Layout &L, const uint8_t *src, uint8_t *dst) {
     }
 }
 
-// CB4 / CB8 / AQ2X8: row code bytes copied in canonical order into 16-byte chunks.
+// CB4 / CB8: row code bytes copied in canonical order into 16-byte chunks.
 void prep_bytes(const Layout &L, const uint8_t *row_codes, uint8_t *dst) {
     for (int64_t n = 0; n < L.N; n++) {
         const uint8_t *row = row_codes + n * L.row_code_bytes;
@@ -84,6 +84,19 @@ void prep_bytes(const Layout &L, const uint8_t *row_codes, uint8_t *dst) {
             int64_t nb = L.row_code_bytes - c * kChunkBytes;
             if (nb > kChunkBytes) nb = kChunkBytes;
             memcpy(chunk_ptr(dst, L, n, c), row + c * kChunkBytes, size_t(nb));
+        }
+    }
+}
+
+// AQ2X8: canonical rows of (c0, c1) pairs -> transposed 8-row x 64-group tiles (layout.h).
+void prep_aq2x8(const Layout &L, const uint8_t *row_codes, uint8_t *dst) {
+    for (int64_t n = 0; n < L.N; n++) {
+        const uint8_t *row = row_codes + n * L.G * 2;
+        const int64_t r8 = n / 8, r = n % 8;
+        for (int64_t g = 0; g < L.G; g++) {
+            uint8_t *t = dst + ((g / 64 * (L.Npad / 8) + r8) * 64 + g % 64) * kChunkBytes + 2 * r;
+            t[0] = row[2 * g];
+            t[1] = row[2 * g + 1];
         }
     }
 }
@@ -127,7 +140,7 @@ WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonica
         memcpy(dst + L.off_cbk, src, 512);
         break;
     case AQ2X8:
-        prep_bytes(L, src + 8192 + 2 * N, dst);
+        prep_aq2x8(L, src + 8192 + 2 * N, dst);
         memcpy(dst + L.off_scales, src + 8192, size_t(2 * N));
         memcpy(dst + L.off_cbk, src, 8192);
         break;
