@@ -24,8 +24,7 @@
 //
 // Work: see AqDesc.  A workgroup walks its pieces in order, slice by slice; the loads of the next
 // slice (of the same or the next piece) are in flight while a slice is processed.  With b > 1
-// K-splits a
-// piece stores one tagged 64-bit partial per row (no fence: a slot is either still zero or holds
+// K-splits a piece stores one tagged 64-bit partial per row (no fence: a slot is either still zero or holds
 // the tag and the value), and the workgroup that ran the last split of a chunk adds the b
 // partials of its rows, in split order, once all of its own pieces are done.
 #include <stddef.h>
@@ -100,6 +99,7 @@ __device__ __forceinline__ T load_uniform(const T *p) {
 // between two pointers rather than two structs keeps the descriptor out of scratch memory.
 __device__ __forceinline__ AqDesc get_desc(const AqParams &P, int p) {
     static_assert(offsetof(AqParams, d0) == 0, "d0 leads the kernel arguments");
+    p = min(max(p, 0), P.ndesc - 1);  // never read outside the table
     const AqDesc *d = P.descs ? P.descs + p
                               : (const AqDesc *)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
     return load_uniform(d);
@@ -152,17 +152,20 @@ template <int RW, int W>
 struct Loader {
     const uint8_t *base;   // code plane (wave-uniform; the lane's 16 bytes are added at the load)
     int64_t s_stride;      // bytes between slices (R8 = Npad/8 KiB)
+    int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
     int rb[RW];            // this wave's row blocks, clamped into the piece
     const uint16_t *x, *cbk;  // operands of the slice's table / activation stage
     int64_t ldx;
     int G;
-    Piece q;
+    Piece q, qn;  // current piece and the next one (looked up a piece ahead)
     int s;
     bool done;
 
-    __device__ __forceinline__ void setup(const AqParams &P, const Piece &n, int wid, int lane) {
+    // (n by value: step() passes the member qn, which is overwritten below)
+    __device__ __forceinline__ void setup(const AqParams &P, const Piece n, int wg, int wid, int lane) {
         q = n;
         s = n.s0;
+        qn = next_piece(P, wg, n);
         const AqDesc D = get_desc(P, n.p);
         base = D.codes;
         s_stride = int64_t(D.Npad / 8) * 1024;
@@ -170,23 +173,24 @@ struct Loader {
         cbk = D.cbk;
         ldx = D.ldx;
         G = D.G;
+        s_max = D.KS - 1;
+        rb_max = D.Npad / 8 - 1;
 #pragma unroll
-        for (int i = 0; i < RW; i++) rb[i] = min(n.rb0 + wid + W * i, n.rb1 - 1);
+        for (int i = 0; i < RW; i++) rb[i] = min(min(n.rb0 + wid + W * i, n.rb1 - 1), rb_max);
     }
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        return base + int64_t(s) * s_stride + int64_t(rb[i]) * 1024;
+        return base + int64_t(min(s, s_max)) * s_stride + int64_t(rb[i]) * 1024;
     }
     // After the last tile of a slice: step to the next slice (or piece).  Past the end of the
     // list the loader keeps re-reading the last tile, so the ring never has a hole.
     __device__ __forceinline__ void step(const AqParams &P, int wg, int wid, int lane) {
         if (done) return;
         if (++s < q.s1) return;
-        const Piece n = next_piece(P, wg, q);
-        if (n.p >= P.ndesc) {
+        if (qn.p >= P.ndesc) {
             done = true;
             s = q.s1 - 1;
         } else {
-            setup(P, n, wid, lane);
+            setup(P, qn, wg, wid, lane);
         }
     }
 };
@@ -216,7 +220,7 @@ __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int
                 uint64_t v[8];
 #pragma unroll
                 for (int j = 0; j < 8; j++)
-                    v[j] = (t0 + j < D.b) ? __hip_atomic_load(slot + int64_t(t0 + j) * D.Npad, __ATOMIC_RELAXED,
+                    v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT)
                                           : (uint64_t(kAqTag) << 32);
 #pragma unroll
@@ -224,7 +228,7 @@ __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int
                     int spins = 0;
                     while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
                         __builtin_amdgcn_s_sleep(2);
-                        v[j] = __hip_atomic_load(slot + int64_t(t0 + j) * D.Npad, __ATOMIC_RELAXED,
+                        v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
                         spins++;
                     }
@@ -234,16 +238,9 @@ __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int
             }
             gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
             for (int t = 0; t < D.b; t++)
-                __hip_atomic_store(slot + int64_t(t) * D.Npad, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(as_global(slot + int64_t(t) * D.Npad), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-}
-
-// LDS-only workgroup barrier: orders LDS traffic, leaves global loads in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <int M>
@@ -283,9 +280,12 @@ void aq_kernel(AqParams P) {
     if (pp.p >= P.ndesc) return;          // no work for this workgroup (same for all its waves)
     int ps = pp.s0;                       // slice being processed
 
+    AqDesc pd = get_desc(P, pp.p);        // its descriptor
+    Piece pn = next_piece(P, wg, pp);     // the next piece, looked up a piece ahead
+
     Loader<RW, W> ld;
     ld.done = false;
-    ld.setup(P, pp, wid, lane);
+    ld.setup(P, pp, wg, wid, lane);
 
     // M = 1 table blocks of this wave: codebook bsel, code blocks cblk0 .. cblk0 + 32/W - 1
     // (32 codes each; 16 blocks over W waves).
@@ -338,28 +338,17 @@ void aq_kernel(AqParams P) {
     for (int i = 0; i < RW; i++)
 #pragma unroll
         for (int r = 0; r < NACC; r++) acc[i][r] = 0.f;
-    uint32_t rs[RW];  // row scale (fp16 bits) of this lane's row (lane >> 3) in each row block
-    auto load_scales = [&](const Piece &q) __attribute__((always_inline)) {
-        const AqDesc D = get_desc(P, q.p);
-#pragma unroll
-        for (int i = 0; i < RW; i++) {  // rows < RB*8 <= Npad: always inside the scale plane
-            const int row = min(q.rb0 + wid + W * i, q.rb1 - 1) * 8 + (lane >> 3);
-            rs[i] = gld<uint16_t>(D.rscale + row);
-        }
-    };
-    load_scales(pp);
 
     u32x4 Xc[M];  // M > 1: this lane's group activations for the current slice
     const uint32_t lk = (uint32_t(lane) << 2) | (1u << 16);
 
     // Piece epilogue: row sums -> y (b == 1) or this split's tagged partial slots.
-    auto epilogue = [&](const Piece &q) __attribute__((always_inline)) {
-        const AqDesc D = get_desc(P, q.p);
+    auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) {
             const int rb = q.rb0 + wid + W * i;
             const int row = rb * 8 + (lane >> 3);
-            const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N;
+            const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N && q.split < D.b;
 #pragma unroll
             for (int m = 0; m < M; m++) {
                 float z;
@@ -367,10 +356,13 @@ void aq_kernel(AqParams P) {
                 else z = acc[i][m];
                 if (ok) {
                     if (D.b == 1) {
-                        gst(D.y + int64_t(m) * D.ldy + row, z * half_bits_to_float(rs[i]));
+                        // (the scale is loaded here, not ahead: an early load's result would be
+                        // waited for behind every tile in flight)
+                        const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
+                        gst(D.y + int64_t(m) * D.ldy + row, z * sc);
                     } else {
                         const uint64_t v = (uint64_t(kAqTag) << 32) | u32(z);
-                        __hip_atomic_store(D.part + (int64_t(m) * D.b + q.split) * D.Npad + row, v, __ATOMIC_RELAXED,
+                        __hip_atomic_store(as_global(D.part + (int64_t(m) * D.b + q.split) * D.Npad + row), v, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
@@ -382,7 +374,7 @@ void aq_kernel(AqParams P) {
 
     // Start of a slice: build its table (M = 1) or stage its activations (M > 1).
     auto slice_start = [&](const SliceOps &o) __attribute__((always_inline)) {
-        const int G = get_desc(P, pp.p).G;
+        const int G = pd.G;
         if constexpr (M == 1) {
             u32x2 B[2];
 #pragma unroll
@@ -479,12 +471,12 @@ void aq_kernel(AqParams P) {
             __builtin_amdgcn_sched_barrier(0);
         }
         if (++ps < pp.s1) return false;
-        epilogue(pp);
-        const Piece n = next_piece(P, wg, pp);
-        if (n.p >= P.ndesc) return true;
-        pp = n;
-        ps = n.s0;
-        load_scales(pp);
+        epilogue(pp, pd);
+        if (pn.p >= P.ndesc) return true;
+        pp = pn;
+        ps = pp.s0;
+        pd = get_desc(P, pp.p);
+        pn = next_piece(P, wg, pp);
         return false;
     };
 

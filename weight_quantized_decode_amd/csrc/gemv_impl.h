@@ -7,8 +7,9 @@
 //   * The activations are the same for all 64 lanes, so they are read with scalar loads into
 //     SGPRs and fed to v_dot2 (two fp16 products accumulated in fp32 per instruction).
 //   * Work unit of a wave = (row group, K-slice).  K is split only as far as needed to give the
-//     GPU enough waves; slices write fp32 partial sums and a second kernel adds them in a fixed
-//     order, so results are the same bits from run to run (no atomics).
+//     GPU enough waves; each slice writes fp32 partial sums and counts itself done on its row
+//     group, and the wave that finishes the last slice adds them in slice order, so results are
+//     the same bits from run to run (the only atomic is the per-row-group arrival counter).
 //   * Codebook formats decode through tables in LDS replicated per lane slot (one copy per bank),
 //     indexed with one v_perm per byte; the block formats decode with AND masks that leave the
 //     codes as fp16 subnormals (code * 2^-24 * 4^j) and apply the -8 / -1 offset through the
@@ -77,6 +78,19 @@ __device__ __forceinline__ uint2 ld8(const uint8_t *p) {
     return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ uint4 ld16(const uint4 *p) { return ld16(reinterpret_cast<const uint8_t *>(p)); }
+// The same pointer in the global address space: atomics through it compile to global_* (a
+// generic pointer gives flat_* instructions, which also count against the LDS/scalar wait
+// counter and so hold up every later LDS wait until they complete).
+template <typename T>
+__device__ __forceinline__ T __attribute__((address_space(1))) *as_global(T *p) {
+    return (T __attribute__((address_space(1))) *)(uintptr_t)p;
+}
+// Workgroup barrier that orders LDS traffic only (global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ void gst(float *p, float v) {
     *(float __attribute__((address_space(1))) *)(uintptr_t)p = v;
 }
@@ -107,17 +121,14 @@ struct FullTag {
 
 template <int FMT>
 struct LdsSize {
-    static constexpr int dwords = (FMT == CB4 || FMT == CB8) ? 256 * kTableCopies
-                                  : (FMT == AQ2X8)          ? 2048
-                                                            : 1;
+    static constexpr int dwords = (FMT == CB4 || FMT == CB8) ? 256 * kTableCopies : 1;
 };
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <int MASK>
 struct LdsSizeMask {
     // tables of the codebook formats; per-wave block sums (WQD_MAX_M x 64 floats) of Q4_0 / TQ2
-    static constexpr int dwords = cmax(cmax(cmax((MASK & (1 << CB4)) ? LdsSize<CB4>::dwords : 1,
-                                                 (MASK & (1 << CB8)) ? LdsSize<CB8>::dwords : 1),
-                                            (MASK & (1 << AQ2X8)) ? LdsSize<AQ2X8>::dwords : 1),
+    static constexpr int dwords = cmax(cmax((MASK & (1 << CB4)) ? LdsSize<CB4>::dwords : 1,
+                                            (MASK & (1 << CB8)) ? LdsSize<CB8>::dwords : 1),
                                        (MASK & ((1 << Q4_0) | (1 << TQ2))) ? kWaves * kMaxM * 64 : 1);
 };
 
@@ -137,9 +148,6 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
                 reinterpret_cast<uint4 *>(lds)[e * (kTableCopies / 4) + jj] = q;
             }
         }
-    } else if constexpr (FMT == AQ2X8) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(D.cbk);
-        for (int i = t; i < 512; i += kThreads) reinterpret_cast<uint4 *>(lds)[i] = ld16(src + i);
     }
 }
 
@@ -348,31 +356,6 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                     acc[m] = fmaf(d, blk, acc[m]);
                 }
             }
-        } else if constexpr (FMT == AQ2X8) {
-            const uint4 *cbv = reinterpret_cast<const uint4 *>(lds);
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const uint32_t c0 = (w4[t] >> (16 * h)) & 0xFFu;
-                    const uint32_t c1 = (w4[t] >> (16 * h + 8)) & 0xFFu;
-                    const uint4 A = cbv[c0], B = cbv[256 + c1];
-                    uint32_t wv[4];
-                    const uint32_t a4[4] = {A.x, A.y, A.z, A.w}, b4[4] = {B.x, B.y, B.z, B.w};
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        h2 sum = as_h2(a4[i]) + as_h2(b4[i]);
-                        wv[i] = __builtin_bit_cast(uint32_t, sum);
-                    }
-#pragma unroll
-                    for (int m = 0; m < M; m++) {
-                        uint32_t xs[4];
-                        load_x<FULL, 4>(xs, xrow[m], c * 64 + (2 * t + h) * 8, D.K);
-#pragma unroll
-                        for (int i = 0; i < 4; i++) acc[m] = dot2(wv[i], xs[i], acc[m]);
-                    }
-                }
-            }
         }
     };
 
@@ -415,11 +398,6 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
         }
     }
 
-    if constexpr (FMT == AQ2X8) {
-        const float sr = half_bits_to_float(gld<uint16_t>(D.scales + 2 * (int64_t)row));
-#pragma unroll
-        for (int m = 0; m < M; m++) acc[m] *= sr;
-    }
     if (D.S == 1) {
         if (row < D.N) {
 #pragma unroll
@@ -434,11 +412,11 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     // complete before the counter is incremented, so whoever sees the final count sees them.
 #pragma unroll
     for (int m = 0; m < M; m++)
-        __hip_atomic_store(D.part + ((int64_t)m * D.S + s) * D.Npad + row, acc[m], __ATOMIC_RELAXED,
+        __hip_atomic_store(as_global(D.part + ((int64_t)m * D.S + s) * D.Npad + row), acc[m], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     int done = 0;
-    if (lane == 0) done = __hip_atomic_fetch_add(D.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) done = __hip_atomic_fetch_add(as_global(D.cnt + g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     done = __builtin_amdgcn_readfirstlane(done);
     if (done == D.S - 1) {
 #pragma unroll
@@ -450,7 +428,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                 float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; j++)
-                    v[j] = (k0 + j < D.S) ? __hip_atomic_load(pm + (int64_t)(k0 + j) * D.Npad, __ATOMIC_RELAXED,
+                    v[j] = (k0 + j < D.S) ? __hip_atomic_load(as_global(pm + (int64_t)(k0 + j) * D.Npad), __ATOMIC_RELAXED,
                                                               __HIP_MEMORY_SCOPE_AGENT)
                                           : 0.f;
 #pragma unroll
@@ -458,7 +436,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
             }
             if (row < D.N) gst(D.y + (int64_t)m * D.ldy + row, sum);
         }
-        if (lane == 0) __hip_atomic_store(D.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(as_global(D.cnt + g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -497,12 +475,11 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
     }
     // All waves take part in the table rebuild (two barriers), after issuing their first loads.
     auto hook = [&]() {
-        if constexpr ((MASK & ((1 << CB4) | (1 << CB8) | (1 << AQ2X8))) != 0) {
+        if constexpr ((MASK & ((1 << CB4) | (1 << CB8))) != 0) {
             if (rebuild) {
                 __syncthreads();
                 if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) build_table<CB4>(lds, D);
                 if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) build_table<CB8>(lds, D);
-                if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) build_table<AQ2X8>(lds, D);
                 __syncthreads();
             }
         }
@@ -513,7 +490,6 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
         if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
         if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds, hook);
         if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds, hook);
-        if constexpr ((MASK & (1 << AQ2X8)) != 0) if (D.fmt == AQ2X8) run_unit<AQ2X8, M>(D, wu, lane, lds, hook);
     } else {
         hook();
     }
@@ -542,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
         while (true) {
             __syncthreads();
             if (threadIdx.x == 0)
-                next_u = nstatic + __hip_atomic_fetch_add(P.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                next_u = nstatic + __hip_atomic_fetch_add(as_global(P.ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             const int u = __builtin_amdgcn_readfirstlane(next_u);
             if (u >= total) break;
@@ -551,10 +527,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
         // Every workgroup has taken its last index once it reaches here; the last one to arrive
         // resets the counters for the next launch on this workspace.
         if (threadIdx.x == 0) {
-            if (__hip_atomic_fetch_add(P.ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            if (__hip_atomic_fetch_add(as_global(P.ctr + 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                 (int)gridDim.x - 1) {
-                __hip_atomic_store(P.ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(P.ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(as_global(P.ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(as_global(P.ctr + 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
