@@ -138,10 +138,11 @@ static int64_t resident_waves(int mask, int64_t M, int cus) {
 
 // Chunks per wave unit for a launch covering `total_cc` chunk-columns (one 1 KiB wave load
 // each): about WQD_UNITS_PER_WAVE units per resident wave, between 8 and WQD_STACK_MIN_CS chunks.
-static int64_t target_cs(int64_t total_cc, int64_t waves) {
+static int64_t target_cs(int64_t total_cc, int64_t waves, int64_t M) {
+    const int64_t cap = M >= WQD_MFMA_MIN_M ? WQD_STACK_MF_CS : WQD_STACK_MIN_CS;
     int64_t cs = total_cc / (waves * WQD_UNITS_PER_WAVE);
     if (cs < 8) cs = 8;
-    if (cs > WQD_STACK_MIN_CS) cs = WQD_STACK_MIN_CS;
+    if (cs > cap) cs = cap;
     return cs;
 }
 
@@ -202,7 +203,7 @@ static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
         P.L = L;
         return P;
     }
-    return plan_cs(fmt, N, K, M, target_cs(L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus)));
+    return plan_cs(fmt, N, K, M, target_cs(L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus), M));
 }
 
 static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
@@ -375,8 +376,8 @@ static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, i
 // region 256-byte aligned.  The slice-counter region is at least kCntRegion bytes and the
 // partial region at least what the largest projection needs alone, so WQD_ORDERED mode uses
 // the same two regions.  Projections are grouped into launches: all CB4/CB8 projections
-// together when both appear, otherwise one launch per format; within a launch, descriptors
-// are in format order.
+// together when both appear and M < WQD_MFMA_MIN_M, otherwise one launch per format; within a
+// launch, descriptors are in format order.
 struct LaunchGroup {
     int mask = 0;
     int first = 0, count = 0;  // range in StackPlan::descs (or StackPlan::aqdescs)
@@ -404,7 +405,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
     const bool has_aq = (present & fmt_bit(AQ2X8)) != 0;
     present &= ~fmt_bit(AQ2X8);
     std::vector<int> masks;
-    if ((present & kMaskCB48) == kMaskCB48) {
+    if ((present & kMaskCB48) == kMaskCB48 && M < WQD_MFMA_MIN_M) {
         masks.push_back(kMaskCB48);
         present &= ~kMaskCB48;
     }
@@ -423,7 +424,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
             Layout L = make_layout(p[i].fmt, p[i].N, p[i].K);
             total_cc += L.RG * L.C;
         }
-        const int64_t cs_target = target_cs(total_cc, resident_waves(mask, M, cus));
+        const int64_t cs_target = target_cs(total_cc, resident_waves(mask, M, cus), M);
         for (int fmt = 1; fmt <= 5; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = 0; i < count; i++) {

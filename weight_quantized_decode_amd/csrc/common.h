@@ -37,6 +37,23 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #ifndef WQD_WG_PER_CU
 #define WQD_WG_PER_CU 2
 #endif
+// Smallest M whose codebook-format kernels multiply on the matrix cores (v_mfma_f32_4x4x4_16b_f16)
+// instead of v_dot2; below it the VALU path stays (it is HBM-bound there).
+#ifndef WQD_MFMA_MIN_M
+#define WQD_MFMA_MIN_M 2
+#endif
+#ifndef WQD_MF_U
+#define WQD_MF_U 4       // chunks per load group of the matrix-core instances
+#endif
+#ifndef WQD_MF_U_WIDE
+#define WQD_MF_U_WIDE 4  // the same for CB4 at M > 4
+#endif
+#ifndef WQD_STACK_MF_CS
+#define WQD_STACK_MF_CS 128  // largest stack K-slice (chunks) of the matrix-core instances
+#endif
+#ifndef WQD_MFMA_WAVES_PER_EU
+#define WQD_MFMA_WAVES_PER_EU 4
+#endif
 constexpr int kMaxM = 8;                  // largest M (activation rows) per call
 constexpr int kWaves = WQD_WAVES;         // waves per workgroup
 constexpr int kThreads = kWaves * 64;

@@ -95,6 +95,36 @@ __device__ __forceinline__ void gst(float *p, float v) {
     *(float __attribute__((address_space(1))) *)(uintptr_t)p = v;
 }
 
+// Compile-time loop: f(Int<0>{}), ..., f(Int<N-1>{}), so the body can use the index where a
+// constant expression is required (an MFMA operand-broadcast field).
+template <int I>
+struct Int {
+    static constexpr int value = I;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(Int<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// Small-M matrix-core step.  v_mfma_f32_4x4x4_16b_f16 computes 16 independent 4x4x4 products,
+// block b on lanes 4b..4b+3: D_b[i][j] += sum_k A_b[i][k] B_b[k][j], lane 4b+i holding row i of A_b
+// and lane 4b+j column j of B_b (4 fp16 values each), and register v of lane 4b+j receiving
+// D_b[v][j].  Here B is 4 consecutive decoded weights of the lane's own row and, with the A
+// operand of block WIN broadcast to all 16 blocks, A[i][k] is activation row i at those 4 k: each
+// lane gets the partial dot products of its row with 4 activation rows.  A window register pair
+// holds 16 such 4-element k-blocks (64 consecutive k) of 4 activation rows: lane 4b+i holds row i,
+// elements 4b..4b+3 of the window.
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int WIN>
+__device__ __forceinline__ f32x4 mfma_xw(u32x2 xwin, u32x2 w, f32x4 d) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h16x4, xwin), __builtin_bit_cast(h16x4, w), d, 4,
+                                              WIN, 0);
+}
+
 // Uniform read of NW consecutive x dwords (2*NW fp16 values starting at element k) of one row.
 // FULL: the whole range lies inside K (scalar loads).  Otherwise elements at or beyond K read as
 // zero (only a partial last chunk takes that path).
@@ -143,6 +173,9 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
             if constexpr (FMT == CB4) v = uint32_t(gld<uint16_t>(D.cbk + (e & 15))) | (uint32_t(gld<uint16_t>(D.cbk + (e >> 4))) << 16);
             else v = uint32_t(gld<uint16_t>(D.cbk + e));
             uint4 q = make_uint4(v, v, v, v);
+            // not unrolled: unrolled, the 16 store addresses are hoisted out of the persistent
+            // loop and held in registers for the whole kernel
+#pragma unroll 1
             for (int j = 0; j < kTableCopies / 4; j++) {
                 int jj = (j + e) % (kTableCopies / 4);
                 reinterpret_cast<uint4 *>(lds)[e * (kTableCopies / 4) + jj] = q;
@@ -175,12 +208,53 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
     // row, if this unit owns it, is handled after the pipelined loop.
     const int cfe = min(ce, D.C_full);
-    auto load_group = [&](uint4 (&buf)[kU], int c) {
+
+    // Matrix-core path (codebook formats, M >= WQD_MFMA_MIN_M): the whole chunks are multiplied by
+    // v_mfma_f32_4x4x4_16b_f16 into MFA (activation rows 4h..4h+3 in MFA[.][h]).  With H = 1 there
+    // are two accumulator chains, so consecutive MFMAs do not wait for each other; with H = 2 the
+    // two activation-row quads already alternate.  A load group of U chunks spans NWIN
+    // activation windows of 64 k, loaded with the group's codes (in-order completion then makes
+    // one wait cover both).  The matrix-core path takes longer per chunk, so it loads larger
+    // groups (more bytes in flight per wave while a group is processed).
+    constexpr bool MF = (M >= WQD_MFMA_MIN_M) && (FMT == CB4 || FMT == CB8);
+    constexpr int WPC = (FMT == CB4) ? 32 : 16;  // weights per chunk (codebook formats)
+    constexpr int CPW = 64 / WPC;                // chunks per window
+    constexpr int H = MF ? (M + 3) / 4 : 1;
+    // CB4 with two activation quads needs twice the window registers: a shorter group keeps it
+    // within 128 VGPRs
+    constexpr int U = MF ? ((FMT == CB4 && H > 1) ? WQD_MF_U_WIDE : WQD_MF_U) : kU;
+    static_assert(!MF || U % CPW == 0, "a load group holds whole activation windows");
+    constexpr int NWIN = MF ? U / CPW : 1;
+    constexpr int NCH = (H == 1) ? 2 : 1;
+    const uint16_t *xw[H];  // lane 4b+i: activation row 4h+i (clamped to M-1), at element 4b
 #pragma unroll
-        for (int j = 0; j < kU; j++) {
+    for (int h = 0; h < H; h++) xw[h] = D.x + (int64_t)min(4 * h + (lane & 3), M - 1) * D.ldx + 4 * (lane >> 2);
+    const int kwin_max = cfe * WPC - 4 - 4 * (lane >> 2);  // window loads stay below K
+    auto load_win = [&](u32x2 (&X)[NWIN][H], int c) {
+        if constexpr (MF) {
+#pragma unroll
+            for (int w = 0; w < NWIN; w++)
+#pragma unroll
+                for (int h = 0; h < H; h++) {
+                    const uint16_t *p = xw[h] + min(c * WPC + 64 * w, kwin_max);
+                    X[w][h] = u32x2{gld<uint32_t>(p), gld<uint32_t>(p + 2)};
+                }
+        }
+    };
+    u32x2 XA[NWIN][H], XB[NWIN][H];
+    f32x4 MFA[NCH][H];
+#pragma unroll
+    for (int q = 0; q < NCH; q++)
+#pragma unroll
+        for (int h = 0; h < H; h++) MFA[q][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_group = [&](uint4 (&buf)[U], u32x2 (&X)[NWIN][H], int c) {
+#pragma unroll
+        for (int j = 0; j < U; j++) {
             const int cc = min(c + j, cfe - 1);
             buf[j] = ld16_stream(cptr + (int64_t)cc * 1024);
         }
+        load_win(X, c);
     };
     // Scale quad of the chunk group starting at c (block formats only).
     auto load_sq = [&](int c) -> uint2 {
@@ -191,11 +265,11 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
             return make_uint2(0, 0);
         }
     };
-    uint4 A[kU], B[kU];
+    uint4 A[U], B[U];
     uint2 sqA = make_uint2(0, 0), sqB = make_uint2(0, 0);
     if (cb < cfe) {
         sqA = load_sq(cb);
-        load_group(A, cb);
+        load_group(A, XA, cb);
     }
     hook();
 
@@ -359,43 +433,111 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
         }
     };
 
-    auto proc_group = [&](const uint4 (&buf)[kU], int c, uint2 sq) {
+    // Matrix-core form of one whole chunk, j-th of its group (static: it fixes the window and the
+    // 4-k block of every MFMA).  Chunk j of a group at chunk c covers k = (c+j)*WPC ..; window w
+    // starts at k = c*WPC + 64w, so chunk j lies in window j / CPW at block (j % CPW) * WPC / 4.
+    auto process_mf = [&](auto jc, const uint4 &v, const u32x2 (&X)[NWIN][H]) {
+        constexpr int j = decltype(jc)::value;
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        static_for<4>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            if constexpr (FMT == CB4) {
+                // word t: byte i -> weights 8t+2i, 8t+2i+1; pair p of bytes -> weights 8t+4p..+3
+                uint32_t e[4];
 #pragma unroll
-        for (int j = 0; j < kU; j++)
-            if (c + j < cfe) process(FullTag<true>{}, buf[j], c + j, sq);
+                for (int i = 0; i < 4; i++)
+                    e[i] = lds_word(lds, __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(i) << 8)));
+                static_for<2>([&](auto pc) {
+                    constexpr int p = decltype(pc)::value;
+                    constexpr int win = j / CPW, blk = 8 * (j % CPW) + 2 * t + p;
+#pragma unroll
+                    for (int h = 0; h < H; h++) MFA[p % NCH][h] = mfma_xw<blk>(X[win][h], u32x2{e[2 * p], e[2 * p + 1]}, MFA[p % NCH][h]);
+                });
+            } else {
+                // word t: weights 4t..4t+3 of the chunk
+                uint32_t pr[2];
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    uint32_t a0 = __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(2 * i) << 8));
+                    uint32_t a1 = __builtin_amdgcn_perm(w4[t], loff, 0x0c0c0400u + (uint32_t(2 * i + 1) << 8));
+                    pr[i] = __builtin_amdgcn_perm(lds_word(lds, a1), lds_word(lds, a0), 0x05040100u);
+                }
+                constexpr int win = j / CPW, blk = 4 * (j % CPW) + t;
+#pragma unroll
+                for (int h = 0; h < H; h++) MFA[t % NCH][h] = mfma_xw<blk>(X[win][h], u32x2{pr[0], pr[1]}, MFA[t % NCH][h]);
+            }
+        });
+    };
+
+    auto proc_group = [&](const uint4 (&buf)[U], const u32x2 (&X)[NWIN][H], int c, uint2 sq) {
+        if constexpr (MF) {
+            static_for<U>([&](auto jc) {
+                if (c + decltype(jc)::value < cfe) process_mf(jc, buf[decltype(jc)::value], X);
+            });
+        } else {
+#pragma unroll
+            for (int j = 0; j < U; j++)
+                if (c + j < cfe) process(FullTag<true>{}, buf[j], c + j, sq);
+        }
     };
 
     // Double-buffered pipeline: the loads of group g+1 are in flight while group g is decoded.
     // Each branch below is straight-line code, so the compiler can wait for exactly the older
-    // group (vmcnt = kU) instead of draining every load.
+    // group (vmcnt = U) instead of draining every load.
     if (cb < cfe) {
-        const int ng = (cfe - cb + kU - 1) / kU;
+        const int ng = (cfe - cb + U - 1) / U;
         int gi = 0;
         while (true) {
-            const int c = cb + gi * kU;
+            const int c = cb + gi * U;
             if (gi + 1 >= ng) {
-                proc_group(A, c, sqA);
+                proc_group(A, XA, c, sqA);
                 break;
             }
-            sqB = load_sq(c + kU);
-            load_group(B, c + kU);
-            proc_group(A, c, sqA);
+            sqB = load_sq(c + U);
+            load_group(B, XB, c + U);
+            proc_group(A, XA, c, sqA);
             gi++;
             if (gi + 1 >= ng) {
-                proc_group(B, c + kU, sqB);
+                proc_group(B, XB, c + U, sqB);
                 break;
             }
-            sqA = load_sq(c + 2 * kU);
-            load_group(A, c + 2 * kU);
-            proc_group(B, c + kU, sqB);
+            sqA = load_sq(c + 2 * U);
+            load_group(A, XA, c + 2 * U);
+            proc_group(B, XB, c + U, sqB);
             gi++;
         }
     }
-    if constexpr (FMT != Q4_0 && FMT != TQ2) {
+    if constexpr (MF) {
+        // The partial last chunk (when this unit owns it): its window reads zero at k >= K, so
+        // the zero padding of the codes (which decodes to a codebook entry) adds nothing.
+        for (int c = max(cb, cfe); c < ce; c++) {
+            const uint4 v = ld16(cptr + (int64_t)c * 1024);
+            u32x2 X[NWIN][H];
+            const int k0 = c * WPC + 4 * (lane >> 2);
+#pragma unroll
+            for (int h = 0; h < H; h++) {
+                const uint16_t *p = D.x + (int64_t)min(4 * h + (lane & 3), M - 1) * D.ldx;
+                uint32_t e[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) e[i] = (k0 + i < D.K) ? uint32_t(gld<uint16_t>(p + k0 + i)) : 0u;
+#pragma unroll
+                for (int w = 0; w < NWIN; w++) X[w][h] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            }
+            process_mf(Int<0>{}, v, X);
+        }
+    } else if constexpr (FMT != Q4_0 && FMT != TQ2) {
         for (int c = max(cb, cfe); c < ce; c++) {
             const uint4 v = ld16(cptr + (int64_t)c * 1024);
             process(FullTag<false>{}, v, c, make_uint2(0, 0));
         }
+    }
+    if constexpr (MF) {
+        // register v of MFA[.][h] is activation row 4h+v of this lane's row
+#pragma unroll
+        for (int h = 0; h < H; h++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                if (4 * h + v < M) acc[4 * h + v] += (NCH == 2) ? MFA[0][h][v] + MFA[NCH - 1][h][v] : MFA[0][h][v];
     }
 
     if (D.S == 1) {
@@ -486,27 +628,43 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
     };
     const int wu = (u - D.wgu_begin) * kWaves + wid;
     if (wu < D.wu_count) {
-        if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds, hook);
-        if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
-        if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds, hook);
-        if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds, hook);
+        if constexpr (MASK == kMaskCB48) {
+            // two formats: one branch or the other (not two independent ifs, which let
+            // the compiler keep values of both bodies live at once)
+            if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
+            else run_unit<CB8, M>(D, wu, lane, lds, hook);
+        } else {
+            if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds, hook);
+            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
+            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds, hook);
+            if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds, hook);
+        }
     } else {
         hook();
     }
 }
+
+// Waves per SIMD a kernel instance is compiled for: the matrix-core instances (codebook formats
+// only, M >= WQD_MFMA_MIN_M) are held to 128 VGPRs, so two 8-wave workgroups share a CU.
+template <int MASK, int M>
+constexpr int kMinWavesPerEU =
+    (M >= WQD_MFMA_MIN_M && (MASK & ~kMaskCB48) == 0) ? WQD_MFMA_WAVES_PER_EU : 1;
 
 // Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
 // [0, pool_begin) are split into equal contiguous ranges, one per workgroup; the rest are handed
 // out one by one from a device-wide counter to whichever workgroup is free, which evens out the
 // finish times (workgroups on different XCDs stream at different speeds).
 template <int MASK, int M>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<MASK, M>))) void gemv_kernel(GemvParams P) {
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
     __shared__ int next_u;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int total = P.total_wgu;
-    const int nstatic = P.ctr ? P.pool_begin : total;
+    // The dynamic tail is compiled in only when WQD_POOL_PERCENT > 0 (a second copy of the unit
+    // loop costs registers in every instance).
+    constexpr bool kPool = WQD_POOL_PERCENT > 0;
+    const int nstatic = (kPool && P.ctr) ? P.pool_begin : total;
     const int per = nstatic / (int)gridDim.x, rem = nstatic % (int)gridDim.x;
     const int b = blockIdx.x;
     const int u0 = b * per + min(b, rem);
@@ -514,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams P) {
     int cur = -1;
     Desc D = P.d0;
     for (int u = u0; u < u1; u++) run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
-    if (P.ctr) {
+    if (kPool && P.ctr) {
         while (true) {
             __syncthreads();
             if (threadIdx.x == 0)
