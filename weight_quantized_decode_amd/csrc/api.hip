@@ -137,9 +137,9 @@ static int64_t resident_waves(int mask, int64_t M, int cus) {
 }
 
 // Chunks per wave unit for a launch covering `total_cc` chunk-columns (one 1 KiB wave load
-// each): about WQD_UNITS_PER_WAVE units per resident wave, between 8 and WQD_STACK_MIN_CS chunks.
+// each): about WQD_UNITS_PER_WAVE units per resident wave, between 8 and WQD_STACK_MAX_CS chunks.
 static int64_t target_cs(int64_t total_cc, int64_t waves, int64_t M) {
-    const int64_t cap = M >= WQD_MFMA_MIN_M ? WQD_STACK_MF_CS : WQD_STACK_MIN_CS;
+    const int64_t cap = M >= WQD_MFMA_MIN_M ? WQD_STACK_MF_CS : WQD_STACK_MAX_CS;
     int64_t cs = total_cc / (waves * WQD_UNITS_PER_WAVE);
     if (cs < 8) cs = 8;
     if (cs > cap) cs = cap;
@@ -380,6 +380,7 @@ static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, i
 // launch, descriptors are in format order.
 struct LaunchGroup {
     int mask = 0;
+    int64_t cs = 0;            // K-slice target of the group (chunks)
     int first = 0, count = 0;  // range in StackPlan::descs (or StackPlan::aqdescs)
     int total_wgu = 0;
     bool aq = false;           // the AQ2X8 launch
@@ -415,6 +416,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
     // plans: the K-slice size of a launch group follows its total work
     std::vector<Plan> plans(count);
     std::vector<int> order, group_of;
+    std::vector<int64_t> group_cs(masks.size(), 0);
     int64_t cnt_total = 0, part_total = 0, single_part = 0;
     for (size_t gi = 0; gi < masks.size(); gi++) {
         const int mask = masks[gi];
@@ -425,6 +427,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
             total_cc += L.RG * L.C;
         }
         const int64_t cs_target = target_cs(total_cc, resident_waves(mask, M, cus), M);
+        group_cs[gi] = cs_target;
         for (int fmt = 1; fmt <= 5; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = 0; i < count; i++) {
@@ -484,6 +487,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *w
         }
         G.count = int(SP.descs.size()) - G.first;
         G.total_wgu = wgu;
+        G.cs = group_cs[gi];
         SP.groups.push_back(G);
     }
     if (!aqplans.empty()) {
@@ -672,7 +676,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         GP.descs = dtab + G.first;
         GP.ndesc = G.count;
         GP.total_wgu = G.total_wgu;
-        if (WQD_POOL_PERCENT > 0) {
+        // The dynamic tail pays a barrier, an atomic and a cold load pipeline per unit it hands
+        // out: only units of long slices amortize that.
+        if (WQD_POOL_PERCENT > 0 && G.cs >= WQD_POOL_MIN_CS) {
             GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr) + 2 * gi;
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }

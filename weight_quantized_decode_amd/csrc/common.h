@@ -19,8 +19,8 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #ifndef WQD_TABLE_COPIES
 #define WQD_TABLE_COPIES 64
 #endif
-#ifndef WQD_STACK_MIN_CS
-#define WQD_STACK_MIN_CS 64
+#ifndef WQD_STACK_MAX_CS
+#define WQD_STACK_MAX_CS 128  // largest stack K-slice (chunks) of the vector-ALU instances
 #endif
 #ifndef WQD_UNITS_PER_WAVE
 #define WQD_UNITS_PER_WAVE 4
@@ -32,7 +32,10 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #define WQD_NT_CODES 1
 #endif
 #ifndef WQD_POOL_PERCENT
-#define WQD_POOL_PERCENT 0
+#define WQD_POOL_PERCENT 15  // share of workgroup units handed out dynamically (the tail)
+#endif
+#ifndef WQD_POOL_MIN_CS
+#define WQD_POOL_MIN_CS 64  // smallest K-slice (chunks) of a launch that uses the dynamic tail
 #endif
 #ifndef WQD_WG_PER_CU
 #define WQD_WG_PER_CU 2
