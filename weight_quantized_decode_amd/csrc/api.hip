@@ -253,7 +253,7 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
 // model per piece, in tile loads (KiB): ns * (nrb + table build) plus a fixed charge for a
 // K-split (its partial round trip); the shape with the cheapest busiest workgroup wins.
 // ------------------------------------------------------------------------------------------
-static int aq_rw_max(int64_t M) { return M == 1 ? 8 : 2; }
+static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : 2; }
 
 static int64_t aq_nwg(int64_t M, int cus) {
     AqFn fn = aq_fn(int(M), aq_rw_max(M));
@@ -296,7 +296,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
         }
     }
     A.RB = RB;
-    A.RW = (M == 1) ? 2 : 1;  // M = 1 kernels exist for RW = 2, 4, 8; M > 1 for 1, 2
+    A.RW = 1;  // M = 1 kernels exist for RW = 1, 2, 4 (and 8 with 8 waves); M > 1 for 1, 2
     while (A.RW * W < A.nrb) A.RW *= 2;
     A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 8, 256) : 0;
     return A;

@@ -106,9 +106,18 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 // row, and the workgroup running split b-1 of a chunk adds the b partials of its rows at the end
 // of its work.
 // ------------------------------------------------------------------------------------------
-// Waves per AQ2X8 workgroup: 8 for M = 1 (one workgroup per CU, 256 VGPRs per wave for a deep
-// load ring), 16 for M > 1.  A piece has at most waves * RW row blocks.
-__host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? 8 : 16; }
+// Waves per AQ2X8 workgroup (one workgroup per CU at M = 1, whose table fills the LDS): 8 or 16
+// for M = 1 (WQD_AQ1_WAVES), 16 for M > 1.  A piece has at most waves * RW row blocks, 64 at
+// M = 1.
+#ifndef WQD_AQ1_WAVES
+#define WQD_AQ1_WAVES 8
+#endif
+__host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? WQD_AQ1_WAVES : 16; }
+#ifndef WQD_AQ1_RW_MAX
+#define WQD_AQ1_RW_MAX (64 / WQD_AQ1_WAVES)  // most 8-row blocks per wave per slice at M = 1
+#endif
+// Waves per SIMD an AQ2X8 instance is compiled for (its VGPR budget).
+__host__ __device__ constexpr int aq_waves_per_simd(int M) { return M == 1 ? WQD_AQ1_WAVES / 4 : 4; }
 constexpr uint32_t kAqTag = 0x7FA5A5A5u;     // high word of a written partial slot (an sNaN,
                                              // which no float arithmetic produces)
 

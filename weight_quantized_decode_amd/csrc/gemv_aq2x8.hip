@@ -8,13 +8,16 @@
 // a per-group lookup table built from the activations, after which only the codes are read.
 //
 // M = 1, lookup tables:
-//   * For one K-slice of 64 groups the workgroup builds T in LDS, fp32, as dword
-//     ((b*256 + c)*64 + g): 128 KiB.  T is the product C_b (256 x 8) . X (8 x 64), X[j][g] =
-//     x[8g+j]; each of the 16 waves computes one (codebook, 32 codes) block with two 32x32x8 f16
-//     MFMAs (exact fp16 products, fp32 sums) and, after a permlane32 swap, writes whole 64-group
-//     rows of the table.
-//   * Lane g reads only bank g, so the lookups never conflict: two LDS reads and two fp32 adds per
-//     8 weights, the address made by one v_perm from the code byte.
+//   * For one K-slice of 64 groups the workgroup builds T in LDS as dword (c*64 + g) holding the
+//     pair (T_0,g[c], T_1,g[c]) in fp16: 64 KiB.  T is the product C_b (256 x 8) . X (8 x 64),
+//     X[j][g] = x[8g+j]; each of the 8 waves computes the 32 codes of one block for both
+//     codebooks with four 32x32x8 f16 MFMAs (exact fp16 products, fp32 sums), rounds them to
+//     fp16 pairs and, after a permlane32 swap, writes whole 64-group rows of the table.
+//   * Two tables alternate: the table of the next slice is built while the current one is read,
+//     with one workgroup barrier per slice.
+//   * Lane g reads only bank g, so the lookups never conflict: two LDS reads per 8 weights (the
+//     addresses made by one v_perm each from the code bytes) and one v_fma_mix that adds the low
+//     fp16 half of one word to the high half of the other in fp32.
 //   * The 64 lanes' terms of a row are summed by a transposed butterfly in a fixed order: per tile
 //     the permlane32 and permlane16 swap stages fold 8 rows x 64 lanes into 2 values per lane,
 //     which accumulate over the slices of a piece; the DPP stages finish the sum once per piece.
@@ -153,7 +156,7 @@ struct Loader {
     const uint8_t *base;   // code plane (wave-uniform; the lane's 16 bytes are added at the load)
     int64_t s_stride;      // bytes between slices (R8 = Npad/8 KiB)
     int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
-    int rb[RW];            // this wave's row blocks, clamped into the piece
+    int rb[RW];            // this wave's row blocks; -1: none (the piece has fewer than W * RW)
     const uint16_t *x, *cbk;  // operands of the slice's table / activation stage
     int64_t ldx;
     int G;
@@ -176,19 +179,28 @@ struct Loader {
         s_max = D.KS - 1;
         rb_max = D.Npad / 8 - 1;
 #pragma unroll
-        for (int i = 0; i < RW; i++) rb[i] = min(min(n.rb0 + wid + W * i, n.rb1 - 1), rb_max);
+        for (int i = 0; i < RW; i++) {
+            const int r = n.rb0 + wid + W * i;
+            rb[i] = r < n.rb1 ? min(r, rb_max) : -1;
+        }
     }
+    // A missing tile still takes its place in the ring (every load stays unconditional): it
+    // reads 1 KiB of the codebooks, which the table build keeps in L2, instead of HBM.
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        return base + int64_t(min(s, s_max)) * s_stride + int64_t(rb[i]) * 1024;
+        return rb[i] < 0 ? reinterpret_cast<const uint8_t *>(cbk)
+                         : base + int64_t(min(s, s_max)) * s_stride + int64_t(rb[i]) * 1024;
     }
     // After the last tile of a slice: step to the next slice (or piece).  Past the end of the
-    // list the loader keeps re-reading the last tile, so the ring never has a hole.
+    // list the loader keeps issuing loads of the L2-resident codebooks, so the ring never has a
+    // hole.
     __device__ __forceinline__ void step(const AqParams &P, int wg, int wid, int lane) {
         if (done) return;
         if (++s < q.s1) return;
         if (qn.p >= P.ndesc) {
             done = true;
             s = q.s1 - 1;
+#pragma unroll
+            for (int i = 0; i < RW; i++) rb[i] = -1;
         } else {
             setup(P, qn, wg, wid, lane);
         }
@@ -262,12 +274,24 @@ struct LdsWords {
 struct SliceOps {
     u32x2 B[2], A[2];
     u32x4 X, C;
+    int gval;  // groups of the slice inside K (M = 1: the table masks the rest)
 };
+
+// fp32 T_0 (low half of d0) + T_1 (high half of d1), both fp16 table entries.
+__device__ __forceinline__ float add_lo_hi(uint32_t d0, uint32_t d1) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
+    return r;
+}
+// fp16 pair (a, b), round to nearest even.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
+}
 
 // M = 1: the 128 KiB table allows one workgroup per CU, i.e. 2 waves per SIMD, so each wave may
 // use 256 VGPRs (the compiler would otherwise aim for more waves than can ever be resident).
 template <int M, int RW>
-__global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, M == 1 ? 2 : 4)))
+__global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, aq_waves_per_simd(M))))
 void aq_kernel(AqParams P) {
     constexpr int W = aq_waves(M);  // waves per workgroup
     __shared__ uint32_t lds[LdsWords<M>::value];
@@ -287,24 +311,23 @@ void aq_kernel(AqParams P) {
     ld.done = false;
     ld.setup(P, pp, wg, wid, lane);
 
-    // M = 1 table blocks of this wave: codebook bsel, code blocks cblk0 .. cblk0 + 32/W - 1
-    // (32 codes each; 16 blocks over W waves).
-    constexpr int NBLK = 16 / W;  // blocks per wave: 2 (M = 1, W = 8)
-    const int bsel = (wid * NBLK) >> 3, cblk0 = (wid * NBLK) & 7;
+    // M = 1 table block of this wave: codes 32*wid .. 32*wid + 31 of both codebooks.
+    static_assert(M != 1 || W == 8, "eight waves build the 8 code blocks of a table");
 
     // Issue the loads of the loader's slice: operands first, then the RW tiles; step the loader.
     // Every load is unconditional with a clamped address (a load under a lane condition makes
     // the compiler wait for it at once); groups past G are zeroed where the operands are used.
     auto load_slice = [&](u32x4 (&t)[RW], SliceOps &o) __attribute__((always_inline)) {
         if constexpr (M == 1) {
+            o.gval = ld.G - ld.s * 64;
 #pragma unroll
             for (int gb = 0; gb < 2; gb++) {
                 const int g = min(ld.s * 64 + gb * 32 + (lane & 31), ld.G - 1);
                 o.B[gb] = gld<u32x2>(ld.x + int64_t(g) * 8 + 4 * (lane >> 5));
             }
 #pragma unroll
-            for (int h = 0; h < NBLK; h++)
-                o.A[h] = gld<u32x2>(ld.cbk + (int64_t(bsel) * 256 + (cblk0 + h) * 32 + (lane & 31)) * 8 + 4 * (lane >> 5));
+            for (int b = 0; b < 2; b++)
+                o.A[b] = gld<u32x2>(ld.cbk + (int64_t(b) * 256 + wid * 32 + (lane & 31)) * 8 + 4 * (lane >> 5));
         } else {
             const int g = min(ld.s * 64 + lane, ld.G - 1);
             o.X = gld<u32x4>(ld.x + int64_t(min(wid, M - 1)) * ld.ldx + int64_t(g) * 8);
@@ -321,9 +344,11 @@ void aq_kernel(AqParams P) {
         ld.step(P, wg, wid, lane);
     };
     // Wait for a slice's tiles and operands: an empty asm statement that reads them.
-    auto settle = [&](u32x4 (&t)[RW], SliceOps &o) __attribute__((always_inline)) {
+    auto settle_tiles = [&](u32x4 (&t)[RW]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) __asm__ volatile("" ::"v"(t[i]));
+    };
+    auto settle_ops = [&](SliceOps &o) __attribute__((always_inline)) {
         if constexpr (M == 1) {
             __asm__ volatile("" ::"v"(o.B[0]), "v"(o.B[1]), "v"(o.A[0]), "v"(o.A[1]));
         } else {
@@ -340,7 +365,7 @@ void aq_kernel(AqParams P) {
         for (int r = 0; r < NACC; r++) acc[i][r] = 0.f;
 
     u32x4 Xc[M];  // M > 1: this lane's group activations for the current slice
-    const uint32_t lk = (uint32_t(lane) << 2) | (1u << 16);
+    int tb = 0;   // M = 1: table buffer of the slice being processed
 
     // Piece epilogue: row sums -> y (b == 1) or this split's tagged partial slots.
     auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
@@ -372,34 +397,48 @@ void aq_kernel(AqParams P) {
         }
     };
 
-    // Start of a slice: build its table (M = 1) or stage its activations (M > 1).
+    // M = 1: build the table of a slice (its operands o) into table buffer tb.
+    auto build_table = [&](const SliceOps &o, int tb) __attribute__((always_inline)) {
+        u32x2 B[2];
+#pragma unroll
+        for (int gb = 0; gb < 2; gb++) {
+            const bool in = gb * 32 + (lane & 31) < o.gval;  // groups past K read as zero
+            B[gb] = in ? o.B[gb] : u32x2{0u, 0u};
+        }
+        const f32x16 zero = {};
+        const h4 B0 = __builtin_bit_cast(h4, B[0]), B1 = __builtin_bit_cast(h4, B[1]);
+        // codebook 0 first, rounded at once (fewer live registers): q[v] = (T_0 of group half 0,
+        // T_0 of group half 1)
+        uint32_t q[16];
+        {
+            const f32x16 d0 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[0]), B0, zero, 0, 0, 0);
+            const f32x16 d1 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[0]), B1, zero, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; v++) q[v] = pack_h2(d0[v], d1[v]);
+        }
+        const f32x16 e0 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[1]), B0, zero, 0, 0, 0);
+        const f32x16 e1 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[1]), B1, zero, 0, 0, 0);
+        uint32_t *tab = lds + tb * (256 * 64);
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            // lane l, register v of a 32x32x8 result: code row 8(v/4) + 4(l/32) + v%4 of the
+            // block, group l%32 of its half.  p0 / p1: the (T_0, T_1) pairs of group half 0 / 1;
+            // after the swap sw[0] holds code row 8(v/4) + v%4 for all 64 groups (lane = group),
+            // sw[1] the row 4 further on.
+            const uint32_t r = pack_h2(e0[v], e1[v]);
+            const uint32_t p0 = __builtin_amdgcn_perm(r, q[v], 0x05040100u);
+            const uint32_t p1 = __builtin_amdgcn_perm(r, q[v], 0x07060302u);
+            const auto sw = __builtin_amdgcn_permlane32_swap(p0, p1, false, false);
+            const int c = wid * 32 + 8 * (v >> 2) + (v & 3);
+            tab[c * 64 + lane] = sw[0];
+            tab[(c + 4) * 64 + lane] = sw[1];
+        }
+    };
+
+    // M > 1: stage the activations of a slice.
     auto slice_start = [&](const SliceOps &o) __attribute__((always_inline)) {
         const int G = pd.G;
         if constexpr (M == 1) {
-            u32x2 B[2];
-#pragma unroll
-            for (int gb = 0; gb < 2; gb++) {
-                const bool in = ps * 64 + gb * 32 + (lane & 31) < G;
-                B[gb] = in ? o.B[gb] : u32x2{0u, 0u};
-            }
-            lds_barrier();  // every wave is done with the previous table
-            const f32x16 zero = {};
-#pragma unroll
-            for (int h = 0; h < NBLK; h++) {
-                const h4 A = __builtin_bit_cast(h4, o.A[h]);
-                const f32x16 d0 = __builtin_amdgcn_mfma_f32_32x32x8f16(A, __builtin_bit_cast(h4, B[0]), zero, 0, 0, 0);
-                const f32x16 d1 = __builtin_amdgcn_mfma_f32_32x32x8f16(A, __builtin_bit_cast(h4, B[1]), zero, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    // d0: groups 0-31, d1: groups 32-63; after the swap sw[0] holds code row
-                    // 8(v/4) + v%4 of the block for all 64 groups, sw[1] the row 4 further on.
-                    const auto sw = __builtin_amdgcn_permlane32_swap(u32(d0[v]), u32(d1[v]), false, false);
-                    const int c = (cblk0 + h) * 32 + 8 * (v >> 2) + (v & 3);
-                    lds[(bsel * 256 + c) * 64 + lane] = sw[0];
-                    lds[(bsel * 256 + c + 4) * 64 + lane] = sw[1];
-                }
-            }
-            lds_barrier();
         } else {
             const bool in = ps * 64 + lane < G;
             const u32x4 X = in ? o.X : u32x4{0u, 0u, 0u, 0u};
@@ -414,19 +453,20 @@ void aq_kernel(AqParams P) {
         }
     };
 
-    // One tile: this lane's group for 8 rows of row block i.
-    auto process = [&](const u32x4 &v, float (&a)[NACC]) __attribute__((always_inline)) {
+    // One tile: this lane's group for 8 rows of row block i (M = 1: lk selects the table).
+    auto process = [&](const u32x4 &v, float (&a)[NACC], uint32_t lk) __attribute__((always_inline)) {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
         if constexpr (M == 1) {
             float v[8];
 #pragma unroll
             for (int t = 0; t < 4; t++) {  // word t: (c0, c1) of rows 2t and 2t+1
-                const uint32_t a0 = __builtin_amdgcn_perm(w4[t], lk, 0x0c0c0400u);
+                // address (tb*256 + c)*256 + 4*lane: byte 0 from lk, byte 1 the code, byte 2 tb
+                const uint32_t a0 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020400u);
                 const uint32_t a1 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020500u);
-                const uint32_t a2 = __builtin_amdgcn_perm(w4[t], lk, 0x0c0c0600u);
+                const uint32_t a2 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020600u);
                 const uint32_t a3 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020700u);
-                v[2 * t] = f32(lds_word(lds, a0)) + f32(lds_word(lds, a1));
-                v[2 * t + 1] = f32(lds_word(lds, a2)) + f32(lds_word(lds, a3));
+                v[2 * t] = add_lo_hi(lds_word(lds, a0), lds_word(lds, a1));
+                v[2 * t + 1] = add_lo_hi(lds_word(lds, a2), lds_word(lds, a3));
             }
             float w[2];
             fold_rows8(v, w);
@@ -460,15 +500,30 @@ void aq_kernel(AqParams P) {
 
     // One slice: wait for it, prefetch the one two ahead, build, process, advance.  Returns true
     // after the last slice of the last piece.
-    auto step = [&](u32x4 (&cur)[RW], SliceOps &oc, u32x4 (&nxt)[RW], SliceOps &on) __attribute__((always_inline)) -> bool {
-        settle(cur, oc);
+    // M = 1: the operands of the slice after it (oa) are waited for too, and its table is built
+    // into the other buffer before this slice's lookups; the barrier at the end makes it
+    // complete for every wave and frees this slice's table for the slice after next.
+    auto step = [&](u32x4 (&cur)[RW], SliceOps &oc, SliceOps &oa, u32x4 (&nxt)[RW], SliceOps &on) __attribute__((always_inline)) -> bool {
+        settle_tiles(cur);
+        if constexpr (M == 1) settle_ops(oa);
+        else settle_ops(oc);
         load_slice(nxt, on);
-        slice_start(oc);
+        auto lookups = [&](uint32_t lk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < RW; i++) {
-            process(cur[i], acc[i]);
-            // one tile at a time: hoisting the address math of every tile blows the register budget
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < RW; i++) {
+                process(cur[i], acc[i], lk);
+                // one tile at a time: hoisting the address math of every tile blows the register budget
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if constexpr (M == 1) {
+            build_table(oa, tb ^ 1);
+            lookups((uint32_t(lane) << 2) | (uint32_t(tb) << 16));
+            lds_barrier();
+            tb ^= 1;
+        } else {
+            slice_start(oc);
+            lookups(0);
         }
         if (++ps < pp.s1) return false;
         epilogue(pp, pd);
@@ -485,10 +540,15 @@ void aq_kernel(AqParams P) {
     SliceOps ops0, ops1, ops2;
     load_slice(buf0, ops0);
     load_slice(buf1, ops1);
+    if constexpr (M == 1) {  // the first table
+        settle_ops(ops0);
+        build_table(ops0, 0);
+        lds_barrier();
+    }
     while (true) {
-        if (step(buf0, ops0, buf2, ops2)) break;
-        if (step(buf1, ops1, buf0, ops0)) break;
-        if (step(buf2, ops2, buf1, ops1)) break;
+        if (step(buf0, ops0, ops1, buf2, ops2)) break;
+        if (step(buf1, ops1, ops2, buf0, ops0)) break;
+        if (step(buf2, ops2, ops0, buf1, ops1)) break;
     }
     finalize<M, RW, W>(P, wg, wid, lane);
 }
@@ -501,7 +561,10 @@ AqFn aq_fn(int M, int RW) {
         return RW == 1 ? aq_kernel<m, 1> : aq_kernel<m, 2>;
     switch (M) {
     case 1:
-        return RW <= 2 ? aq_kernel<1, 2> : RW == 4 ? aq_kernel<1, 4> : aq_kernel<1, 8>;
+        if (RW <= 1) return aq_kernel<1, 1>;
+        if (RW == 2) return aq_kernel<1, 2>;
+        if (RW == 4) return aq_kernel<1, 4>;
+        return 64 / aq_waves(1) >= 8 ? aq_kernel<1, 64 / aq_waves(1)> : nullptr;
         WQD_AQ_CASE(2)
         WQD_AQ_CASE(3)
         WQD_AQ_CASE(4)
