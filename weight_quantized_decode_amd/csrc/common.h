@@ -110,7 +110,7 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 // for M = 1 (WQD_AQ1_WAVES), 16 for M > 1.  A piece has at most waves * RW row blocks, 64 at
 // M = 1.
 #ifndef WQD_AQ1_WAVES
-#define WQD_AQ1_WAVES 8
+#define WQD_AQ1_WAVES 16
 #endif
 __host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? WQD_AQ1_WAVES : 16; }
 #ifndef WQD_AQ1_RW_MAX

@@ -10,9 +10,10 @@
 // M = 1, lookup tables:
 //   * For one K-slice of 64 groups the workgroup builds T in LDS as dword (c*64 + g) holding the
 //     pair (T_0,g[c], T_1,g[c]) in fp16: 64 KiB.  T is the product C_b (256 x 8) . X (8 x 64),
-//     X[j][g] = x[8g+j]; each of the 8 waves computes the 32 codes of one block for both
-//     codebooks with four 32x32x8 f16 MFMAs (exact fp16 products, fp32 sums), rounds them to
-//     fp16 pairs and, after a permlane32 swap, writes whole 64-group rows of the table.
+//     X[j][g] = x[8g+j], on the 4x4x4 matrix core: with 4 codebook rows broadcast as the A
+//     operand and each lane's own group activations as B, one pair of MFMAs (k = 0..3, 4..7)
+//     leaves T[c][g = lane] for 4 codes in 4 registers of lane g (exact fp16 products, fp32
+//     sums), already in table order.  Each wave builds 256/W codes of both codebooks.
 //   * Two tables alternate: the table of the next slice is built while the current one is read,
 //     with one workgroup barrier per slice.
 //   * Lane g reads only bank g, so the lookups never conflict: two LDS reads per 8 weights (the
@@ -311,8 +312,12 @@ void aq_kernel(AqParams P) {
     ld.done = false;
     ld.setup(P, pp, wg, wid, lane);
 
-    // M = 1 table block of this wave: codes 32*wid .. 32*wid + 31 of both codebooks.
-    static_assert(M != 1 || W == 8, "eight waves build the 8 code blocks of a table");
+    // M = 1 table share of this wave: NQ quads of codes (4NQ codes from 4NQ*wid) of both
+    // codebooks.  Its MFMA A operands hold 4NQ blocks (codebook, quad, k-half) of 4 codebook
+    // rows: block n = 16r + b sits in lanes 4b..4b+3 of A[r], as codebook n / 2NQ, quad
+    // (n % 2NQ) / 2, k-half n % 2.
+    constexpr int NQ = 64 / W;
+    static_assert(M != 1 || (4 * NQ <= 32 && W * NQ == 64), "the A operands hold the wave's blocks");
 
     // Issue the loads of the loader's slice: operands first, then the RW tiles; step the loader.
     // Every load is unconditional with a clamped address (a load under a lane condition makes
@@ -320,14 +325,16 @@ void aq_kernel(AqParams P) {
     auto load_slice = [&](u32x4 (&t)[RW], SliceOps &o) __attribute__((always_inline)) {
         if constexpr (M == 1) {
             o.gval = ld.G - ld.s * 64;
+            const int g = min(ld.s * 64 + lane, ld.G - 1);  // lane = group
 #pragma unroll
-            for (int gb = 0; gb < 2; gb++) {
-                const int g = min(ld.s * 64 + gb * 32 + (lane & 31), ld.G - 1);
-                o.B[gb] = gld<u32x2>(ld.x + int64_t(g) * 8 + 4 * (lane >> 5));
+            for (int h = 0; h < 2; h++) o.B[h] = gld<u32x2>(ld.x + int64_t(g) * 8 + 4 * h);
+#pragma unroll
+            for (int r = 0; r < (4 * NQ + 15) / 16; r++) {
+                const int n = min(16 * r + (lane >> 2), 4 * NQ - 1);
+                const int cb = n / (2 * NQ), quad = (n % (2 * NQ)) / 2, half = n % 2;
+                const int code = wid * 4 * NQ + 4 * quad + (lane & 3);
+                o.A[r] = gld<u32x2>(ld.cbk + (int64_t(cb) * 256 + code) * 8 + 4 * half);
             }
-#pragma unroll
-            for (int b = 0; b < 2; b++)
-                o.A[b] = gld<u32x2>(ld.cbk + (int64_t(b) * 256 + wid * 32 + (lane & 31)) * 8 + 4 * (lane >> 5));
         } else {
             const int g = min(ld.s * 64 + lane, ld.G - 1);
             o.X = gld<u32x4>(ld.x + int64_t(min(wid, M - 1)) * ld.ldx + int64_t(g) * 8);
@@ -399,40 +406,22 @@ void aq_kernel(AqParams P) {
 
     // M = 1: build the table of a slice (its operands o) into table buffer tb.
     auto build_table = [&](const SliceOps &o, int tb) __attribute__((always_inline)) {
-        u32x2 B[2];
-#pragma unroll
-        for (int gb = 0; gb < 2; gb++) {
-            const bool in = gb * 32 + (lane & 31) < o.gval;  // groups past K read as zero
-            B[gb] = in ? o.B[gb] : u32x2{0u, 0u};
-        }
-        const f32x16 zero = {};
-        const h4 B0 = __builtin_bit_cast(h4, B[0]), B1 = __builtin_bit_cast(h4, B[1]);
-        // codebook 0 first, rounded at once (fewer live registers): q[v] = (T_0 of group half 0,
-        // T_0 of group half 1)
-        uint32_t q[16];
-        {
-            const f32x16 d0 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[0]), B0, zero, 0, 0, 0);
-            const f32x16 d1 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[0]), B1, zero, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 16; v++) q[v] = pack_h2(d0[v], d1[v]);
-        }
-        const f32x16 e0 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[1]), B0, zero, 0, 0, 0);
-        const f32x16 e1 = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A[1]), B1, zero, 0, 0, 0);
+        const bool in = lane < o.gval;  // groups past K read as zero
+        const u32x2 B0 = in ? o.B[0] : u32x2{0u, 0u}, B1 = in ? o.B[1] : u32x2{0u, 0u};
         uint32_t *tab = lds + tb * (256 * 64);
+        static_for<NQ>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            f32x4 D[2];
+            static_for<2>([&](auto cc) {
+                constexpr int cb = decltype(cc)::value;
+                constexpr int n0 = cb * 2 * NQ + 2 * q, n1 = n0 + 1;  // k-halves 0 and 1
+                const f32x4 d = mfma_xw<n0 % 16>(o.A[n0 / 16], B0, f32x4{0.f, 0.f, 0.f, 0.f});
+                D[cb] = mfma_xw<n1 % 16>(o.A[n1 / 16], B1, d);
+            });
+            // register i of lane g: T_b[code 4NQ*wid + 4q + i][group g]
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            // lane l, register v of a 32x32x8 result: code row 8(v/4) + 4(l/32) + v%4 of the
-            // block, group l%32 of its half.  p0 / p1: the (T_0, T_1) pairs of group half 0 / 1;
-            // after the swap sw[0] holds code row 8(v/4) + v%4 for all 64 groups (lane = group),
-            // sw[1] the row 4 further on.
-            const uint32_t r = pack_h2(e0[v], e1[v]);
-            const uint32_t p0 = __builtin_amdgcn_perm(r, q[v], 0x05040100u);
-            const uint32_t p1 = __builtin_amdgcn_perm(r, q[v], 0x07060302u);
-            const auto sw = __builtin_amdgcn_permlane32_swap(p0, p1, false, false);
-            const int c = wid * 32 + 8 * (v >> 2) + (v & 3);
-            tab[c * 64 + lane] = sw[0];
-            tab[(c + 4) * 64 + lane] = sw[1];
-        }
+            for (int i = 0; i < 4; i++) tab[(wid * 4 * NQ + 4 * q + i) * 64 + lane] = pack_h2(D[0][i], D[1][i]);
+        });
     };
 
     // M > 1: stage the activations of a slice.
