@@ -253,7 +253,7 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
 // model per piece, in tile loads (KiB): ns * (nrb + table build) plus a fixed charge for a
 // K-split (its partial round trip); the shape with the cheapest busiest workgroup wins.
 // ------------------------------------------------------------------------------------------
-static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : 2; }
+static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : M <= 4 ? 2 : 1; }  // (M > 4, RW 2: spills)
 
 static int64_t aq_nwg(int64_t M, int cus) {
     AqFn fn = aq_fn(int(M), aq_rw_max(M));

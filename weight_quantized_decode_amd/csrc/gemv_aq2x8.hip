@@ -80,11 +80,6 @@ __device__ __forceinline__ float finish_rows8(const float (&w)[2], int lane) {
     z = z + dpp<kDppHalfMirror>(z);
     return z;
 }
-__device__ __forceinline__ float reduce_rows8(const float (&v)[8], int lane) {
-    float w[2];
-    fold_rows8(v, w);
-    return finish_rows8(w, lane);
-}
 
 template <typename T>
 __device__ __forceinline__ T load_uniform(const T *p) {
@@ -363,15 +358,15 @@ void aq_kernel(AqParams P) {
         }
     };
 
-    // per row block: two folded row sums (M = 1, see fold_rows8) or M finished row sums
-    constexpr int NACC = (M == 1) ? 2 : M;
+    // per row block and activation row: two folded row sums (see fold_rows8), finished once per
+    // piece
+    constexpr int NACC = 2 * M;
     float acc[RW][NACC];
 #pragma unroll
     for (int i = 0; i < RW; i++)
 #pragma unroll
         for (int r = 0; r < NACC; r++) acc[i][r] = 0.f;
 
-    u32x4 Xc[M];  // M > 1: this lane's group activations for the current slice
     int tb = 0;   // M = 1: table buffer of the slice being processed
 
     // Piece epilogue: row sums -> y (b == 1) or this split's tagged partial slots.
@@ -383,9 +378,8 @@ void aq_kernel(AqParams P) {
             const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N && q.split < D.b;
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                float z;
-                if constexpr (M == 1) z = finish_rows8(acc[i], lane);
-                else z = acc[i][m];
+                const float w2[2] = {acc[i][2 * m], acc[i][2 * m + 1]};
+                const float z = finish_rows8(w2, lane);
                 if (ok) {
                     if (D.b == 1) {
                         // (the scale is loaded here, not ahead: an early load's result would be
@@ -437,8 +431,6 @@ void aq_kernel(AqParams P) {
             if (threadIdx.x < 512) cbl[threadIdx.x] = o.C;
             if (wid < M) xl[wid * 64 + lane] = X;  // (waves >= M loaded a copy of row M-1)
             lds_barrier();
-#pragma unroll
-            for (int m = 0; m < M; m++) Xc[m] = xl[m * 64 + lane];
         }
     };
 
@@ -462,28 +454,37 @@ void aq_kernel(AqParams P) {
             a[0] += w[0];
             a[1] += w[1];
         } else {
+            // decode the 8 rows of this lane's group once, then take the activation rows one at a
+            // time (staged in LDS), folding each row's 64 lane terms to two per lane
             const u32x4 *cbl = reinterpret_cast<const u32x4 *>(lds);
-            float val[M][8];
+            const u32x4 *xl = cbl + 512;
+            uint32_t wv[8][4];
 #pragma unroll
             for (int r = 0; r < 8; r++) {
                 const uint32_t c0 = (w4[r >> 1] >> (16 * (r & 1))) & 0xFFu;
                 const uint32_t c1 = (w4[r >> 1] >> (16 * (r & 1) + 8)) & 0xFFu;
                 const u32x4 E0 = cbl[c0], E1 = cbl[256 + c1];
                 const uint32_t e0[4] = {E0.x, E0.y, E0.z, E0.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
-                uint32_t wv[4];
 #pragma unroll
-                for (int k = 0; k < 4; k++) wv[k] = __builtin_bit_cast(uint32_t, as_h2(e0[k]) + as_h2(e1[k]));
-#pragma unroll
-                for (int m = 0; m < M; m++) {
-                    const uint32_t xw[4] = {Xc[m].x, Xc[m].y, Xc[m].z, Xc[m].w};
-                    float sm = 0.f;
-#pragma unroll
-                    for (int k = 0; k < 4; k++) sm = dot2(wv[k], xw[k], sm);
-                    val[m][r] = sm;
-                }
+                for (int k = 0; k < 4; k++) wv[r][k] = __builtin_bit_cast(uint32_t, as_h2(e0[k]) + as_h2(e1[k]));
             }
 #pragma unroll
-            for (int m = 0; m < M; m++) a[m] += reduce_rows8(val[m], lane);
+            for (int m = 0; m < M; m++) {
+                const u32x4 X = xl[m * 64 + lane];
+                const uint32_t xw[4] = {X.x, X.y, X.z, X.w};
+                float val[8];
+#pragma unroll
+                for (int r = 0; r < 8; r++) {
+                    float sm = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 4; k++) sm = dot2(wv[r][k], xw[k], sm);
+                    val[r] = sm;
+                }
+                float w2[2];
+                fold_rows8(val, w2);
+                a[2 * m] += w2[0];
+                a[2 * m + 1] += w2[1];
+            }
         }
     };
 
