@@ -209,21 +209,25 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     // row, if this unit owns it, is handled after the pipelined loop.
     const int cfe = min(ce, D.C_full);
 
-    // Matrix-core path (codebook formats, M >= WQD_MFMA_MIN_M): the whole chunks are multiplied by
+    // Matrix-core path (M >= WQD_MFMA_MIN_M): the whole chunks are multiplied by
     // v_mfma_f32_4x4x4_16b_f16 into MFA (activation rows 4h..4h+3 in MFA[.][h]).  With H = 1 there
     // are two accumulator chains, so consecutive MFMAs do not wait for each other; with H = 2 the
     // two activation-row quads already alternate.  A load group of U chunks spans NWIN
     // activation windows of 64 k, loaded with the group's codes (in-order completion then makes
     // one wait cover both).  The matrix-core path takes longer per chunk, so it loads larger
     // groups (more bytes in flight per wave while a group is processed).
-    constexpr bool MF = (M >= WQD_MFMA_MIN_M) && (FMT == CB4 || FMT == CB8);
-    constexpr int WPC = (FMT == CB4) ? 32 : 16;  // weights per chunk (codebook formats)
+    // The block formats decode to exact fp16 values (code - 8, code - 1) for it, and their
+    // MFA holds one scale block at a time, added to acc times the block scale.
+    constexpr bool MF = (M >= WQD_MFMA_MIN_M) && (FMT == CB4 || FMT == CB8 || FMT == Q4_0 || FMT == TQ2);
+    constexpr bool BLK = (FMT == Q4_0 || FMT == TQ2);
+    constexpr int WPC = (FMT == CB8) ? 16 : (FMT == TQ2) ? 64 : 32;  // weights per chunk
     constexpr int CPW = 64 / WPC;                // chunks per window
     constexpr int H = MF ? (M + 3) / 4 : 1;
     // CB4 with two activation quads needs twice the window registers: a shorter group keeps it
     // within 128 VGPRs
     constexpr int U = MF ? ((FMT == CB4 && H > 1) ? WQD_MF_U_WIDE : WQD_MF_U) : kU;
     static_assert(!MF || U % CPW == 0, "a load group holds whole activation windows");
+    static_assert(!MF || !BLK || U == 4, "a load group of a block format lies in one scale quad");
     constexpr int NWIN = MF ? U / CPW : 1;
     constexpr int NCH = (H == 1) ? 2 : 1;
     const uint16_t *xw[H];  // lane 4b+i: activation row 4h+i (clamped to M-1), at element 4b
@@ -280,7 +284,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     int b0 = 0;
     constexpr int WPB = (FMT == Q4_0) ? 32 : 128;   // weights per scale block
     float *bs = nullptr;
-    if constexpr (FMT == Q4_0 || FMT == TQ2) {
+    if constexpr ((FMT == Q4_0 || FMT == TQ2) && !MF) {
         const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         bs = reinterpret_cast<float *>(lds) + wid * (kMaxM * 64);
         b0 = (FMT == Q4_0) ? cb : cb / 2;
@@ -436,12 +440,30 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     // Matrix-core form of one whole chunk, j-th of its group (static: it fixes the window and the
     // 4-k block of every MFMA).  Chunk j of a group at chunk c covers k = (c+j)*WPC ..; window w
     // starts at k = c*WPC + 64w, so chunk j lies in window j / CPW at block (j % CPW) * WPC / 4.
-    auto process_mf = [&](auto jc, const uint4 &v, const u32x2 (&X)[NWIN][H]) {
+    auto process_mf = [&](auto jc, const uint4 &v, const u32x2 (&X)[NWIN][H], int c, uint2 sq) {
         constexpr int j = decltype(jc)::value;
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
         static_for<4>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
-            if constexpr (FMT == CB4) {
+            if constexpr (BLK) {
+                // Q4_0 word t: nibbles i and i+4 are weights 8t+2i, 8t+2i+1; TQ2 word t: fields i
+                // and i+8 are weights 16t+2i, 16t+2i+1.  OR-ing a code into 0x6400 (fp16 1024)
+                // gives 1024 + code exactly; one packed fp16 add of -1032 / -1025 leaves code - 8
+                // / code - 1.  B operand q: weights 4q..4q+3 of the word.
+                constexpr int NP = (FMT == Q4_0) ? 4 : 8, SH = (FMT == Q4_0) ? 4 : 2;
+                constexpr uint32_t MSK = (FMT == Q4_0) ? 0x000F000Fu : 0x00030003u;
+                constexpr uint32_t OFF = (FMT == Q4_0) ? 0xE408E408u : 0xE401E401u;
+                uint32_t pr[NP];
+#pragma unroll
+                for (int i = 0; i < NP; i++)
+                    pr[i] = __builtin_bit_cast(uint32_t, as_h2(((w4[t] >> (SH * i)) & MSK) | 0x64006400u) + as_h2(OFF));
+                static_for<NP / 2>([&](auto qc) {
+                    constexpr int q = decltype(qc)::value;
+                    constexpr int win = j / CPW, blk = (FMT == Q4_0) ? 8 * (j % CPW) + 2 * t + q : 4 * t + q;
+#pragma unroll
+                    for (int h = 0; h < H; h++) MFA[q % NCH][h] = mfma_xw<blk>(X[win][h], u32x2{pr[2 * q], pr[2 * q + 1]}, MFA[q % NCH][h]);
+                });
+            } else if constexpr (FMT == CB4) {
                 // word t: byte i -> weights 8t+2i, 8t+2i+1; pair p of bytes -> weights 8t+4p..+3
                 uint32_t e[4];
 #pragma unroll
@@ -467,12 +489,30 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                 for (int h = 0; h < H; h++) MFA[t % NCH][h] = mfma_xw<blk>(X[win][h], u32x2{pr[0], pr[1]}, MFA[t % NCH][h]);
             }
         });
+        if constexpr (BLK) {
+            // end of a scale block (every Q4_0 chunk; every second TQ2 chunk, groups start even)
+            if constexpr (FMT == Q4_0 || (j & 1) == 1) {
+                const int bq = (FMT == Q4_0) ? ((c + j) & 3) : (((c + j) >> 1) & 3);
+                const uint32_t dbits = (bq < 2 ? sq.x : sq.y) >> ((bq & 1) * 16);
+                const float d = half_bits_to_float(dbits & 0xFFFFu);
+#pragma unroll
+                for (int h = 0; h < H; h++) {
+#pragma unroll
+                    for (int vv = 0; vv < 4; vv++) {
+                        const float bsum = (NCH == 2) ? MFA[0][h][vv] + MFA[NCH - 1][h][vv] : MFA[0][h][vv];
+                        if (4 * h + vv < M) acc[4 * h + vv] = fmaf(d, bsum, acc[4 * h + vv]);
+                    }
+#pragma unroll
+                    for (int qq = 0; qq < NCH; qq++) MFA[qq][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
     };
 
     auto proc_group = [&](const uint4 (&buf)[U], const u32x2 (&X)[NWIN][H], int c, uint2 sq) {
         if constexpr (MF) {
             static_for<U>([&](auto jc) {
-                if (c + decltype(jc)::value < cfe) process_mf(jc, buf[decltype(jc)::value], X);
+                if (c + decltype(jc)::value < cfe) process_mf(jc, buf[decltype(jc)::value], X, c, sq);
             });
         } else {
 #pragma unroll
@@ -507,7 +547,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
             gi++;
         }
     }
-    if constexpr (MF) {
+    if constexpr (MF && !BLK) {
         // The partial last chunk (when this unit owns it): its window reads zero at k >= K, so
         // the zero padding of the codes (which decodes to a codebook entry) adds nothing.
         for (int c = max(cb, cfe); c < ce; c++) {
@@ -523,7 +563,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
 #pragma unroll
                 for (int w = 0; w < NWIN; w++) X[w][h] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
             }
-            process_mf(Int<0>{}, v, X);
+            process_mf(Int<0>{}, v, X, c, make_uint2(0, 0));
         }
     } else if constexpr (FMT != Q4_0 && FMT != TQ2) {
         for (int c = max(cb, cfe); c < ce; c++) {
@@ -531,7 +571,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
             process(FullTag<false>{}, v, c, make_uint2(0, 0));
         }
     }
-    if constexpr (MF) {
+    if constexpr (MF && !BLK) {
         // register v of MFA[.][h] is activation row 4h+v of this lane's row
 #pragma unroll
         for (int h = 0; h < H; h++)
@@ -644,11 +684,11 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
     }
 }
 
-// Waves per SIMD a kernel instance is compiled for: the matrix-core instances (codebook formats
-// only, M >= WQD_MFMA_MIN_M) are held to 128 VGPRs, so two 8-wave workgroups share a CU.
+// Waves per SIMD a kernel instance is compiled for: the matrix-core instances (M >=
+// WQD_MFMA_MIN_M) are held to 128 VGPRs, so two 8-wave workgroups share a CU.
 template <int MASK, int M>
 constexpr int kMinWavesPerEU =
-    (M >= WQD_MFMA_MIN_M && (MASK & ~kMaskCB48) == 0) ? WQD_MFMA_WAVES_PER_EU : 1;
+    (M >= WQD_MFMA_MIN_M && (MASK & (1 << AQ2X8)) == 0) ? WQD_MFMA_WAVES_PER_EU : 1;
 
 // Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
 // [0, pool_begin) are split into equal contiguous ranges, one per workgroup; the rest are handed
