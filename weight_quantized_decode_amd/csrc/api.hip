@@ -273,7 +273,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
     A.L = make_layout(AQ2X8, N, K);
     if (!A.L.ok) return A;
     const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = aq_rw_max(M), W = aq_waves(int(M));
-    const int64_t build = (M == 1) ? 16 : 2, split_charge = 32;
+    const int64_t build = (M == 1) ? WQD_AQ_BUILD_CHARGE : 2, split_charge = WQD_AQ_SPLIT_CHARGE;
     if (nwg < 1) nwg = 1;
     double best = 1e300;
     for (int64_t b = 1; b <= KS; b++) {
@@ -296,7 +296,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
         }
     }
     A.RB = RB;
-    A.RW = 1;  // M = 1 kernels exist for RW = 1, 2, 4 (and 8 with 8 waves); M > 1 for 1, 2
+    A.RW = 1;  // M = 1 kernels exist for RW = 1, 2, 4 and 8 (two passes of 4); M > 1 for 1, 2
     while (A.RW * W < A.nrb) A.RW *= 2;
     A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 8, 256) : 0;
     return A;

@@ -103,8 +103,8 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 // tiles are cut into a x b rectangular pieces, a row chunks of nrb blocks times b K-splits of ns
 // slices.  Piece j = split * a + chunk runs on workgroup (j + off) % nwg (and j + nwg, ... when
 // there are more pieces than workgroups).  With b > 1 each piece stores one tagged partial per
-// row, and the workgroup running split b-1 of a chunk adds the b partials of its rows at the end
-// of its work.
+// row, and at the end of their work the b workgroups of a chunk each add the b partials of a
+// share (1/b) of its rows.
 // ------------------------------------------------------------------------------------------
 // Waves per AQ2X8 workgroup (one workgroup per CU at M = 1, whose table fills the LDS): 8 or 16
 // for M = 1 (WQD_AQ1_WAVES), 16 for M > 1.  A piece has at most waves * RW row blocks, 64 at
@@ -114,7 +114,15 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 #endif
 __host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? WQD_AQ1_WAVES : 16; }
 #ifndef WQD_AQ1_RW_MAX
-#define WQD_AQ1_RW_MAX (64 / WQD_AQ1_WAVES)  // most 8-row blocks per wave per slice at M = 1
+#define WQD_AQ1_RW_MAX 8  // most 8-row blocks per wave per slice at M = 1 (8: two passes of 4)
+#endif
+// AQ2X8 planner charges, in tile loads: building a slice's table (M = 1) and a K-split's
+// partial round trip.
+#ifndef WQD_AQ_BUILD_CHARGE
+#define WQD_AQ_BUILD_CHARGE 16
+#endif
+#ifndef WQD_AQ_SPLIT_CHARGE
+#define WQD_AQ_SPLIT_CHARGE 32
 #endif
 // Waves per SIMD an AQ2X8 instance is compiled for (its VGPR budget).
 __host__ __device__ constexpr int aq_waves_per_simd(int M) { return M == 1 ? WQD_AQ1_WAVES / 4 : 4; }

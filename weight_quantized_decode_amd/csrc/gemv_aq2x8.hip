@@ -29,8 +29,8 @@
 // Work: see AqDesc.  A workgroup walks its pieces in order, slice by slice; the loads of the next
 // slice (of the same or the next piece) are in flight while a slice is processed.  With b > 1
 // K-splits a piece stores one tagged 64-bit partial per row (no fence: a slot is either still zero or holds
-// the tag and the value), and the workgroup that ran the last split of a chunk adds the b
-// partials of its rows, in split order, once all of its own pieces are done.
+// the tag and the value), and once all of its own pieces are done each of the b workgroups of a
+// chunk adds the b partials, in split order, of its share of the chunk's rows.
 #include <stddef.h>
 
 #include "gemv_impl.h"
@@ -146,25 +146,28 @@ __device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Pie
     return find_piece(P, wg, q.p, q.j + P.nwg);
 }
 
-// Tile loader running ahead of the processing: (piece, slice), RW tiles per slice.
-template <int RW, int W>
+// Tile loader running ahead of the processing.  It walks units (piece, slice, pass): each slice
+// of a piece is read in NP passes of RW tiles per wave, pass p covering row blocks
+// rb0 + wid + W*(i + RW*p), so one table serves NP * W * RW row blocks.
+template <int RW, int W, int NP>
 struct Loader {
     const uint8_t *base;   // code plane (wave-uniform; the lane's 16 bytes are added at the load)
     int64_t s_stride;      // bytes between slices (R8 = Npad/8 KiB)
     int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
-    int rb[RW];            // this wave's row blocks; -1: none (the piece has fewer than W * RW)
+    int rbw, rb1;          // this wave's first row block of the piece; the piece's end
     const uint16_t *x, *cbk;  // operands of the slice's table / activation stage
     int64_t ldx;
     int G;
-    Piece q, qn;  // current piece and the next one (looked up a piece ahead)
-    int s;
+    Piece q;  // current piece
+    int s, pass;
     bool done;
 
-    // (n by value: step() passes the member qn, which is overwritten below)
+    // (the next piece is looked up only when this one ends: at the start of the kernel, one
+    // descriptor read stands before the first loads instead of two)
     __device__ __forceinline__ void setup(const AqParams &P, const Piece n, int wg, int wid, int lane) {
         q = n;
         s = n.s0;
-        qn = next_piece(P, wg, n);
+        pass = 0;
         const AqDesc D = get_desc(P, n.p);
         base = D.codes;
         s_stride = int64_t(D.Npad / 8) * 1024;
@@ -174,29 +177,27 @@ struct Loader {
         G = D.G;
         s_max = D.KS - 1;
         rb_max = D.Npad / 8 - 1;
-#pragma unroll
-        for (int i = 0; i < RW; i++) {
-            const int r = n.rb0 + wid + W * i;
-            rb[i] = r < n.rb1 ? min(r, rb_max) : -1;
-        }
+        rbw = n.rb0 + wid;
+        rb1 = n.rb1;
     }
-    // A missing tile still takes its place in the ring (every load stays unconditional): it
-    // reads 1 KiB of the codebooks, which the table build keeps in L2, instead of HBM.
+    // A missing tile (past the piece, or past the end of the list) still takes its place in the
+    // ring (every load stays unconditional): it reads 1 KiB of the codebooks, which the table
+    // build keeps in L2, instead of HBM.
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        return rb[i] < 0 ? reinterpret_cast<const uint8_t *>(cbk)
-                         : base + int64_t(min(s, s_max)) * s_stride + int64_t(rb[i]) * 1024;
+        const int r = rbw + W * (i + RW * pass);
+        return (done || r >= rb1) ? reinterpret_cast<const uint8_t *>(cbk)
+                                  : base + int64_t(min(s, s_max)) * s_stride + int64_t(min(r, rb_max)) * 1024;
     }
-    // After the last tile of a slice: step to the next slice (or piece).  Past the end of the
-    // list the loader keeps issuing loads of the L2-resident codebooks, so the ring never has a
-    // hole.
+    // After the tiles of a unit: step to the next pass, slice or piece.
     __device__ __forceinline__ void step(const AqParams &P, int wg, int wid, int lane) {
         if (done) return;
+        if (++pass < NP) return;
+        pass = 0;
         if (++s < q.s1) return;
+        const Piece qn = next_piece(P, wg, q);
         if (qn.p >= P.ndesc) {
             done = true;
             s = q.s1 - 1;
-#pragma unroll
-            for (int i = 0; i < RW; i++) rb[i] = -1;
         } else {
             setup(P, qn, wg, wid, lane);
         }
@@ -204,49 +205,53 @@ struct Loader {
 };
 
 constexpr int kSpinMax = 1 << 22;   // polls of a missing partial before giving up (NaN result)
+constexpr int kFinLoads = 8;        // partial loads in flight per row in the finalize (32 measured slower)
 
-// Adds the b tagged partials of rows [8*rb, 8*rb + 8) of every row block of this wave in the
-// pieces whose last split this workgroup ran, in split order, then scales and writes y and clears
-// the slots.  Runs after all of the workgroup's own pieces.
-template <int M, int RW, int W>
+// Adds the b tagged partials of rows of the pieces this workgroup ran, in split order, then scales
+// and writes y and clears the slots.  The rows of a row chunk are shared out over its b splits:
+// the workgroup that ran split t finalizes rows [t*R/b, (t+1)*R/b) of the chunk's R rows, one
+// row per lane.  Runs after all of the workgroup's own pieces; a partial not yet written is polled
+// again (bounded), and its writer never waits on another workgroup, so the wait ends.
+template <int M, int W>
 __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int lane) {
     for (Piece q = find_piece(P, wg, 0, -1); q.p < P.ndesc; q = next_piece(P, wg, q)) {
         const AqDesc D = get_desc(P, q.p);
-        if (D.b == 1 || q.split != D.b - 1) continue;
-        const int i = lane >> 3, r = lane & 7;
-        const int rb = q.rb0 + wid + W * i;
-        const int row = rb * 8 + r;
-        if (i >= RW || rb >= q.rb1 || row >= D.N) continue;
-        const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
+        if (D.b == 1) continue;
+        const int r0 = q.rb0 * 8, R = min((q.rb1 - q.rb0) * 8, D.N - r0);
+        const int lo = r0 + (R * q.split) / D.b, hi = r0 + (R * (q.split + 1)) / D.b;
+        for (int row = lo + wid * 64 + lane; row < hi; row += W * 64) {
+            const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            uint64_t *slot = D.part + (int64_t(m) * D.b) * D.Npad + row;
-            float sum = 0.f;
-            bool ok = true;
-            // up to 8 slot loads in flight; a slot still untagged is polled again (bounded)
-            for (int t0 = 0; t0 < D.b; t0 += 8) {
-                uint64_t v[8];
+            for (int m = 0; m < M; m++) {
+                uint64_t *slot = D.part + (int64_t(m) * D.b) * D.Npad + row;
+                float sum = 0.f;
+                bool ok = true;
+                // up to kFinLoads slot loads in flight (one round trip for b <= kFinLoads)
+                for (int t0 = 0; t0 < D.b; t0 += kFinLoads) {
+                    uint64_t v[kFinLoads];
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                          : (uint64_t(kAqTag) << 32);
+                    for (int j = 0; j < kFinLoads; j++)
+                        v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT)
+                                              : (uint64_t(kAqTag) << 32);
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    int spins = 0;
-                    while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
-                        __builtin_amdgcn_s_sleep(2);
-                        v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                        spins++;
+                    for (int j = 0; j < kFinLoads; j++) {
+                        int spins = 0;
+                        while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
+                            __builtin_amdgcn_s_sleep(2);
+                            v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                            spins++;
+                        }
+                        ok = ok && uint32_t(v[j] >> 32) == kAqTag;
+                        if (t0 + j < D.b) sum += f32(uint32_t(v[j]));  // split order
                     }
-                    ok = ok && uint32_t(v[j] >> 32) == kAqTag;
-                    if (t0 + j < D.b) sum += f32(uint32_t(v[j]));  // split order
                 }
+                gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
+                for (int t = 0; t < D.b; t++)
+                    __hip_atomic_store(as_global(slot + int64_t(t) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
-            gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
-            for (int t = 0; t < D.b; t++)
-                __hip_atomic_store(as_global(slot + int64_t(t) * D.Npad), uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -286,7 +291,7 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 
 // M = 1: the 128 KiB table allows one workgroup per CU, i.e. 2 waves per SIMD, so each wave may
 // use 256 VGPRs (the compiler would otherwise aim for more waves than can ever be resident).
-template <int M, int RW>
+template <int M, int RW, int NP>
 __global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, aq_waves_per_simd(M))))
 void aq_kernel(AqParams P) {
     constexpr int W = aq_waves(M);  // waves per workgroup
@@ -301,9 +306,9 @@ void aq_kernel(AqParams P) {
     int ps = pp.s0;                       // slice being processed
 
     AqDesc pd = get_desc(P, pp.p);        // its descriptor
-    Piece pn = next_piece(P, wg, pp);     // the next piece, looked up a piece ahead
 
-    Loader<RW, W> ld;
+    Loader<RW, W, NP> ld;
+    static_assert(M == 1 || NP == 1, "passes share a lookup table (M = 1)");
     ld.done = false;
     ld.setup(P, pp, wg, wid, lane);
 
@@ -361,24 +366,27 @@ void aq_kernel(AqParams P) {
     // per row block and activation row: two folded row sums (see fold_rows8), finished once per
     // piece
     constexpr int NACC = 2 * M;
-    float acc[RW][NACC];
+    float acc[NP][RW][NACC];
 #pragma unroll
-    for (int i = 0; i < RW; i++)
+    for (int p = 0; p < NP; p++)
 #pragma unroll
-        for (int r = 0; r < NACC; r++) acc[i][r] = 0.f;
+        for (int i = 0; i < RW; i++)
+#pragma unroll
+            for (int r = 0; r < NACC; r++) acc[p][i][r] = 0.f;
 
     int tb = 0;   // M = 1: table buffer of the slice being processed
 
     // Piece epilogue: row sums -> y (b == 1) or this split's tagged partial slots.
     auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < RW; i++) {
-            const int rb = q.rb0 + wid + W * i;
+        for (int pi = 0; pi < NP * RW; pi++) {
+            const int p = pi / RW, i = pi % RW;
+            const int rb = q.rb0 + wid + W * pi;
             const int row = rb * 8 + (lane >> 3);
             const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N && q.split < D.b;
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                const float w2[2] = {acc[i][2 * m], acc[i][2 * m + 1]};
+                const float w2[2] = {acc[p][i][2 * m], acc[p][i][2 * m + 1]};
                 const float z = finish_rows8(w2, lane);
                 if (ok) {
                     if (D.b == 1) {
@@ -394,7 +402,7 @@ void aq_kernel(AqParams P) {
                 }
             }
 #pragma unroll
-            for (int r = 0; r < NACC; r++) acc[i][r] = 0.f;
+            for (int r = 0; r < NACC; r++) acc[p][i][r] = 0.f;
         }
     };
 
@@ -493,35 +501,45 @@ void aq_kernel(AqParams P) {
     // M = 1: the operands of the slice after it (oa) are waited for too, and its table is built
     // into the other buffer before this slice's lookups; the barrier at the end makes it
     // complete for every wave and frees this slice's table for the slice after next.
-    auto step = [&](u32x4 (&cur)[RW], SliceOps &oc, SliceOps &oa, u32x4 (&nxt)[RW], SliceOps &on) __attribute__((always_inline)) -> bool {
+    // A unit is one pass over a slice; the table of the next slice is built (and the barrier
+    // taken) in the last pass.
+    auto step = [&](auto pc, u32x4 (&cur)[RW], SliceOps &oc, SliceOps &oa, u32x4 (&nxt)[RW], SliceOps &on) __attribute__((always_inline)) -> bool {
+        constexpr int pass = decltype(pc)::value;
+        constexpr bool last = pass == NP - 1;
         settle_tiles(cur);
-        if constexpr (M == 1) settle_ops(oa);
-        else settle_ops(oc);
+        if constexpr (M == 1) {
+            if constexpr (last) settle_ops(oa);
+        } else {
+            settle_ops(oc);
+        }
         load_slice(nxt, on);
         auto lookups = [&](uint32_t lk) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < RW; i++) {
-                process(cur[i], acc[i], lk);
+                process(cur[i], acc[pass][i], lk);
                 // one tile at a time: hoisting the address math of every tile blows the register budget
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
         if constexpr (M == 1) {
-            build_table(oa, tb ^ 1);
+            if constexpr (last) build_table(oa, tb ^ 1);
             lookups((uint32_t(lane) << 2) | (uint32_t(tb) << 16));
-            lds_barrier();
-            tb ^= 1;
+            if constexpr (last) {
+                lds_barrier();
+                tb ^= 1;
+            }
         } else {
             slice_start(oc);
             lookups(0);
         }
+        if constexpr (!last) return false;
         if (++ps < pp.s1) return false;
         epilogue(pp, pd);
+        const Piece pn = next_piece(P, wg, pp);
         if (pn.p >= P.ndesc) return true;
         pp = pn;
         ps = pp.s0;
         pd = get_desc(P, pp.p);
-        pn = next_piece(P, wg, pp);
         return false;
     };
 
@@ -535,12 +553,18 @@ void aq_kernel(AqParams P) {
         build_table(ops0, 0);
         lds_barrier();
     }
+    // (the ring has 3 buffers and a slice NP passes: 3 * NP steps per round)
     while (true) {
-        if (step(buf0, ops0, ops1, buf2, ops2)) break;
-        if (step(buf1, ops1, ops2, buf0, ops0)) break;
-        if (step(buf2, ops2, ops0, buf1, ops1)) break;
+        if (step(Int<0>{}, buf0, ops0, ops1, buf2, ops2)) break;
+        if (step(Int<1 % NP>{}, buf1, ops1, ops2, buf0, ops0)) break;
+        if (step(Int<2 % NP>{}, buf2, ops2, ops0, buf1, ops1)) break;
+        if constexpr (NP == 2) {
+            if (step(Int<1>{}, buf0, ops0, ops1, buf2, ops2)) break;
+            if (step(Int<0>{}, buf1, ops1, ops2, buf0, ops0)) break;
+            if (step(Int<1>{}, buf2, ops2, ops0, buf1, ops1)) break;
+        }
     }
-    finalize<M, RW, W>(P, wg, wid, lane);
+    finalize<M, W>(P, wg, wid, lane);
 }
 
 }  // namespace
@@ -548,13 +572,13 @@ void aq_kernel(AqParams P) {
 AqFn aq_fn(int M, int RW) {
 #define WQD_AQ_CASE(m)                                   \
     case m:                                              \
-        return RW == 1 ? aq_kernel<m, 1> : aq_kernel<m, 2>;
+        return RW == 1 ? aq_kernel<m, 1, 1> : aq_kernel<m, 2, 1>;
     switch (M) {
-    case 1:
-        if (RW <= 1) return aq_kernel<1, 1>;
-        if (RW == 2) return aq_kernel<1, 2>;
-        if (RW == 4) return aq_kernel<1, 4>;
-        return 64 / aq_waves(1) >= 8 ? aq_kernel<1, 64 / aq_waves(1)> : nullptr;
+    case 1:  // RW: row blocks per wave per slice; 8 = two passes of 4
+        if (RW <= 1) return aq_kernel<1, 1, 1>;
+        if (RW == 2) return aq_kernel<1, 2, 1>;
+        if (RW == 4) return aq_kernel<1, 4, 1>;
+        return aq_kernel<1, 4, 2>;
         WQD_AQ_CASE(2)
         WQD_AQ_CASE(3)
         WQD_AQ_CASE(4)
