@@ -128,7 +128,8 @@ static int resident_per_cu(const void *fn, int threads) {
     cache.push_back({fn, dev, n});
     return n;
 }
-static int resident_per_cu(GemvFn fn) { return resident_per_cu(reinterpret_cast<const void *>(fn), kThreads); }
+// The row kernels are compiled for WQD_WG_PER_CU resident workgroups per CU (see gemv_impl.h).
+static int resident_per_cu(GemvFn fn) { return fn ? WQD_WG_PER_CU : 1; }
 
 // Wave slots resident at once for a kernel instance (the persistent grid's capacity).
 static int64_t resident_waves(int mask, int64_t M, int cus) {
@@ -137,11 +138,11 @@ static int64_t resident_waves(int mask, int64_t M, int cus) {
 }
 
 // Chunks per wave unit for a launch covering `total_cc` chunk-columns (one 1 KiB wave load
-// each): about WQD_UNITS_PER_WAVE units per resident wave, between 8 and WQD_STACK_MAX_CS chunks.
+// each): about WQD_UNITS_PER_WAVE units per resident wave, between WQD_MIN_CS and the cap chunks.
 static int64_t target_cs(int64_t total_cc, int64_t waves, int64_t M) {
     const int64_t cap = M >= WQD_MFMA_MIN_M ? WQD_STACK_MF_CS : WQD_STACK_MAX_CS;
     int64_t cs = total_cc / (waves * WQD_UNITS_PER_WAVE);
-    if (cs < 8) cs = 8;
+    if (cs < WQD_MIN_CS) cs = WQD_MIN_CS;
     if (cs > cap) cs = cap;
     return cs;
 }
@@ -276,7 +277,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
     const int64_t build = (M == 1) ? WQD_AQ_BUILD_CHARGE : 2, split_charge = WQD_AQ_SPLIT_CHARGE;
     if (nwg < 1) nwg = 1;
     double best = 1e300;
-    for (int64_t b = 1; b <= KS; b++) {
+    for (int64_t b = 1; b <= KS && b <= WQD_AQ_MAX_SPLITS; b++) {
         const int64_t ns = (KS + b - 1) / b;
         if ((KS + ns - 1) / ns != b) continue;  // same split as a smaller b
         int64_t a = nwg / b;

@@ -22,8 +22,11 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #ifndef WQD_STACK_MAX_CS
 #define WQD_STACK_MAX_CS 128  // largest stack K-slice (chunks) of the vector-ALU instances
 #endif
+#ifndef WQD_MIN_CS
+#define WQD_MIN_CS 16  // shortest K-slice (chunks) a launch is cut into
+#endif
 #ifndef WQD_UNITS_PER_WAVE
-#define WQD_UNITS_PER_WAVE 4
+#define WQD_UNITS_PER_WAVE 1
 #endif
 #ifndef WQD_STACK_UNITS
 #define WQD_STACK_UNITS 1
@@ -38,7 +41,7 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #define WQD_POOL_MIN_CS 64  // smallest K-slice (chunks) of a launch that uses the dynamic tail
 #endif
 #ifndef WQD_WG_PER_CU
-#define WQD_WG_PER_CU 2
+#define WQD_WG_PER_CU 2  // resident workgroups per CU of the row kernels (they are compiled for it)
 #endif
 // Smallest M whose codebook-format kernels multiply on the matrix cores (v_mfma_f32_4x4x4_16b_f16)
 // instead of v_dot2; below it the VALU path stays (it is HBM-bound there).
@@ -53,9 +56,6 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #endif
 #ifndef WQD_STACK_MF_CS
 #define WQD_STACK_MF_CS 128  // largest stack K-slice (chunks) of the matrix-core instances
-#endif
-#ifndef WQD_MFMA_WAVES_PER_EU
-#define WQD_MFMA_WAVES_PER_EU 4
 #endif
 constexpr int kMaxM = 8;                  // largest M (activation rows) per call
 constexpr int kWaves = WQD_WAVES;         // waves per workgroup
@@ -120,6 +120,9 @@ __host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? WQD_AQ1_WAVE
 // partial round trip.
 #ifndef WQD_AQ_BUILD_CHARGE
 #define WQD_AQ_BUILD_CHARGE 16
+#endif
+#ifndef WQD_AQ_MAX_SPLITS
+#define WQD_AQ_MAX_SPLITS 64  // most K-splits of an AQ2X8 projection
 #endif
 #ifndef WQD_AQ_SPLIT_CHARGE
 #define WQD_AQ_SPLIT_CHARGE 32

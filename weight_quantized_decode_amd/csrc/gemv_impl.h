@@ -684,11 +684,11 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
     }
 }
 
-// Waves per SIMD a kernel instance is compiled for: the matrix-core instances (M >=
-// WQD_MFMA_MIN_M) are held to 128 VGPRs, so two 8-wave workgroups share a CU.
+// Every instance is compiled for WQD_WG_PER_CU (2) resident 8-wave workgroups per CU, i.e. 4
+// waves per SIMD and at most 128 VGPRs; the launch sizes its persistent grid from the same
+// constant (the runtime occupancy query under-reports kernels without AGPRs).
 template <int MASK, int M>
-constexpr int kMinWavesPerEU =
-    (M >= WQD_MFMA_MIN_M && (MASK & (1 << AQ2X8)) == 0) ? WQD_MFMA_WAVES_PER_EU : 1;
+constexpr int kMinWavesPerEU = WQD_WG_PER_CU * kWaves / 4;
 
 // Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
 // [0, pool_begin) are split into equal contiguous ranges, one per workgroup; the rest are handed
