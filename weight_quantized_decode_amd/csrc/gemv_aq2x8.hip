@@ -207,49 +207,60 @@ struct Loader {
 constexpr int kSpinMax = 1 << 22;   // polls of a missing partial before giving up (NaN result)
 constexpr int kFinLoads = 8;        // partial loads in flight per row in the finalize (32 measured slower)
 
-// Adds the b tagged partials of rows of the pieces this workgroup ran, in split order, then scales
-// and writes y and clears the slots.  The rows of a row chunk are shared out over its b splits:
-// the workgroup that ran split t finalizes rows [t*R/b, (t+1)*R/b) of the chunk's R rows, one
-// row per lane.  Runs after all of the workgroup's own pieces; a partial not yet written is polled
-// again (bounded), and its writer never waits on another workgroup, so the wait ends.
+// Adds the b tagged partials of rows of the pieces this workgroup ran, then scales and writes y
+// and clears the slots.  The rows of a row chunk are shared out over its b splits: the workgroup
+// that ran split t finalizes rows [t*R/b, (t+1)*R/b) of the chunk's R rows.  A row takes L lanes
+// (L = b/8 rounded up to a power of two): lane j of the row loads partials 8j..8j+7 in one round
+// and adds them in split order, then the L lane sums are combined in a fixed tree.  Runs after all
+// of the workgroup's own pieces; a partial not yet written is polled again (bounded), and its
+// writer never waits on another workgroup, so the wait ends.
 template <int M, int W>
 __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int lane) {
     for (Piece q = find_piece(P, wg, 0, -1); q.p < P.ndesc; q = next_piece(P, wg, q)) {
         const AqDesc D = get_desc(P, q.p);
         if (D.b == 1) continue;
+        int L = 1;
+        while (L * kFinLoads < D.b) L *= 2;  // (b <= 64 keeps L <= 8)
         const int r0 = q.rb0 * 8, R = min((q.rb1 - q.rb0) * 8, D.N - r0);
         const int lo = r0 + (R * q.split) / D.b, hi = r0 + (R * (q.split + 1)) / D.b;
-        for (int row = lo + wid * 64 + lane; row < hi; row += W * 64) {
+        const int sub = lane & (L - 1);             // this lane's group of partials
+        const int stride = W * 64 / L;              // rows per round of the workgroup
+        // all L lanes of a row take the same iterations (the lane combine below pairs them)
+        for (int k = (wid * 64 + lane) / L; k < hi - lo; k += stride) {
+            const int row = lo + k;
             const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
 #pragma unroll
             for (int m = 0; m < M; m++) {
                 uint64_t *slot = D.part + (int64_t(m) * D.b) * D.Npad + row;
+                const int t0 = sub * kFinLoads;
+                uint64_t v[kFinLoads];
+#pragma unroll
+                for (int j = 0; j < kFinLoads; j++)
+                    v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                          : (uint64_t(kAqTag) << 32);
                 float sum = 0.f;
-                bool ok = true;
-                // up to kFinLoads slot loads in flight (one round trip for b <= kFinLoads)
-                for (int t0 = 0; t0 < D.b; t0 += kFinLoads) {
-                    uint64_t v[kFinLoads];
+                int ok = 1;
 #pragma unroll
-                    for (int j = 0; j < kFinLoads; j++)
-                        v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                                  __HIP_MEMORY_SCOPE_AGENT)
-                                              : (uint64_t(kAqTag) << 32);
-#pragma unroll
-                    for (int j = 0; j < kFinLoads; j++) {
-                        int spins = 0;
-                        while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
-                            __builtin_amdgcn_s_sleep(2);
-                            v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                            spins++;
-                        }
-                        ok = ok && uint32_t(v[j] >> 32) == kAqTag;
-                        if (t0 + j < D.b) sum += f32(uint32_t(v[j]));  // split order
+                for (int j = 0; j < kFinLoads; j++) {
+                    int spins = 0;
+                    while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
+                        __builtin_amdgcn_s_sleep(2);
+                        v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                        spins++;
                     }
+                    ok &= uint32_t(v[j] >> 32) == kAqTag;
+                    if (t0 + j < D.b) sum += f32(uint32_t(v[j]));  // split order
                 }
-                gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
-                for (int t = 0; t < D.b; t++)
-                    __hip_atomic_store(as_global(slot + int64_t(t) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
+                // combine the L lanes of the row: pairs, then pairs of pairs (a fixed order)
+                for (int o = 1; o < L; o <<= 1) {
+                    sum += __shfl_xor(sum, o);
+                    ok &= __shfl_xor(ok, o);
+                }
+                if (sub == 0) gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
+                for (int j = 0; j < kFinLoads && t0 + j < D.b; j++)
+                    __hip_atomic_store(as_global(slot + int64_t(t0 + j) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
         }
