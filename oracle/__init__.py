@@ -45,6 +45,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_f32.argtypes = [ctypes.c_int, i64, i64, vp, i64, i64, vp]
         L.oracle_gemm_f64.restype = ctypes.c_int
         L.oracle_gemm_f64.argtypes = [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, vp]
+        L.oracle_silu.restype = ctypes.c_double
+        L.oracle_silu.argtypes = [ctypes.c_double]
+        L.oracle_silu_mul_f64.restype = ctypes.c_int
+        L.oracle_silu_mul_f64.argtypes = [vp, vp, i64, vp]
+        L.oracle_residual_add_f64.restype = ctypes.c_int
+        L.oracle_residual_add_f64.argtypes = [vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -100,3 +106,43 @@ def gemm_f64(fmt: int, N: int, K: int, canon: np.ndarray, x_bits: np.ndarray, ro
     if rc:
         raise ValueError(f"oracle_gemm_f64 failed: {rc}")
     return y, a
+
+
+def silu(g: float) -> float:
+    """SiLU(g) = g / (1 + e^-g) in fp64."""
+    return float(lib().oracle_silu(float(g)))
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Elementwise SiLU(g) * u in fp64 (the gate/up epilogue)."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    if g.shape != u.shape:
+        raise ValueError("gate and up results differ in shape")
+    h = np.empty_like(g)
+    rc = lib().oracle_silu_mul_f64(_ptr(g), _ptr(u), g.size, _ptr(h))
+    if rc:
+        raise ValueError(f"oracle_silu_mul_f64 failed: {rc}")
+    return h
+
+
+def residual_add(r: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """Elementwise r + y in fp64, r an fp32 residual, y an fp64 projection result."""
+    r = np.ascontiguousarray(r, dtype=np.float32)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    if r.shape != y.shape:
+        raise ValueError("residual and projection result differ in shape")
+    out = np.empty_like(y)
+    rc = lib().oracle_residual_add_f64(_ptr(r), _ptr(y), y.size, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_residual_add_f64 failed: {rc}")
+    return out
+
+
+def silu_pair_f64(fmt: int, N: int, K: int, canon_gate: np.ndarray, canon_up: np.ndarray,
+                  x_gate: np.ndarray, x_up: np.ndarray, rows=None):
+    """The fused gate/up projection: returns (h, g, u, a_g, a_u), each (M, nrows), with
+    h = SiLU(g) * u, g and u the fp64 gate and up products, a_g and a_u their sums of |x*w|."""
+    g, ag = gemm_f64(fmt, N, K, canon_gate, x_gate, rows=rows)
+    u, au = gemm_f64(fmt, N, K, canon_up, x_up, rows=rows)
+    return silu_mul(g, u), g, u, ag, au

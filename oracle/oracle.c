@@ -17,6 +17,11 @@
  *  - AQ2x8: trapetum "Benchmarks", "Additive vector-quantization GEMV (AQLM-style, 2-bit)":
  *    two codebooks of 256 entries of 8 values, the weight group is the sum of the two selected
  *    entries, with a per-output-row scale.
+ *  - Epilogues: trapetum "Benchmarks", "Short-context decode, step by step" (the fused decode
+ *    kernels): the gate and up projections share one launch whose reduce applies SiLU to the
+ *    gate result and multiplies by the up result, and the o and down projections add the
+ *    residual inside their reduce.  SiLU is the sigmoid-weighted linear unit g * sigma(g); the
+ *    page names it and leaves its definition to the usual one.
  */
 #include "oracle.h"
 
@@ -175,5 +180,27 @@ int oracle_gemm_f64(int fmt, int64_t N, int64_t K, const uint8_t *canon,
     }
     free(wrow);
     free(xd);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ projection epilogues */
+
+/* SiLU(g) = g * sigma(g) = g / (1 + e^-g), in fp64.  For g below about -709 e^-g overflows to
+ * +inf and the quotient is -0, the limit of SiLU there; for large g it is g. */
+double oracle_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Gated MLP activation, elementwise: h[i] = SiLU(g[i]) * u[i] (g: gate projection result,
+ * u: up projection result, both exact fp64 products from oracle_gemm_f64). */
+int oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h) {
+    if (n < 0 || (n > 0 && (!g || !u || !h))) return -3;
+    for (int64_t i = 0; i < n; i++) h[i] = oracle_silu(g[i]) * u[i];
+    return 0;
+}
+
+/* Residual add of the o and down reduces, elementwise: out[i] = r[i] + y[i], with r the fp32
+ * residual stream (converted exactly) and y the exact fp64 projection result. */
+int oracle_residual_add_f64(const float *r, const double *y, int64_t n, double *out) {
+    if (n < 0 || (n > 0 && (!r || !y || !out))) return -3;
+    for (int64_t i = 0; i < n; i++) out[i] = (double)r[i] + y[i];
     return 0;
 }

@@ -15,7 +15,9 @@
  *   5 AQ2X8 : C[2][256][8] fp16, then s[N] fp16, then codes [N][K/8][2] (codebook 0 first);
  *             value s[n] * (C[0][c0][j] + C[1][c1][j]) for weight j of group k/8.
  *
- * All functions return 0 on success and a negative value on bad arguments.
+ * Epilogues of the fused projections: SiLU(gate) * up for a gate/up pair, and a residual add.
+ *
+ * Functions returning int return 0 on success and a negative value on bad arguments.
  */
 #ifndef WQD_ORACLE_H
 #define WQD_ORACLE_H
@@ -47,6 +49,15 @@ int oracle_dequant_f32(int fmt, int64_t N, int64_t K, const uint8_t *canon,
 int oracle_gemm_f64(int fmt, int64_t N, int64_t K, const uint8_t *canon,
                     const uint16_t *x, int64_t M, int64_t ldx,
                     const int64_t *rows, int64_t nrows, double *y, double *a);
+
+/* SiLU(g) = g / (1 + e^-g) in fp64 (the gate activation of the fused gate/up epilogue). */
+double oracle_silu(double g);
+
+/* h[i] = SiLU(g[i]) * u[i] for i < n (gate result g, up result u). */
+int oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h);
+
+/* out[i] = (double)r[i] + y[i] for i < n (residual r in fp32, projection result y). */
+int oracle_residual_add_f64(const float *r, const double *y, int64_t n, double *out);
 
 #ifdef __cplusplus
 }

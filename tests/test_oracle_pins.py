@@ -297,3 +297,98 @@ def test_dequant_f32_is_the_rounded_exact_value_for_exact_formats():
         w64 = oracle.decode_f64(fmt, 4, 256, canon)
         w32 = oracle.dequant_f32(fmt, 4, 256, canon)
         assert np.array_equal(w32.astype(np.float64), w64)  # exact in fp32
+
+
+# ----------------------------------------------------------------------------- epilogues
+# The fused gate/up reduce applies SiLU(gate) * up and the o/down reduces add the residual
+# (trapetum "Benchmarks", "Short-context decode, step by step").
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    # SiLU(2t) = 2t * sigma(2t) = t * (1 + tanh t): checked through libm's tanh, not exp (for
+    # t << 0 the tanh form cancels, hence the absolute term of |t| ulps of 1)
+    for t in np.linspace(-20.0, 20.0, 161):
+        want = t * (1.0 + math.tanh(t))
+        assert oracle.silu(2.0 * t) == pytest.approx(want, rel=4e-15, abs=4e-16 * abs(t))
+    # the odd part of SiLU is the identity: SiLU(x) - SiLU(-x) = x * (sigma(x) + sigma(-x)) = x
+    for x in np.linspace(-30.0, 30.0, 241):
+        assert oracle.silu(x) - oracle.silu(-x) == pytest.approx(x, rel=1e-14, abs=1e-14)
+
+
+def test_silu_minimum_is_minus_lambert_w_of_1_over_e():
+    # SiLU'(x) = 0 at x* = -1 - W(1/e), where SiLU(x*) = -W(1/e) (W the Lambert function)
+    from scipy.special import lambertw
+    w = float(lambertw(1.0 / math.e).real)
+    xs = -1.0 - w + np.linspace(-1e-4, 1e-4, 201)
+    vals = np.array([oracle.silu(x) for x in xs])
+    assert vals.min() == pytest.approx(-w, rel=1e-12)
+    assert abs(xs[vals.argmin()] - (-1.0 - w)) < 2e-6
+
+
+def test_silu_slope_and_limits():
+    h = 1e-6
+    assert (oracle.silu(h) - oracle.silu(-h)) / (2 * h) == pytest.approx(0.5, rel=1e-9)  # SiLU'(0) = 1/2
+    assert oracle.silu(800.0) == 800.0
+    assert oracle.silu(40.0) == 40.0
+    lo = oracle.silu(-800.0)
+    assert lo == 0.0 and not math.isnan(lo)
+
+
+def _cb8_canon(codes_nk):
+    cb = ((np.arange(256) - 128) / 4.0).astype(np.float16)
+    return np.concatenate([cb.view(np.uint16).astype("<u2").view(np.uint8),
+                           np.asarray(codes_nk, dtype=np.uint8).reshape(-1)])
+
+
+def test_silu_pair_hand_rows():
+    g = read_golden("silu_pair.txt")
+    gc = np.array([int(v) for v in g["gate_codes"]])
+    uc = np.array([int(v) for v in g["up_codes"]])
+    N, K = len(gc), 3
+    r = np.random.default_rng(5)
+    gate = r.integers(0, 256, size=(N, K))
+    up = r.integers(0, 256, size=(N, K))
+    gate[:, 1], up[:, 1] = gc, uc
+    x = np.zeros((1, K), dtype=np.uint16)
+    x[0, 1] = f16(1.0)
+    h, gg, uu, ag, au = oracle.silu_pair_f64(I.CB8, N, K, _cb8_canon(gate), _cb8_canon(up), x, x)
+    assert np.array_equal(gg[0], np.array([float(v) for v in g["g"]]))
+    assert np.array_equal(uu[0], np.array([float(v) for v in g["u"]]))
+    want = np.array([float(v) for v in g["h"]])
+    np.testing.assert_allclose(h[0], want, rtol=4e-16, atol=0)
+    # gate and up are not interchangeable: the swapped pair gives other values
+    assert not np.allclose(oracle.silu_mul(uu, gg)[0], want)
+
+
+def test_silu_pair_of_random_projections_is_silu_of_gate_times_up():
+    N, K = 70, 96
+    cg = I.gen_weight(I.CB4, N, K, (77, 0))
+    cu = I.gen_weight(I.CB4, N, K, (77, 1))
+    xg = I.gen_x(2, K, (77, 2))
+    xu = I.gen_x(2, K, (77, 3))
+    h, g, u, _, _ = oracle.silu_pair_f64(I.CB4, N, K, cg, cu, xg, xu)
+    g2, _ = oracle.gemm_f64(I.CB4, N, K, cg, xg)
+    u2, _ = oracle.gemm_f64(I.CB4, N, K, cu, xu)
+    assert np.array_equal(g, g2) and np.array_equal(u, u2)
+    # h / u = sigma(g) * g where u != 0, and sigma(g) lies in (0, 1) with the sign of h = sign(g*u)
+    nz = u != 0
+    sig = h[nz] / (u[nz] * g[nz])
+    assert np.all((sig > 0) & (sig < 1))
+    np.testing.assert_allclose(sig, 0.5 * (1 + np.tanh(g[nz] / 2)), rtol=1e-13)
+
+
+def test_residual_add_is_exact_on_one_hot_activation():
+    N, K, k0 = 9, 64, 17
+    canon = I.gen_weight(I.CB8, N, K, (78, 0))
+    x = np.zeros((1, K), dtype=np.uint16)
+    x[0, k0] = f16(1.0)
+    res = np.random.default_rng(6).standard_normal((1, N)).astype(np.float32)
+    y, _ = oracle.gemm_f64(I.CB8, N, K, canon, x)
+    out = oracle.residual_add(res, y)
+    col = oracle.decode_f64(I.CB8, N, K, canon)[:, k0]
+    for n in range(N):
+        assert Fraction(out[0, n]) == Fraction(float(res[0, n])) + Fraction(col[n])
+    # zero activation: the residual comes back unchanged
+    y0, _ = oracle.gemm_f64(I.CB8, N, K, canon, np.zeros((1, K), dtype=np.uint16))
+    assert np.array_equal(oracle.residual_add(res, y0), res.astype(np.float64))
