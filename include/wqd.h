@@ -107,9 +107,25 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
 
 /* ---------------------------------------------------------------- layer / stack */
 
+/* Epilogue of a projection in a list (trapetum "Benchmarks", "Short-context decode, step by
+ * step": the fused decode kernels apply SiLU(gate) times up in the reduce of the gate/up
+ * projection and add the residual inside the reduces of the o and down projections).  The
+ * epilogue runs where the projection's K-slices are summed, so it costs no extra launch and no
+ * extra pass over y.  AQ2X8 entries take WQD_EPI_NONE only. */
+typedef enum {
+    WQD_EPI_NONE = 0,      /* y[m][n] = sum_k x[m][k] W[n][k] */
+    WQD_EPI_ADD = 1,       /* y[m][n] += sum_k x[m][k] W[n][k]: y holds the residual on entry */
+    WQD_EPI_SILU_GATE = 2, /* gate of a gate/up pair; the next entry must be its WQD_EPI_SILU_UP */
+    WQD_EPI_SILU_UP = 3    /* up of the pair (same fmt and N as the gate; K, w and x its own):
+                              the gate entry's y[m][n] = SiLU(g[m][n]) * u[m][n], with
+                              g = x_gate W_gate^T, u = x_up W_up^T and SiLU(g) = g / (1 + e^-g),
+                              evaluated in fp32 on the fp32 sums.  This entry's y and ldy are
+                              not used (y may be NULL). */
+} wqd_epilogue;
+
 typedef struct {
     int32_t fmt;
-    int32_t reserved; /* must be 0 */
+    int32_t epi;      /* wqd_epilogue */
     int64_t N, K;
     const void *w;    /* prepared weights */
     const void *x;    /* fp16 activations, M rows of ldx */
@@ -119,39 +135,52 @@ typedef struct {
 } wqd_proj;
 
 enum {
-    WQD_ORDERED = 0,   /* projections one after another, each its own launches */
-    WQD_PERSISTENT = 1 /* one persistent launch per format set (CB4 and CB8 together); valid when
-                          no projection's x is another projection's y */
+    WQD_ORDERED = 0,    /* entries one after another, each its own launch (a gate/up pair is one
+                           entry) */
+    WQD_PERSISTENT = 1, /* one persistent launch per format set (CB4 and CB8 together at M = 1)
+                           over the whole list; valid when no entry's x is another entry's y and
+                           no two entries write the same y elements.  Needs wqd_stack_setup. */
+    WQD_FUSED = 2       /* runs of consecutive entries of one format that read the same x (same
+                           pointer and ldx) share one launch, at most 4 entries per launch and a
+                           gate/up pair never split (q/k/v in one launch, gate/up in one); runs
+                           follow one another in list order, so a later run may read what an
+                           earlier one wrote.  AQ2X8 entries launch one at a time.  Entries of
+                           one run must not write the same y elements. */
 };
 
-/* Device workspace bytes for wqd_run_projections over this list (descriptor table, counters and
- * partial sums).  In WQD_ORDERED mode the workspace is used like wqd_gemm's (zero-filled before
- * its first use); in WQD_PERSISTENT mode wqd_stack_setup initialises it. */
+/* Device workspace bytes for wqd_run_projections over this list in any mode (descriptor
+ * tables, counters and partial sums).  In WQD_ORDERED and WQD_FUSED modes the workspace is used
+ * like wqd_gemm's: zero-filled before its first use (or initialised by wqd_stack_setup), and
+ * left with its counters at zero by every call; it may be NULL when no launch of the list splits
+ * K and the list holds no gate/up pair.  In WQD_PERSISTENT mode wqd_stack_setup initialises it. */
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
 
-/* Write the descriptor table of this projection list into the workspace and zero its counters
- * (blocking copies).
+/* Write the WQD_PERSISTENT descriptor tables of this projection list into the workspace and
+ * zero its counters (blocking copies).
  * Must be called once before wqd_run_projections in WQD_PERSISTENT mode, and again whenever a
  * pointer or shape in the list changes. */
 WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, void *workspace,
                             int64_t workspace_bytes, void *stream);
 
-/* Run every projection of the list (same semantics as wqd_gemm for each).  `mode` is
- * WQD_ORDERED or WQD_PERSISTENT. */
+/* Run every projection of the list with its epilogue.  `mode` is WQD_ORDERED, WQD_PERSISTENT
+ * or WQD_FUSED.  Errors: WQD_EINVAL for a bad mode or epilogue, a gate entry not followed by
+ * its up entry (or an up entry without its gate, or the two differing in fmt or N), an epilogue
+ * on an AQ2X8 entry, or a NULL workspace in WQD_PERSISTENT mode; WQD_ESPACE for a workspace
+ * smaller than wqd_stack_workspace_bytes when one is needed; the wqd_gemm checks per entry. */
 WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
-/* Profiling variant: the same work as wqd_run_projections in WQD_PERSISTENT mode, with hipEvent_t
- * events[2i] recorded on the stream just before the i-th kernel launch of the call and
- * events[2i+1] just after it.  Launch order: the CB4+CB8 launch if both formats are present, then
- * one launch per remaining format (ascending format id).
+/* Profiling variant: the same work as wqd_run_projections, with hipEvent_t events[2i] recorded
+ * on the stream just before the i-th kernel launch of the call and events[2i+1] just after it.
+ * Launch order in WQD_PERSISTENT mode: the CB4+CB8 launch if both formats are present, then one
+ * launch per remaining format (ascending format id); in the other modes, list order.
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,
                                       void *stream, void *const *events, int32_t n_events);
 
-/* Number of kernel launches one WQD_PERSISTENT call issues for this list (or a negative status). */
-WQD_API int wqd_stack_launches(const wqd_proj *projs_host, int32_t count, int64_t M);
+/* Number of kernel launches one call in `mode` issues for this list (or a negative status). */
+WQD_API int wqd_stack_launches(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode);
 
 /* ---------------------------------------------------------------- errors */
 

@@ -161,9 +161,84 @@ def test_run_projections_rejects_bad_mode_and_lists():
     L = W.lib()
     assert L.wqd_run_projections(arr, 1, 1, 7, FAKE, 1 << 20, None) == W.WQD_EINVAL
     assert L.wqd_run_projections(arr, 1, 0, 0, FAKE, 1 << 20, None) == W.WQD_ESHAPE
-    arr[0].reserved = 1
+    arr[0].epi = 7  # no such epilogue
     assert L.wqd_run_projections(arr, 1, 1, 0, FAKE, 1 << 20, None) == W.WQD_EINVAL
     assert L.wqd_stack_workspace_bytes(arr, 1, 1) == W.WQD_EINVAL
+
+
+def _fake_list(entries):
+    """wqd_proj array of (fmt, N, K, epi, x) entries on never-dereferenced pointers."""
+    arr = (W.wqd_proj * len(entries))()
+    for i, (fmt, N, K, epi, x) in enumerate(entries):
+        arr[i].fmt, arr[i].N, arr[i].K, arr[i].epi = fmt, N, K, epi
+        arr[i].w, arr[i].x, arr[i].ldx = FAKE + (i << 24), x, K
+        arr[i].y, arr[i].ldy = FAKE + (i << 24) + (1 << 23), N
+    return arr
+
+
+G, U, A, E0 = W.WQD_EPI_SILU_GATE, W.WQD_EPI_SILU_UP, W.WQD_EPI_ADD, W.WQD_EPI_NONE
+
+
+@pytest.mark.parametrize("entries", [
+    [(I.CB4, 64, 64, G, FAKE)],                                   # gate without its up
+    [(I.CB4, 64, 64, U, FAKE)],                                   # up without its gate
+    [(I.CB4, 64, 64, G, FAKE), (I.CB4, 64, 64, E0, FAKE)],        # gate followed by a plain entry
+    [(I.CB4, 64, 64, G, FAKE), (I.CB4, 128, 64, U, FAKE)],        # pair with different N
+    [(I.CB4, 64, 64, G, FAKE), (I.CB8, 64, 64, U, FAKE)],         # pair with different formats
+    [(I.CB4, 64, 64, E0, FAKE), (I.CB4, 64, 64, U, FAKE)],        # up after a plain entry
+    [(I.AQ2X8, 64, 64, A, FAKE)],                                 # no epilogue on AQ2X8
+])
+def test_epilogue_list_errors(entries):
+    arr = _fake_list(entries)
+    L = W.lib()
+    for mode in (W.WQD_ORDERED, W.WQD_PERSISTENT, W.WQD_FUSED):
+        assert L.wqd_run_projections(arr, len(arr), 1, mode, FAKE, 1 << 30, None) == W.WQD_EINVAL
+        assert L.wqd_stack_launches(arr, len(arr), 1, mode) == W.WQD_EINVAL
+    assert L.wqd_stack_workspace_bytes(arr, len(arr), 1) == W.WQD_EINVAL
+
+
+def test_up_entry_may_have_no_output():
+    arr = _fake_list([(I.CB4, 64, 64, G, FAKE), (I.CB4, 64, 64, U, FAKE)])
+    arr[1].y, arr[1].ldy = None, 0
+    assert W.lib().wqd_stack_workspace_bytes(arr, 2, 1) > 0
+    arr[0].y = None  # but the gate's output is where the pair writes
+    assert W.lib().wqd_stack_workspace_bytes(arr, 2, 1) == W.WQD_EINVAL
+
+
+def _layer(x_in, x_attn, x_mlp):
+    # a 7B layer with its epilogues: q, k, v on the layer input; o + residual; gate/up pair;
+    # down + residual
+    return [(I.CB4, 4096, 4096, E0, x_in), (I.CB4, 4096, 4096, E0, x_in), (I.CB4, 4096, 4096, E0, x_in),
+            (I.CB4, 4096, 4096, A, x_attn), (I.CB4, 11008, 4096, G, x_in), (I.CB4, 11008, 4096, U, x_in),
+            (I.CB4, 4096, 11008, A, x_mlp)]
+
+
+def test_launch_counts_per_mode():
+    L = W.lib()
+    X = [FAKE + (1 << 40) + (j << 20) for j in range(8)]
+    arr = _fake_list(_layer(X[0], X[1], X[2]) + _layer(X[3], X[4], X[5]))
+    n = len(arr)
+    assert L.wqd_stack_launches(arr, n, 1, W.WQD_PERSISTENT) == 1
+    assert L.wqd_stack_launches(arr, n, 1, W.WQD_ORDERED) == 12   # the pair is one launch
+    assert L.wqd_stack_launches(arr, n, 1, W.WQD_FUSED) == 8      # qkv, o, gate/up, down per layer
+    assert L.wqd_stack_launches(arr, n, 1, 3) == W.WQD_EINVAL
+    # runs hold at most 4 entries and never split a pair
+    same = _fake_list([(I.CB4, 64, 64, E0, X[6])] * 3 + [(I.CB4, 64, 64, G, X[6]), (I.CB4, 64, 64, U, X[6])]
+                      + [(I.CB4, 64, 64, E0, X[6])] * 6)
+    assert L.wqd_stack_launches(same, len(same), 1, W.WQD_FUSED) == 3  # 3 | pair + 2 | 4
+    # a different x or format ends a run; AQ2X8 entries run alone
+    mixed = _fake_list([(I.CB4, 64, 64, E0, X[6]), (I.CB4, 64, 64, E0, X[7]), (I.CB8, 64, 64, E0, X[7]),
+                        (I.AQ2X8, 64, 64, E0, X[7]), (I.AQ2X8, 64, 64, E0, X[7])])
+    assert L.wqd_stack_launches(mixed, len(mixed), 1, W.WQD_FUSED) == 5
+
+
+def test_pair_needs_a_workspace():
+    arr = _fake_list([(I.CB4, 64, 64, G, FAKE), (I.CB4, 64, 64, U, FAKE)])
+    L = W.lib()
+    for mode in (W.WQD_ORDERED, W.WQD_FUSED):
+        assert L.wqd_run_projections(arr, 2, 1, mode, None, 0, None) == W.WQD_ESPACE
+    need = L.wqd_stack_workspace_bytes(arr, 2, 1)
+    assert L.wqd_run_projections(arr, 2, 1, W.WQD_FUSED, FAKE, need - 256, None) == W.WQD_ESPACE
 
 
 def test_status_strings():

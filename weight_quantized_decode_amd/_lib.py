@@ -17,7 +17,8 @@ SO_PATH = os.path.join(_HERE, "libwqd.so")
 
 WQD_Q4_0, WQD_CB4, WQD_CB8, WQD_TQ2, WQD_AQ2X8 = 1, 2, 3, 4, 5
 WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP = 0, -1, -2, -3, -4, -5
-WQD_ORDERED, WQD_PERSISTENT = 0, 1
+WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED = 0, 1, 2
+WQD_EPI_NONE, WQD_EPI_ADD, WQD_EPI_SILU_GATE, WQD_EPI_SILU_UP = 0, 1, 2, 3
 WQD_MAX_M = 8
 
 EXPORTED = [
@@ -38,7 +39,7 @@ class WqdError(RuntimeError):
 
 
 class wqd_proj(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("N", ctypes.c_int64),
+    _fields_ = [("fmt", ctypes.c_int32), ("epi", ctypes.c_int32), ("N", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("w", ctypes.c_void_p), ("x", ctypes.c_void_p),
                 ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
             "wqd_run_projections": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
             "wqd_run_projections_timed": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp,
                                                          ctypes.POINTER(ctypes.c_void_p), i32]),
-            "wqd_stack_launches": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64]),
+            "wqd_stack_launches": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32]),
             "wqd_stream_check": (ctypes.c_int, [vp]),
             "wqd_last_hip_error": (ctypes.c_int, []),
             "wqd_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -140,18 +141,20 @@ def wqd_dequant_f32(fmt: int, N: int, K: int, w, out, stream=None) -> None:
 # ------------------------------------------------------------------------- layer / stack
 
 def make_proj_array(projs: Sequence[dict]):
-    """projs: dicts with fmt, N, K, w, x, y (torch tensors); returns a ctypes array of wqd_proj."""
+    """projs: dicts with fmt, N, K, w, x, y (torch tensors) and optionally epi (a WQD_EPI_*
+    value; y may be None for a WQD_EPI_SILU_UP entry); returns a ctypes array of wqd_proj."""
     arr = (wqd_proj * len(projs))()
     for i, p in enumerate(projs):
         arr[i].fmt = p["fmt"]
-        arr[i].reserved = 0
+        arr[i].epi = p.get("epi", WQD_EPI_NONE)
         arr[i].N = p["N"]
         arr[i].K = p["K"]
         arr[i].w = p["w"].data_ptr()
         arr[i].x = p["x"].data_ptr()
         arr[i].ldx = p["x"].stride(0)
-        arr[i].y = p["y"].data_ptr()
-        arr[i].ldy = p["y"].stride(0)
+        y = p.get("y")
+        arr[i].y = None if y is None else y.data_ptr()
+        arr[i].ldy = 0 if y is None else y.stride(0)
     return arr
 
 
@@ -170,8 +173,8 @@ def wqd_run_projections(arr, M: int, mode: int, workspace, stream=None) -> None:
                                                             _stream(stream)))
 
 
-def wqd_stack_launches(arr, M: int) -> int:
-    return _check("wqd_stack_launches", lib().wqd_stack_launches(arr, len(arr), M))
+def wqd_stack_launches(arr, M: int, mode: int = WQD_PERSISTENT) -> int:
+    return _check("wqd_stack_launches", lib().wqd_stack_launches(arr, len(arr), M, mode))
 
 
 def wqd_run_projections_timed(arr, M: int, mode: int, workspace, events, stream=None) -> None:

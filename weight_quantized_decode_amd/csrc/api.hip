@@ -233,6 +233,10 @@ static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, 
     D.wu_count = int32_t(P.L.RG * P.S);
     D.wgu_begin = 0;
     D.fmt = P.L.fmt;
+    D.epi = kEpiNone;
+    D.slot0 = 0;
+    D.S_all = int32_t(P.S);
+    D.S_first = int32_t(P.S);
     return D;
 }
 
@@ -366,25 +370,35 @@ static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, i
                        int64_t ldy, int *cnt, float *part, hipStream_t st, int cus) {
     GemvParams GP;
     memset(&GP, 0, sizeof(GP));
-    GP.d0 = make_desc(P, w, x, ldx, y, ldy, part, cnt);
+    GP.d[0] = make_desc(P, w, x, ldx, y, ldy, part, cnt);
     GP.descs = nullptr;
     GP.ndesc = 1;
-    GP.total_wgu = int32_t((GP.d0.wu_count + kWaves - 1) / kWaves);
+    GP.total_wgu = int32_t((GP.d[0].wu_count + kWaves - 1) / kWaves);
     return launch_gemv(fmt_bit(P.L.fmt), int(M), GP, st, cus);
 }
 
-// Stack workspace: [Desc table][launch-group counters, 256 B][slice counters][partials], each
-// region 256-byte aligned.  The slice-counter region is at least kCntRegion bytes and the
-// partial region at least what the largest projection needs alone, so WQD_ORDERED mode uses
-// the same two regions.  Projections are grouped into launches: all CB4/CB8 projections
-// together when both appear and M < WQD_MFMA_MIN_M, otherwise one launch per format; within a
-// launch, descriptors are in format order.
+// ------------------------------------------------------------------------------------------
+// Projection lists.  A list is cut into segments, run one after another in stream order:
+//   WQD_PERSISTENT  one segment, the whole list;
+//   WQD_ORDERED     one entry per segment (a gate/up pair is one entry);
+//   WQD_FUSED       runs of consecutive entries of one row format that read the same x (q/k/v,
+//                   a gate/up pair), at most kInlineDescs descriptors, a pair never split.
+// Within a segment the row-format projections are grouped into launches (all CB4/CB8 together
+// when both appear, in WQD_PERSISTENT mode at M < WQD_MFMA_MIN_M, otherwise one launch per
+// format; descriptors in format order), then one AQ2X8 launch.
+//
+// Workspace (the same layout in every mode): [Desc table, count entries][AqDesc table, count
+// entries][launch-group counters, 256 B][slice counters][partials], each region 256-byte
+// aligned.  The slice-counter region holds one counter array per entry, at least kCntRegion
+// bytes; segments after the first reuse the counter and partial regions from their start (the
+// launches before them have finished and left their counters at zero).
+// ------------------------------------------------------------------------------------------
 struct LaunchGroup {
     int mask = 0;
     int64_t cs = 0;            // K-slice target of the group (chunks)
     int first = 0, count = 0;  // range in StackPlan::descs (or StackPlan::aqdescs)
     int total_wgu = 0;
-    bool aq = false;           // the AQ2X8 launch
+    bool aq = false;           // an AQ2X8 launch
     int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
 };
 
@@ -392,126 +406,197 @@ struct StackPlan {
     std::vector<Desc> descs;
     std::vector<AqDesc> aqdescs;
     std::vector<LaunchGroup> groups;
-    int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0, total = 0;
+    int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0;
+    int64_t part_bytes = 0;    // partial bytes this mode uses
+    bool needs_ws = false;     // some launch counts slices (split K or a gate/up pair)
+    int64_t total() const { return off_part + part_bytes; }
 };
 
-static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, void *ws, StackPlan &SP, int cus) {
+// Entries, with the epilogue rules: a WQD_EPI_SILU_GATE entry is followed by its
+// WQD_EPI_SILU_UP entry (same format and N; the pair writes the gate entry's y), and AQ2X8
+// entries take no epilogue.
+static int check_list(const wqd_proj *p, int32_t count, int64_t M) {
     if (!p || count < 1) return WQD_EINVAL;
-    int present = 0;
+    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     for (int i = 0; i < count; i++) {
-        if (p[i].reserved != 0) return WQD_EINVAL;
-        int rc = check_proj(p[i].fmt, p[i].N, p[i].K, p[i].w, p[i].x, M, p[i].ldx, p[i].y, p[i].ldy);
+        const wqd_proj &q = p[i];
+        if (q.epi < WQD_EPI_NONE || q.epi > WQD_EPI_SILU_UP) return WQD_EINVAL;
+        if (q.epi != WQD_EPI_NONE && q.fmt == AQ2X8) return WQD_EINVAL;
+        const wqd_proj *out = &q;
+        if (q.epi == WQD_EPI_SILU_GATE) {
+            if (i + 1 >= count || p[i + 1].epi != WQD_EPI_SILU_UP || p[i + 1].fmt != q.fmt || p[i + 1].N != q.N)
+                return WQD_EINVAL;
+        } else if (q.epi == WQD_EPI_SILU_UP) {
+            if (i == 0 || p[i - 1].epi != WQD_EPI_SILU_GATE) return WQD_EINVAL;
+            out = &p[i - 1];
+        }
+        const int rc = check_proj(q.fmt, q.N, q.K, q.w, q.x, M, q.ldx, out->y, out->ldy);
         if (rc != WQD_OK) return rc;
-        present |= fmt_bit(p[i].fmt);
     }
+    return WQD_OK;
+}
+
+static bool fuse_with(const wqd_proj &a, const wqd_proj &b) {
+    return a.fmt == b.fmt && a.fmt != AQ2X8 && a.x == b.x && a.ldx == b.ldx;
+}
+
+static void list_segments(const wqd_proj *p, int count, int mode, std::vector<std::pair<int, int>> &seg) {
+    seg.clear();
+    if (mode == WQD_PERSISTENT) {
+        seg.push_back({0, count});
+        return;
+    }
+    int i = 0;
+    while (i < count) {
+        int j = (p[i].epi == WQD_EPI_SILU_GATE) ? i + 2 : i + 1;
+        if (mode == WQD_FUSED) {
+            while (j < count && fuse_with(p[i], p[j])) {
+                const int take = (p[j].epi == WQD_EPI_SILU_GATE) ? 2 : 1;
+                if (j + take - i > kInlineDescs) break;
+                j += take;
+            }
+        }
+        seg.push_back({i, j});
+        i = j;
+    }
+}
+
+// Plans the launches of entries [b, e) onto counters from cnt_off and partials from part_off
+// (offsets into the workspace at `base`, which may be null when only sizes are wanted).
+static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, uint8_t *base, int64_t &cnt_off,
+                         int64_t &part_off, StackPlan &SP, int cus) {
+    int present = 0;
+    for (int i = b; i < e; i++) present |= fmt_bit(p[i].fmt);
     const bool has_aq = (present & fmt_bit(AQ2X8)) != 0;
     present &= ~fmt_bit(AQ2X8);
     std::vector<int> masks;
-    if ((present & kMaskCB48) == kMaskCB48 && M < WQD_MFMA_MIN_M) {
+    if ((present & kMaskCB48) == kMaskCB48 && mode == WQD_PERSISTENT && M < WQD_MFMA_MIN_M) {
         masks.push_back(kMaskCB48);
         present &= ~kMaskCB48;
     }
     for (int fmt = 1; fmt <= 5; fmt++)
         if (present & fmt_bit(fmt)) masks.push_back(fmt_bit(fmt));
 
-    // plans: the K-slice size of a launch group follows its total work
-    std::vector<Plan> plans(count);
-    std::vector<int> order, group_of;
-    std::vector<int64_t> group_cs(masks.size(), 0);
-    int64_t cnt_total = 0, part_total = 0, single_part = 0;
-    for (size_t gi = 0; gi < masks.size(); gi++) {
-        const int mask = masks[gi];
+    for (const int mask : masks) {
+        // the K-slice size of a launch group follows its total work
         int64_t total_cc = 0;
-        for (int i = 0; i < count; i++) {
+        for (int i = b; i < e; i++) {
             if (!(mask & fmt_bit(p[i].fmt))) continue;
             Layout L = make_layout(p[i].fmt, p[i].N, p[i].K);
             total_cc += L.RG * L.C;
         }
-        const int64_t cs_target = target_cs(total_cc, resident_waves(mask, M, cus), M);
-        group_cs[gi] = cs_target;
-        for (int fmt = 1; fmt <= 5; fmt++) {
-            if (!(mask & fmt_bit(fmt))) continue;
-            for (int i = 0; i < count; i++) {
-                if (p[i].fmt != fmt) continue;
-                plans[i] = plan_cs(fmt, p[i].N, p[i].K, M, cs_target);
-                cnt_total += plans[i].cnt_bytes;
-                part_total += plans[i].part_bytes;
-                Plan Q = plan_single(fmt, p[i].N, p[i].K, M, cus);
-                if (Q.part_bytes > single_part) single_part = Q.part_bytes;
-                order.push_back(i);
-                group_of.push_back(int(gi));
-            }
-        }
-    }
-    // AQ2X8 projections: one launch, every workgroup taking one piece of each
-    std::vector<AqPlan> aqplans;
-    std::vector<int> aqidx;
-    const int64_t aq_wg = has_aq ? aq_nwg(M, cus) : 0;
-    int64_t aq_part_total = 0;
-    for (int i = 0; has_aq && i < count; i++) {
-        if (p[i].fmt != AQ2X8) continue;
-        AqPlan A = plan_aq(p[i].N, p[i].K, M, aq_wg);  // also the plan of a WQD_ORDERED launch
-        aq_part_total += A.part_bytes;
-        if (A.part_bytes > single_part) single_part = A.part_bytes;
-        aqplans.push_back(A);
-        aqidx.push_back(i);
-    }
-    part_total += aq_part_total;
-
-    SP.off_descs = 0;
-    SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
-    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * int64_t(aqplans.size()), 256);
-    SP.off_cnt = SP.off_ctr + 256;
-    SP.cnt_bytes = cnt_total > kCntRegion ? cnt_total : kCntRegion;
-    SP.off_part = SP.off_cnt + SP.cnt_bytes;
-    SP.total = SP.off_part + (part_total > single_part ? part_total : single_part);
-
-    uint8_t *base = static_cast<uint8_t *>(ws);
-    int64_t cnt_off = SP.off_cnt, part_off = SP.off_part;
-    size_t oi = 0;
-    for (size_t gi = 0; gi < masks.size(); gi++) {
         LaunchGroup G;
-        G.mask = masks[gi];
+        G.mask = mask;
+        G.cs = target_cs(total_cc, resident_waves(mask, M, cus), M);
         G.first = int(SP.descs.size());
         int wgu = 0;
-        for (; oi < order.size() && group_of[oi] == int(gi); oi++) {
-            const int i = order[oi];
-            const Plan &P = plans[i];
-            int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
-            float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
-            cnt_off += P.cnt_bytes;
-            part_off += P.part_bytes;
-            Desc D = make_desc(P, p[i].w, p[i].x, p[i].ldx, p[i].y, p[i].ldy, part, cnt);
+        auto push = [&](Desc D) {
             D.wgu_begin = wgu;
             wgu += (D.wu_count + kWaves - 1) / kWaves;
             SP.descs.push_back(D);
+        };
+        for (int fmt = 1; fmt <= 5; fmt++) {
+            if (!(mask & fmt_bit(fmt))) continue;
+            for (int i = b; i < e; i++) {
+                const wqd_proj &q = p[i];
+                if (q.fmt != fmt || q.epi == WQD_EPI_SILU_UP) continue;
+                const Plan P = plan_cs(fmt, q.N, q.K, M, G.cs);
+                if (q.epi == WQD_EPI_SILU_GATE) {
+                    // gate and up share one slice counter per row group and one partial array
+                    const wqd_proj &r = p[i + 1];
+                    const Plan U = plan_cs(fmt, r.N, r.K, M, G.cs);
+                    const int64_t S_all = P.S + U.S;
+                    int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
+                    float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
+                    cnt_off += align_up(P.L.RG * 4, 256);
+                    part_off += align_up(M * S_all * P.L.Npad * 4, 256);
+                    Desc Dg = make_desc(P, q.w, q.x, q.ldx, q.y, q.ldy, part, cnt);
+                    Desc Du = make_desc(U, r.w, r.x, r.ldx, q.y, q.ldy, part, cnt);
+                    Dg.part = Du.part = part;
+                    Dg.cnt = Du.cnt = cnt;
+                    Dg.epi = Du.epi = kEpiSiluPair;
+                    Dg.S_all = Du.S_all = int32_t(S_all);
+                    Dg.S_first = Du.S_first = int32_t(P.S);
+                    Dg.slot0 = 0;
+                    Du.slot0 = int32_t(P.S);
+                    push(Dg);
+                    push(Du);
+                    SP.needs_ws = true;
+                } else {
+                    int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
+                    float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
+                    cnt_off += P.cnt_bytes;
+                    part_off += P.part_bytes;
+                    Desc D = make_desc(P, q.w, q.x, q.ldx, q.y, q.ldy, part, cnt);
+                    D.epi = (q.epi == WQD_EPI_ADD) ? kEpiAdd : kEpiNone;
+                    push(D);
+                    SP.needs_ws |= P.S > 1;
+                }
+            }
         }
         G.count = int(SP.descs.size()) - G.first;
         G.total_wgu = wgu;
-        G.cs = group_cs[gi];
         SP.groups.push_back(G);
     }
-    if (!aqplans.empty()) {
+    if (has_aq) {
+        // AQ2X8 projections: one launch, every workgroup taking one piece of each
+        const int64_t aq_wg = aq_nwg(M, cus);
         LaunchGroup G;
         G.mask = fmt_bit(AQ2X8);
         G.aq = true;
-        G.first = 0;
-        G.count = int(aqplans.size());
+        G.first = int(SP.aqdescs.size());
+        std::vector<AqPlan> plans;
+        std::vector<int> idx;
         int64_t total_pieces = 0;
-        for (const AqPlan &A : aqplans) total_pieces += A.a * A.b;
+        for (int i = b; i < e; i++) {
+            if (p[i].fmt != AQ2X8) continue;
+            plans.push_back(plan_aq(p[i].N, p[i].K, M, aq_wg));
+            idx.push_back(i);
+            total_pieces += plans.back().a * plans.back().b;
+        }
         G.nwg = total_pieces < aq_wg ? total_pieces : aq_wg;  // no idle workgroups
         int64_t off = 0;
-        for (size_t k = 0; k < aqplans.size(); k++) {
-            const AqPlan &A = aqplans[k];
-            const wqd_proj &q = p[aqidx[k]];
+        for (size_t k = 0; k < plans.size(); k++) {
+            const AqPlan &A = plans[k];
+            const wqd_proj &q = p[idx[k]];
             void *part = base ? static_cast<void *>(base + part_off) : nullptr;
             part_off += A.part_bytes;
+            SP.needs_ws |= A.b > 1;
             SP.aqdescs.push_back(make_aq_desc(A, q.w, q.x, q.ldx, q.y, q.ldy, part, off % G.nwg));
             off += A.a * A.b;
             if (A.RW > G.rw) G.rw = A.RW;
         }
+        G.count = int(plans.size());
         SP.groups.push_back(G);
     }
+}
+
+static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mode, void *ws, StackPlan &SP,
+                            int cus) {
+    if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
+    int rc = check_list(p, count, M);
+    if (rc != WQD_OK) return rc;
+    SP.off_descs = 0;
+    SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
+    SP.off_cnt = SP.off_ctr + 256;
+    int64_t cnt_all = 0;
+    for (int i = 0; i < count; i++) {
+        if (p[i].fmt == AQ2X8 || p[i].epi == WQD_EPI_SILU_UP) continue;
+        cnt_all += align_up(make_layout(p[i].fmt, p[i].N, p[i].K).RG * 4, 256);
+    }
+    SP.cnt_bytes = cnt_all > kCntRegion ? cnt_all : kCntRegion;
+    SP.off_part = SP.off_cnt + SP.cnt_bytes;
+    std::vector<std::pair<int, int>> seg;
+    list_segments(p, count, mode, seg);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int64_t part_used = 0;
+    for (const auto &sg : seg) {
+        int64_t cnt_off = SP.off_cnt, part_off = SP.off_part;
+        plan_segment(p, sg.first, sg.second, M, mode, base, cnt_off, part_off, SP, cus);
+        if (part_off - SP.off_part > part_used) part_used = part_off - SP.off_part;
+    }
+    SP.part_bytes = part_used;
     return WQD_OK;
 }
 
@@ -575,21 +660,24 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
 }
 
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs, int32_t count, int64_t M) {
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
-    StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, nullptr, SP, device_cus());
-    if (rc != WQD_OK) return rc;
-    return SP.total;
+    // enough for every mode
+    int64_t need = 0;
+    for (int mode : {WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED}) {
+        StackPlan SP;
+        int rc = build_stack_plan(projs, count, M, mode, nullptr, SP, device_cus());
+        if (rc != WQD_OK) return rc;
+        if (SP.total() > need) need = SP.total();
+    }
+    return need;
 }
 
 WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, void *workspace,
                             int64_t workspace_bytes, void *stream) {
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     if (!workspace) return WQD_EINVAL;
     StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, workspace, SP, device_cus());
+    int rc = build_stack_plan(projs, count, M, WQD_PERSISTENT, workspace, SP, device_cus());
     if (rc != WQD_OK) return rc;
-    if (workspace_bytes < SP.total) return WQD_ESPACE;
+    if (workspace_bytes < SP.total()) return WQD_ESPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *base = static_cast<uint8_t *>(workspace);
     hipError_t e = hipSuccess;
@@ -610,41 +698,16 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, voi
 static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
                                 void *workspace, int64_t workspace_bytes, hipStream_t st,
                                 void *const *events, int32_t n_events) {
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
-    if (mode != WQD_ORDERED && mode != WQD_PERSISTENT) return WQD_EINVAL;
     if (n_events < 0 || (n_events > 0 && !events)) return WQD_EINVAL;
     const int cus = device_cus();
     StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, workspace, SP, cus);
+    int rc = build_stack_plan(projs, count, M, mode, workspace, SP, cus);
     if (rc != WQD_OK) return rc;
     uint8_t *base = static_cast<uint8_t *>(workspace);
-    if (mode == WQD_ORDERED) {
-        // one launch per projection, on the stack workspace's counter and partial regions
-        if (n_events != 0) return WQD_EINVAL;
-        const int64_t aq_wg = aq_nwg(M, cus);
-        bool split = false;
-        for (int i = 0; i < count; i++) {
-            if (projs[i].fmt == AQ2X8) split |= plan_aq(projs[i].N, projs[i].K, M, aq_wg).b > 1;
-            else split |= plan_single(projs[i].fmt, projs[i].N, projs[i].K, M, cus).S > 1;
-        }
-        if (split && (!base || workspace_bytes < SP.total)) return WQD_ESPACE;
-        int *cnt = base ? reinterpret_cast<int *>(base + SP.off_cnt) : nullptr;
-        float *part = base ? reinterpret_cast<float *>(base + SP.off_part) : nullptr;
-        for (int i = 0; i < count; i++) {
-            const wqd_proj &q = projs[i];
-            if (q.fmt == AQ2X8) {
-                AqPlan A = plan_aq(q.N, q.K, M, aq_wg);
-                rc = aq_gemm_launch(A, aq_wg, q.w, q.x, M, q.ldx, q.y, q.ldy, part, st);
-            } else {
-                Plan P = plan_single(q.fmt, q.N, q.K, M, cus);
-                rc = gemm_launch(P, q.w, q.x, M, q.ldx, q.y, q.ldy, cnt, part, st, cus);
-            }
-            if (rc != WQD_OK) return rc;
-        }
-        return WQD_OK;
-    }
-    if (!base) return WQD_EINVAL;
-    if (workspace_bytes < SP.total) return WQD_ESPACE;
+    // WQD_PERSISTENT reads the descriptor tables wqd_stack_setup wrote; the other modes pass
+    // their descriptors in the kernel arguments and need the workspace only to count slices.
+    if (mode == WQD_PERSISTENT && !base) return WQD_EINVAL;
+    if ((mode == WQD_PERSISTENT || SP.needs_ws) && (!base || workspace_bytes < SP.total())) return WQD_ESPACE;
     const int launches = int(SP.groups.size());
     if (n_events != 0 && n_events != 2 * launches) return WQD_ESPACE;
     int li = 0;
@@ -653,17 +716,19 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * li + which]), st);
         return e == hipSuccess ? WQD_OK : hip_fail(e);
     };
-    const Desc *dtab = reinterpret_cast<const Desc *>(base + SP.off_descs);
-    const AqDesc *atab = reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs);
+    const bool table = (mode == WQD_PERSISTENT);
+    const Desc *dtab = table ? reinterpret_cast<const Desc *>(base + SP.off_descs) : nullptr;
+    const AqDesc *atab = table ? reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs) : nullptr;
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
         const LaunchGroup &G = SP.groups[gi];
         if (G.aq) {
             AqParams AP;
             memset(&AP, 0, sizeof(AP));
             AP.d0 = SP.aqdescs[G.first];
-            AP.descs = atab + G.first;
+            AP.descs = table ? atab + G.first : nullptr;
             AP.ndesc = G.count;
             AP.nwg = int32_t(G.nwg);
+            if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
             rc = launch_aq(M, G.rw, AP, st);
             if (rc != WQD_OK) return rc;
@@ -673,14 +738,20 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         }
         GemvParams GP;
         memset(&GP, 0, sizeof(GP));
-        GP.d0 = SP.descs[G.first];
-        GP.descs = dtab + G.first;
+        if (table) {
+            GP.descs = dtab + G.first;
+        } else {
+            if (G.count > kInlineDescs) return WQD_EINVAL;  // (segments are cut to fit)
+            for (int k = 0; k < G.count; k++) GP.d[k] = SP.descs[G.first + k];
+            GP.descs = nullptr;
+        }
         GP.ndesc = G.count;
         GP.total_wgu = G.total_wgu;
         // The dynamic tail pays a barrier, an atomic and a cold load pipeline per unit it hands
-        // out: only units of long slices amortize that.
-        if (WQD_POOL_PERCENT > 0 && G.cs >= WQD_POOL_MIN_CS) {
-            GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr) + 2 * gi;
+        // out: only units of long slices amortize that.  (Launches run one after another, and
+        // each leaves its two counters at zero.)
+        if (WQD_POOL_PERCENT > 0 && G.cs >= WQD_POOL_MIN_CS && base) {
+            GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr) + (table ? 2 * gi : 0);
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }
         if ((rc = mark(0)) != WQD_OK) return rc;
@@ -698,10 +769,9 @@ WQD_API int wqd_run_projections(const wqd_proj *projs, int32_t count, int64_t M,
                                 static_cast<hipStream_t>(stream), nullptr, 0);
 }
 
-WQD_API int wqd_stack_launches(const wqd_proj *projs, int32_t count, int64_t M) {
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+WQD_API int wqd_stack_launches(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode) {
     StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, nullptr, SP, device_cus());
+    int rc = build_stack_plan(projs, count, M, mode, nullptr, SP, device_cus());
     if (rc != WQD_OK) return rc;
     return int(SP.groups.size());
 }

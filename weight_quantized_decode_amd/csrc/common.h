@@ -76,10 +76,24 @@ struct Desc {
     int32_t wgu_begin;  // first workgroup-unit of this projection
     int32_t wu_count;   // wave units = RG * S
     int32_t fmt;        // wqd format id of this projection
+    // Epilogue and split-K slots.  Partial sums live at part[m][slot][Npad] with S_all slots per
+    // activation row; this projection's K-slice s writes slot slot0 + s, and the row group is
+    // done when S_all slices have arrived.  A gate/up pair (kEpiSiluPair) shares cnt, part and y:
+    // gate slots [0, S_first), up slots [S_first, S_all).  S_all == 1: no split, y written directly.
+    int32_t epi;        // kEpiNone, kEpiAdd or kEpiSiluPair
+    int32_t slot0, S_all, S_first;
 };
 
+constexpr int kEpiNone = 0;      // y = x W^T
+constexpr int kEpiAdd = 1;       // y += x W^T (the residual add of the o and down projections)
+constexpr int kEpiSiluPair = 2;  // y = SiLU(x Wg^T) * (x Wu^T), both descriptors of a gate/up pair
+
+// Descriptors a launch carries in its kernel arguments (a fused group of projections: q/k/v, a
+// gate/up pair); larger lists use a table in device memory.
+constexpr int kInlineDescs = 4;
+
 struct GemvParams {
-    Desc d0;             // used when descs == nullptr
+    Desc d[kInlineDescs]; // the descriptors when descs == nullptr
     const Desc *descs;   // device array (stack)
     int32_t ndesc;
     int32_t total_wgu;

@@ -580,57 +580,83 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                 if (4 * h + v < M) acc[4 * h + v] += (NCH == 2) ? MFA[0][h][v] + MFA[NCH - 1][h][v] : MFA[0][h][v];
     }
 
-    if (D.S == 1) {
+    if (D.S_all == 1) {
         if (row < D.N) {
 #pragma unroll
-            for (int m = 0; m < M; m++) gst(D.y + (int64_t)m * D.ldy + row, acc[m]);
+            for (int m = 0; m < M; m++) {
+                float *py = D.y + (int64_t)m * D.ldy + row;
+                gst(py, D.epi == kEpiAdd ? gld<float>(py) + acc[m] : acc[m]);
+            }
         }
         return;
     }
     // Split K: publish this slice's partial sums, then count the finished slices of the row
-    // group; the wave that finishes the last slice adds all slices in ascending order and writes
-    // y.  The partials are written and read with device-coherent (agent scope) accesses, which
-    // go through to memory instead of a single XCD's L2; the wait below makes the stores
-    // complete before the counter is incremented, so whoever sees the final count sees them.
+    // group; the wave that finishes the last slice adds all slices in ascending order, applies
+    // the epilogue and writes y.  A gate/up pair shares one counter and one partial array: the
+    // gate's slices are slots [0, S_first), the up's [S_first, S_all), and the last of all its
+    // slices writes SiLU(gate) * up.  The partials are written and read with device-coherent
+    // (agent scope) accesses, which go through to memory instead of a single XCD's L2; the wait
+    // below makes the stores complete before the counter is incremented, so whoever sees the
+    // final count sees them.
 #pragma unroll
     for (int m = 0; m < M; m++)
-        __hip_atomic_store(as_global(D.part + ((int64_t)m * D.S + s) * D.Npad + row), acc[m], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(as_global(D.part + ((int64_t)m * D.S_all + D.slot0 + s) * D.Npad + row), acc[m],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     int done = 0;
     if (lane == 0) done = __hip_atomic_fetch_add(as_global(D.cnt + g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     done = __builtin_amdgcn_readfirstlane(done);
-    if (done == D.S - 1) {
-#pragma unroll
-        for (int m = 0; m < M; m++) {
-            const float *pm = D.part + (int64_t)m * D.S * D.Npad + row;
+    if (done == D.S_all - 1) {
+        // slots [s0, s1) of one activation row, 8 loads in flight at a time, added in ascending order
+        auto slot_sum = [&](const float *pm, int s0, int s1) {
             float sum = 0.f;
-            // 8 loads in flight at a time, added in ascending slice order
-            for (int k0 = 0; k0 < D.S; k0 += 8) {
+            for (int k0 = s0; k0 < s1; k0 += 8) {
                 float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; j++)
-                    v[j] = (k0 + j < D.S) ? __hip_atomic_load(as_global(pm + (int64_t)(k0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                          : 0.f;
+                    v[j] = (k0 + j < s1) ? __hip_atomic_load(as_global(pm + (int64_t)(k0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; j++) sum += v[j];
             }
-            if (row < D.N) gst(D.y + (int64_t)m * D.ldy + row, sum);
+            return sum;
+        };
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float *pm = D.part + (int64_t)m * D.S_all * D.Npad + row;
+            float *py = D.y + (int64_t)m * D.ldy + row;
+            float out;
+            if (D.epi == kEpiSiluPair) {
+                const float gsum = slot_sum(pm, 0, D.S_first);
+                const float usum = slot_sum(pm, D.S_first, D.S_all);
+                out = gsum / (1.f + expf(-gsum)) * usum;  // SiLU(g) = g * sigma(g); -0 for g -> -inf
+            } else {
+                out = slot_sum(pm, 0, D.S_all);
+                if (D.epi == kEpiAdd && row < D.N) out = gld<float>(py) + out;
+            }
+            if (row < D.N) gst(py, out);
         }
         if (lane == 0) __hip_atomic_store(as_global(D.cnt + g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // Index of the projection owning workgroup unit u (uniform binary search over the descriptors).
-__device__ __forceinline__ int find_proj(const GemvParams &P, int u) {
-    if (!P.descs) return 0;
-    int lo = 0, hi = P.ndesc - 1;
+__device__ __forceinline__ int find_proj(const Desc *tab, int ndesc, int u) {
+    int lo = 0, hi = ndesc - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (load_wgu_begin(P.descs + mid) <= u) lo = mid; else hi = mid - 1;
+        if (load_wgu_begin(tab + mid) <= u) lo = mid; else hi = mid - 1;
     }
     return lo;
+}
+// The launch's descriptors: a table in device memory, or the array in the kernel arguments.  The
+// latter is addressed in the kernel-argument segment, where the kernel's only argument (the
+// GemvParams, descriptor array first) starts at offset 0; taking the address of the parameter
+// itself would make the compiler copy all of it to scratch memory.
+__device__ __forceinline__ const Desc *desc_table(const GemvParams &P) {
+    static_assert(offsetof(GemvParams, d) == 0, "inline descriptors open the kernel arguments");
+    return P.descs ? P.descs : (const Desc *)(uintptr_t)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
 // One workgroup unit: kWaves wave units of one projection, one per wave.  The LDS table is
@@ -640,18 +666,17 @@ template <int MASK, int M>
 __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, int wid,
                                         int lane) {
     // Units are visited in increasing order: search only for the first one, then step forward.
-    int p = 0;
-    if (P.descs) {
-        if (cur < 0) {
-            p = find_proj(P, u);
-        } else {
-            p = cur;
-            while (p + 1 < P.ndesc && load_wgu_begin(P.descs + p + 1) <= u) p++;
-        }
+    const Desc *tab = desc_table(P);
+    int p;
+    if (cur < 0) {
+        p = find_proj(tab, P.ndesc, u);
+    } else {
+        p = cur;
+        while (p + 1 < P.ndesc && load_wgu_begin(tab + p + 1) <= u) p++;
     }
     bool rebuild = false;
     if (p != cur) {
-        if (P.descs) D = load_desc(P.descs + p);
+        D = load_desc(tab + p);
         rebuild = true;
         cur = p;
     }
@@ -710,7 +735,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     const int u0 = b * per + min(b, rem);
     const int u1 = u0 + per + (b < rem ? 1 : 0);
     int cur = -1;
-    Desc D = P.d0;
+    Desc D;
     for (int u = u0; u < u1; u++) run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
     if (kPool && P.ctr) {
         while (true) {
