@@ -215,3 +215,42 @@ def test_fused_runs_are_deterministic_and_leave_counters_zero():
     for o in outs[2:]:
         for a, b in zip(outs[0], o):
             np.testing.assert_allclose(a, b, rtol=1e-3, atol=1e-3)
+
+
+def test_fused_layer_in_a_graph_replays_like_eager():
+    """A FUSED call captured in a HIP graph: every replay (with eager work and synchronization
+    in between) gives the eager call's bits."""
+    import torch
+    M = 1
+    note("fused layer captured in a graph, 3 replays")
+    ent, host = _layer_entries(M, 3, scale=4)
+    arr = W.make_proj_array(ent)
+    ws = workspace(W.wqd_stack_workspace_bytes(arr, M))
+    outs = [e["y"] for e in ent if e["y"] is not None]
+
+    def reset():
+        for y in outs:
+            y.fill_(0.5)
+
+    reset()
+    W.wqd_run_projections(arr, M, W.WQD_FUSED, ws)
+    W.wqd_stream_check()
+    eager = [y.cpu().numpy().copy() for y in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        W.wqd_run_projections(arr, M, W.WQD_FUSED, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        W.wqd_run_projections(arr, M, W.WQD_FUSED, ws)
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, y in zip(eager, outs):
+            assert np.array_equal(a, y.cpu().numpy()), f"replay {rep} differs from the eager call"
+    del g
