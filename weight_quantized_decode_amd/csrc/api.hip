@@ -103,13 +103,13 @@ static int device_cus() {
     return cached_cus;
 }
 
-static GemvFn pick_gemv(int mask, int M) {
+static GemvFn pick_gemv(int mask, int M, bool epi = false) {
     switch (mask) {
-    case 1 << Q4_0: return gemv_fn_q4_0(M);
-    case 1 << CB4: return gemv_fn_cb4(M);
-    case 1 << CB8: return gemv_fn_cb8(M);
-    case 1 << TQ2: return gemv_fn_tq2(M);
-    case kMaskCB48: return gemv_fn_cb48(M);
+    case 1 << Q4_0: return gemv_fn_q4_0(M, epi);
+    case 1 << CB4: return gemv_fn_cb4(M, epi);
+    case 1 << CB8: return gemv_fn_cb8(M, epi);
+    case 1 << TQ2: return gemv_fn_tq2(M, epi);
+    case kMaskCB48: return gemv_fn_cb48(M, epi);
     }
     return nullptr;
 }
@@ -172,6 +172,7 @@ constexpr int64_t kMaxSplitRG = kCntRegion / 4;  // row groups one split call ca
 struct Plan {
     Layout L;
     int64_t CS = 0, S = 1;
+    bool wsplit = false;     // workgroup-split units (CS = kWaves pieces of CS / kWaves chunks)
     int64_t cnt_bytes = 0;   // one int per row group when S > 1 (256-byte aligned)
     int64_t part_bytes = 0;  // M * S * Npad * 4 when S > 1 (256-byte aligned)
     // wqd_gemm workspace: [kCntRegion bytes of counters][partials]
@@ -196,6 +197,56 @@ static Plan plan_cs(int fmt, int64_t N, int64_t K, int64_t M, int64_t cs_target)
     return finish_plan(P, M);
 }
 
+// A projection in workgroup-split units of about `cw_target` chunks per wave: slices of
+// kWaves * cw chunks, made as equal as the format's alignment allows.  (Falls back to plan_cs
+// when the row groups are too many to count and one slice cannot cover a row.)
+static Plan plan_ws(int fmt, int64_t N, int64_t K, int64_t M, int64_t cw_target) {
+    Plan P;
+    P.L = make_layout(fmt, N, K);
+    if (!P.L.ok) return P;
+    const int64_t mult = (fmt == TQ2) ? 8 : (fmt == Q4_0) ? 4 : 1;
+    const int64_t cap = (fmt == Q4_0) ? 64 : (fmt == TQ2) ? 128 : (int64_t(1) << 30);
+    const int64_t C = P.L.C;
+    int64_t cw = align_up(cw_target < 1 ? 1 : cw_target, mult);
+    if (cw > cap) cw = cap;
+    int64_t S = (C + kWaves * cw - 1) / (kWaves * cw);
+    if (P.L.RG > kMaxSplitRG) S = 1;
+    cw = align_up((C + kWaves * S - 1) / (kWaves * S), mult);
+    if (cw > cap) {
+        if (P.L.RG > kMaxSplitRG) return plan_cs(fmt, N, K, M, C);
+        cw = cap;
+    }
+    P.wsplit = true;
+    P.CS = kWaves * cw;
+    P.S = (C + P.CS - 1) / P.CS;
+    P.cnt_bytes = (P.S > 1) ? align_up(P.L.RG * 4, 256) : 0;
+    P.part_bytes = (P.S > 1) ? align_up(M * P.S * P.L.Npad * 4, 256) : 0;
+    return P;
+}
+
+// K-slicing of a launch group: chunks per wave and whether units are workgroup-split.  A group
+// whose work per resident wave is short splits each slice over a workgroup's waves, so all
+// waves get work without cutting rows into many slices whose partial sums go through memory.
+struct SliceTarget {
+    int64_t cs = 0;
+    bool ws = false;
+};
+static SliceTarget slice_target(int mask, int64_t total_cc, int64_t waves, int64_t M) {
+    SliceTarget t;
+    const int64_t per = total_cc / waves;
+    // (TQ2 slices move in 8-chunk scale quads, too coarse to share a row between 8 waves)
+    if (per < WQD_WSPLIT_BELOW && !(mask & fmt_bit(TQ2))) {
+        t.ws = true;
+        t.cs = per < WQD_WSPLIT_MIN ? WQD_WSPLIT_MIN : per;
+    } else {
+        t.cs = target_cs(total_cc, waves, M);
+    }
+    return t;
+}
+static Plan plan_target(int fmt, int64_t N, int64_t K, int64_t M, const SliceTarget &t) {
+    return t.ws ? plan_ws(fmt, N, K, M, t.cs) : plan_cs(fmt, N, K, M, t.cs);
+}
+
 // One projection alone.
 static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
     Layout L = make_layout(fmt, N, K);
@@ -204,7 +255,7 @@ static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
         P.L = L;
         return P;
     }
-    return plan_cs(fmt, N, K, M, target_cs(L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus), M));
+    return plan_target(fmt, N, K, M, slice_target(fmt_bit(fmt), L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus), M));
 }
 
 static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
@@ -230,7 +281,8 @@ static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, 
     D.Q = int32_t(P.L.Q);
     D.RG = int32_t(P.L.RG);
     D.Npad = int32_t(P.L.Npad);
-    D.wu_count = int32_t(P.L.RG * P.S);
+    D.wsplit = P.wsplit ? 1 : 0;
+    D.wu_count = int32_t(P.L.RG * P.S * (P.wsplit ? kWaves : 1));
     D.wgu_begin = 0;
     D.fmt = P.L.fmt;
     D.epi = kEpiNone;
@@ -240,8 +292,8 @@ static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, 
     return D;
 }
 
-static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus) {
-    GemvFn fn = pick_gemv(mask, M);
+static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus, bool epi = false) {
+    GemvFn fn = pick_gemv(mask, M, epi);
     if (!fn) return WQD_EINVAL;
     int64_t grid = int64_t(cus) * resident_per_cu(fn);
     if (grid > GP.total_wgu) grid = GP.total_wgu;
@@ -399,6 +451,7 @@ struct LaunchGroup {
     int first = 0, count = 0;  // range in StackPlan::descs (or StackPlan::aqdescs)
     int total_wgu = 0;
     bool aq = false;           // an AQ2X8 launch
+    bool epi = false;          // some descriptor applies an epilogue
     int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
 };
 
@@ -487,7 +540,8 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
         }
         LaunchGroup G;
         G.mask = mask;
-        G.cs = target_cs(total_cc, resident_waves(mask, M, cus), M);
+        const SliceTarget tgt = slice_target(mask, total_cc, resident_waves(mask, M, cus), M);
+        G.cs = tgt.ws ? 0 : tgt.cs;  // (the dynamic tail serves long slices only)
         G.first = int(SP.descs.size());
         int wgu = 0;
         auto push = [&](Desc D) {
@@ -500,11 +554,11 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
             for (int i = b; i < e; i++) {
                 const wqd_proj &q = p[i];
                 if (q.fmt != fmt || q.epi == WQD_EPI_SILU_UP) continue;
-                const Plan P = plan_cs(fmt, q.N, q.K, M, G.cs);
+                const Plan P = plan_target(fmt, q.N, q.K, M, tgt);
                 if (q.epi == WQD_EPI_SILU_GATE) {
                     // gate and up share one slice counter per row group and one partial array
                     const wqd_proj &r = p[i + 1];
-                    const Plan U = plan_cs(fmt, r.N, r.K, M, G.cs);
+                    const Plan U = plan_target(fmt, r.N, r.K, M, tgt);
                     const int64_t S_all = P.S + U.S;
                     int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
                     float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
@@ -536,6 +590,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
         }
         G.count = int(SP.descs.size()) - G.first;
         G.total_wgu = wgu;
+        for (int k = G.first; k < G.first + G.count; k++) G.epi |= SP.descs[k].epi != kEpiNone;
         SP.groups.push_back(G);
     }
     if (has_aq) {
@@ -755,7 +810,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }
         if ((rc = mark(0)) != WQD_OK) return rc;
-        rc = launch_gemv(G.mask, int(M), GP, st, cus);
+        rc = launch_gemv(G.mask, int(M), GP, st, cus, G.epi);
         if (rc != WQD_OK) return rc;
         if ((rc = mark(1)) != WQD_OK) return rc;
         li++;

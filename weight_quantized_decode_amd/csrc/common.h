@@ -54,6 +54,14 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #ifndef WQD_MF_U_WIDE
 #define WQD_MF_U_WIDE 4  // the same for CB4 at M > 4
 #endif
+// Launch groups whose work per resident wave is below WQD_WSPLIT_BELOW chunks use workgroup-split
+// units of at least WQD_WSPLIT_MIN chunks per wave.
+#ifndef WQD_WSPLIT_BELOW
+#define WQD_WSPLIT_BELOW 64
+#endif
+#ifndef WQD_WSPLIT_MIN
+#define WQD_WSPLIT_MIN 4
+#endif
 #ifndef WQD_STACK_MF_CS
 #define WQD_STACK_MF_CS 128  // largest stack K-slice (chunks) of the matrix-core instances
 #endif
@@ -69,7 +77,7 @@ struct Desc {
     const uint16_t *cbk;
     const uint16_t *x;
     float *y;
-    float *part;        // split-K partials [M][S][Npad], or null when S == 1
+    float *part;        // split-K partials [M][S_all][Npad], or null when S_all == 1
     int *cnt;           // per row group: K-slices finished (zero between calls), or null
     int64_t ldx, ldy;
     int32_t N, K, C, C_full, S, CS, Q, RG, Npad;
@@ -82,6 +90,12 @@ struct Desc {
     // gate slots [0, S_first), up slots [S_first, S_all).  S_all == 1: no split, y written directly.
     int32_t epi;        // kEpiNone, kEpiAdd or kEpiSiluPair
     int32_t slot0, S_all, S_first;
+    // Workgroup split (launches too small to give every wave a long slice): a workgroup unit is
+    // row group g times one K-slice of CS chunks, cut into kWaves consecutive pieces of CS/kWaves
+    // chunks, one per wave, added through LDS; wu_count = RG * S * kWaves.  Otherwise a wave
+    // unit is one slice of CS chunks and wu_count = RG * S.
+    int32_t wsplit;
+    int32_t pad_;
 };
 
 constexpr int kEpiNone = 0;      // y = x W^T
@@ -174,11 +188,12 @@ typedef void (*AqFn)(AqParams);
 AqFn aq_fn(int M, int RW);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
-// 8-bit head), each defined in its own translation unit.
-GemvFn gemv_fn_q4_0(int M);
-GemvFn gemv_fn_cb4(int M);
-GemvFn gemv_fn_cb8(int M);
-GemvFn gemv_fn_tq2(int M);
-GemvFn gemv_fn_cb48(int M);
+// 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies
+// epilogues (residual add, SiLU pair).
+GemvFn gemv_fn_q4_0(int M, bool epi);
+GemvFn gemv_fn_cb4(int M, bool epi);
+GemvFn gemv_fn_cb8(int M, bool epi);
+GemvFn gemv_fn_tq2(int M, bool epi);
+GemvFn gemv_fn_cb48(int M, bool epi);
 
 }  // namespace wqd

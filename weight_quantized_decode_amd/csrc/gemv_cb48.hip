@@ -5,11 +5,11 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_cb48(int M) {
+GemvFn gemv_fn_cb48(int M, bool epi) {
     switch (M) {
-    case 1: return gemv_kernel<kMaskCB48, 1>;
+    case 1: return epi ? gemv_kernel<kMaskCB48, 1, true> : gemv_kernel<kMaskCB48, 1, false>;
 #if WQD_MFMA_MIN_M > 2
-    case 2: return gemv_kernel<kMaskCB48, 2>;
+    case 2: return epi ? gemv_kernel<kMaskCB48, 2, true> : gemv_kernel<kMaskCB48, 2, false>;
 #endif
     }
     static_assert(WQD_MFMA_MIN_M >= 2 && WQD_MFMA_MIN_M <= 3, "instances listed for M < WQD_MFMA_MIN_M");

@@ -189,12 +189,25 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
 // ------------------------------------------------------------------------------------------
 // `hook` runs once, right after the first loads of the unit are issued: the workgroup uses it
 // to (re)build its LDS table while those loads are in flight.
-template <int FMT, int M, typename Hook>
-__device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32_t *lds, Hook &&hook) {
-    const int g = wu / D.S;
-    const int s = wu - g * D.S;
-    const int cb = s * D.CS;
-    const int ce = min(D.C, cb + D.CS);
+template <int FMT, int M, bool EPI, typename Hook>
+__device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32_t *lds, float *red, Hook &&hook) {
+    // Wave unit -> (row group g, K-slice s, chunks [cb, ce)).  Workgroup-split descriptors give
+    // the kWaves waves of a workgroup unit consecutive pieces of one slice of D.CS chunks (the
+    // last pieces of a row may be empty); otherwise a wave unit is a whole slice.
+    int g, s, cb, ce;
+    if (D.wsplit) {
+        const int q = wu / kWaves, w = wu - q * kWaves;
+        g = q / D.S;
+        s = q - g * D.S;
+        const int cw = D.CS / kWaves;
+        cb = min(D.C, s * D.CS + w * cw);
+        ce = min(D.C, cb + cw);
+    } else {
+        g = wu / D.S;
+        s = wu - g * D.S;
+        cb = s * D.CS;
+        ce = min(D.C, cb + D.CS);
+    }
     const int row = g * 64 + lane;
     const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
     const uint16_t *xrow[M];
@@ -580,12 +593,46 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                 if (4 * h + v < M) acc[4 * h + v] += (NCH == 2) ? MFA[0][h][v] + MFA[NCH - 1][h][v] : MFA[0][h][v];
     }
 
-    if (D.S_all == 1) {
-        if (row < D.N) {
+    if (D.wsplit) {
+        // Workgroup split: add the kWaves pieces in wave order through LDS (RM activation rows
+        // per round); wave 0 goes on with the slice's sums.  The first barrier of a round keeps
+        // the buffer until wave 0 has read the previous round (or the previous unit).
+        const int w = wu % kWaves;
+        constexpr int RM = M < 4 ? M : 4;
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                float *py = D.y + (int64_t)m * D.ldy + row;
-                gst(py, D.epi == kEpiAdd ? gld<float>(py) + acc[m] : acc[m]);
+        for (int m0 = 0; m0 < M; m0 += RM) {
+            lds_barrier();
+#pragma unroll
+            for (int r = 0; r < RM; r++)
+                if (m0 + r < M) red[(r * kWaves + w) * 64 + lane] = acc[m0 + r];
+            lds_barrier();
+            if (w == 0) {
+#pragma unroll
+                for (int r = 0; r < RM; r++) {
+                    if (m0 + r < M) {
+                        float t = red[(r * kWaves) * 64 + lane];
+#pragma unroll
+                        for (int v = 1; v < kWaves; v++) t += red[(r * kWaves + v) * 64 + lane];
+                        acc[m0 + r] = t;
+                    }
+                }
+            }
+        }
+        if (w != 0) return;
+    }
+
+    if (D.S_all == 1) {
+        // (two uniform branches: the residual is loaded only when it is added)
+        if (row < D.N) {
+            if (EPI && D.epi == kEpiAdd) {
+                float old[M];
+#pragma unroll
+                for (int m = 0; m < M; m++) old[m] = gld<float>(D.y + (int64_t)m * D.ldy + row);
+#pragma unroll
+                for (int m = 0; m < M; m++) gst(D.y + (int64_t)m * D.ldy + row, old[m] + acc[m]);
+            } else {
+#pragma unroll
+                for (int m = 0; m < M; m++) gst(D.y + (int64_t)m * D.ldy + row, acc[m]);
             }
         }
         return;
@@ -627,13 +674,13 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
             const float *pm = D.part + (int64_t)m * D.S_all * D.Npad + row;
             float *py = D.y + (int64_t)m * D.ldy + row;
             float out;
-            if (D.epi == kEpiSiluPair) {
+            if (EPI && D.epi == kEpiSiluPair) {
                 const float gsum = slot_sum(pm, 0, D.S_first);
                 const float usum = slot_sum(pm, D.S_first, D.S_all);
                 out = gsum / (1.f + expf(-gsum)) * usum;  // SiLU(g) = g * sigma(g); -0 for g -> -inf
             } else {
                 out = slot_sum(pm, 0, D.S_all);
-                if (D.epi == kEpiAdd && row < D.N) out = gld<float>(py) + out;
+                if (EPI && D.epi == kEpiAdd && row < D.N) out = gld<float>(py) + out;
             }
             if (row < D.N) gst(py, out);
         }
@@ -662,8 +709,8 @@ __device__ __forceinline__ const Desc *desc_table(const GemvParams &P) {
 // One workgroup unit: kWaves wave units of one projection, one per wave.  The LDS table is
 // rebuilt (between two barriers, so all waves of the workgroup take part) when the projection
 // changes.
-template <int MASK, int M>
-__device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, int wid,
+template <int MASK, int M, bool EPI>
+__device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, float *red, int wid,
                                         int lane) {
     // Units are visited in increasing order: search only for the first one, then step forward.
     const Desc *tab = desc_table(P);
@@ -696,13 +743,13 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
         if constexpr (MASK == kMaskCB48) {
             // two formats: one branch or the other (not two independent ifs, which let
             // the compiler keep values of both bodies live at once)
-            if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
-            else run_unit<CB8, M>(D, wu, lane, lds, hook);
+            if (D.fmt == CB4) run_unit<CB4, M, EPI>(D, wu, lane, lds, red, hook);
+            else run_unit<CB8, M, EPI>(D, wu, lane, lds, red, hook);
         } else {
-            if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M>(D, wu, lane, lds, hook);
-            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M>(D, wu, lane, lds, hook);
-            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M>(D, wu, lane, lds, hook);
-            if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M>(D, wu, lane, lds, hook);
+            if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M, EPI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M, EPI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M, EPI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M, EPI>(D, wu, lane, lds, red, hook);
         }
     } else {
         hook();
@@ -712,16 +759,17 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
 // Every instance is compiled for WQD_WG_PER_CU (2) resident 8-wave workgroups per CU, i.e. 4
 // waves per SIMD and at most 128 VGPRs; the launch sizes its persistent grid from the same
 // constant (the runtime occupancy query under-reports kernels without AGPRs).
-template <int MASK, int M>
 constexpr int kMinWavesPerEU = WQD_WG_PER_CU * kWaves / 4;
 
 // Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
 // [0, pool_begin) are split into equal contiguous ranges, one per workgroup; the rest are handed
 // out one by one from a device-wide counter to whichever workgroup is free, which evens out the
-// finish times (workgroups on different XCDs stream at different speeds).
-template <int MASK, int M>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<MASK, M>))) void gemv_kernel(GemvParams P) {
+// finish times (workgroups on different XCDs stream at different speeds).  EPI: the instance
+// applies the descriptors' epilogues (lists without any use the instance without that code).
+template <int MASK, int M, bool EPI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU))) void gemv_kernel(GemvParams P) {
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
+    __shared__ float red[kWaves * (M < 4 ? M : 4) * 64];  // workgroup-split sums
     __shared__ int next_u;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -736,7 +784,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     const int u1 = u0 + per + (b < rem ? 1 : 0);
     int cur = -1;
     Desc D;
-    for (int u = u0; u < u1; u++) run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
+    for (int u = u0; u < u1; u++) run_wgu<MASK, M, EPI>(P, u, cur, D, lds, red, wid, lane);
     if (kPool && P.ctr) {
         while (true) {
             __syncthreads();
@@ -745,7 +793,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
             __syncthreads();
             const int u = __builtin_amdgcn_readfirstlane(next_u);
             if (u >= total) break;
-            run_wgu<MASK, M>(P, u, cur, D, lds, wid, lane);
+            run_wgu<MASK, M, EPI>(P, u, cur, D, lds, red, wid, lane);
         }
         // Every workgroup has taken its last index once it reaches here; the last one to arrive
         // resets the counters for the next launch on this workspace.
@@ -759,19 +807,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     }
 }
 
-template <int MASK>
-GemvFn gemv_fn(int M) {
+template <int MASK, bool EPI>
+GemvFn gemv_fn_epi(int M) {
     switch (M) {
-    case 1: return gemv_kernel<MASK, 1>;
-    case 2: return gemv_kernel<MASK, 2>;
-    case 3: return gemv_kernel<MASK, 3>;
-    case 4: return gemv_kernel<MASK, 4>;
-    case 5: return gemv_kernel<MASK, 5>;
-    case 6: return gemv_kernel<MASK, 6>;
-    case 7: return gemv_kernel<MASK, 7>;
-    case 8: return gemv_kernel<MASK, 8>;
+    case 1: return gemv_kernel<MASK, 1, EPI>;
+    case 2: return gemv_kernel<MASK, 2, EPI>;
+    case 3: return gemv_kernel<MASK, 3, EPI>;
+    case 4: return gemv_kernel<MASK, 4, EPI>;
+    case 5: return gemv_kernel<MASK, 5, EPI>;
+    case 6: return gemv_kernel<MASK, 6, EPI>;
+    case 7: return gemv_kernel<MASK, 7, EPI>;
+    case 8: return gemv_kernel<MASK, 8, EPI>;
     }
     return nullptr;
+}
+template <int MASK>
+GemvFn gemv_fn(int M, bool epi) {
+    return epi ? gemv_fn_epi<MASK, true>(M) : gemv_fn_epi<MASK, false>(M);
 }
 
 }  // namespace wqd

@@ -2,5 +2,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_tq2(int M) { return gemv_fn<fmt_bit(TQ2)>(M); }
+GemvFn gemv_fn_tq2(int M, bool epi) { return gemv_fn<fmt_bit(TQ2)>(M, epi); }
 }  // namespace wqd
