@@ -148,6 +148,16 @@ enum {
                            one run must not write the same y elements. */
 };
 
+/* Flag OR-ed into a mode: batch-invariant results (trapetum "Benchmarks", November update: a
+ * draft of M tokens verified in one pass whose rows carry, bit for bit, the logits of M decode
+ * steps).  With it, row m of a call with M activation rows is bitwise equal to the same call
+ * made with row m alone (M = 1), for every M <= 8, in every mode and whatever else the list
+ * holds: every projection is sliced as it would be alone at M = 1, and every M runs the same
+ * per-row instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
+ * A verify of 9..16 rows is two calls.  Row formats only: a list with an AQ2X8 entry returns
+ * WQD_EINVAL.  Results differ in rounding (within the bound) from calls without the flag. */
+enum { WQD_BATCH_INVARIANT = 0x10 };
+
 /* Device workspace bytes for wqd_run_projections over this list in any mode (descriptor
  * tables, counters and partial sums).  In WQD_ORDERED and WQD_FUSED modes the workspace is used
  * like wqd_gemm's: zero-filled before its first use (or initialised by wqd_stack_setup), and
@@ -155,15 +165,15 @@ enum {
  * K and the list holds no gate/up pair.  In WQD_PERSISTENT mode wqd_stack_setup initialises it. */
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
 
-/* Write the WQD_PERSISTENT descriptor tables of this projection list into the workspace and
- * zero its counters (blocking copies).
- * Must be called once before wqd_run_projections in WQD_PERSISTENT mode, and again whenever a
- * pointer or shape in the list changes. */
-WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, void *workspace,
-                            int64_t workspace_bytes, void *stream);
+/* Write the descriptor tables of this projection list for `mode` (WQD_PERSISTENT, optionally
+ * with WQD_BATCH_INVARIANT) into the workspace and zero its counters (blocking copies).
+ * Must be called once before wqd_run_projections in that mode, and again whenever a pointer or
+ * shape in the list changes.  Errors: WQD_EINVAL for another mode. */
+WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
+                            void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Run every projection of the list with its epilogue.  `mode` is WQD_ORDERED, WQD_PERSISTENT
- * or WQD_FUSED.  Errors: WQD_EINVAL for a bad mode or epilogue, a gate entry not followed by
+ * or WQD_FUSED, optionally OR-ed with WQD_BATCH_INVARIANT.  Errors: WQD_EINVAL for a bad mode or epilogue, a gate entry not followed by
  * its up entry (or an up entry without its gate, or the two differing in fmt or N), an epilogue
  * on an AQ2X8 entry, or a NULL workspace in WQD_PERSISTENT mode; WQD_ESPACE for a workspace
  * smaller than wqd_stack_workspace_bytes when one is needed; the wqd_gemm checks per entry. */

@@ -148,9 +148,10 @@ def test_gemm_argument_errors_before_any_launch(args, status):
 
 
 def test_gemm_workspace_too_small_is_reported():
-    need = W.wqd_gemm_workspace_bytes(I.Q4_0, 4096, 4096, 1)
+    # one 64-row group with a long K: its K is split, so it needs counters and partials
+    need = W.wqd_gemm_workspace_bytes(I.Q4_0, 64, 32768, 1)
     assert need > 0
-    assert W.lib().wqd_gemm(I.Q4_0, 4096, 4096, FAKE, FAKE, 1, 4096, FAKE, 4096, FAKE, need - 4,
+    assert W.lib().wqd_gemm(I.Q4_0, 64, 32768, FAKE, FAKE, 1, 32768, FAKE, 64, FAKE, need - 4,
                             None) == W.WQD_ESPACE
 
 
@@ -244,3 +245,19 @@ def test_pair_needs_a_workspace():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5):
         assert W.wqd_status_str(s)
+
+
+def test_batch_invariant_flag_rules():
+    L = W.lib()
+    BI = W.WQD_BATCH_INVARIANT
+    aq = _fake_list([(I.CB4, 64, 64, E0, FAKE), (I.AQ2X8, 64, 64, E0, FAKE)])
+    for mode in (W.WQD_ORDERED, W.WQD_PERSISTENT, W.WQD_FUSED):
+        assert L.wqd_run_projections(aq, 2, 1, mode | BI, FAKE, 1 << 30, None) == W.WQD_EINVAL
+        assert L.wqd_stack_launches(aq, 2, 1, mode | BI) == W.WQD_EINVAL
+    assert L.wqd_stack_workspace_bytes(aq, 2, 1) > 0  # the modes without the flag still plan
+    X = FAKE + (1 << 40)
+    mixed = _fake_list([(I.CB4, 4096, 4096, E0, X), (I.CB8, 4096, 4096, E0, X)])
+    assert L.wqd_stack_launches(mixed, 2, 1, W.WQD_PERSISTENT) == 1        # CB4 and CB8 together
+    assert L.wqd_stack_launches(mixed, 2, 1, W.WQD_PERSISTENT | BI) == 2   # one instance each
+    assert L.wqd_stack_setup(mixed, 2, 1, W.WQD_ORDERED, FAKE, 1 << 30, None) == W.WQD_EINVAL
+    assert L.wqd_run_projections(mixed, 2, 1, 3 | BI, FAKE, 1 << 30, None) == W.WQD_EINVAL

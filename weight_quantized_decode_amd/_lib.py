@@ -18,6 +18,7 @@ SO_PATH = os.path.join(_HERE, "libwqd.so")
 WQD_Q4_0, WQD_CB4, WQD_CB8, WQD_TQ2, WQD_AQ2X8 = 1, 2, 3, 4, 5
 WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP = 0, -1, -2, -3, -4, -5
 WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED = 0, 1, 2
+WQD_BATCH_INVARIANT = 0x10
 WQD_EPI_NONE, WQD_EPI_ADD, WQD_EPI_SILU_GATE, WQD_EPI_SILU_UP = 0, 1, 2, 3
 WQD_MAX_M = 8
 
@@ -63,7 +64,7 @@ def lib() -> ctypes.CDLL:
             "wqd_gemm": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
             "wqd_dequant_f32": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp]),
             "wqd_stack_workspace_bytes": (i64, [ctypes.POINTER(wqd_proj), i32, i64]),
-            "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, vp, i64, vp]),
+            "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
             "wqd_run_projections": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
             "wqd_run_projections_timed": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp,
                                                          ctypes.POINTER(ctypes.c_void_p), i32]),
@@ -162,9 +163,10 @@ def wqd_stack_workspace_bytes(arr, M: int) -> int:
     return _check("wqd_stack_workspace_bytes", lib().wqd_stack_workspace_bytes(arr, len(arr), M))
 
 
-def wqd_stack_setup(arr, M: int, workspace, stream=None) -> None:
+def wqd_stack_setup(arr, M: int, workspace, stream=None, mode: int = WQD_PERSISTENT) -> None:
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("wqd_stack_setup", lib().wqd_stack_setup(arr, len(arr), M, _dptr(workspace), ws_bytes, _stream(stream)))
+    _check("wqd_stack_setup", lib().wqd_stack_setup(arr, len(arr), M, mode, _dptr(workspace), ws_bytes,
+                                                    _stream(stream)))
 
 
 def wqd_run_projections(arr, M: int, mode: int, workspace, stream=None) -> None:

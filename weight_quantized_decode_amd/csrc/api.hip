@@ -103,13 +103,13 @@ static int device_cus() {
     return cached_cus;
 }
 
-static GemvFn pick_gemv(int mask, int M, bool epi = false) {
+static GemvFn pick_gemv(int mask, int M, bool epi = false, bool bi = false) {
     switch (mask) {
-    case 1 << Q4_0: return gemv_fn_q4_0(M, epi);
-    case 1 << CB4: return gemv_fn_cb4(M, epi);
-    case 1 << CB8: return gemv_fn_cb8(M, epi);
-    case 1 << TQ2: return gemv_fn_tq2(M, epi);
-    case kMaskCB48: return gemv_fn_cb48(M, epi);
+    case 1 << Q4_0: return gemv_fn_q4_0(M, epi, bi);
+    case 1 << CB4: return gemv_fn_cb4(M, epi, bi);
+    case 1 << CB8: return gemv_fn_cb8(M, epi, bi);
+    case 1 << TQ2: return gemv_fn_tq2(M, epi, bi);
+    case kMaskCB48: return bi ? nullptr : gemv_fn_cb48(M, epi);
     }
     return nullptr;
 }
@@ -230,6 +230,7 @@ static Plan plan_ws(int fmt, int64_t N, int64_t K, int64_t M, int64_t cw_target)
 struct SliceTarget {
     int64_t cs = 0;
     bool ws = false;
+    bool tiny = false;  // under WQD_WSPLIT_MIN chunks per resident wave
 };
 static SliceTarget slice_target(int mask, int64_t total_cc, int64_t waves, int64_t M) {
     SliceTarget t;
@@ -237,7 +238,8 @@ static SliceTarget slice_target(int mask, int64_t total_cc, int64_t waves, int64
     // (TQ2 slices move in 8-chunk scale quads, too coarse to share a row between 8 waves)
     if (per < WQD_WSPLIT_BELOW && !(mask & fmt_bit(TQ2))) {
         t.ws = true;
-        t.cs = per < WQD_WSPLIT_MIN ? WQD_WSPLIT_MIN : per;
+        t.tiny = per < WQD_WSPLIT_MIN;
+        t.cs = t.tiny ? WQD_WSPLIT_MIN : per;
     } else {
         t.cs = target_cs(total_cc, waves, M);
     }
@@ -292,8 +294,9 @@ static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, 
     return D;
 }
 
-static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus, bool epi = false) {
-    GemvFn fn = pick_gemv(mask, M, epi);
+static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, int cus, bool epi = false,
+                       bool bi = false) {
+    GemvFn fn = pick_gemv(mask, M, epi, bi);
     if (!fn) return WQD_EINVAL;
     int64_t grid = int64_t(cus) * resident_per_cu(fn);
     if (grid > GP.total_wgu) grid = GP.total_wgu;
@@ -452,6 +455,7 @@ struct LaunchGroup {
     int total_wgu = 0;
     bool aq = false;           // an AQ2X8 launch
     bool epi = false;          // some descriptor applies an epilogue
+    bool bi = false;           // batch-invariant instance
     int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
 };
 
@@ -516,14 +520,14 @@ static void list_segments(const wqd_proj *p, int count, int mode, std::vector<st
 
 // Plans the launches of entries [b, e) onto counters from cnt_off and partials from part_off
 // (offsets into the workspace at `base`, which may be null when only sizes are wanted).
-static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, uint8_t *base, int64_t &cnt_off,
-                         int64_t &part_off, StackPlan &SP, int cus) {
+static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, bool bi, uint8_t *base,
+                         int64_t &cnt_off, int64_t &part_off, StackPlan &SP, int cus) {
     int present = 0;
     for (int i = b; i < e; i++) present |= fmt_bit(p[i].fmt);
     const bool has_aq = (present & fmt_bit(AQ2X8)) != 0;
     present &= ~fmt_bit(AQ2X8);
     std::vector<int> masks;
-    if ((present & kMaskCB48) == kMaskCB48 && mode == WQD_PERSISTENT && M < WQD_MFMA_MIN_M) {
+    if ((present & kMaskCB48) == kMaskCB48 && mode == WQD_PERSISTENT && M < WQD_MFMA_MIN_M && !bi) {
         masks.push_back(kMaskCB48);
         present &= ~kMaskCB48;
     }
@@ -542,7 +546,18 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
         G.mask = mask;
         const SliceTarget tgt = slice_target(mask, total_cc, resident_waves(mask, M, cus), M);
         G.cs = tgt.ws ? 0 : tgt.cs;  // (the dynamic tail serves long slices only)
+        // The shortest M = 1 launches run the matrix-core instance (the batch-invariant one):
+        // its activation windows arrive with the code loads, where the vector-ALU instance waits
+        // for scalar loads of x at the start of each of its few units.
+        G.bi = bi || (WQD_M1_MF_SHORT && M == 1 && tgt.tiny && mask != kMaskCB48);
         G.first = int(SP.descs.size());
+        // Batch-invariant lists cut every projection the same way whatever M and whatever else
+        // is in the list (workgroup-split slices of about WQD_BI_CW chunks per wave, or wave
+        // slices of WQD_BI_CS chunks when WQD_BI_CW is 0), so its sums are added in one order.
+        auto plan_of = [&](int f, int64_t N, int64_t K) {
+            if (!bi) return plan_target(f, N, K, M, tgt);
+            return WQD_BI_CW > 0 ? plan_ws(f, N, K, M, WQD_BI_CW) : plan_cs(f, N, K, M, WQD_BI_CS);
+        };
         int wgu = 0;
         auto push = [&](Desc D) {
             D.wgu_begin = wgu;
@@ -554,11 +569,11 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
             for (int i = b; i < e; i++) {
                 const wqd_proj &q = p[i];
                 if (q.fmt != fmt || q.epi == WQD_EPI_SILU_UP) continue;
-                const Plan P = plan_target(fmt, q.N, q.K, M, tgt);
+                const Plan P = plan_of(fmt, q.N, q.K);
                 if (q.epi == WQD_EPI_SILU_GATE) {
                     // gate and up share one slice counter per row group and one partial array
                     const wqd_proj &r = p[i + 1];
-                    const Plan U = plan_target(fmt, r.N, r.K, M, tgt);
+                    const Plan U = plan_of(fmt, r.N, r.K);
                     const int64_t S_all = P.S + U.S;
                     int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
                     float *part = base ? reinterpret_cast<float *>(base + part_off) : nullptr;
@@ -626,11 +641,16 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, u
     }
 }
 
-static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mode, void *ws, StackPlan &SP,
+static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mode_flags, void *ws, StackPlan &SP,
                             int cus) {
+    const bool bi = (mode_flags & WQD_BATCH_INVARIANT) != 0;
+    const int mode = mode_flags & ~WQD_BATCH_INVARIANT;
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
     int rc = check_list(p, count, M);
     if (rc != WQD_OK) return rc;
+    if (bi)
+        for (int i = 0; i < count; i++)
+            if (p[i].fmt == AQ2X8) return WQD_EINVAL;  // (no batch-invariant AQ2X8 kernel)
     SP.off_descs = 0;
     SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
     SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
@@ -648,7 +668,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
     int64_t part_used = 0;
     for (const auto &sg : seg) {
         int64_t cnt_off = SP.off_cnt, part_off = SP.off_part;
-        plan_segment(p, sg.first, sg.second, M, mode, base, cnt_off, part_off, SP, cus);
+        plan_segment(p, sg.first, sg.second, M, mode, bi, base, cnt_off, part_off, SP, cus);
         if (part_off - SP.off_part > part_used) part_used = part_off - SP.off_part;
     }
     SP.part_bytes = part_used;
@@ -722,15 +742,21 @@ WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs, int32_t count, 
         int rc = build_stack_plan(projs, count, M, mode, nullptr, SP, device_cus());
         if (rc != WQD_OK) return rc;
         if (SP.total() > need) need = SP.total();
+        // the batch-invariant plans too, where the list allows them
+        StackPlan SB;
+        if (build_stack_plan(projs, count, M, mode | WQD_BATCH_INVARIANT, nullptr, SB, device_cus()) == WQD_OK &&
+            SB.total() > need)
+            need = SB.total();
     }
     return need;
 }
 
-WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, void *workspace,
+WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode, void *workspace,
                             int64_t workspace_bytes, void *stream) {
     if (!workspace) return WQD_EINVAL;
+    if ((mode & ~WQD_BATCH_INVARIANT) != WQD_PERSISTENT) return WQD_EINVAL;
     StackPlan SP;
-    int rc = build_stack_plan(projs, count, M, WQD_PERSISTENT, workspace, SP, device_cus());
+    int rc = build_stack_plan(projs, count, M, mode, workspace, SP, device_cus());
     if (rc != WQD_OK) return rc;
     if (workspace_bytes < SP.total()) return WQD_ESPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -761,8 +787,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     uint8_t *base = static_cast<uint8_t *>(workspace);
     // WQD_PERSISTENT reads the descriptor tables wqd_stack_setup wrote; the other modes pass
     // their descriptors in the kernel arguments and need the workspace only to count slices.
-    if (mode == WQD_PERSISTENT && !base) return WQD_EINVAL;
-    if ((mode == WQD_PERSISTENT || SP.needs_ws) && (!base || workspace_bytes < SP.total())) return WQD_ESPACE;
+    const bool persistent = (mode & ~WQD_BATCH_INVARIANT) == WQD_PERSISTENT;
+    if (persistent && !base) return WQD_EINVAL;
+    if ((persistent || SP.needs_ws) && (!base || workspace_bytes < SP.total())) return WQD_ESPACE;
     const int launches = int(SP.groups.size());
     if (n_events != 0 && n_events != 2 * launches) return WQD_ESPACE;
     int li = 0;
@@ -771,7 +798,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[2 * li + which]), st);
         return e == hipSuccess ? WQD_OK : hip_fail(e);
     };
-    const bool table = (mode == WQD_PERSISTENT);
+    const bool table = persistent;
     const Desc *dtab = table ? reinterpret_cast<const Desc *>(base + SP.off_descs) : nullptr;
     const AqDesc *atab = table ? reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs) : nullptr;
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
@@ -810,7 +837,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }
         if ((rc = mark(0)) != WQD_OK) return rc;
-        rc = launch_gemv(G.mask, int(M), GP, st, cus, G.epi);
+        rc = launch_gemv(G.mask, int(M), GP, st, cus, G.epi, G.bi);
         if (rc != WQD_OK) return rc;
         if ((rc = mark(1)) != WQD_OK) return rc;
         li++;

@@ -55,12 +55,22 @@ typedef const uint32_t __attribute__((address_space(4))) *cu32p;  // scalar-load
 #define WQD_MF_U_WIDE 4  // the same for CB4 at M > 4
 #endif
 // Launch groups whose work per resident wave is below WQD_WSPLIT_BELOW chunks use workgroup-split
-// units of at least WQD_WSPLIT_MIN chunks per wave.
+// units of at least WQD_WSPLIT_MIN chunks per wave (fewer, longer units: a row group's slices
+// then mostly stay inside one workgroup instead of going through memory).
 #ifndef WQD_WSPLIT_BELOW
 #define WQD_WSPLIT_BELOW 64
 #endif
 #ifndef WQD_WSPLIT_MIN
-#define WQD_WSPLIT_MIN 4
+#define WQD_WSPLIT_MIN 16
+#endif
+#ifndef WQD_M1_MF_SHORT
+#define WQD_M1_MF_SHORT 1  // M = 1 launches under WQD_WSPLIT_MIN chunks per wave use the matrix cores
+#endif
+#ifndef WQD_BI_CW
+#define WQD_BI_CW 16   // chunks per wave of the workgroup-split slices of a batch-invariant list
+#endif
+#ifndef WQD_BI_CS
+#define WQD_BI_CS 128  // K-slice (chunks) of a batch-invariant list when WQD_BI_CW is 0
 #endif
 #ifndef WQD_STACK_MF_CS
 #define WQD_STACK_MF_CS 128  // largest stack K-slice (chunks) of the matrix-core instances
@@ -189,11 +199,11 @@ AqFn aq_fn(int M, int RW);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies
-// epilogues (residual add, SiLU pair).
-GemvFn gemv_fn_q4_0(int M, bool epi);
-GemvFn gemv_fn_cb4(int M, bool epi);
-GemvFn gemv_fn_cb8(int M, bool epi);
-GemvFn gemv_fn_tq2(int M, bool epi);
+// epilogues (residual add, SiLU pair), `bi` the batch-invariant one (single formats only).
+GemvFn gemv_fn_q4_0(int M, bool epi, bool bi);
+GemvFn gemv_fn_cb4(int M, bool epi, bool bi);
+GemvFn gemv_fn_cb8(int M, bool epi, bool bi);
+GemvFn gemv_fn_tq2(int M, bool epi, bool bi);
 GemvFn gemv_fn_cb48(int M, bool epi);
 
 }  // namespace wqd

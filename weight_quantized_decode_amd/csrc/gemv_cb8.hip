@@ -2,5 +2,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_cb8(int M, bool epi) { return gemv_fn<fmt_bit(CB8)>(M, epi); }
+GemvFn gemv_fn_cb8(int M, bool epi, bool bi) { return gemv_fn<fmt_bit(CB8)>(M, epi, bi); }
 }  // namespace wqd

@@ -189,7 +189,7 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
 // ------------------------------------------------------------------------------------------
 // `hook` runs once, right after the first loads of the unit are issued: the workgroup uses it
 // to (re)build its LDS table while those loads are in flight.
-template <int FMT, int M, bool EPI, typename Hook>
+template <int FMT, int M, bool EPI, bool BI, typename Hook>
 __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32_t *lds, float *red, Hook &&hook) {
     // Wave unit -> (row group g, K-slice s, chunks [cb, ce)).  Workgroup-split descriptors give
     // the kWaves waves of a workgroup unit consecutive pieces of one slice of D.CS chunks (the
@@ -231,7 +231,9 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     // groups (more bytes in flight per wave while a group is processed).
     // The block formats decode to exact fp16 values (code - 8, code - 1) for it, and their
     // MFA holds one scale block at a time, added to acc times the block scale.
-    constexpr bool MF = (M >= WQD_MFMA_MIN_M) && (FMT == CB4 || FMT == CB8 || FMT == Q4_0 || FMT == TQ2);
+    // Batch-invariant instances (BI) take the matrix-core path at every M, with one accumulator
+    // chain per activation quad, so a row's instruction sequence does not depend on M.
+    constexpr bool MF = (M >= WQD_MFMA_MIN_M || BI) && (FMT == CB4 || FMT == CB8 || FMT == Q4_0 || FMT == TQ2);
     constexpr bool BLK = (FMT == Q4_0 || FMT == TQ2);
     constexpr int WPC = (FMT == CB8) ? 16 : (FMT == TQ2) ? 64 : 32;  // weights per chunk
     constexpr int CPW = 64 / WPC;                // chunks per window
@@ -242,7 +244,7 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     static_assert(!MF || U % CPW == 0, "a load group holds whole activation windows");
     static_assert(!MF || !BLK || U == 4, "a load group of a block format lies in one scale quad");
     constexpr int NWIN = MF ? U / CPW : 1;
-    constexpr int NCH = (H == 1) ? 2 : 1;
+    constexpr int NCH = (H == 1 && !BI) ? 2 : 1;
     const uint16_t *xw[H];  // lane 4b+i: activation row 4h+i (clamped to M-1), at element 4b
 #pragma unroll
     for (int h = 0; h < H; h++) xw[h] = D.x + (int64_t)min(4 * h + (lane & 3), M - 1) * D.ldx + 4 * (lane >> 2);
@@ -709,7 +711,7 @@ __device__ __forceinline__ const Desc *desc_table(const GemvParams &P) {
 // One workgroup unit: kWaves wave units of one projection, one per wave.  The LDS table is
 // rebuilt (between two barriers, so all waves of the workgroup take part) when the projection
 // changes.
-template <int MASK, int M, bool EPI>
+template <int MASK, int M, bool EPI, bool BI>
 __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, float *red, int wid,
                                         int lane) {
     // Units are visited in increasing order: search only for the first one, then step forward.
@@ -743,13 +745,13 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
         if constexpr (MASK == kMaskCB48) {
             // two formats: one branch or the other (not two independent ifs, which let
             // the compiler keep values of both bodies live at once)
-            if (D.fmt == CB4) run_unit<CB4, M, EPI>(D, wu, lane, lds, red, hook);
-            else run_unit<CB8, M, EPI>(D, wu, lane, lds, red, hook);
+            if (D.fmt == CB4) run_unit<CB4, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            else run_unit<CB8, M, EPI, BI>(D, wu, lane, lds, red, hook);
         } else {
-            if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M, EPI>(D, wu, lane, lds, red, hook);
-            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M, EPI>(D, wu, lane, lds, red, hook);
-            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M, EPI>(D, wu, lane, lds, red, hook);
-            if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M, EPI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << Q4_0)) != 0) if (D.fmt == Q4_0) run_unit<Q4_0, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M, EPI, BI>(D, wu, lane, lds, red, hook);
         }
     } else {
         hook();
@@ -766,7 +768,8 @@ constexpr int kMinWavesPerEU = WQD_WG_PER_CU * kWaves / 4;
 // out one by one from a device-wide counter to whichever workgroup is free, which evens out the
 // finish times (workgroups on different XCDs stream at different speeds).  EPI: the instance
 // applies the descriptors' epilogues (lists without any use the instance without that code).
-template <int MASK, int M, bool EPI>
+// BI: the batch-invariant instance (every M on the matrix cores, one chain per quad).
+template <int MASK, int M, bool EPI, bool BI = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU))) void gemv_kernel(GemvParams P) {
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
     __shared__ float red[kWaves * (M < 4 ? M : 4) * 64];  // workgroup-split sums
@@ -784,7 +787,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     const int u1 = u0 + per + (b < rem ? 1 : 0);
     int cur = -1;
     Desc D;
-    for (int u = u0; u < u1; u++) run_wgu<MASK, M, EPI>(P, u, cur, D, lds, red, wid, lane);
+    for (int u = u0; u < u1; u++) run_wgu<MASK, M, EPI, BI>(P, u, cur, D, lds, red, wid, lane);
     if (kPool && P.ctr) {
         while (true) {
             __syncthreads();
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
             __syncthreads();
             const int u = __builtin_amdgcn_readfirstlane(next_u);
             if (u >= total) break;
-            run_wgu<MASK, M, EPI>(P, u, cur, D, lds, red, wid, lane);
+            run_wgu<MASK, M, EPI, BI>(P, u, cur, D, lds, red, wid, lane);
         }
         // Every workgroup has taken its last index once it reaches here; the last one to arrive
         // resets the counters for the next launch on this workspace.
@@ -807,23 +810,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     }
 }
 
-template <int MASK, bool EPI>
-GemvFn gemv_fn_epi(int M) {
+template <int MASK, bool EPI, bool BI>
+GemvFn gemv_fn_var(int M) {
     switch (M) {
-    case 1: return gemv_kernel<MASK, 1, EPI>;
-    case 2: return gemv_kernel<MASK, 2, EPI>;
-    case 3: return gemv_kernel<MASK, 3, EPI>;
-    case 4: return gemv_kernel<MASK, 4, EPI>;
-    case 5: return gemv_kernel<MASK, 5, EPI>;
-    case 6: return gemv_kernel<MASK, 6, EPI>;
-    case 7: return gemv_kernel<MASK, 7, EPI>;
-    case 8: return gemv_kernel<MASK, 8, EPI>;
+    case 1: return gemv_kernel<MASK, 1, EPI, BI>;
+    case 2: return gemv_kernel<MASK, 2, EPI, BI>;
+    case 3: return gemv_kernel<MASK, 3, EPI, BI>;
+    case 4: return gemv_kernel<MASK, 4, EPI, BI>;
+    case 5: return gemv_kernel<MASK, 5, EPI, BI>;
+    case 6: return gemv_kernel<MASK, 6, EPI, BI>;
+    case 7: return gemv_kernel<MASK, 7, EPI, BI>;
+    case 8: return gemv_kernel<MASK, 8, EPI, BI>;
     }
     return nullptr;
 }
+// The batch-invariant instances always carry the epilogue code (one set of them per format).
 template <int MASK>
-GemvFn gemv_fn(int M, bool epi) {
-    return epi ? gemv_fn_epi<MASK, true>(M) : gemv_fn_epi<MASK, false>(M);
+GemvFn gemv_fn(int M, bool epi, bool bi) {
+    if (bi) return gemv_fn_var<MASK, true, true>(M);
+    return epi ? gemv_fn_var<MASK, true, false>(M) : gemv_fn_var<MASK, false, false>(M);
 }
 
 }  // namespace wqd

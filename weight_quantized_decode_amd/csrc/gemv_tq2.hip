@@ -2,5 +2,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_tq2(int M, bool epi) { return gemv_fn<fmt_bit(TQ2)>(M, epi); }
+GemvFn gemv_fn_tq2(int M, bool epi, bool bi) { return gemv_fn<fmt_bit(TQ2)>(M, epi, bi); }
 }  // namespace wqd
