@@ -17,6 +17,10 @@
  *  - AQ2x8: trapetum "Benchmarks", "Additive vector-quantization GEMV (AQLM-style, 2-bit)":
  *    two codebooks of 256 entries of 8 values, the weight group is the sum of the two selected
  *    entries, with a per-output-row scale.
+ *  - AQ1X16: trapetum "Benchmarks", the November update's Llama-2-70B PV-tuned in the 1x16
+ *    layout: one codebook of 65,536 entries of 8 fp16 values per matrix and one 16-bit code per
+ *    group of 8 weights (2 bits per weight), with the per-row scales the exporter copies; the
+ *    products are formed in f32.  Codebook, then scales, then codes is this build's reading.
  *  - Epilogues: trapetum "Benchmarks", "Short-context decode, step by step" (the fused decode
  *    kernels): the gate and up projections share one launch whose reduce applies SiLU to the
  *    gate result and multiplies by the up result, and the o and down projections add the
@@ -55,6 +59,7 @@ int64_t oracle_canonical_bytes(int fmt, int64_t N, int64_t K) {
     case 3: return 512 + N * K;
     case 4: return (K % 128) ? -1 : N * (K / 128) * 34;
     case 5: return (K % 8) ? -1 : 8192 + 2 * N + N * (K / 8) * 2;
+    case 6: return (K % 8) ? -1 : 65536 * 8 * 2 + 2 * N + N * (K / 8) * 2;
     default: return -1;
     }
 }
@@ -99,6 +104,17 @@ static double weight_f64(int fmt, int64_t N, int64_t K, const uint8_t *canon, in
         double e1 = oracle_half_to_double(rd16(cbk + ((1 * 256 + c1) * 8 + j) * 2));
         double s = oracle_half_to_double(rd16(sc + 2 * n));
         return s * (e0 + e1);
+    }
+    case 6: { /* AQ1X16 */
+        const uint8_t *cbk = canon;
+        const uint8_t *sc = canon + 65536 * 8 * 2;
+        const uint8_t *codes = sc + 2 * N;
+        int64_t g = k / 8;
+        int j = (int)(k % 8);
+        int code = rd16(codes + (n * (K / 8) + g) * 2);
+        double e = oracle_half_to_double(rd16(cbk + ((int64_t)code * 8 + j) * 2));
+        double s = oracle_half_to_double(rd16(sc + 2 * n));
+        return s * e;
     }
     }
     return NAN;

@@ -14,6 +14,8 @@
  *             byte j/4 at bits 2*(j%4); value (code - 1) * d, so codes 0,1,2,3 -> -d, 0, +d, +2d.
  *   5 AQ2X8 : C[2][256][8] fp16, then s[N] fp16, then codes [N][K/8][2] (codebook 0 first);
  *             value s[n] * (C[0][c0][j] + C[1][c1][j]) for weight j of group k/8.
+ *   6 AQ1X16: C[65536][8] fp16 (1 MiB), then s[N] fp16, then codes [N][K/8] uint16
+ *             little-endian; value s[n] * C[code][j] for weight j of group k/8 (exact in fp32).
  *
  * Epilogues of the fused projections: SiLU(gate) * up for a gate/up pair, and a residual add.
  *

@@ -86,6 +86,20 @@ def test_aq2x8_code_bytes_at_4096_square():
     assert MX.bits_per_weight(codes, N * K) == 2.0
 
 
+def test_aq1x16_is_2_bits_per_weight_with_a_1_mib_codebook():
+    # trapetum "Benchmarks", the 70B 1x16 model: one codebook of 65,536 entries of 8 fp16 values
+    # (1 MiB, too large for shared memory) and one 16-bit code per group of 8 weights, still
+    # 2 bits per weight.
+    N = K = 4096
+    total = oracle.canonical_bytes(6, N, K)
+    codebook = 65536 * 8 * 2
+    assert codebook == 1 << 20
+    codes = total - codebook - 2 * N
+    assert codes == N * K // 8 * 2 == 4_194_304
+    assert MX.bits_per_weight(codes, N * K) == 2.0
+    assert oracle.canonical_bytes(6, 4, 12) == -1  # K not a whole number of groups
+
+
 def test_byte_counts_of_the_workloads():
     total = sum(oracle.canonical_bytes(p.fmt, p.N, p.K) for p in I.config_projections(3))
     assert total == 3_369_082_368
@@ -207,6 +221,27 @@ def test_aq2x8_fp32_dequant_rounds_sum_then_product():
     assert np.all(w32 == np.float32(0.75))
 
 
+def _aq1x16_canon(g):
+    C = np.zeros((65536, 8), dtype=np.float64)
+    c = np.arange(65536)
+    hi, lo = (c >> 8).astype(np.float64), (c & 0xFF).astype(np.float64)
+    C[:, 0], C[:, 1], C[:, 2], C[:, 3], C[:, 4], C[:, 5], C[:, 6] = hi, lo, -hi, -lo, 0.5 * hi, 1, -1
+    cbk = C.astype(np.float16).view(np.uint16).astype("<u2").view(np.uint8).reshape(-1)
+    sc = np.array(sum((le16(f16(float(v))) for v in g["scales"]), []), dtype=np.uint8)
+    codes = np.array([int(v, 16) for v in g["code_bytes_row0"] + g["code_bytes_row1"]], dtype=np.uint8)
+    return np.concatenate([cbk, sc, codes])
+
+
+def test_aq1x16_hand_rows():
+    g = read_golden("aq1x16_rows.txt")
+    canon = _aq1x16_canon(g)
+    w = oracle.decode_f64(6, 2, 16, canon)
+    assert list(w[0]) == [float(v) for v in g["weights_row0"]]
+    assert list(w[1]) == [float(v) for v in g["weights_row1"]]
+    # the fp32 decode is the exact value (an fp16 scale times an fp16 entry fits in fp32)
+    assert np.array_equal(oracle.dequant_f32(6, 2, 16, canon), w.astype(np.float32))
+
+
 def test_subnormal_scales_are_kept():
     # an fp16 subnormal scale (2^-24) is kept, not flushed: Q4_0 code 15 -> 7 * 2^-24
     canon = np.array(le16(0x0001) + [0xFF] * 16, dtype=np.uint8)
@@ -218,7 +253,7 @@ def test_subnormal_scales_are_kept():
 # ----------------------------------------------------------------------------- the multiply
 
 
-SHAPES = [(1, 5, 96), (2, 7, 256), (3, 3, 128), (4, 6, 384), (5, 4, 40)]
+SHAPES = [(1, 5, 96), (2, 7, 256), (3, 3, 128), (4, 6, 384), (5, 4, 40), (6, 5, 48)]
 
 
 @pytest.mark.parametrize("fmt,N,K", SHAPES)

@@ -19,6 +19,9 @@ Canonical byte layouts (little-endian, fp16 = IEEE binary16 bit patterns):
 * AQ2x8 -- codebooks C[2][256][8] fp16 (8192 bytes), per-row scales s[N] fp16,
   then codes [N][K/8][2] uint8, codebook 0 first (trapetum benchmarks page,
   "Additive vector-quantization GEMV (AQLM-style, 2-bit)").
+* AQ1x16 -- one codebook C[65536][8] fp16 (1 MiB), per-row scales s[N] fp16, then
+  codes [N][K/8] uint16 (trapetum benchmarks page, the November update's 70B
+  PV-tuned model in AQLM's 1x16 layout).
 
 Seeds: every tensor is drawn from ``PCG64(SeedSequence([0, *key]))`` where the
 key names the config, layer, projection and tensor, so any piece can be
@@ -31,10 +34,10 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-Q4_0, CB4, CB8, TQ2, AQ2X8 = 1, 2, 3, 4, 5
-FORMAT_NAMES = {Q4_0: "q4_0", CB4: "cb4", CB8: "cb8", TQ2: "tq2", AQ2X8: "aq2x8"}
+Q4_0, CB4, CB8, TQ2, AQ2X8, AQ1X16 = 1, 2, 3, 4, 5, 6
+FORMAT_NAMES = {Q4_0: "q4_0", CB4: "cb4", CB8: "cb8", TQ2: "tq2", AQ2X8: "aq2x8", AQ1X16: "aq1x16"}
 # K must be a multiple of this (whole blocks / whole groups / whole bytes).
-K_MULTIPLE = {Q4_0: 32, CB4: 2, CB8: 1, TQ2: 128, AQ2X8: 8}
+K_MULTIPLE = {Q4_0: 32, CB4: 2, CB8: 1, TQ2: 128, AQ2X8: 8, AQ1X16: 8}
 
 
 def rng(*key: int) -> np.random.Generator:
@@ -58,6 +61,8 @@ def canonical_bytes(fmt: int, N: int, K: int) -> int:
         return N * (K // 128) * 34
     if fmt == AQ2X8:
         return 8192 + 2 * N + N * (K // 8) * 2
+    if fmt == AQ1X16:
+        return 65536 * 8 * 2 + 2 * N + N * (K // 8) * 2
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -74,7 +79,9 @@ def gen_weight(fmt: int, N: int, K: int, key: Sequence[int], *, cb_sigma: float 
     d = fp16(|N(0,1)|*0.01); CB4/CB8 centroids sorted fp16(N(0, cb_sigma)) with
     uniform codes; TQ2 codes 0/1/2 with probabilities .25/.5/.25 (code 3 never
     drawn) and d = fp16(|N(0,1)|*0.02); AQ2x8 codebooks fp16(N(0,0.01)),
-    uniform 8-bit codes and row scales fp16(U(0.5,1.5)).
+    uniform 8-bit codes and row scales fp16(U(0.5,1.5)); AQ1x16 one codebook
+    fp16(N(0,0.014)) (about the spread of a sum of two AQ2x8 entries), uniform
+    16-bit codes and row scales fp16(U(0.5,1.5)).
     """
     _check(fmt, N, K)
     key = tuple(int(k) for k in key)
@@ -111,6 +118,13 @@ def gen_weight(fmt: int, N: int, K: int, key: Sequence[int], *, cb_sigma: float 
         codes = rng(*key, 1).integers(0, 256, size=N * (K // 8) * 2, dtype=np.uint8)
         return np.concatenate([C.astype("<u2").view(np.uint8).reshape(-1),
                                s.astype("<u2").view(np.uint8).reshape(-1), codes])
+    if fmt == AQ1X16:
+        C = f16_bits(rng(*key, 0).standard_normal((65536, 8)) * 0.014)
+        s = f16_bits(rng(*key, 2).uniform(0.5, 1.5, size=N))
+        codes = rng(*key, 1).integers(0, 65536, size=N * (K // 8), dtype=np.uint16)
+        return np.concatenate([C.astype("<u2").view(np.uint8).reshape(-1),
+                               s.astype("<u2").view(np.uint8).reshape(-1),
+                               codes.astype("<u2").view(np.uint8)])
     raise ValueError(fmt)
 
 
@@ -144,6 +158,7 @@ CONFIG_NAMES = {
     3: "cb4_llama7b_stack_cb8_head",
     4: "tq2_mlp_17408x5120",
     5: "aq2x8_llama70b_mlp",
+    6: "aq1x16_llama70b_mlp",
 }
 
 
@@ -167,6 +182,11 @@ def config_projections(cfg: int, layers: int | None = None) -> List[Proj]:
         out.append(Proj("gate", AQ2X8, 28672, 8192, (5, 0, 0), (5, 0, 100)))
         out.append(Proj("up", AQ2X8, 28672, 8192, (5, 0, 1), (5, 0, 100)))
         out.append(Proj("down", AQ2X8, 8192, 28672, (5, 0, 2), (5, 0, 102)))
+    elif cfg == 6:
+        # the 70B MLP in AQLM's 1x16 layout (the PV-tuned 70B of the trapetum November update)
+        out.append(Proj("gate", AQ1X16, 28672, 8192, (6, 0, 0), (6, 0, 100)))
+        out.append(Proj("up", AQ1X16, 28672, 8192, (6, 0, 1), (6, 0, 100)))
+        out.append(Proj("down", AQ1X16, 8192, 28672, (6, 0, 2), (6, 0, 102)))
     else:
         raise ValueError(cfg)
     return out
