@@ -36,7 +36,11 @@
  *   WQD_AQ2X8 codebooks C[2][256][8] fp16 (8192 B), row scales s[N] fp16, codes [N][K/8][2]
  *             (codebook 0 first); weight k of row n = s[n] * (C[0][c0][k%8] + C[1][c1][k%8]) with
  *             (c0, c1) the codes of group k/8.
- *   K must be a multiple of 32 (Q4_0), 2 (CB4), 1 (CB8), 128 (TQ2) or 8 (AQ2X8).
+ *   WQD_AQ1X16 one codebook C[65536][8] fp16 (1 MiB), row scales s[N] fp16, codes [N][K/8] as
+ *             little-endian uint16; weight k of row n = s[n] * C[code][k%8] with code the code of
+ *             group k/8 (trapetum "Benchmarks", November update: the 70B PV-tuned model in AQLM's
+ *             1x16 layout, 2 bits per weight).
+ *   K must be a multiple of 32 (Q4_0), 2 (CB4), 1 (CB8), 128 (TQ2) or 8 (AQ2X8, AQ1X16).
  *
  * Prepared (device) layout: the same bytes re-laid once at load time into planes ("prepared
  * weights": a contiguous code plane, then the scale plane, then codebooks), built by
@@ -54,7 +58,7 @@ extern "C" {
 
 #define WQD_API __attribute__((visibility("default")))
 
-typedef enum { WQD_Q4_0 = 1, WQD_CB4 = 2, WQD_CB8 = 3, WQD_TQ2 = 4, WQD_AQ2X8 = 5 } wqd_format;
+typedef enum { WQD_Q4_0 = 1, WQD_CB4 = 2, WQD_CB8 = 3, WQD_TQ2 = 4, WQD_AQ2X8 = 5, WQD_AQ1X16 = 6 } wqd_format;
 
 typedef enum {
     WQD_OK = 0,
@@ -101,7 +105,7 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
                      void *stream);
 
 /* Debug decode: out[n*K + k] = dequantized weight in fp32, bit-exact: the exact value for Q4_0,
- * CB4, CB8 and TQ2 (all representable in fp32); for AQ2X8 fp32(fp32(C0 + C1) * s) with
+ * CB4, CB8, TQ2 and AQ1X16 (all representable in fp32); for AQ2X8 fp32(fp32(C0 + C1) * s) with
  * round-to-nearest-even after the add and after the product. */
 WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream);
 

@@ -22,6 +22,7 @@ SHAPES = [
     (I.CB4, 77, 4098), (I.CB4, 300, 11008),
     (I.CB8, 200, 1001), (I.CB8, 3, 1),
     (I.TQ2, 70, 128), (I.TQ2, 130, 17408),
+    (I.AQ1X16, 100, 4104),
 ]
 
 

@@ -24,6 +24,7 @@ SMALL = [
     (I.CB8, 200, 1001), (I.CB8, 65, 16), (I.CB8, 3, 1),
     (I.TQ2, 200, 1280), (I.TQ2, 70, 128), (I.TQ2, 130, 17408),
     (I.AQ2X8, 200, 1000), (I.AQ2X8, 64, 8), (I.AQ2X8, 129, 8192),
+    (I.AQ1X16, 200, 1024), (I.AQ1X16, 65, 8), (I.AQ1X16, 130, 8200),
 ]
 
 
@@ -78,7 +79,7 @@ def test_gemm_parity_small(fmt, N, K, M):
     check_parity(y.cpu().numpy(), yref, aref, f"fmt={fmt} N={N} K={K} M={M}")
 
 
-@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8])
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
 def test_gemm_strided_x_and_y(fmt):
     N, K, M = 150, 1024, 3
     note(f"gemm strided fmt={fmt}")
@@ -94,7 +95,7 @@ def test_gemm_strided_x_and_y(fmt):
     check_parity(full[:, :N], yref, aref, f"strided fmt={fmt}")
 
 
-@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8])
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
 def test_gemm_deterministic(fmt):
     N, K, M = 300, 2048, 2
     note(f"gemm determinism fmt={fmt}")
@@ -106,7 +107,7 @@ def test_gemm_deterministic(fmt):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8])
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
 def test_gemm_one_hot_and_zero_activations(fmt):
     # One-hot x returns a column of the dequantized matrix: exactly for the formats whose weights
     # are exact in fp16 arithmetic; for AQ2x8 the kernel adds the two fp16 codebook entries in
@@ -126,7 +127,7 @@ def test_gemm_one_hot_and_zero_activations(fmt):
     assert np.all(np.abs(y[0] - W64[:, k]) <= rtol * np.abs(W64[:, k]))
 
 
-@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8])
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
 def test_workspace_reuse_leaves_counters_zero(fmt):
     # The split-K slice counters in the workspace must be back at zero after every call, so one
     # workspace serves many calls (and differently shaped ones) in a row.

@@ -11,7 +11,7 @@ from weight_quantized_decode_amd import _lib as W
 from weight_quantized_decode_amd import inputs as I
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FMTS = [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8]
+FMTS = [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16]
 
 
 def declared_symbols():
@@ -37,7 +37,7 @@ def test_canonical_bytes_agree_with_oracle(fmt):
 def test_prepared_sizes_are_canonical_plus_padding_only():
     # at the workload shapes (N multiple of 64, rows a whole number of 16-byte chunks) the
     # prepared planes hold exactly the canonical bytes, plus plane alignment (<= 3 x 255 bytes)
-    for cfg in (1, 2, 4, 5):
+    for cfg in (1, 2, 4, 5, 6):
         for p in I.config_projections(cfg):
             c = W.wqd_canonical_bytes(p.fmt, p.N, p.K)
             q = W.wqd_prepared_bytes(p.fmt, p.N, p.K)
@@ -47,23 +47,26 @@ def test_prepared_sizes_are_canonical_plus_padding_only():
 def _tile_rows(prep, fmt, N, K):
     """Code plane back to [N][C*16] row order (inverse of the 64-row tiling)."""
     L = W.wqd_prepared_bytes(fmt, N, K)
-    row_bytes = {I.Q4_0: K // 2, I.CB4: K // 2, I.CB8: K, I.TQ2: K // 4, I.AQ2X8: K // 4}[fmt]
+    row_bytes = {I.Q4_0: K // 2, I.CB4: K // 2, I.CB8: K, I.TQ2: K // 4, I.AQ2X8: K // 4, I.AQ1X16: K // 4}[fmt]
     C = (row_bytes + 15) // 16
     RG = (N + 63) // 64
     codes = prep[:RG * C * 64 * 16].reshape(RG, C, 64, 16).transpose(0, 2, 1, 3).reshape(RG * 64, C * 16)
     return codes[:N], row_bytes, C, RG
 
 
-@pytest.mark.parametrize("fmt,N,K", [(I.CB4, 70, 1002), (I.CB8, 70, 1001)])
+@pytest.mark.parametrize("fmt,N,K", [(I.CB4, 70, 1002), (I.CB8, 70, 1001), (I.AQ1X16, 70, 1000)])
 def test_prepare_keeps_canonical_byte_order_for_byte_formats(fmt, N, K):
     canon = I.gen_weight(fmt, N, K, (5, fmt))
     prep = W.wqd_prepare_host(fmt, N, K, canon)
     rows, row_bytes, C, RG = _tile_rows(prep, fmt, N, K)
-    head = {I.CB4: 32, I.CB8: 512, I.AQ2X8: 8192 + 2 * N}[fmt]
+    head = {I.CB4: 32, I.CB8: 512, I.AQ2X8: 8192 + 2 * N, I.AQ1X16: 65536 * 16 + 2 * N}[fmt]
     assert np.array_equal(rows[:, :row_bytes], canon[head:].reshape(N, row_bytes))
     assert np.all(rows[:, row_bytes:] == 0)  # tail padding is zero
     full = prep[:RG * C * 1024].reshape(RG, C, 64, 16)
     assert np.all(full[:, :, (N - (RG - 1) * 64):, :][-1] == 0)  # padded rows are zero
+    if fmt == I.AQ1X16:  # scales and the 1 MiB codebook are copied as they are
+        L_off = W.wqd_prepared_bytes(fmt, N, K) - ((65536 * 16 + 255) // 256 * 256)
+        assert np.array_equal(prep[L_off:L_off + 65536 * 16], canon[:65536 * 16])
 
 
 @pytest.mark.parametrize("N,K", [(70, 1000), (64, 512), (8, 8), (130, 8 * 200)])

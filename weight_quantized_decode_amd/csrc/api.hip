@@ -61,6 +61,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, Layout L
     }
 }
 
+// Debug decode of AQ1X16, one thread per (row, group of 8 weights): fp16 scale times fp16 entry
+// (exact in fp32).
+__global__ __launch_bounds__(256) void dequant_aq1x16_kernel(const uint8_t *w, Layout L, float *out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= L.N * (L.K / 8)) return;
+    const int64_t G = L.K / 8;
+    const int64_t n = i / G, g = i - n * G;
+    const int64_t g64 = n / 64, r = n % 64, c = g / 8;
+    const uint16_t code = reinterpret_cast<const uint16_t *>(w + ((g64 * L.C + c) * 64 + r) * 16)[g % 8];
+    const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
+    const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
+    float *o = out + n * L.K + g * 8;
+    for (int j = 0; j < 8; j++) o[j] = __fmul_rn(half_bits_to_float(cbk[(int64_t)code * 8 + j]), s);
+}
+
 // Debug decode of the AQ2X8 tile layout, one thread per (row, group of 8 weights).
 __global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, Layout L, float *out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -109,6 +124,7 @@ static GemvFn pick_gemv(int mask, int M, bool epi = false, bool bi = false) {
     case 1 << CB4: return gemv_fn_cb4(M, epi, bi);
     case 1 << CB8: return gemv_fn_cb8(M, epi, bi);
     case 1 << TQ2: return gemv_fn_tq2(M, epi, bi);
+    case 1 << AQ1X16: return gemv_fn_aq1x16(M, epi, bi);
     case kMaskCB48: return bi ? nullptr : gemv_fn_cb48(M, epi);
     }
     return nullptr;
@@ -531,7 +547,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         masks.push_back(kMaskCB48);
         present &= ~kMaskCB48;
     }
-    for (int fmt = 1; fmt <= 5; fmt++)
+    for (int fmt = 1; fmt <= 6; fmt++)
         if (present & fmt_bit(fmt)) masks.push_back(fmt_bit(fmt));
 
     for (const int mask : masks) {
@@ -564,7 +580,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
             wgu += (D.wu_count + kWaves - 1) / kWaves;
             SP.descs.push_back(D);
         };
-        for (int fmt = 1; fmt <= 5; fmt++) {
+        for (int fmt = 1; fmt <= 6; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = b; i < e; i++) {
                 const wqd_proj &q = p[i];
@@ -719,7 +735,7 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
     Layout L = make_layout(fmt, N, K);
     if (!L.ok) return WQD_ESHAPE;
     if (reinterpret_cast<uintptr_t>(w) & 15) return WQD_EALIGN;
-    const int64_t threads = (fmt == AQ2X8) ? L.N * L.G : L.N * L.C;
+    const int64_t threads = (fmt == AQ2X8) ? L.N * L.G : (fmt == AQ1X16) ? L.N * (L.K / 8) : L.N * L.C;
     const unsigned blocks = unsigned((threads + 255) / 256);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const uint8_t *wb = static_cast<const uint8_t *>(w);
@@ -729,6 +745,7 @@ WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float 
     case CB8: hipLaunchKernelGGL(dequant_kernel<CB8>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     case TQ2: hipLaunchKernelGGL(dequant_kernel<TQ2>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     case AQ2X8: hipLaunchKernelGGL(dequant_aq2x8_kernel, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
+    case AQ1X16: hipLaunchKernelGGL(dequant_aq1x16_kernel, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
     }
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);

@@ -185,6 +185,70 @@ __device__ void build_table(uint32_t *lds, const Desc &D) {
 }
 
 // ------------------------------------------------------------------------------------------
+// AQ1X16 chunks [cb, ce) of row group g (lane = row): a chunk is 8 16-bit codes, 64 weights.  Each
+// code selects a 16-byte entry (8 fp16) of the projection's 1 MiB codebook, gathered from the L2
+// cache; the products are fp16 x fp16 summed in fp32 (v_dot2).  A ring of P code chunks stays in
+// flight: the 8 gathers of a chunk are issued before the code load P chunks ahead, so the wait for
+// the gathers leaves that prefetch outstanding.
+// ------------------------------------------------------------------------------------------
+template <int M, typename Hook>
+__device__ __forceinline__ void aq16_chunks(const Desc &D, int g, int cb, int ce, int lane,
+                                            const uint16_t *const (&xrow)[M], float (&acc)[M], Hook &&hook) {
+    constexpr int P = 4;
+    const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
+    const uint8_t *cbk = reinterpret_cast<const uint8_t *>(D.cbk);
+    uint4 q[P];
+    if (cb < ce) {
+#pragma unroll
+        for (int j = 0; j < P; j++) q[j] = ld16_stream(cptr + (int64_t)min(cb + j, ce - 1) * 1024);
+    }
+    hook();
+    for (int c = cb; c < ce; c += P) {
+        static_for<P>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int cc = c + j;
+            if (cc < ce) {
+                const uint32_t w[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+                u32x4 e[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const uint32_t code = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                    e[i] = gld<u32x4>(cbk + (size_t)code * 16);
+                }
+                q[j] = ld16_stream(cptr + (int64_t)min(cc + P, ce - 1) * 1024);
+                const int ng = min(8, (D.K - cc * 64) >> 3);  // groups inside K (8 but in a tail)
+                if (ng == 8) {
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        cu32p xs = scalar_ptr(xrow[m] + cc * 64);
+#pragma unroll
+                        for (int i = 0; i < 8; i++)
+#pragma unroll
+                            for (int t = 0; t < 4; t++) acc[m] = dot2(e[i][t], xs[4 * i + t], acc[m]);
+                    }
+                } else {
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+#pragma unroll
+                        for (int i = 0; i < 8; i++) {
+                            if (i < ng) {
+                                cu32p xs = scalar_ptr(xrow[m] + cc * 64 + 8 * i);
+#pragma unroll
+                                for (int t = 0; t < 4; t++) acc[m] = dot2(e[i][t], xs[t], acc[m]);
+                            }
+                        }
+                    }
+                }
+            }
+        });
+    }
+    // the row scale, once per unit
+    const float sc = half_bits_to_float(reinterpret_cast<const uint16_t *>(D.scales)[g * 64 + lane]);
+#pragma unroll
+    for (int m = 0; m < M; m++) acc[m] *= sc;
+}
+
+// ------------------------------------------------------------------------------------------
 // One wave unit: rows 64g..64g+63 (one per lane) times chunks [cb, ce).
 // ------------------------------------------------------------------------------------------
 // `hook` runs once, right after the first loads of the unit are issued: the workgroup uses it
@@ -218,6 +282,9 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
 
+    if constexpr (FMT == AQ1X16) {
+        aq16_chunks<M>(D, g, cb, ce, lane, xrow, acc, hook);
+    } else {
     // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
     // row, if this unit owns it, is handled after the pipelined loop.
     const int cfe = min(ce, D.C_full);
@@ -595,6 +662,8 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
                 if (4 * h + v < M) acc[4 * h + v] += (NCH == 2) ? MFA[0][h][v] + MFA[NCH - 1][h][v] : MFA[0][h][v];
     }
 
+    }  // (generic formats)
+
     if (D.wsplit) {
         // Workgroup split: add the kWaves pieces in wave order through LDS (RM activation rows
         // per round); wave 0 goes on with the slice's sums.  The first barrier of a round keeps
@@ -752,6 +821,7 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
             if constexpr ((MASK & (1 << CB4)) != 0) if (D.fmt == CB4) run_unit<CB4, M, EPI, BI>(D, wu, lane, lds, red, hook);
             if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M, EPI, BI>(D, wu, lane, lds, red, hook);
             if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << AQ1X16)) != 0) if (D.fmt == AQ1X16) run_unit<AQ1X16, M, EPI, BI>(D, wu, lane, lds, red, hook);
         }
     } else {
         hook();

@@ -6,7 +6,7 @@
 // of row 64g+r at ((g*C + c)*64 + r)*16.  One wavefront load instruction therefore reads 1 KiB
 // of contiguous memory: chunk c of 64 consecutive rows.  This is the "re-lay the misaligned
 // blocks into planes at load time" step of the ternary vLLM page ("Anatomy of a PQ2_0 block",
-// prepared weights: a code plane, then a scale plane, rows 16-byte aligned), applied to all five
+// prepared weights: a code plane, then a scale plane, rows 16-byte aligned), applied to all six
 // formats.  Within a chunk the codes are permuted so that the decoder can extract two weights
 // with one AND (see the per-format notes below).  Byte counts per weight are unchanged; only
 // the zero padding of the last row group (N up to a multiple of 64) and of a last partial chunk
@@ -15,8 +15,8 @@
 // Planes, each starting at a 256-byte aligned offset from the weight base pointer:
 //   codes   : RG*C*64*16 bytes
 //   scales  : Q4_0 / TQ2: per row group g, per quad q of blocks, per lane r: 4 fp16 scales of
-//             blocks 4q..4q+3 (8 bytes), at ((g*Q + q)*64 + r)*8.  AQ2X8: s[Npad] fp16.
-//   codebook: CB4 16 fp16, CB8 256 fp16, AQ2X8 C[2][256][8] fp16.
+//             blocks 4q..4q+3 (8 bytes), at ((g*Q + q)*64 + r)*8.  AQ2X8, AQ1X16: s[Npad] fp16.
+//   codebook: CB4 16 fp16, CB8 256 fp16, AQ2X8 C[2][256][8] fp16, AQ1X16 C[65536][8] fp16.
 //
 // Intra-chunk code order (w = one 32-bit word of the chunk, t = its index 0..3):
 //   Q4_0  chunk = one block of 32 weights.  Word t holds weights 8t..8t+7; weight 8t+i sits in
@@ -27,6 +27,8 @@
 //         w>>10 (j < 3) each give a pair of consecutive weights scaled by 4^j.
 //   CB4   chunk = 32 weights in canonical order: byte b holds weights 2b (low) and 2b+1 (high).
 //   CB8   chunk = 16 weights, byte b = weight b.
+//   AQ1X16 chunk = 8 groups of 8 weights, 64 weights: the 8 little-endian 16-bit codes in
+//         canonical order.
 //   AQ2X8 is tiled the other way round (one lane per group of 8 weights, not per row): tiles of
 //         8 rows x 64 groups.  With G = K/8 groups, KS = ceil(G/64) slices of 64 groups,
 //         R8 = Npad/8 row blocks and row block r8 = n/8, the tile (r8, s) sits at
@@ -44,7 +46,7 @@ constexpr int kRowsPerGroup = 64;
 constexpr int kChunkBytes = 16;
 constexpr int64_t kPlaneAlign = 256;
 
-enum Fmt : int { Q4_0 = 1, CB4 = 2, CB8 = 3, TQ2 = 4, AQ2X8 = 5 };
+enum Fmt : int { Q4_0 = 1, CB4 = 2, CB8 = 3, TQ2 = 4, AQ2X8 = 5, AQ1X16 = 6 };
 
 struct Layout {
     int fmt = 0;
@@ -71,6 +73,7 @@ inline int k_multiple(int fmt) {
     case CB8: return 1;
     case TQ2: return 128;
     case AQ2X8: return 8;
+    case AQ1X16: return 8;
     default: return 0;
     }
 }
@@ -91,6 +94,7 @@ inline Layout make_layout(int fmt, int64_t N, int64_t K) {
     case CB8: L.row_code_bytes = K; L.weights_per_chunk = 16; break;
     case TQ2: L.row_code_bytes = K / 4; L.weights_per_chunk = 64; L.blocks = K / 128; break;
     case AQ2X8: L.row_code_bytes = K / 4; L.weights_per_chunk = 64; break;
+    case AQ1X16: L.row_code_bytes = K / 4; L.weights_per_chunk = 64; break;
     }
     L.C = (L.row_code_bytes + kChunkBytes - 1) / kChunkBytes;
     L.C_full = K / L.weights_per_chunk;
@@ -104,10 +108,11 @@ inline Layout make_layout(int fmt, int64_t N, int64_t K) {
     int64_t codes = L.RG * L.C * kRowsPerGroup * kChunkBytes;
     int64_t scales = 0, cbk = 0;
     if (fmt == Q4_0 || fmt == TQ2) scales = L.RG * L.Q * kRowsPerGroup * 8;
-    if (fmt == AQ2X8) scales = L.Npad * 2;
+    if (fmt == AQ2X8 || fmt == AQ1X16) scales = L.Npad * 2;
     if (fmt == CB4) cbk = 32;
     if (fmt == CB8) cbk = 512;
     if (fmt == AQ2X8) cbk = 8192;
+    if (fmt == AQ1X16) cbk = 65536 * 8 * 2;
     L.off_scales = align_up(codes, kPlaneAlign);
     L.off_cbk = align_up(L.off_scales + scales, kPlaneAlign);
     L.total = align_up(L.off_cbk + cbk, kPlaneAlign);
@@ -122,6 +127,7 @@ inline int64_t canonical_bytes(int fmt, int64_t N, int64_t K) {
     case CB8: return 512 + N * K;
     case TQ2: return N * (K / 128) * 34;
     case AQ2X8: return 8192 + 2 * N + N * (K / 8) * 2;
+    case AQ1X16: return 65536 * 8 * 2 + 2 * N + N * (K / 8) * 2;
     default: return -1;
     }
 }

@@ -144,6 +144,13 @@ WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonica
         memcpy(dst + L.off_scales, src + 8192, size_t(2 * N));
         memcpy(dst + L.off_cbk, src, 8192);
         break;
+    case AQ1X16: {
+        const int64_t cbk = 65536 * 8 * 2;
+        prep_bytes(L, src + cbk + 2 * N, dst);
+        memcpy(dst + L.off_scales, src + cbk, size_t(2 * N));
+        memcpy(dst + L.off_cbk, src, size_t(cbk));
+        break;
+    }
     }
     return WQD_OK;
 }
