@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_silu_mul_f64.argtypes = [vp, vp, i64, vp]
         L.oracle_residual_add_f64.restype = ctypes.c_int
         L.oracle_residual_add_f64.argtypes = [vp, vp, i64, vp]
+        L.oracle_quantize_x_i8.restype = ctypes.c_int
+        L.oracle_quantize_x_i8.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        L.oracle_tq2_i8_f64.restype = ctypes.c_int
+        L.oracle_tq2_i8_f64.argtypes = [i64, i64, vp, vp, vp, i64, vp, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -146,3 +150,38 @@ def silu_pair_f64(fmt: int, N: int, K: int, canon_gate: np.ndarray, canon_up: np
     g, ag = gemm_f64(fmt, N, K, canon_gate, x_gate, rows=rows)
     u, au = gemm_f64(fmt, N, K, canon_up, x_up, rows=rows)
     return silu_mul(g, u), g, u, ag, au
+
+
+def quantize_x_i8(x_bits: np.ndarray):
+    """Per-128-group int8 quantization of fp16 activations: returns (q int8 [M,K], a fp32
+    [M,K/128], qsum int32 [M,K/128])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x_bits.ndim == 1:
+        x_bits = x_bits[None, :]
+    M, K = x_bits.shape
+    q = np.empty((M, K), dtype=np.int8)
+    a = np.empty((M, K // 128), dtype=np.float32)
+    qs = np.empty((M, K // 128), dtype=np.int32)
+    rc = lib().oracle_quantize_x_i8(_ptr(x_bits), M, K, K, _ptr(q), _ptr(a), _ptr(qs))
+    if rc:
+        raise ValueError(f"oracle_quantize_x_i8 failed: {rc}")
+    return q, a, qs
+
+
+def tq2_i8_f64(N: int, K: int, canon: np.ndarray, q: np.ndarray, a: np.ndarray, rows=None):
+    """TQ2 rows times int8 activations: returns (y, t), each (M, nrows)."""
+    canon = np.ascontiguousarray(canon, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    M = q.shape[0]
+    if rows is None:
+        nrows, rp = N, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rp = rows.shape[0], _ptr(rows)
+    y = np.empty((M, nrows), dtype=np.float64)
+    t = np.empty((M, nrows), dtype=np.float64)
+    rc = lib().oracle_tq2_i8_f64(N, K, _ptr(canon), _ptr(q), _ptr(a), M, rp, nrows, _ptr(y), _ptr(t))
+    if rc:
+        raise ValueError(f"oracle_tq2_i8_f64 failed: {rc}")
+    return y, t

@@ -21,6 +21,11 @@
  *    layout: one codebook of 65,536 entries of 8 fp16 values per matrix and one 16-bit code per
  *    group of 8 weights (2 bits per weight), with the per-row scales the exporter copies; the
  *    products are formed in f32.  Codebook, then scales, then codes is this build's reading.
+ *  - TQ2 with int8 activations: "Making a ternary reasoning model fast in vLLM", "Why small
+ *    integers are a good fit": each 128-element group of x is scaled to signed int8
+ *    (x ~ a_g * q, q in [-127, 127]), the inner sums over a block are integers, and floating
+ *    point is applied once per group (block scale times a_g).  The scale a_g = max|x| / 127 and
+ *    rounding to nearest even, both in fp32, are this build's reading.
  *  - Epilogues: trapetum "Benchmarks", "Short-context decode, step by step" (the fused decode
  *    kernels): the gate and up projections share one launch whose reduce applies SiLU to the
  *    gate result and multiplies by the up result, and the o and down projections add the
@@ -218,5 +223,72 @@ int oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h) 
 int oracle_residual_add_f64(const float *r, const double *y, int64_t n, double *out) {
     if (n < 0 || (n > 0 && (!r || !y || !out))) return -3;
     for (int64_t i = 0; i < n; i++) out[i] = (double)r[i] + y[i];
+    return 0;
+}
+
+/* ------------------------------------------------------------------ TQ2 with int8 activations */
+
+/* Quantize each 128-element group of each activation row to int8: a = max|x| / 127 in fp32
+ * (x converted exactly from fp16), q = x / a rounded to nearest even in fp32 (0 when a == 0),
+ * qsum = sum of the group's q.  q[m*K + k] in natural order, a and qsum [m*(K/128) + group]. */
+int oracle_quantize_x_i8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *a,
+                         int32_t *qsum) {
+    if (!x || !q || !a || !qsum || M < 1 || K < 128 || K % 128 || ldx < K) return -3;
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t b = 0; b < K / 128; b++) {
+            volatile float amax = 0.0f;
+            for (int i = 0; i < 128; i++) {
+                float v = fabsf((float)oracle_half_to_double(x[m * ldx + b * 128 + i]));
+                if (v > amax) amax = v;
+            }
+            volatile float sc = amax / 127.0f;
+            int32_t sum = 0;
+            for (int i = 0; i < 128; i++) {
+                int qi = 0;
+                if (sc > 0.0f) {
+                    volatile float r = (float)oracle_half_to_double(x[m * ldx + b * 128 + i]) / sc;
+                    qi = (int)rintf(r);
+                    if (qi > 127) qi = 127;
+                    if (qi < -127) qi = -127;
+                }
+                q[m * K + b * 128 + i] = (int8_t)qi;
+                sum += qi;
+            }
+            a[m * (K / 128) + b] = sc;
+            qsum[m * (K / 128) + b] = sum;
+        }
+    }
+    return 0;
+}
+
+/* y[m*nrows + i] = sum over blocks b of d_b * a[m][b] * sum_{k in b} (code_k - 1) * q[m][k] for TQ2
+ * row rows[i], with the integer sums exact and the products in fp64; t[m*nrows + i] = the same
+ * with every block term taken in absolute value (the scale of the fp rounding). */
+int oracle_tq2_i8_f64(int64_t N, int64_t K, const uint8_t *canon, const int8_t *q, const float *a,
+                      int64_t M, const int64_t *rows, int64_t nrows, double *y, double *t) {
+    if (oracle_canonical_bytes(4, N, K) < 0) return -1;
+    if (!canon || !q || !a || !y || M < 1) return -3;
+    if (!rows && nrows != N) return -2;
+    for (int64_t i = 0; i < nrows; i++) {
+        int64_t n = rows ? rows[i] : i;
+        if (n < 0 || n >= N) return -2;
+        for (int64_t m = 0; m < M; m++) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t b = 0; b < K / 128; b++) {
+                const uint8_t *blk = canon + (n * (K / 128) + b) * 34;
+                double d = oracle_half_to_double(rd16(blk));
+                int64_t isum = 0;
+                for (int j = 0; j < 128; j++) {
+                    int code = (blk[2 + j / 4] >> (2 * (j % 4))) & 3;
+                    isum += (int64_t)(code - 1) * q[m * K + b * 128 + j];
+                }
+                double term = d * (double)a[m * (K / 128) + b] * (double)isum;
+                acc += term;
+                aacc += fabs(term);
+            }
+            y[m * nrows + i] = acc;
+            if (t) t[m * nrows + i] = aacc;
+        }
+    }
     return 0;
 }

@@ -61,6 +61,17 @@ int oracle_silu_mul_f64(const double *g, const double *u, int64_t n, double *h);
 /* out[i] = (double)r[i] + y[i] for i < n (residual r in fp32, projection result y). */
 int oracle_residual_add_f64(const float *r, const double *y, int64_t n, double *out);
 
+/* TQ2 with int8 activations.  Per 128-element group of each row of x: a = max|x| / 127 (fp32),
+ * q = round-to-nearest-even(x / a) in fp32 (0 when a == 0), qsum = sum of q.  q is [M][K] in
+ * natural order, a and qsum [M][K/128]. */
+int oracle_quantize_x_i8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *a,
+                         int32_t *qsum);
+
+/* y = sum_b d_b * a_b * sum_{k in b} (code_k - 1) * q_k (exact integers, fp64 products) for TQ2
+ * rows rows[0..nrows) (NULL: all N); t = the sum of the terms' absolute values. */
+int oracle_tq2_i8_f64(int64_t N, int64_t K, const uint8_t *canon, const int8_t *q, const float *a,
+                      int64_t M, const int64_t *rows, int64_t nrows, double *y, double *t);
+
 #ifdef __cplusplus
 }
 #endif

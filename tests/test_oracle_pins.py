@@ -427,3 +427,68 @@ def test_residual_add_is_exact_on_one_hot_activation():
     # zero activation: the residual comes back unchanged
     y0, _ = oracle.gemm_f64(I.CB8, N, K, canon, np.zeros((1, K), dtype=np.uint16))
     assert np.array_equal(oracle.residual_add(res, y0), res.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- TQ2, int8 x
+# "Making a ternary reasoning model fast in vLLM", "Why small integers are a good fit".
+
+
+def test_int8_quantization_hand_group():
+    g = read_golden("tq2_i8_group.txt")
+    x = np.zeros((1, 128), dtype=np.float16)
+    vals = [float(v) for v in g["x"]]
+    x[0, :len(vals)] = vals
+    q, a, qs = oracle.quantize_x_i8(x.view(np.uint16))
+    want = [int(v) for v in g["q"]]
+    assert list(q[0, :len(want)]) == want and not q[0, len(want):].any()
+    assert a[0, 0] == float(g["a"][0]) and qs[0, 0] == int(g["qsum"][0])
+
+
+def test_int8_quantization_properties():
+    x = I.gen_x(3, 1024, (80, 0))
+    x[1, 128:256] = 0  # an all-zero group
+    q, a, qs = oracle.quantize_x_i8(x)
+    xv = x.view(np.float16).astype(np.float64).reshape(3, 8, 128)
+    qv = q.astype(np.float64).reshape(3, 8, 128)
+    av = a.astype(np.float64)[:, :, None]
+    # rounding to nearest: |x - a q| <= a / 2 (plus the fp32 rounding of x / a)
+    assert np.all(np.abs(xv - av * qv) <= av * (0.5 + 2.0 ** -20) + 1e-300)
+    # the largest |x| of a group maps to +-127; every |q| <= 127
+    nz = a[:, :] > 0
+    assert np.all(np.abs(q).reshape(3, 8, 128).max(axis=2)[nz] == 127)
+    assert a[1, 1] == 0 and not q[1, 128:256].any()
+    assert np.array_equal(qs, q.astype(np.int32).reshape(3, 8, 128).sum(axis=2))
+    # a = max|x| / 127 in fp32
+    amax = np.abs(xv).max(axis=2).astype(np.float32)
+    assert np.array_equal(a, (amax / np.float32(127)).astype(np.float32))
+
+
+def test_int8_path_equals_exact_path_on_grid_activations():
+    # x = q * 2^-7 with one |q| = 127 per group is exactly representable, so quantization gives
+    # q back and the int8 product is the exact product
+    N, K, M = 40, 512, 2
+    r = np.random.default_rng(81)
+    qi = r.integers(-127, 128, size=(M, K))
+    qi[:, ::128] = 127
+    x = (qi * 2.0 ** -7).astype(np.float16)
+    canon = I.gen_weight(I.TQ2, N, K, (81, 1))
+    q, a, _ = oracle.quantize_x_i8(x.view(np.uint16))
+    assert np.array_equal(q, qi) and np.all(a == 2.0 ** -7)
+    y8, t = oracle.tq2_i8_f64(N, K, canon, q, a)
+    y, _ = oracle.gemm_f64(I.TQ2, N, K, canon, x.view(np.uint16))
+    np.testing.assert_allclose(y8, y, rtol=1e-12, atol=1e-12)
+
+
+def test_int8_path_error_within_the_rounding_bound():
+    # |y_i8 - y| <= sum_k |w_k| * a_g(k) / 2 (each activation moves by at most half a step)
+    N, K, M = 30, 1024, 3
+    canon = I.gen_weight(I.TQ2, N, K, (82, 0))
+    x = I.gen_x(M, K, (82, 1))
+    q, a, _ = oracle.quantize_x_i8(x)
+    y8, _ = oracle.tq2_i8_f64(N, K, canon, q, a)
+    y, _ = oracle.gemm_f64(I.TQ2, N, K, canon, x)
+    w = np.abs(oracle.decode_f64(I.TQ2, N, K, canon))
+    step = np.repeat(a.astype(np.float64), 128, axis=1)  # a_g per k
+    bound = (w[None, :, :] * step[:, None, :] * (0.5 + 2.0 ** -20)).sum(axis=2)
+    assert np.all(np.abs(y8 - y) <= bound)
+    assert np.abs(y8 - y).max() > 0  # the path is lossy
