@@ -104,6 +104,31 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
                      int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
 
+/* ---------------------------------------------------------------- TQ2 with int8 activations */
+
+/* Device workspace wqd_gemm_i8 needs (always > 0): the quantized activations and wqd_gemm's
+ * counters and partial sums.  fmt must be WQD_TQ2 (WQD_EINVAL otherwise). */
+WQD_API int64_t wqd_gemm_i8_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
+
+/* The TQ2 projection with int8 activations ("Making a ternary reasoning model fast in vLLM", "Why
+ * small integers are a good fit"): each 128-element block of each row of x is quantized to int8,
+ * a = max|x| / 127 and q = x / a rounded to nearest even (both fp32; q = 0 for an all-zero
+ * block), then y[m][n] = sum_b d_b * a[m][b] * sum_{k in b} (code_k - 1) * q[m][k] with exact
+ * integer block sums (v_dot4_i32_i8) and fp32 accumulation over blocks.  Two launches: the
+ * quantizer, then the product.  Lossy against wqd_gemm: each activation moves by at most a/2, so
+ * |y_i8 - y| <= sum_k |w[n][k]| * a(k) / 2.  Arguments as wqd_gemm (fmt must be WQD_TQ2, so K is a
+ * multiple of 128); the workspace (256-byte aligned, at least wqd_gemm_i8_workspace_bytes) is
+ * required and must be zero-filled before its first use, like wqd_gemm's. */
+WQD_API int wqd_gemm_i8(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
+                        int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                        void *stream);
+
+/* Inspection of the quantizer wqd_gemm_i8 runs first: q[m*K + k] (int8, natural order), a[m*(K/128)
+ * + b] (fp32) and qsum[m*(K/128) + b] (int32, the block's sum of q) for M <= 8 rows of x, K a
+ * multiple of 128.  The values are those wqd_gemm_i8 uses (it stores q in another order). */
+WQD_API int wqd_quantize_i8(const void *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *a,
+                            int32_t *qsum, void *stream);
+
 /* Debug decode: out[n*K + k] = dequantized weight in fp32, bit-exact: the exact value for Q4_0,
  * CB4, CB8, TQ2 and AQ1X16 (all representable in fp32); for AQ2X8 fp32(fp32(C0 + C1) * s) with
  * round-to-nearest-even after the add and after the product. */

@@ -264,3 +264,15 @@ def test_batch_invariant_flag_rules():
     assert L.wqd_stack_launches(mixed, 2, 1, W.WQD_PERSISTENT | BI) == 2   # one instance each
     assert L.wqd_stack_setup(mixed, 2, 1, W.WQD_ORDERED, FAKE, 1 << 30, None) == W.WQD_EINVAL
     assert L.wqd_run_projections(mixed, 2, 1, 3 | BI, FAKE, 1 << 30, None) == W.WQD_EINVAL
+
+
+def test_int8_entry_point_rules():
+    L = W.lib()
+    assert L.wqd_gemm_i8_workspace_bytes(I.CB4, 64, 1024, 1) == W.WQD_EINVAL  # TQ2 only
+    assert L.wqd_gemm_i8_workspace_bytes(I.TQ2, 64, 1024, 1) > 0
+    assert L.wqd_gemm_i8(I.TQ2, 64, 1024, FAKE, FAKE, 1, 1024, FAKE, 64, None, 0, None) == W.WQD_EINVAL
+    need = L.wqd_gemm_i8_workspace_bytes(I.TQ2, 64, 1024, 1)
+    assert L.wqd_gemm_i8(I.TQ2, 64, 1024, FAKE, FAKE, 1, 1024, FAKE, 64, FAKE, need - 1, None) == W.WQD_ESPACE
+    assert L.wqd_gemm_i8(I.TQ2, 64, 1000, FAKE, FAKE, 1, 1024, FAKE, 64, FAKE, need, None) == W.WQD_ESHAPE
+    assert L.wqd_quantize_i8(FAKE, 1, 100, 128, FAKE, FAKE, FAKE, None) == W.WQD_ESHAPE
+    assert L.wqd_quantize_i8(None, 1, 128, 128, FAKE, FAKE, FAKE, None) == W.WQD_EINVAL

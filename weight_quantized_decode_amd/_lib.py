@@ -26,7 +26,7 @@ EXPORTED = [
     "wqd_canonical_bytes", "wqd_prepared_bytes", "wqd_prepare_host", "wqd_gemm_workspace_bytes",
     "wqd_gemm", "wqd_dequant_f32", "wqd_stack_workspace_bytes", "wqd_stack_setup",
     "wqd_run_projections", "wqd_run_projections_timed", "wqd_stack_launches", "wqd_stream_check",
-    "wqd_last_hip_error", "wqd_status_str",
+    "wqd_last_hip_error", "wqd_status_str", "wqd_gemm_i8_workspace_bytes", "wqd_gemm_i8", "wqd_quantize_i8",
 ]
 
 
@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
             "wqd_gemm_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
             "wqd_gemm": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
             "wqd_dequant_f32": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp]),
+            "wqd_gemm_i8_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
+            "wqd_gemm_i8": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
+            "wqd_quantize_i8": (ctypes.c_int, [vp, i64, i64, i64, vp, vp, vp, vp]),
             "wqd_stack_workspace_bytes": (i64, [ctypes.POINTER(wqd_proj), i32, i64]),
             "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
             "wqd_run_projections": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
@@ -133,6 +136,25 @@ def wqd_gemm(fmt: int, N: int, K: int, w, x, y, workspace=None, stream=None) -> 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("wqd_gemm", lib().wqd_gemm(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
                                       _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wqd_gemm_i8_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
+    return _check("wqd_gemm_i8_workspace_bytes", lib().wqd_gemm_i8_workspace_bytes(fmt, N, K, M))
+
+
+def wqd_gemm_i8(fmt: int, N: int, K: int, w, x, y, workspace, stream=None) -> None:
+    """TQ2 times int8-quantized x (quantized inside the call); x and y may have row strides."""
+    M = x.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("wqd_gemm_i8", lib().wqd_gemm_i8(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
+                                            _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wqd_quantize_i8(x, q, a, qsum, stream=None) -> None:
+    """q (int8 [M, K]), a (fp32 [M, K/128]) and qsum (int32 [M, K/128]) of fp16 x [M, K]."""
+    M, K = x.shape
+    _check("wqd_quantize_i8", lib().wqd_quantize_i8(_dptr(x), M, K, x.stride(0), _dptr(q), _dptr(a), _dptr(qsum),
+                                                    _stream(stream)))
 
 
 def wqd_dequant_f32(fmt: int, N: int, K: int, w, out, stream=None) -> None:

@@ -93,6 +93,48 @@ __global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, La
     }
 }
 
+// Int8 activations for the TQ2 int8 path: one wave per (row m, 128-element block b).  PERM = false
+// stores q in natural order (the inspection entry point).  a = max|x|
+// / 127 and q = x / a rounded to nearest even, both in fp32 (q = 0 when a == 0); q is stored in
+// the field order of the TQ2 chunk words (layout.h): within each 16-weight word, dword j holds the
+// activations of weights 2j, 2j+8, 2j+1, 2j+9.  Also writes a and the block's sum of q.
+template <bool PERM>
+__global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t *x, int64_t ldx, int M, int nb, int8_t *q,
+                                                          int64_t ldq, float *a, int32_t *qs) {
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= M * nb) return;
+    const int lane = threadIdx.x & 63;
+    const int m = wv / nb, b = wv - m * nb;
+    const uint32_t pair = *reinterpret_cast<const uint32_t *>(x + (int64_t)m * ldx + (int64_t)b * 128 + 2 * lane);
+    const float x0 = half_bits_to_float(pair & 0xFFFFu), x1 = half_bits_to_float(pair >> 16);
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float sc = __fdiv_rn(amax, 127.0f);
+    int q0 = 0, q1 = 0;
+    if (sc > 0.f) {
+        q0 = (int)rintf(__fdiv_rn(x0, sc));
+        q1 = (int)rintf(__fdiv_rn(x1, sc));
+        q0 = min(127, max(-127, q0));
+        q1 = min(127, max(-127, q1));
+    }
+    int sum = q0 + q1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o);
+    int8_t *qrow = q + (int64_t)m * ldq + (int64_t)b * 128;
+    for (int e = 0; e < 2; e++) {
+        const int k = 2 * lane + e;                 // element of the block
+        const int base = k & ~15, i = k & 15;       // word start, weight in the word
+        const int j = (i & 1) ? ((i >= 9) ? (i - 9) >> 1 : (i - 1) >> 1) : ((i >= 8) ? (i - 8) >> 1 : i >> 1);
+        const int f = (i & 1) ? ((i >= 9) ? 3 : 2) : ((i >= 8) ? 1 : 0);
+        qrow[PERM ? base + 4 * j + f : k] = (int8_t)(e ? q1 : q0);
+    }
+    if (lane == 0) {
+        a[(int64_t)m * nb + b] = sc;
+        qs[(int64_t)m * nb + b] = sum;
+    }
+}
+
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
@@ -125,6 +167,7 @@ static GemvFn pick_gemv(int mask, int M, bool epi = false, bool bi = false) {
     case 1 << CB8: return gemv_fn_cb8(M, epi, bi);
     case 1 << TQ2: return gemv_fn_tq2(M, epi, bi);
     case 1 << AQ1X16: return gemv_fn_aq1x16(M, epi, bi);
+    case 1 << TQ2I8: return gemv_fn_tq2i8(M, epi, bi);
     case kMaskCB48: return bi ? nullptr : gemv_fn_cb48(M, epi);
     }
     return nullptr;
@@ -728,6 +771,77 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
     int *cnt = reinterpret_cast<int *>(ws);
     float *part = ws ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr;
     return gemm_launch(P, w, x, M, ldx, y, ldy, cnt, part, static_cast<hipStream_t>(stream), cus);
+}
+
+// Workspace of wqd_gemm_i8: [wqd_gemm's counters and partials][q: M x K bytes][a: M x K/128 fp32]
+// [sums of q: M x K/128 int32], each region 256-byte aligned.
+struct I8Ws {
+    int64_t off_q = 0, off_a = 0, off_s = 0, total = 0;
+};
+static I8Ws i8_workspace(const Plan &P, int64_t M, int64_t K) {
+    I8Ws w;
+    w.off_q = align_up(P.ws_bytes(), 256);
+    w.off_a = align_up(w.off_q + M * K, 256);
+    w.off_s = w.off_a + M * (K / 128) * 4;
+    w.total = align_up(w.off_s + M * (K / 128) * 4, 256);
+    return w;
+}
+
+WQD_API int64_t wqd_gemm_i8_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M) {
+    if (fmt != TQ2) return WQD_EINVAL;
+    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+    Plan P = plan_single(TQ2, N, K, M, device_cus());
+    if (!P.L.ok) return WQD_ESHAPE;
+    return i8_workspace(P, M, K).total;
+}
+
+WQD_API int wqd_gemm_i8(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
+                        float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
+    if (fmt != TQ2) return WQD_EINVAL;
+    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+    if (rc != WQD_OK) return rc;
+    const int cus = device_cus();
+    Plan P = plan_single(TQ2, N, K, M, cus);
+    const I8Ws iw = i8_workspace(P, M, K);
+    if (!workspace) return WQD_EINVAL;
+    if (workspace_bytes < iw.total) return WQD_ESPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return WQD_EALIGN;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int8_t *q = reinterpret_cast<int8_t *>(ws + iw.off_q);
+    float *a = reinterpret_cast<float *>(ws + iw.off_a);
+    int32_t *qs = reinterpret_cast<int32_t *>(ws + iw.off_s);
+    const int nb = int(K / 128);
+    const unsigned blocks = unsigned((M * nb + 3) / 4);
+    hipLaunchKernelGGL(quantize_i8_kernel<true>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(x), ldx,
+                       int(M), nb, q, K, a, qs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+    GemvParams GP;
+    memset(&GP, 0, sizeof(GP));
+    GP.d[0] = make_desc(P, w, q, K, y, ldy, P.S > 1 ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr,
+                        reinterpret_cast<int *>(ws));
+    GP.d[0].fmt = TQ2I8;
+    GP.d[0].cbk = reinterpret_cast<const uint16_t *>(a);  // activation scales, then the sums of q
+    GP.descs = nullptr;
+    GP.ndesc = 1;
+    GP.total_wgu = int32_t((GP.d[0].wu_count + kWaves - 1) / kWaves);
+    return launch_gemv(fmt_bit(TQ2I8), int(M), GP, st, cus);
+}
+
+WQD_API int wqd_quantize_i8(const void *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *a, int32_t *qsum,
+                            void *stream) {
+    if (!x || !q || !a || !qsum) return WQD_EINVAL;
+    if (M < 1 || M > WQD_MAX_M || K < 128 || K % 128 || ldx < K || K > (int64_t(1) << 31)) return WQD_ESHAPE;
+    if ((reinterpret_cast<uintptr_t>(x) & 3) || (ldx & 1) || (reinterpret_cast<uintptr_t>(a) & 3) ||
+        (reinterpret_cast<uintptr_t>(qsum) & 3))
+        return WQD_EALIGN;
+    const int nb = int(K / 128);
+    hipLaunchKernelGGL(quantize_i8_kernel<false>, dim3(unsigned((M * nb + 3) / 4)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(x), ldx, int(M), nb, q, K, a,
+                       qsum);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
 
 WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream) {

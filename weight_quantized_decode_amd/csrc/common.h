@@ -205,6 +205,7 @@ GemvFn gemv_fn_cb4(int M, bool epi, bool bi);
 GemvFn gemv_fn_cb8(int M, bool epi, bool bi);
 GemvFn gemv_fn_tq2(int M, bool epi, bool bi);
 GemvFn gemv_fn_aq1x16(int M, bool epi, bool bi);
+GemvFn gemv_fn_tq2i8(int M, bool epi, bool bi);
 GemvFn gemv_fn_cb48(int M, bool epi);
 
 }  // namespace wqd

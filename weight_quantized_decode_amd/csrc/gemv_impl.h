@@ -249,6 +249,68 @@ __device__ __forceinline__ void aq16_chunks(const Desc &D, int g, int cb, int ce
 }
 
 // ------------------------------------------------------------------------------------------
+// TQ2 times int8 activations, chunks [cb, ce) of row group g (lane = row; the slice is a whole
+// number of 128-weight blocks).  Per block: the 2-bit codes of a word shifted by 2j and masked with
+// 0x03030303 give 4 codes in 4 bytes; v_dot4_i32_i8 multiplies them with the matching 4 int8
+// activations (the quantizer stores each block's q in this field order) into an int32 sum, 32 per
+// block; the -1 code offset comes off as the block's sum of q, and floating point is applied once
+// per block: acc += (d * a) * (sum code*q - sum q).  D.x holds q ([M][ldx] bytes), D.cbk the
+// per-block activation scales a[M][K/128] (fp32) followed by the sums of q [M][K/128] (int32).
+// ------------------------------------------------------------------------------------------
+template <int M, typename Hook>
+__device__ __forceinline__ void tq2i8_chunks(const Desc &D, int g, int cb, int ce, int lane, float (&acc)[M],
+                                             Hook &&hook) {
+    constexpr int P = 4;  // code chunks in flight (two blocks)
+    const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
+    const int nb = D.K / 128;
+    const int8_t *qb = reinterpret_cast<const int8_t *>(D.x);
+    const float *ab = reinterpret_cast<const float *>(D.cbk);
+    const int32_t *sb = reinterpret_cast<const int32_t *>(ab + (int64_t)M * nb);
+    uint4 q[P];
+    if (cb < ce) {
+#pragma unroll
+        for (int j = 0; j < P; j++) q[j] = ld16_stream(cptr + (int64_t)min(cb + j, ce - 1) * 1024);
+    }
+    hook();
+    for (int c = cb; c < ce; c += P) {
+        static_for<P / 2>([&](auto bc) {
+            constexpr int jb = decltype(bc)::value;  // block of this round: chunks 2jb, 2jb+1
+            const int cc = c + 2 * jb;
+            if (cc < ce) {
+                const int b = cc >> 1;
+                const uint32_t dbits = gld<uint16_t>(D.scales + (((int64_t)g * D.Q + (b >> 2)) * 64 + lane) * 8 + (b & 3) * 2);
+                int32_t isum[M];
+#pragma unroll
+                for (int m = 0; m < M; m++) isum[m] = 0;
+                static_for<2>([&](auto hc) {
+                    constexpr int h = decltype(hc)::value;
+                    const uint4 v = q[2 * jb + h];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        cu32p xs = scalar_ptr(qb + (int64_t)m * D.ldx + (int64_t)b * 128 + 64 * h);
+#pragma unroll
+                        for (int t = 0; t < 4; t++)
+#pragma unroll
+                            for (int j = 0; j < 4; j++)
+                                isum[m] = __builtin_amdgcn_sdot4((int)((w4[t] >> (2 * j)) & 0x03030303u),
+                                                                 (int)xs[4 * t + j], isum[m], false);
+                    }
+                });
+                q[2 * jb] = ld16_stream(cptr + (int64_t)min(cc + P, ce - 1) * 1024);
+                q[2 * jb + 1] = ld16_stream(cptr + (int64_t)min(cc + P + 1, ce - 1) * 1024);
+                const float d = half_bits_to_float(dbits);
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    const float da = d * __builtin_bit_cast(float, scalar_ptr(ab + (int64_t)m * nb + b)[0]);
+                    acc[m] = fmaf(da, (float)(isum[m] - (int32_t)scalar_ptr(sb + (int64_t)m * nb + b)[0]), acc[m]);
+                }
+            }
+        });
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // One wave unit: rows 64g..64g+63 (one per lane) times chunks [cb, ce).
 // ------------------------------------------------------------------------------------------
 // `hook` runs once, right after the first loads of the unit are issued: the workgroup uses it
@@ -284,6 +346,8 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
 
     if constexpr (FMT == AQ1X16) {
         aq16_chunks<M>(D, g, cb, ce, lane, xrow, acc, hook);
+    } else if constexpr (FMT == TQ2I8) {
+        tq2i8_chunks<M>(D, g, cb, ce, lane, acc, hook);
     } else {
     // Chunks [cb, cfe) are whole chunks (x read with scalar loads); a partial last chunk of the
     // row, if this unit owns it, is handled after the pipelined loop.
@@ -822,6 +886,7 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
             if constexpr ((MASK & (1 << CB8)) != 0) if (D.fmt == CB8) run_unit<CB8, M, EPI, BI>(D, wu, lane, lds, red, hook);
             if constexpr ((MASK & (1 << TQ2)) != 0) if (D.fmt == TQ2) run_unit<TQ2, M, EPI, BI>(D, wu, lane, lds, red, hook);
             if constexpr ((MASK & (1 << AQ1X16)) != 0) if (D.fmt == AQ1X16) run_unit<AQ1X16, M, EPI, BI>(D, wu, lane, lds, red, hook);
+            if constexpr ((MASK & (1 << TQ2I8)) != 0) if (D.fmt == TQ2I8) run_unit<TQ2I8, M, EPI, BI>(D, wu, lane, lds, red, hook);
         }
     } else {
         hook();

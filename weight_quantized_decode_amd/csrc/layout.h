@@ -47,6 +47,8 @@ constexpr int kChunkBytes = 16;
 constexpr int64_t kPlaneAlign = 256;
 
 enum Fmt : int { Q4_0 = 1, CB4 = 2, CB8 = 3, TQ2 = 4, AQ2X8 = 5, AQ1X16 = 6 };
+// Kernel-side id of a TQ2 projection multiplied by int8-quantized activations (TQ2 weights).
+constexpr int TQ2I8 = 7;
 
 struct Layout {
     int fmt = 0;
