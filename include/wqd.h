@@ -181,10 +181,11 @@ enum {
  * draft of M tokens verified in one pass whose rows carry, bit for bit, the logits of M decode
  * steps).  With it, row m of a call with M activation rows is bitwise equal to the same call
  * made with row m alone (M = 1), for every M <= 8, in every mode and whatever else the list
- * holds: every projection is sliced as it would be alone at M = 1, and every M runs the same
- * per-row instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
- * A verify of 9..16 rows is two calls.  Row formats only: a list with an AQ2X8 entry returns
- * WQD_EINVAL.  Results differ in rounding (within the bound) from calls without the flag. */
+ * holds: every projection is sliced the same way at every M, and every M runs the same per-row
+ * instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
+ * A verify of 9..16 rows is two calls.  AQ2X8 entries then use the direct decode at every M
+ * (their M = 1 lookup-table kernel rounds differently), one workgroup per CU and one row block per
+ * wave.  Results differ in rounding (within the bound) from calls without the flag. */
 enum { WQD_BATCH_INVARIANT = 0x10 };
 
 /* Device workspace bytes for wqd_run_projections over this list in any mode (descriptor

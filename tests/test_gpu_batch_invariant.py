@@ -23,6 +23,7 @@ SHAPES = [
     (I.CB8, 200, 1001), (I.CB8, 3, 1),
     (I.TQ2, 70, 128), (I.TQ2, 130, 17408),
     (I.AQ1X16, 100, 4104),
+    (I.AQ2X8, 200, 1000), (I.AQ2X8, 129, 8192),
 ]
 
 
@@ -71,7 +72,7 @@ def test_modes_and_list_contents_do_not_change_bits(M):
     bits equal the entry run alone."""
     note(f"batch-invariant list in every mode M={M}")
     specs = [(I.CB4, 4096, 4096), (I.CB4, 1100, 4096), (I.CB8, 2000, 4096), (I.Q4_0, 640, 2048),
-             (I.TQ2, 512, 5120)]
+             (I.TQ2, 512, 5120), (I.AQ2X8, 1024, 4096)]
     xs = {K: I.gen_x(M, K, (61, K, M)) for K in {k for _, _, k in specs}}
     xd = {K: upload_x(v) for K, v in xs.items()}
     ws_ = [upload_weight(f, N, K, I.gen_weight(f, N, K, (61, f, N, K))) for f, N, K in specs]

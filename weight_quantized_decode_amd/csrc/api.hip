@@ -387,12 +387,14 @@ struct AqPlan {
     int64_t ws_bytes() const { return b > 1 ? kCntRegion + part_bytes : 0; }
 };
 
-static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg) {
+// bi: the batch-invariant plan (direct decode, one row block per wave per slice, and the caller
+// passes a workgroup count that does not depend on M), so the pieces do not depend on M.
+static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg, bool bi = false) {
     AqPlan A;
     A.L = make_layout(AQ2X8, N, K);
     if (!A.L.ok) return A;
-    const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = aq_rw_max(M), W = aq_waves(int(M));
-    const int64_t build = (M == 1) ? WQD_AQ_BUILD_CHARGE : 2, split_charge = WQD_AQ_SPLIT_CHARGE;
+    const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = bi ? 1 : aq_rw_max(M), W = aq_waves(int(M));
+    const int64_t build = (M == 1 && !bi) ? WQD_AQ_BUILD_CHARGE : 2, split_charge = WQD_AQ_SPLIT_CHARGE;
     if (nwg < 1) nwg = 1;
     double best = 1e300;
     for (int64_t b = 1; b <= KS && b <= WQD_AQ_MAX_SPLITS; b++) {
@@ -448,8 +450,8 @@ static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_
     return D;
 }
 
-static int launch_aq(int64_t M, int64_t RW, const AqParams &AP, hipStream_t st) {
-    AqFn fn = aq_fn(int(M), int(RW));
+static int launch_aq(int64_t M, int64_t RW, const AqParams &AP, hipStream_t st, bool bi = false) {
+    AqFn fn = aq_fn(int(M), int(RW), bi);
     if (!fn) return WQD_EINVAL;
     hipLaunchKernelGGL(fn, dim3(unsigned(AP.nwg)), dim3(aq_waves(int(M)) * 64), 0, st, AP);
     hipError_t e = hipGetLastError();
@@ -669,17 +671,18 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
     }
     if (has_aq) {
         // AQ2X8 projections: one launch, every workgroup taking one piece of each
-        const int64_t aq_wg = aq_nwg(M, cus);
+        const int64_t aq_wg = bi ? cus : aq_nwg(M, cus);  // (batch-invariant: one workgroup per CU at every M)
         LaunchGroup G;
         G.mask = fmt_bit(AQ2X8);
         G.aq = true;
+        G.bi = bi;
         G.first = int(SP.aqdescs.size());
         std::vector<AqPlan> plans;
         std::vector<int> idx;
         int64_t total_pieces = 0;
         for (int i = b; i < e; i++) {
             if (p[i].fmt != AQ2X8) continue;
-            plans.push_back(plan_aq(p[i].N, p[i].K, M, aq_wg));
+            plans.push_back(plan_aq(p[i].N, p[i].K, M, aq_wg, bi));
             idx.push_back(i);
             total_pieces += plans.back().a * plans.back().b;
         }
@@ -707,9 +710,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
     int rc = check_list(p, count, M);
     if (rc != WQD_OK) return rc;
-    if (bi)
-        for (int i = 0; i < count; i++)
-            if (p[i].fmt == AQ2X8) return WQD_EINVAL;  // (no batch-invariant AQ2X8 kernel)
+
     SP.off_descs = 0;
     SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
     SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
@@ -943,7 +944,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.nwg = int32_t(G.nwg);
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
-            rc = launch_aq(M, G.rw, AP, st);
+            rc = launch_aq(M, G.rw, AP, st, G.bi);
             if (rc != WQD_OK) return rc;
             if ((rc = mark(1)) != WQD_OK) return rc;
             li++;

@@ -194,8 +194,8 @@ struct AqParams {
 
 typedef void (*AqFn)(AqParams);
 // AQ2X8 kernel for M activation rows with RW 8-row blocks per wave per K-slice (M = 1: 2, 4 or
-// 8; M > 1: 1 or 2).
-AqFn aq_fn(int M, int RW);
+// 8; M > 1: 1 or 2); bi: the batch-invariant instance (direct decode at every M, RW = 1).
+AqFn aq_fn(int M, int RW, bool bi = false);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies

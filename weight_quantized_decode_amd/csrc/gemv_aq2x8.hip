@@ -267,9 +267,9 @@ __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int
     }
 }
 
-template <int M>
+template <int M, bool LUT>
 struct LdsWords {
-    static constexpr int value = (M == 1) ? 2 * 256 * 64 : 2048 + 256 * M;
+    static constexpr int value = LUT ? 2 * 256 * 64 : 2048 + 256 * M;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -302,11 +302,14 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
 
 // M = 1: the 128 KiB table allows one workgroup per CU, i.e. 2 waves per SIMD, so each wave may
 // use 256 VGPRs (the compiler would otherwise aim for more waves than can ever be resident).
-template <int M, int RW, int NP>
+// BI: the batch-invariant instance, which takes the direct decode at every M (M = 1 included), so
+// that a row's arithmetic does not depend on M.
+template <int M, int RW, int NP, bool BI = false>
 __global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, aq_waves_per_simd(M))))
 void aq_kernel(AqParams P) {
     constexpr int W = aq_waves(M);  // waves per workgroup
-    __shared__ uint32_t lds[LdsWords<M>::value];
+    constexpr bool LUT = (M == 1 && !BI);  // lookup tables (else the direct decode)
+    __shared__ uint32_t lds[LdsWords<M, LUT>::value];
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -319,7 +322,7 @@ void aq_kernel(AqParams P) {
     AqDesc pd = get_desc(P, pp.p);        // its descriptor
 
     Loader<RW, W, NP> ld;
-    static_assert(M == 1 || NP == 1, "passes share a lookup table (M = 1)");
+    static_assert(LUT || NP == 1, "passes share a lookup table (M = 1)");
     ld.done = false;
     ld.setup(P, pp, wg, wid, lane);
 
@@ -328,13 +331,13 @@ void aq_kernel(AqParams P) {
     // rows: block n = 16r + b sits in lanes 4b..4b+3 of A[r], as codebook n / 2NQ, quad
     // (n % 2NQ) / 2, k-half n % 2.
     constexpr int NQ = 64 / W;
-    static_assert(M != 1 || (4 * NQ <= 32 && W * NQ == 64), "the A operands hold the wave's blocks");
+    static_assert(!LUT || (4 * NQ <= 32 && W * NQ == 64), "the A operands hold the wave's blocks");
 
     // Issue the loads of the loader's slice: operands first, then the RW tiles; step the loader.
     // Every load is unconditional with a clamped address (a load under a lane condition makes
     // the compiler wait for it at once); groups past G are zeroed where the operands are used.
     auto load_slice = [&](u32x4 (&t)[RW], SliceOps &o) __attribute__((always_inline)) {
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
             o.gval = ld.G - ld.s * 64;
             const int g = min(ld.s * 64 + lane, ld.G - 1);  // lane = group
 #pragma unroll
@@ -367,7 +370,7 @@ void aq_kernel(AqParams P) {
         for (int i = 0; i < RW; i++) __asm__ volatile("" ::"v"(t[i]));
     };
     auto settle_ops = [&](SliceOps &o) __attribute__((always_inline)) {
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
             __asm__ volatile("" ::"v"(o.B[0]), "v"(o.B[1]), "v"(o.A[0]), "v"(o.A[1]));
         } else {
             __asm__ volatile("" ::"v"(o.X), "v"(o.C));
@@ -440,7 +443,7 @@ void aq_kernel(AqParams P) {
     // M > 1: stage the activations of a slice.
     auto slice_start = [&](const SliceOps &o) __attribute__((always_inline)) {
         const int G = pd.G;
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
         } else {
             const bool in = ps * 64 + lane < G;
             const u32x4 X = in ? o.X : u32x4{0u, 0u, 0u, 0u};
@@ -456,7 +459,7 @@ void aq_kernel(AqParams P) {
     // One tile: this lane's group for 8 rows of row block i (M = 1: lk selects the table).
     auto process = [&](const u32x4 &v, float (&a)[NACC], uint32_t lk) __attribute__((always_inline)) {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
             float v[8];
 #pragma unroll
             for (int t = 0; t < 4; t++) {  // word t: (c0, c1) of rows 2t and 2t+1
@@ -518,7 +521,7 @@ void aq_kernel(AqParams P) {
         constexpr int pass = decltype(pc)::value;
         constexpr bool last = pass == NP - 1;
         settle_tiles(cur);
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
             if constexpr (last) settle_ops(oa);
         } else {
             settle_ops(oc);
@@ -532,7 +535,7 @@ void aq_kernel(AqParams P) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if constexpr (M == 1) {
+        if constexpr (LUT) {
             if constexpr (last) build_table(oa, tb ^ 1);
             lookups((uint32_t(lane) << 2) | (uint32_t(tb) << 16));
             if constexpr (last) {
@@ -559,7 +562,7 @@ void aq_kernel(AqParams P) {
     SliceOps ops0, ops1, ops2;
     load_slice(buf0, ops0);
     load_slice(buf1, ops1);
-    if constexpr (M == 1) {  // the first table
+    if constexpr (LUT) {  // the first table
         settle_ops(ops0);
         build_table(ops0, 0);
         lds_barrier();
@@ -580,7 +583,20 @@ void aq_kernel(AqParams P) {
 
 }  // namespace
 
-AqFn aq_fn(int M, int RW) {
+AqFn aq_fn(int M, int RW, bool bi) {
+    if (bi) {  // one row block per wave per slice at every M
+        switch (M) {
+        case 1: return aq_kernel<1, 1, 1, true>;
+        case 2: return aq_kernel<2, 1, 1, true>;
+        case 3: return aq_kernel<3, 1, 1, true>;
+        case 4: return aq_kernel<4, 1, 1, true>;
+        case 5: return aq_kernel<5, 1, 1, true>;
+        case 6: return aq_kernel<6, 1, 1, true>;
+        case 7: return aq_kernel<7, 1, 1, true>;
+        case 8: return aq_kernel<8, 1, 1, true>;
+        }
+        return nullptr;
+    }
 #define WQD_AQ_CASE(m)                                   \
     case m:                                              \
         return RW == 1 ? aq_kernel<m, 1, 1> : aq_kernel<m, 2, 1>;
