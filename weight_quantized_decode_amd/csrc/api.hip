@@ -232,6 +232,7 @@ struct Plan {
     Layout L;
     int64_t CS = 0, S = 1;
     bool wsplit = false;     // workgroup-split units (CS = kWaves pieces of CS / kWaves chunks)
+    bool tiny = false;       // (plan_single) under WQD_WSPLIT_MIN chunks per resident wave
     int64_t cnt_bytes = 0;   // one int per row group when S > 1 (256-byte aligned)
     int64_t part_bytes = 0;  // M * S * Npad * 4 when S > 1 (256-byte aligned)
     // wqd_gemm workspace: [kCntRegion bytes of counters][partials]
@@ -316,7 +317,10 @@ static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
         P.L = L;
         return P;
     }
-    return plan_target(fmt, N, K, M, slice_target(fmt_bit(fmt), L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus), M));
+    const SliceTarget t = slice_target(fmt_bit(fmt), L.RG * L.C, resident_waves(fmt_bit(fmt), M, cus), M);
+    Plan P = plan_target(fmt, N, K, M, t);
+    P.tiny = t.tiny;
+    return P;
 }
 
 static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
@@ -490,7 +494,8 @@ static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, i
     GP.descs = nullptr;
     GP.ndesc = 1;
     GP.total_wgu = int32_t((GP.d[0].wu_count + kWaves - 1) / kWaves);
-    return launch_gemv(fmt_bit(P.L.fmt), int(M), GP, st, cus);
+    // the shortest M = 1 launches run the matrix-core instance, as in the list launches
+    return launch_gemv(fmt_bit(P.L.fmt), int(M), GP, st, cus, false, WQD_M1_MF_SHORT && M == 1 && P.tiny);
 }
 
 // ------------------------------------------------------------------------------------------
