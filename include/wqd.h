@@ -188,6 +188,14 @@ enum {
  * wave.  Results differ in rounding (within the bound) from calls without the flag. */
 enum { WQD_BATCH_INVARIANT = 0x10 };
 
+/* Flag OR-ed into a mode: the TQ2 entries of the list multiply int8-quantized activations, as
+ * wqd_gemm_i8 does ("Making a ternary reasoning model fast in vLLM": "Why small integers are a
+ * good fit", and "prepare each input once" of its checklist).  Each distinct activation (x, ldx,
+ * K) of the list's TQ2 entries is quantized once per call, by a launch placed before the first
+ * launch that reads it (after the launches before it, which may have written x); entries that
+ * share x share its int8 copy.  Other formats are unaffected. */
+enum { WQD_INT8_ACTIVATIONS = 0x20 };
+
 /* Device workspace bytes for wqd_run_projections over this list in any mode (descriptor
  * tables, counters and partial sums).  In WQD_ORDERED and WQD_FUSED modes the workspace is used
  * like wqd_gemm's: zero-filled before its first use (or initialised by wqd_stack_setup), and
@@ -196,14 +204,15 @@ enum { WQD_BATCH_INVARIANT = 0x10 };
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
 
 /* Write the descriptor tables of this projection list for `mode` (WQD_PERSISTENT, optionally
- * with WQD_BATCH_INVARIANT) into the workspace and zero its counters (blocking copies).
+ * with WQD_BATCH_INVARIANT and WQD_INT8_ACTIVATIONS) into the workspace and zero its counters
+ * (blocking copies).
  * Must be called once before wqd_run_projections in that mode, and again whenever a pointer or
  * shape in the list changes.  Errors: WQD_EINVAL for another mode. */
 WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
                             void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Run every projection of the list with its epilogue.  `mode` is WQD_ORDERED, WQD_PERSISTENT
- * or WQD_FUSED, optionally OR-ed with WQD_BATCH_INVARIANT.  Errors: WQD_EINVAL for a bad mode or epilogue, a gate entry not followed by
+ * or WQD_FUSED, optionally OR-ed with WQD_BATCH_INVARIANT and WQD_INT8_ACTIVATIONS.  Errors: WQD_EINVAL for a bad mode or epilogue, a gate entry not followed by
  * its up entry (or an up entry without its gate, or the two differing in fmt or N), an epilogue
  * on an AQ2X8 entry, or a NULL workspace in WQD_PERSISTENT mode; WQD_ESPACE for a workspace
  * smaller than wqd_stack_workspace_bytes when one is needed; the wqd_gemm checks per entry. */
@@ -212,8 +221,9 @@ WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64
 
 /* Profiling variant: the same work as wqd_run_projections, with hipEvent_t events[2i] recorded
  * on the stream just before the i-th kernel launch of the call and events[2i+1] just after it.
- * Launch order in WQD_PERSISTENT mode: the CB4+CB8 launch if both formats are present, then one
- * launch per remaining format (ascending format id); in the other modes, list order.
+ * Launch order in WQD_PERSISTENT mode: the int8 quantizers (WQD_INT8_ACTIVATIONS), the CB4+CB8
+ * launch if both formats are present, then one launch per remaining format (ascending format id);
+ * in the other modes, list order (a segment's quantizers first).
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,

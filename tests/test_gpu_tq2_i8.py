@@ -80,3 +80,63 @@ def test_int8_gemm_repeats_bits_and_reuses_its_workspace():
         W.wqd_stream_check()
         outs.append(y.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+MODES = {"ordered": W.WQD_ORDERED, "persistent": W.WQD_PERSISTENT, "fused": W.WQD_FUSED}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("M", [1, 3])
+def test_int8_list_quantizes_each_x_once_and_matches_the_oracle(M, mode):
+    """A TQ2 MLP list (gate and up on one x, down on another, plus a CB4 entry that stays fp16)
+    with WQD_INT8_ACTIVATIONS, in every mode."""
+    import torch
+    note(f"int8 list M={M} mode={mode}")
+    specs = [("gate", I.TQ2, 700, 1280, 0), ("up", I.TQ2, 700, 1280, 0), ("down", I.TQ2, 300, 2560, 1),
+             ("cb4", I.CB4, 200, 1280, 0)]
+    xs = {r: I.gen_x(M, K, (93, r, M)) for r, K in ((0, 1280), (1, 2560))}
+    xd = {r: upload_x(v) for r, v in xs.items()}
+    canon = {n: I.gen_weight(f, N, K, (93, i)) for i, (n, f, N, K, _) in enumerate(specs)}
+    ent = [dict(fmt=f, N=N, K=K, w=upload_weight(f, N, K, canon[n]), x=xd[r], y=new_y(M, N))
+           for n, f, N, K, r in specs]
+    arr = W.make_proj_array(ent)
+    ws = workspace(W.wqd_stack_workspace_bytes(arr, M))
+    flags = MODES[mode] | W.WQD_INT8_ACTIVATIONS
+    if mode == "persistent":
+        W.wqd_stack_setup(arr, M, ws, mode=flags)
+    W.wqd_run_projections(arr, M, flags, ws)
+    W.wqd_stream_check()
+    for (n, f, N, K, r), e in zip(specs, ent):
+        got = e["y"].cpu().numpy().astype(np.float64)
+        if f == I.TQ2:
+            q, a, _ = oracle.quantize_x_i8(xs[r])
+            yref, t = oracle.tq2_i8_f64(N, K, canon[n], q, a)
+            bound = (K // 128 + 16) * 2.0 ** -23 * t + 1e-30
+        else:
+            yref, aref = oracle.gemm_f64(f, N, K, canon[n], xs[r])
+            bound = 2e-3 * aref + 1e-6
+        assert np.all(np.abs(got - yref) <= bound), f"{n} outside the bound"
+
+
+def test_int8_list_with_a_silu_pair():
+    import torch
+    M, N, K = 2, 400, 2560
+    note("int8 list with a gate/up pair")
+    cg, cu = I.gen_weight(I.TQ2, N, K, (94, 0)), I.gen_weight(I.TQ2, N, K, (94, 1))
+    xb = I.gen_x(M, K, (94, 2))
+    x = upload_x(xb)
+    h = new_y(M, N)
+    ent = [dict(fmt=I.TQ2, N=N, K=K, w=upload_weight(I.TQ2, N, K, cg), x=x, y=h, epi=W.WQD_EPI_SILU_GATE),
+           dict(fmt=I.TQ2, N=N, K=K, w=upload_weight(I.TQ2, N, K, cu), x=x, y=None, epi=W.WQD_EPI_SILU_UP)]
+    arr = W.make_proj_array(ent)  # (the array holds raw pointers: `ent` keeps the buffers alive)
+    ws = workspace(W.wqd_stack_workspace_bytes(arr, M))
+    W.wqd_run_projections(arr, M, W.WQD_FUSED | W.WQD_INT8_ACTIVATIONS, ws)
+    W.wqd_stream_check()
+    q, a, _ = oracle.quantize_x_i8(xb)
+    g, tg = oracle.tq2_i8_f64(N, K, cg, q, a)
+    u, tu = oracle.tq2_i8_f64(N, K, cu, q, a)
+    eg, eu = (K // 128 + 16) * 2.0 ** -23 * tg, (K // 128 + 16) * 2.0 ** -23 * tu
+    href = oracle.silu_mul(g, u)
+    sg = np.abs(oracle.silu_mul(g, np.ones_like(g)))
+    bound = 1.1 * eg * (np.abs(u) + eu) + sg * eu + 1e-6 * np.abs(href) + 1e-6
+    assert np.all(np.abs(h.cpu().numpy() - href) <= bound)

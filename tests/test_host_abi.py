@@ -275,3 +275,18 @@ def test_int8_entry_point_rules():
     assert L.wqd_gemm_i8(I.TQ2, 64, 1000, FAKE, FAKE, 1, 1024, FAKE, 64, FAKE, need, None) == W.WQD_ESHAPE
     assert L.wqd_quantize_i8(FAKE, 1, 100, 128, FAKE, FAKE, FAKE, None) == W.WQD_ESHAPE
     assert L.wqd_quantize_i8(None, 1, 128, 128, FAKE, FAKE, FAKE, None) == W.WQD_EINVAL
+
+
+def test_int8_list_launch_counts():
+    L = W.lib()
+    I8 = W.WQD_INT8_ACTIVATIONS
+    X = [FAKE + (1 << 40) + (j << 20) for j in range(3)]
+    mlp = _fake_list([(I.TQ2, 17408, 5120, E0, X[0]), (I.TQ2, 17408, 5120, E0, X[0]),
+                      (I.TQ2, 5120, 17408, E0, X[1])])
+    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_PERSISTENT | I8) == 3  # 2 quantizers + 1 product
+    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_FUSED | I8) == 4       # q(x0) [gate, up] q(x1) [down]
+    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_ORDERED | I8) == 5
+    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_PERSISTENT) == 1
+    cb = _fake_list([(I.CB4, 64, 64, E0, X[2])])
+    assert L.wqd_stack_launches(cb, 1, 1, W.WQD_PERSISTENT | I8) == 1    # no TQ2 entry: no quantizer
+    assert L.wqd_stack_workspace_bytes(mlp, 3, 1) > 0

@@ -19,6 +19,7 @@ WQD_Q4_0, WQD_CB4, WQD_CB8, WQD_TQ2, WQD_AQ2X8, WQD_AQ1X16 = 1, 2, 3, 4, 5, 6
 WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP = 0, -1, -2, -3, -4, -5
 WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED = 0, 1, 2
 WQD_BATCH_INVARIANT = 0x10
+WQD_INT8_ACTIVATIONS = 0x20
 WQD_EPI_NONE, WQD_EPI_ADD, WQD_EPI_SILU_GATE, WQD_EPI_SILU_UP = 0, 1, 2, 3
 WQD_MAX_M = 8
 

@@ -296,7 +296,7 @@ static SliceTarget slice_target(int mask, int64_t total_cc, int64_t waves, int64
     SliceTarget t;
     const int64_t per = total_cc / waves;
     // (TQ2 slices move in 8-chunk scale quads, too coarse to share a row between 8 waves)
-    if (per < WQD_WSPLIT_BELOW && !(mask & fmt_bit(TQ2))) {
+    if (per < WQD_WSPLIT_BELOW && !(mask & (fmt_bit(TQ2) | fmt_bit(TQ2I8)))) {
         t.ws = true;
         t.tiny = per < WQD_WSPLIT_MIN;
         t.cs = t.tiny ? WQD_WSPLIT_MIN : per;
@@ -523,13 +523,24 @@ struct LaunchGroup {
     bool epi = false;          // some descriptor applies an epilogue
     bool bi = false;           // batch-invariant instance
     int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
+    int xq = -1;               // >= 0: the int8 quantizer launch of StackPlan::xqs[xq]
+};
+
+// An activation quantized to int8 for the TQ2 entries of a list (WQD_INT8_ACTIVATIONS): q, the
+// block scales a and the block sums of q, in the workspace at base + off_*.
+struct XQ {
+    const void *x = nullptr;
+    int64_t ldx = 0, K = 0;
+    int64_t off_q = 0, off_a = 0, off_s = 0;
+    bool issued = false;       // (planning) its quantizer launch is placed
 };
 
 struct StackPlan {
     std::vector<Desc> descs;
     std::vector<AqDesc> aqdescs;
     std::vector<LaunchGroup> groups;
-    int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_part = 0;
+    std::vector<XQ> xqs;
+    int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_xq = 0, off_part = 0;
     int64_t part_bytes = 0;    // partial bytes this mode uses
     bool needs_ws = false;     // some launch counts slices (split K or a gate/up pair)
     int64_t total() const { return off_part + part_bytes; }
@@ -586,10 +597,30 @@ static void list_segments(const wqd_proj *p, int count, int mode, std::vector<st
 
 // Plans the launches of entries [b, e) onto counters from cnt_off and partials from part_off
 // (offsets into the workspace at `base`, which may be null when only sizes are wanted).
-static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, bool bi, uint8_t *base,
+// The index in SP.xqs of entry q's quantized activation (int8 lists, TQ2 entries), or -1.
+static int xq_of(const StackPlan &SP, const wqd_proj &q) {
+    for (size_t k = 0; k < SP.xqs.size(); k++)
+        if (SP.xqs[k].x == q.x && SP.xqs[k].ldx == q.ldx && SP.xqs[k].K == q.K) return int(k);
+    return -1;
+}
+
+static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, bool bi, bool i8, uint8_t *base,
                          int64_t &cnt_off, int64_t &part_off, StackPlan &SP, int cus) {
+    // kernel format of entry i: TQ2 entries of an int8 list run the int8 product
+    auto kfmt = [&](int i) { return (i8 && p[i].fmt == TQ2) ? TQ2I8 : p[i].fmt; };
+    // quantize the activations this segment is the first to use (after the launches before it,
+    // which may have produced them)
+    for (int i = b; i < e; i++) {
+        if (kfmt(i) != TQ2I8) continue;
+        XQ &xq = SP.xqs[xq_of(SP, p[i])];
+        if (xq.issued) continue;
+        xq.issued = true;
+        LaunchGroup Q;
+        Q.xq = xq_of(SP, p[i]);
+        SP.groups.push_back(Q);
+    }
     int present = 0;
-    for (int i = b; i < e; i++) present |= fmt_bit(p[i].fmt);
+    for (int i = b; i < e; i++) present |= fmt_bit(kfmt(i));
     const bool has_aq = (present & fmt_bit(AQ2X8)) != 0;
     present &= ~fmt_bit(AQ2X8);
     std::vector<int> masks;
@@ -597,14 +628,14 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         masks.push_back(kMaskCB48);
         present &= ~kMaskCB48;
     }
-    for (int fmt = 1; fmt <= 6; fmt++)
+    for (int fmt = 1; fmt <= TQ2I8; fmt++)
         if (present & fmt_bit(fmt)) masks.push_back(fmt_bit(fmt));
 
     for (const int mask : masks) {
         // the K-slice size of a launch group follows its total work
         int64_t total_cc = 0;
         for (int i = b; i < e; i++) {
-            if (!(mask & fmt_bit(p[i].fmt))) continue;
+            if (!(mask & fmt_bit(kfmt(i)))) continue;
             Layout L = make_layout(p[i].fmt, p[i].N, p[i].K);
             total_cc += L.RG * L.C;
         }
@@ -621,8 +652,18 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         // is in the list (workgroup-split slices of about WQD_BI_CW chunks per wave, or wave
         // slices of WQD_BI_CS chunks when WQD_BI_CW is 0), so its sums are added in one order.
         auto plan_of = [&](int f, int64_t N, int64_t K) {
+            if (f == TQ2I8) f = TQ2;  // (TQ2 weights)
             if (!bi) return plan_target(f, N, K, M, tgt);
             return WQD_BI_CW > 0 ? plan_ws(f, N, K, M, WQD_BI_CW) : plan_cs(f, N, K, M, WQD_BI_CS);
+        };
+        // int8 activations of a TQ2 entry: the descriptor reads q, a and the sums of q
+        auto to_i8 = [&](Desc &D, const wqd_proj &q) {
+            if (D.fmt != TQ2 || !i8) return;
+            const XQ &xq = SP.xqs[xq_of(SP, q)];
+            D.fmt = TQ2I8;
+            D.x = base ? reinterpret_cast<const uint16_t *>(base + xq.off_q) : nullptr;
+            D.ldx = xq.K;
+            D.cbk = base ? reinterpret_cast<const uint16_t *>(base + xq.off_a) : nullptr;
         };
         int wgu = 0;
         auto push = [&](Desc D) {
@@ -630,11 +671,11 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
             wgu += (D.wu_count + kWaves - 1) / kWaves;
             SP.descs.push_back(D);
         };
-        for (int fmt = 1; fmt <= 6; fmt++) {
+        for (int fmt = 1; fmt <= TQ2I8; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = b; i < e; i++) {
                 const wqd_proj &q = p[i];
-                if (q.fmt != fmt || q.epi == WQD_EPI_SILU_UP) continue;
+                if (kfmt(i) != fmt || q.epi == WQD_EPI_SILU_UP) continue;
                 const Plan P = plan_of(fmt, q.N, q.K);
                 if (q.epi == WQD_EPI_SILU_GATE) {
                     // gate and up share one slice counter per row group and one partial array
@@ -654,6 +695,8 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
                     Dg.S_first = Du.S_first = int32_t(P.S);
                     Dg.slot0 = 0;
                     Du.slot0 = int32_t(P.S);
+                    to_i8(Dg, q);
+                    to_i8(Du, r);
                     push(Dg);
                     push(Du);
                     SP.needs_ws = true;
@@ -664,6 +707,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
                     part_off += P.part_bytes;
                     Desc D = make_desc(P, q.w, q.x, q.ldx, q.y, q.ldy, part, cnt);
                     D.epi = (q.epi == WQD_EPI_ADD) ? kEpiAdd : kEpiNone;
+                    to_i8(D, q);
                     push(D);
                     SP.needs_ws |= P.S > 1;
                 }
@@ -711,7 +755,8 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
 static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mode_flags, void *ws, StackPlan &SP,
                             int cus) {
     const bool bi = (mode_flags & WQD_BATCH_INVARIANT) != 0;
-    const int mode = mode_flags & ~WQD_BATCH_INVARIANT;
+    const bool i8 = (mode_flags & WQD_INT8_ACTIVATIONS) != 0;
+    const int mode = mode_flags & ~(WQD_BATCH_INVARIANT | WQD_INT8_ACTIVATIONS);
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
     int rc = check_list(p, count, M);
     if (rc != WQD_OK) return rc;
@@ -726,17 +771,34 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
         cnt_all += align_up(make_layout(p[i].fmt, p[i].N, p[i].K).RG * 4, 256);
     }
     SP.cnt_bytes = cnt_all > kCntRegion ? cnt_all : kCntRegion;
-    SP.off_part = SP.off_cnt + SP.cnt_bytes;
+    // int8 activations: one region per distinct TQ2 activation (the same layout in every mode,
+    // with or without the flag, so the workspace is one size for all)
+    SP.off_xq = SP.off_cnt + SP.cnt_bytes;
+    int64_t xq_off = SP.off_xq;
+    for (int i = 0; i < count; i++) {
+        if (p[i].fmt != TQ2 || xq_of(SP, p[i]) >= 0) continue;
+        XQ xq;
+        xq.x = p[i].x;
+        xq.ldx = p[i].ldx;
+        xq.K = p[i].K;
+        xq.off_q = xq_off;
+        xq.off_a = align_up(xq.off_q + M * xq.K, 256);
+        xq.off_s = xq.off_a + M * (xq.K / 128) * 4;
+        xq_off = align_up(xq.off_s + M * (xq.K / 128) * 4, 256);
+        SP.xqs.push_back(xq);
+    }
+    SP.off_part = xq_off;
     std::vector<std::pair<int, int>> seg;
     list_segments(p, count, mode, seg);
     uint8_t *base = static_cast<uint8_t *>(ws);
     int64_t part_used = 0;
     for (const auto &sg : seg) {
         int64_t cnt_off = SP.off_cnt, part_off = SP.off_part;
-        plan_segment(p, sg.first, sg.second, M, mode, bi, base, cnt_off, part_off, SP, cus);
+        plan_segment(p, sg.first, sg.second, M, mode, bi, i8, base, cnt_off, part_off, SP, cus);
         if (part_off - SP.off_part > part_used) part_used = part_off - SP.off_part;
     }
     SP.part_bytes = part_used;
+    if (i8 && !SP.xqs.empty()) SP.needs_ws = true;
     return WQD_OK;
 }
 
@@ -879,7 +941,7 @@ WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs, int32_t count, 
         int rc = build_stack_plan(projs, count, M, mode, nullptr, SP, device_cus());
         if (rc != WQD_OK) return rc;
         if (SP.total() > need) need = SP.total();
-        // the batch-invariant plans too, where the list allows them
+        // the batch-invariant plans too (the int8 flag changes no region's size)
         StackPlan SB;
         if (build_stack_plan(projs, count, M, mode | WQD_BATCH_INVARIANT, nullptr, SB, device_cus()) == WQD_OK &&
             SB.total() > need)
@@ -891,7 +953,7 @@ WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs, int32_t count, 
 WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode, void *workspace,
                             int64_t workspace_bytes, void *stream) {
     if (!workspace) return WQD_EINVAL;
-    if ((mode & ~WQD_BATCH_INVARIANT) != WQD_PERSISTENT) return WQD_EINVAL;
+    if ((mode & ~(WQD_BATCH_INVARIANT | WQD_INT8_ACTIVATIONS)) != WQD_PERSISTENT) return WQD_EINVAL;
     StackPlan SP;
     int rc = build_stack_plan(projs, count, M, mode, workspace, SP, device_cus());
     if (rc != WQD_OK) return rc;
@@ -924,7 +986,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     uint8_t *base = static_cast<uint8_t *>(workspace);
     // WQD_PERSISTENT reads the descriptor tables wqd_stack_setup wrote; the other modes pass
     // their descriptors in the kernel arguments and need the workspace only to count slices.
-    const bool persistent = (mode & ~WQD_BATCH_INVARIANT) == WQD_PERSISTENT;
+    const bool persistent = (mode & ~(WQD_BATCH_INVARIANT | WQD_INT8_ACTIVATIONS)) == WQD_PERSISTENT;
     if (persistent && !base) return WQD_EINVAL;
     if ((persistent || SP.needs_ws) && (!base || workspace_bytes < SP.total())) return WQD_ESPACE;
     const int launches = int(SP.groups.size());
@@ -940,6 +1002,20 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     const AqDesc *atab = table ? reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs) : nullptr;
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
         const LaunchGroup &G = SP.groups[gi];
+        if (G.xq >= 0) {
+            const XQ &xq = SP.xqs[G.xq];
+            const int nb = int(xq.K / 128);
+            if ((rc = mark(0)) != WQD_OK) return rc;
+            hipLaunchKernelGGL(quantize_i8_kernel<true>, dim3(unsigned((M * nb + 3) / 4)), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(xq.x), xq.ldx, int(M), nb,
+                               reinterpret_cast<int8_t *>(base + xq.off_q), xq.K,
+                               reinterpret_cast<float *>(base + xq.off_a), reinterpret_cast<int32_t *>(base + xq.off_s));
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e);
+            if ((rc = mark(1)) != WQD_OK) return rc;
+            li++;
+            continue;
+        }
         if (G.aq) {
             AqParams AP;
             memset(&AP, 0, sizeof(AP));
@@ -968,9 +1044,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         GP.total_wgu = G.total_wgu;
         // The dynamic tail pays a barrier, an atomic and a cold load pipeline per unit it hands
         // out: only units of long slices amortize that.  (Launches run one after another, and
-        // each leaves its two counters at zero.)
+        // each leaves its two counters at zero, so they share them.)
         if (WQD_POOL_PERCENT > 0 && G.cs >= WQD_POOL_MIN_CS && base) {
-            GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr) + (table ? 2 * gi : 0);
+            GP.ctr = reinterpret_cast<int *>(base + SP.off_ctr);
             GP.pool_begin = int32_t(int64_t(G.total_wgu) * (100 - WQD_POOL_PERCENT) / 100);
         }
         if ((rc = mark(0)) != WQD_OK) return rc;
