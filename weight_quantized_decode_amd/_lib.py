@@ -166,7 +166,8 @@ def wqd_dequant_f32(fmt: int, N: int, K: int, w, out, stream=None) -> None:
 
 def make_proj_array(projs: Sequence[dict]):
     """projs: dicts with fmt, N, K, w, x, y (torch tensors) and optionally epi (a WQD_EPI_*
-    value; y may be None for a WQD_EPI_SILU_UP entry); returns a ctypes array of wqd_proj."""
+    value; y may be None for a WQD_EPI_SILU_UP entry); returns a ctypes array of wqd_proj.
+    The array holds raw device pointers: the caller keeps the tensors alive while it is used."""
     arr = (wqd_proj * len(projs))()
     for i, p in enumerate(projs):
         arr[i].fmt = p["fmt"]
