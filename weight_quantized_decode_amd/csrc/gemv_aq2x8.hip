@@ -211,11 +211,15 @@ constexpr int kFinLoads = 8;        // partial loads in flight per row in the fi
 // and clears the slots.  The rows of a row chunk are shared out over its b splits: the workgroup
 // that ran split t finalizes rows [t*R/b, (t+1)*R/b) of the chunk's R rows.  A row takes L lanes
 // (L = b/8 rounded up to a power of two): lane j of the row loads partials 8j..8j+7 in one round
-// and adds them in split order, then the L lane sums are combined in a fixed tree.  Runs after all
-// of the workgroup's own pieces; a partial not yet written is polled again (bounded), and its
-// writer never waits on another workgroup, so the wait ends.
+// and adds them in split order, then the L lane sums are combined in a fixed tree.  The shares of
+// all of the workgroup's pieces are finalized at once: each share takes whole waves (its rows x L
+// lanes, rounded up to 64), numbered over the pieces in order, and wave w takes numbers w, w + W,
+// ..., so the partial loads of the pieces are in flight together rather than one memory round
+// trip per piece.  Runs after all of the workgroup's own pieces; a partial not yet written is
+// polled again (bounded), and its writer never waits on another workgroup, so the wait ends.
 template <int M, int W>
 __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int lane) {
+    int first = 0;  // first wave number of the piece's share
     for (Piece q = find_piece(P, wg, 0, -1); q.p < P.ndesc; q = next_piece(P, wg, q)) {
         const AqDesc D = get_desc(P, q.p);
         if (D.b == 1) continue;
@@ -223,47 +227,51 @@ __device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int
         while (L * kFinLoads < D.b) L *= 2;  // (b <= 64 keeps L <= 8)
         const int r0 = q.rb0 * 8, R = min((q.rb1 - q.rb0) * 8, D.N - r0);
         const int lo = r0 + (R * q.split) / D.b, hi = r0 + (R * (q.split + 1)) / D.b;
-        const int sub = lane & (L - 1);             // this lane's group of partials
-        const int stride = W * 64 / L;              // rows per round of the workgroup
-        // all L lanes of a row take the same iterations (the lane combine below pairs them)
-        for (int k = (wid * 64 + lane) / L; k < hi - lo; k += stride) {
-            const int row = lo + k;
+        const int nw = ((hi - lo) * L + 63) / 64;  // waves of this share
+        const int sub = lane & (L - 1);            // this lane's group of partials
+        const int t0 = sub * kFinLoads;
+        // wave numbers [first, first + nw) are this share's; wave wid takes those = wid mod W
+        for (int v = first + ((wid - first) % W + W) % W; v < first + nw; v += W) {
+            const int k = ((v - first) * 64 + lane) / L;  // row of the share (L lanes per row)
+            const bool live = k < hi - lo;                // (every lane still takes the combine)
+            const int row = lo + min(k, hi - lo - 1);
             const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
 #pragma unroll
             for (int m = 0; m < M; m++) {
                 uint64_t *slot = D.part + (int64_t(m) * D.b) * D.Npad + row;
-                const int t0 = sub * kFinLoads;
-                uint64_t v[kFinLoads];
+                uint64_t v8[kFinLoads];
 #pragma unroll
                 for (int j = 0; j < kFinLoads; j++)
-                    v[j] = (t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                          : (uint64_t(kAqTag) << 32);
+                    v8[j] = (live && t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                                   : (uint64_t(kAqTag) << 32);
                 float sum = 0.f;
                 int ok = 1;
 #pragma unroll
                 for (int j = 0; j < kFinLoads; j++) {
                     int spins = 0;
-                    while (uint32_t(v[j] >> 32) != kAqTag && spins < kSpinMax) {
+                    while (uint32_t(v8[j] >> 32) != kAqTag && spins < kSpinMax) {
                         __builtin_amdgcn_s_sleep(2);
-                        v[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+                        v8[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
                         spins++;
                     }
-                    ok &= uint32_t(v[j] >> 32) == kAqTag;
-                    if (t0 + j < D.b) sum += f32(uint32_t(v[j]));  // split order
+                    ok &= uint32_t(v8[j] >> 32) == kAqTag;
+                    if (t0 + j < D.b) sum += f32(uint32_t(v8[j]));  // split order
                 }
                 // combine the L lanes of the row: pairs, then pairs of pairs (a fixed order)
                 for (int o = 1; o < L; o <<= 1) {
                     sum += __shfl_xor(sum, o);
                     ok &= __shfl_xor(ok, o);
                 }
-                if (sub == 0) gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
-                for (int j = 0; j < kFinLoads && t0 + j < D.b; j++)
-                    __hip_atomic_store(as_global(slot + int64_t(t0 + j) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (live && sub == 0) gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
+                if (live)
+                    for (int j = 0; j < kFinLoads && t0 + j < D.b; j++)
+                        __hip_atomic_store(as_global(slot + int64_t(t0 + j) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        first += nw;
     }
 }
 
@@ -530,7 +538,8 @@ void aq_kernel(AqParams P) {
         auto lookups = [&](uint32_t lk) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < RW; i++) {
-                process(cur[i], acc[pass][i], lk);
+                // (the ring slots past the piece's end hold no tile)
+                if (pp.rb0 + wid + W * (i + RW * pass) < pp.rb1) process(cur[i], acc[pass][i], lk);
                 // one tile at a time: hoisting the address math of every tile blows the register budget
                 __builtin_amdgcn_sched_barrier(0);
             }
