@@ -146,15 +146,24 @@ __device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Pie
     return find_piece(P, wg, q.p, q.j + P.nwg);
 }
 
+// Row block (from the piece's first) of tile i of wave wid in pass `pass` of a slice: a pass covers
+// W * RW consecutive row blocks, RW consecutive ones per wave (each wave's tiles of a slice are
+// one contiguous run of RW KiB; wave-interleaved tiles measured 2.5% slower on the 70B MLP).
+template <int RW, int W>
+__device__ __forceinline__ int tile_rb(int wid, int i, int pass) {
+    return RW * (wid + W * pass) + i;
+}
+
 // Tile loader running ahead of the processing.  It walks units (piece, slice, pass): each slice
-// of a piece is read in NP passes of RW tiles per wave, pass p covering row blocks
-// rb0 + wid + W*(i + RW*p), so one table serves NP * W * RW row blocks.
+// of a piece is read in NP passes of RW tiles per wave (tile_rb), so one table serves
+// NP * W * RW row blocks.
 template <int RW, int W, int NP>
 struct Loader {
     const uint8_t *base;   // code plane (wave-uniform; the lane's 16 bytes are added at the load)
     int64_t s_stride;      // bytes between slices (R8 = Npad/8 KiB)
     int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
-    int rbw, rb1;          // this wave's first row block of the piece; the piece's end
+    int rb0, rb1;          // the piece's row blocks
+    int wv;                // this wave
     const uint16_t *x, *cbk;  // operands of the slice's table / activation stage
     int64_t ldx;
     int G;
@@ -177,14 +186,15 @@ struct Loader {
         G = D.G;
         s_max = D.KS - 1;
         rb_max = D.Npad / 8 - 1;
-        rbw = n.rb0 + wid;
+        rb0 = n.rb0;
+        wv = wid;
         rb1 = n.rb1;
     }
     // A missing tile (past the piece, or past the end of the list) still takes its place in the
     // ring (every load stays unconditional): it reads 1 KiB of the codebooks, which the table
     // build keeps in L2, instead of HBM.
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        const int r = rbw + W * (i + RW * pass);
+        const int r = rb0 + tile_rb<RW, W>(wv, i, pass);
         return (done || r >= rb1) ? reinterpret_cast<const uint8_t *>(cbk)
                                   : base + int64_t(min(s, s_max)) * s_stride + int64_t(min(r, rb_max)) * 1024;
     }
@@ -403,7 +413,7 @@ void aq_kernel(AqParams P) {
 #pragma unroll
         for (int pi = 0; pi < NP * RW; pi++) {
             const int p = pi / RW, i = pi % RW;
-            const int rb = q.rb0 + wid + W * pi;
+            const int rb = q.rb0 + tile_rb<RW, W>(wid, i, p);
             const int row = rb * 8 + (lane >> 3);
             const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N && q.split < D.b;
 #pragma unroll
@@ -539,7 +549,7 @@ void aq_kernel(AqParams P) {
 #pragma unroll
             for (int i = 0; i < RW; i++) {
                 // (the ring slots past the piece's end hold no tile)
-                if (pp.rb0 + wid + W * (i + RW * pass) < pp.rb1) process(cur[i], acc[pass][i], lk);
+                if (pp.rb0 + tile_rb<RW, W>(wid, i, pass) < pp.rb1) process(cur[i], acc[pass][i], lk);
                 // one tile at a time: hoisting the address math of every tile blows the register budget
                 __builtin_amdgcn_sched_barrier(0);
             }
