@@ -63,13 +63,17 @@ typedef enum { WQD_Q4_0 = 1, WQD_CB4 = 2, WQD_CB8 = 3, WQD_TQ2 = 4, WQD_AQ2X8 = 
 typedef enum {
     WQD_OK = 0,
     WQD_EINVAL = -1, /* null pointer, unknown format or mode */
-    WQD_ESHAPE = -2, /* N < 1, K not a whole number of blocks/groups, M outside 1..8, ld too small */
+    WQD_ESHAPE = -2, /* N or K outside 1..2^30, K not a whole number of blocks/groups, M outside
+                        1..8, ld too small */
     WQD_EALIGN = -3, /* weight not 16-byte aligned, x or y not 4-byte aligned, odd ldx */
     WQD_ESPACE = -4, /* a capacity or workspace argument is smaller than required */
     WQD_EHIP = -5    /* a HIP call failed; wqd_last_hip_error() gives its hipError_t */
 } wqd_status;
 
 enum { WQD_MAX_M = 8 };
+/* Largest N and K any call accepts (2^30 each): the kernels keep N, K and their chunk counts in
+ * 32-bit fields. */
+enum { WQD_MAX_N = 1 << 30, WQD_MAX_K = 1 << 30 };
 
 /* ---------------------------------------------------------------- layout (host only, no HIP) */
 

@@ -290,3 +290,19 @@ def test_int8_list_launch_counts():
     cb = _fake_list([(I.CB4, 64, 64, E0, X[2])])
     assert L.wqd_stack_launches(cb, 1, 1, W.WQD_PERSISTENT | I8) == 1    # no TQ2 entry: no quantizer
     assert L.wqd_stack_workspace_bytes(mlp, 3, 1) > 0
+
+
+@pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
+def test_size_limits(fmt):
+    """N and K up to 2^30 are accepted (sizes only; nothing is allocated), one block more is not."""
+    kb = {I.Q4_0: 32, I.CB4: 2, I.CB8: 1, I.TQ2: 128, I.AQ2X8: 8, I.AQ1X16: 8}[fmt]
+    assert W.wqd_prepared_bytes(fmt, W.WQD_MAX_N, 1024) > 0
+    assert W.wqd_prepared_bytes(fmt, 64, W.WQD_MAX_K) > 0
+    assert W.wqd_canonical_bytes(fmt, W.WQD_MAX_N, 1024) > 0
+    assert W.lib().wqd_prepared_bytes(fmt, W.WQD_MAX_N + 1, 1024) == W.WQD_ESHAPE
+    assert W.lib().wqd_prepared_bytes(fmt, 64, W.WQD_MAX_K + kb) == W.WQD_ESHAPE
+    assert W.lib().wqd_canonical_bytes(fmt, 64, W.WQD_MAX_K + kb) == W.WQD_ESHAPE
+    assert W.lib().wqd_gemm(fmt, W.WQD_MAX_N + 1, 1024, FAKE, FAKE, 1, 1024, FAKE, W.WQD_MAX_N + 1,
+                            None, 0, None) == W.WQD_ESHAPE
+    assert W.lib().wqd_gemm(fmt, 64, W.WQD_MAX_K + kb, FAKE, FAKE, 1, W.WQD_MAX_K + kb, FAKE, 64,
+                            None, 0, None) == W.WQD_ESHAPE

@@ -900,7 +900,7 @@ WQD_API int wqd_gemm_i8(int fmt, int64_t N, int64_t K, const void *w, const void
 WQD_API int wqd_quantize_i8(const void *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, float *a, int32_t *qsum,
                             void *stream) {
     if (!x || !q || !a || !qsum) return WQD_EINVAL;
-    if (M < 1 || M > WQD_MAX_M || K < 128 || K % 128 || ldx < K || K > (int64_t(1) << 31)) return WQD_ESHAPE;
+    if (M < 1 || M > WQD_MAX_M || K < 128 || K % 128 || ldx < K || K > kMaxK) return WQD_ESHAPE;
     if ((reinterpret_cast<uintptr_t>(x) & 3) || (ldx & 1) || (reinterpret_cast<uintptr_t>(a) & 3) ||
         (reinterpret_cast<uintptr_t>(qsum) & 3))
         return WQD_EALIGN;

@@ -46,6 +46,9 @@ constexpr int kRowsPerGroup = 64;
 constexpr int kChunkBytes = 16;
 constexpr int64_t kPlaneAlign = 256;
 
+// Largest N and K (the kernels keep N, K, Npad and chunk counts in 32-bit fields).
+constexpr int64_t kMaxN = int64_t(1) << 30;
+constexpr int64_t kMaxK = int64_t(1) << 30;
 enum Fmt : int { Q4_0 = 1, CB4 = 2, CB8 = 3, TQ2 = 4, AQ2X8 = 5, AQ1X16 = 6 };
 // Kernel-side id of a TQ2 projection multiplied by int8-quantized activations (TQ2 weights).
 constexpr int TQ2I8 = 7;
@@ -86,7 +89,7 @@ inline Layout make_layout(int fmt, int64_t N, int64_t K) {
     L.N = N;
     L.K = K;
     int km = k_multiple(fmt);
-    if (km == 0 || N < 1 || K < 1 || K % km != 0 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
+    if (km == 0 || N < 1 || K < 1 || K % km != 0 || N > kMaxN || K > kMaxK)
         return L;
     L.RG = (N + kRowsPerGroup - 1) / kRowsPerGroup;
     L.Npad = L.RG * kRowsPerGroup;

@@ -7,6 +7,8 @@
 #include "../../include/wqd.h"
 #include "layout.h"
 
+static_assert(WQD_MAX_N == wqd::kMaxN && WQD_MAX_K == wqd::kMaxK, "the header states the layout limits");
+
 using namespace wqd;
 
 namespace {
