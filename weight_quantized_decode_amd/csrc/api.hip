@@ -376,7 +376,7 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
 // model per piece, in tile loads (KiB): ns * (nrb + table build) plus a fixed charge for a
 // K-split (its partial round trip); the shape with the cheapest busiest workgroup wins.
 // ------------------------------------------------------------------------------------------
-static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : M <= 4 ? 2 : 1; }  // (M > 4, RW 2: spills)
+static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : M == 2 ? 4 : M <= 4 ? 2 : 1; }  // (M > 4, RW 2: spills)
 
 static int64_t aq_nwg(int64_t M, int cus) {
     AqFn fn = aq_fn(int(M), aq_rw_max(M));
@@ -398,7 +398,9 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg, bool bi = fa
     A.L = make_layout(AQ2X8, N, K);
     if (!A.L.ok) return A;
     const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = bi ? 1 : aq_rw_max(M), W = aq_waves(int(M));
-    const int64_t build = (M == 1 && !bi) ? WQD_AQ_BUILD_CHARGE : 2, split_charge = WQD_AQ_SPLIT_CHARGE;
+    // a slice's table (M = 1; M = 2: twice the matrix work, not overlapped) or staging (M > 2)
+    const int64_t build = bi ? 2 : M == 1 ? WQD_AQ_BUILD_CHARGE : M == 2 ? 2 * WQD_AQ_BUILD_CHARGE : 2;
+    const int64_t split_charge = WQD_AQ_SPLIT_CHARGE;
     if (nwg < 1) nwg = 1;
     double best = 1e300;
     for (int64_t b = 1; b <= KS && b <= WQD_AQ_MAX_SPLITS; b++) {

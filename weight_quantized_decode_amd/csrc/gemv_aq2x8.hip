@@ -303,6 +303,7 @@ struct LdsWords {
 // this wave's two codebook rows) or of the stage (M > 1: one activation row, a codebook part).
 struct SliceOps {
     u32x2 B[2], A[2];
+    u32x2 B1[2];  // M = 2 tables: the second activation row's halves
     u32x4 X, C;
     int gval;  // groups of the slice inside K (M = 1: the table masks the rest)
 };
@@ -311,6 +312,17 @@ struct SliceOps {
 __device__ __forceinline__ float add_lo_hi(uint32_t d0, uint32_t d1) {
     float r;
     __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
+    return r;
+}
+// fp32 sums of the low halves and of the high halves of two fp16 pairs.
+__device__ __forceinline__ float add_lo_lo(uint32_t d0, uint32_t d1) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
+    return r;
+}
+__device__ __forceinline__ float add_hi_hi(uint32_t d0, uint32_t d1) {
+    float r;
+    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
     return r;
 }
 // fp16 pair (a, b), round to nearest even.
@@ -326,7 +338,8 @@ template <int M, int RW, int NP, bool BI = false>
 __global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, aq_waves_per_simd(M))))
 void aq_kernel(AqParams P) {
     constexpr int W = aq_waves(M);  // waves per workgroup
-    constexpr bool LUT = (M == 1 && !BI);  // lookup tables (else the direct decode)
+    constexpr bool LUT = (M <= 2 && !BI);  // lookup tables (else the direct decode)
+    constexpr bool LUT2 = LUT && M == 2;   // one table of both activation rows, single-buffered
     __shared__ uint32_t lds[LdsWords<M, LUT>::value];
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -360,6 +373,10 @@ void aq_kernel(AqParams P) {
             const int g = min(ld.s * 64 + lane, ld.G - 1);  // lane = group
 #pragma unroll
             for (int h = 0; h < 2; h++) o.B[h] = gld<u32x2>(ld.x + int64_t(g) * 8 + 4 * h);
+            if constexpr (LUT2) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) o.B1[h] = gld<u32x2>(ld.x + ld.ldx + int64_t(g) * 8 + 4 * h);
+            }
 #pragma unroll
             for (int r = 0; r < (4 * NQ + 15) / 16; r++) {
                 const int n = min(16 * r + (lane >> 2), 4 * NQ - 1);
@@ -390,6 +407,7 @@ void aq_kernel(AqParams P) {
     auto settle_ops = [&](SliceOps &o) __attribute__((always_inline)) {
         if constexpr (LUT) {
             __asm__ volatile("" ::"v"(o.B[0]), "v"(o.B[1]), "v"(o.A[0]), "v"(o.A[1]));
+            if constexpr (LUT2) __asm__ volatile("" ::"v"(o.B1[0]), "v"(o.B1[1]));
         } else {
             __asm__ volatile("" ::"v"(o.X), "v"(o.C));
         }
@@ -443,6 +461,24 @@ void aq_kernel(AqParams P) {
         const bool in = lane < o.gval;  // groups past K read as zero
         const u32x2 B0 = in ? o.B[0] : u32x2{0u, 0u}, B1 = in ? o.B[1] : u32x2{0u, 0u};
         uint32_t *tab = lds + tb * (256 * 64);
+        if constexpr (LUT2) {
+            // dword (cb*256 + c)*64 + g holds (T_cb[c] for row 0, for row 1) of group g
+            const u32x2 R0 = in ? o.B1[0] : u32x2{0u, 0u}, R1 = in ? o.B1[1] : u32x2{0u, 0u};
+            static_for<NQ>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                static_for<2>([&](auto cc) {
+                    constexpr int cb = decltype(cc)::value;
+                    constexpr int n0 = cb * 2 * NQ + 2 * q, n1 = n0 + 1;
+                    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const f32x4 D0 = mfma_xw<n1 % 16>(o.A[n1 / 16], B1, mfma_xw<n0 % 16>(o.A[n0 / 16], B0, z));
+                    const f32x4 D1 = mfma_xw<n1 % 16>(o.A[n1 / 16], R1, mfma_xw<n0 % 16>(o.A[n0 / 16], R0, z));
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        tab[(cb * 256 + wid * 4 * NQ + 4 * q + i) * 64 + lane] = pack_h2(D0[i], D1[i]);
+                });
+            });
+            return;
+        }
         static_for<NQ>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
             f32x4 D[2];
@@ -477,7 +513,30 @@ void aq_kernel(AqParams P) {
     // One tile: this lane's group for 8 rows of row block i (M = 1: lk selects the table).
     auto process = [&](const u32x4 &v, float (&a)[NACC], uint32_t lk) __attribute__((always_inline)) {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (LUT) {
+        if constexpr (LUT2) {
+            // codebook 0 entries in table half 0, codebook 1 in half 1 (byte 2 of the address);
+            // each dword gives the term of both activation rows
+            const uint32_t lk1 = lk | 0x10000u;
+            float v0[8], v1[8];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t d0 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk, 0x0c020400u));
+                const uint32_t d1 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk1, 0x0c020500u));
+                const uint32_t d2 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk, 0x0c020600u));
+                const uint32_t d3 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk1, 0x0c020700u));
+                v0[2 * t] = add_lo_lo(d0, d1);
+                v1[2 * t] = add_hi_hi(d0, d1);
+                v0[2 * t + 1] = add_lo_lo(d2, d3);
+                v1[2 * t + 1] = add_hi_hi(d2, d3);
+            }
+            float w[2];
+            fold_rows8(v0, w);
+            a[0] += w[0];
+            a[1] += w[1];
+            fold_rows8(v1, w);
+            a[2] += w[0];
+            a[3] += w[1];
+        } else if constexpr (LUT) {
             float v[8];
 #pragma unroll
             for (int t = 0; t < 4; t++) {  // word t: (c0, c1) of rows 2t and 2t+1
@@ -539,7 +598,9 @@ void aq_kernel(AqParams P) {
         constexpr int pass = decltype(pc)::value;
         constexpr bool last = pass == NP - 1;
         settle_tiles(cur);
-        if constexpr (LUT) {
+        if constexpr (LUT2) {
+            if constexpr (pass == 0) settle_ops(oc);
+        } else if constexpr (LUT) {
             if constexpr (last) settle_ops(oa);
         } else {
             settle_ops(oc);
@@ -554,7 +615,14 @@ void aq_kernel(AqParams P) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if constexpr (LUT) {
+        if constexpr (LUT2) {
+            if constexpr (pass == 0) {  // the slice's table replaces the previous slice's
+                lds_barrier();          // every wave is done with the previous table
+                build_table(oc, 0);
+                lds_barrier();          // the table is complete
+            }
+            lookups(uint32_t(lane) << 2);
+        } else if constexpr (LUT) {
             if constexpr (last) build_table(oa, tb ^ 1);
             lookups((uint32_t(lane) << 2) | (uint32_t(tb) << 16));
             if constexpr (last) {
@@ -581,7 +649,7 @@ void aq_kernel(AqParams P) {
     SliceOps ops0, ops1, ops2;
     load_slice(buf0, ops0);
     load_slice(buf1, ops1);
-    if constexpr (LUT) {  // the first table
+    if constexpr (LUT && !LUT2) {  // the first table (M = 2: built by the first slice's step)
         settle_ops(ops0);
         build_table(ops0, 0);
         lds_barrier();
@@ -625,7 +693,10 @@ AqFn aq_fn(int M, int RW, bool bi) {
         if (RW == 2) return aq_kernel<1, 2, 1>;
         if (RW == 4) return aq_kernel<1, 4, 1>;
         return aq_kernel<1, 4, 2>;
-        WQD_AQ_CASE(2)
+    case 2:  // lookup tables: RW 4 = two passes of 2
+        if (RW <= 1) return aq_kernel<2, 1, 1>;
+        if (RW == 2) return aq_kernel<2, 2, 1>;
+        return aq_kernel<2, 2, 2>;
         WQD_AQ_CASE(3)
         WQD_AQ_CASE(4)
         WQD_AQ_CASE(5)
