@@ -22,9 +22,12 @@
 //   * The 64 lanes' terms of a row are summed by a transposed butterfly in a fixed order: per tile
 //     the permlane32 and permlane16 swap stages fold 8 rows x 64 lanes into 2 values per lane,
 //     which accumulate over the slices of a piece; the DPP stages finish the sum once per piece.
-// M = 2..8, direct decode: the codebooks sit in LDS, each lane decodes its group's 8 rows (two
-//   16-byte LDS reads and one packed fp16 add per row) and multiplies them with each activation
-//   row; the 8 row sums are reduced across lanes per tile.
+// M = 2, one table for both rows: dword (b*256 + c)*64 + g holds the fp16 pair (T_b,g[c] of row 0,
+//   of row 1), 128 KiB, so it is single-buffered (a barrier, the build, a barrier per slice); the
+//   same two lookups per 8 weights give both rows' terms.
+// M = 3..8 (and batch-invariant calls), direct decode: the codebooks sit in LDS, each lane decodes
+//   its group's 8 rows (two 16-byte LDS reads and one packed fp16 add per row) and multiplies them
+//   with each activation row; the 8 row sums are reduced across lanes per tile.
 //
 // Work: see AqDesc.  A workgroup walks its pieces in order, slice by slice; the loads of the next
 // slice (of the same or the next piece) are in flight while a slice is processed.  With b > 1
