@@ -383,6 +383,19 @@ static int64_t aq_nwg(int64_t M, int cus) {
     return int64_t(cus) * (fn ? resident_per_cu(reinterpret_cast<const void *>(fn), aq_waves(int(M)) * 64) : 1);
 }
 
+// AQ2X8 at M = 3 and 4 runs as two row parts on the lookup-table kernels, rows 0-1 (M = 2) and
+// the rest (M = 1 or 2), one launch each: they read the weights twice, against one pass of the
+// direct decode, and still take about 0.9 of its time on the 70B MLP (M = 3: 129 against 143 us
+// per step; M = 4: 146 against 162).  Batch-invariant calls keep the direct decode at every M.
+static int aq_row_parts(int64_t M, bool bi, int64_t (&r0)[2], int64_t (&rm)[2]) {
+    if (!bi && (M == 3 || M == 4)) {
+        r0[0] = 0, rm[0] = 2, r0[1] = 2, rm[1] = M - 2;
+        return 2;
+    }
+    r0[0] = 0, rm[0] = M;
+    return 1;
+}
+
 struct AqPlan {
     Layout L;
     int64_t RB = 0, a = 1, b = 1, nrb = 1, ns = 1, RW = 1;
@@ -525,6 +538,7 @@ struct LaunchGroup {
     bool epi = false;          // some descriptor applies an epilogue
     bool bi = false;           // batch-invariant instance
     int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
+    int64_t m = 0;             // AQ2X8 row part: its activation rows (0: the call's M)
     int xq = -1;               // >= 0: the int8 quantizer launch of StackPlan::xqs[xq]
 };
 
@@ -721,36 +735,44 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         SP.groups.push_back(G);
     }
     if (has_aq) {
-        // AQ2X8 projections: one launch, every workgroup taking one piece of each
-        const int64_t aq_wg = bi ? cus : aq_nwg(M, cus);  // (batch-invariant: one workgroup per CU at every M)
-        LaunchGroup G;
-        G.mask = fmt_bit(AQ2X8);
-        G.aq = true;
-        G.bi = bi;
-        G.first = int(SP.aqdescs.size());
-        std::vector<AqPlan> plans;
-        std::vector<int> idx;
-        int64_t total_pieces = 0;
-        for (int i = b; i < e; i++) {
-            if (p[i].fmt != AQ2X8) continue;
-            plans.push_back(plan_aq(p[i].N, p[i].K, M, aq_wg, bi));
-            idx.push_back(i);
-            total_pieces += plans.back().a * plans.back().b;
+        // AQ2X8 projections: one launch per row part, every workgroup taking one piece of each
+        int64_t r0[2], rm[2];
+        const int nparts = aq_row_parts(M, bi, r0, rm);
+        for (int part_i = 0; part_i < nparts; part_i++) {
+            const int64_t Mp = rm[part_i];
+            const int64_t aq_wg = bi ? cus : aq_nwg(Mp, cus);  // (batch-invariant: one workgroup per CU at every M)
+            LaunchGroup G;
+            G.mask = fmt_bit(AQ2X8);
+            G.aq = true;
+            G.bi = bi;
+            G.m = Mp;
+            G.first = int(SP.aqdescs.size());
+            std::vector<AqPlan> plans;
+            std::vector<int> idx;
+            int64_t total_pieces = 0;
+            for (int i = b; i < e; i++) {
+                if (p[i].fmt != AQ2X8) continue;
+                plans.push_back(plan_aq(p[i].N, p[i].K, Mp, aq_wg, bi));
+                idx.push_back(i);
+                total_pieces += plans.back().a * plans.back().b;
+            }
+            G.nwg = total_pieces < aq_wg ? total_pieces : aq_wg;  // no idle workgroups
+            int64_t off = 0;
+            for (size_t k = 0; k < plans.size(); k++) {
+                const AqPlan &A = plans[k];
+                const wqd_proj &q = p[idx[k]];
+                void *part = base ? static_cast<void *>(base + part_off) : nullptr;
+                part_off += A.part_bytes;
+                SP.needs_ws |= A.b > 1;
+                const uint16_t *xr = static_cast<const uint16_t *>(q.x) + r0[part_i] * q.ldx;
+                float *yr = q.y + r0[part_i] * q.ldy;
+                SP.aqdescs.push_back(make_aq_desc(A, q.w, xr, q.ldx, yr, q.ldy, part, off % G.nwg));
+                off += A.a * A.b;
+                if (A.RW > G.rw) G.rw = A.RW;
+            }
+            G.count = int(plans.size());
+            SP.groups.push_back(G);
         }
-        G.nwg = total_pieces < aq_wg ? total_pieces : aq_wg;  // no idle workgroups
-        int64_t off = 0;
-        for (size_t k = 0; k < plans.size(); k++) {
-            const AqPlan &A = plans[k];
-            const wqd_proj &q = p[idx[k]];
-            void *part = base ? static_cast<void *>(base + part_off) : nullptr;
-            part_off += A.part_bytes;
-            SP.needs_ws |= A.b > 1;
-            SP.aqdescs.push_back(make_aq_desc(A, q.w, q.x, q.ldx, q.y, q.ldy, part, off % G.nwg));
-            off += A.a * A.b;
-            if (A.RW > G.rw) G.rw = A.RW;
-        }
-        G.count = int(plans.size());
-        SP.groups.push_back(G);
     }
 }
 
@@ -765,7 +787,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
 
     SP.off_descs = 0;
     SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
-    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count * 2, 256);  // (two row parts)
     SP.off_cnt = SP.off_ctr + 256;
     int64_t cnt_all = 0;
     for (int i = 0; i < count; i++) {
@@ -814,9 +836,15 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     if (k_multiple(fmt) == 0) return WQD_EINVAL;
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     if (fmt == AQ2X8) {
-        AqPlan A = plan_aq(N, K, M, aq_nwg(M, device_cus()));
-        if (!A.L.ok) return WQD_ESHAPE;
-        return A.ws_bytes();
+        // the row parts run one after the other on the stream and share the partial slots
+        int64_t r0[2], rm[2], need = 0;
+        const int nparts = aq_row_parts(M, false, r0, rm);
+        for (int i = 0; i < nparts; i++) {
+            AqPlan A = plan_aq(N, K, rm[i], aq_nwg(rm[i], device_cus()));
+            if (!A.L.ok) return WQD_ESHAPE;
+            if (A.ws_bytes() > need) need = A.ws_bytes();
+        }
+        return need;
     }
     Plan P = plan_single(fmt, N, K, M, device_cus());
     if (!P.L.ok) return WQD_ESHAPE;
@@ -830,11 +858,23 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
     const int cus = device_cus();
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     if (fmt == AQ2X8) {
-        const int64_t nwg = aq_nwg(M, cus);
-        AqPlan A = plan_aq(N, K, M, nwg);
-        if (A.ws_bytes() > 0 && (!workspace || workspace_bytes < A.ws_bytes())) return WQD_ESPACE;
-        return aq_gemm_launch(A, nwg, w, x, M, ldx, y, ldy, ws ? ws + kCntRegion : nullptr,
-                              static_cast<hipStream_t>(stream));
+        // row parts (M = 3, 4) run one after the other and share the partial slots: each launch
+        // leaves them cleared
+        int64_t r0[2], rm[2];
+        const int nparts = aq_row_parts(M, false, r0, rm);
+        AqPlan A[2];
+        int64_t nwg[2];
+        for (int i = 0; i < nparts; i++) {
+            nwg[i] = aq_nwg(rm[i], cus);
+            A[i] = plan_aq(N, K, rm[i], nwg[i]);
+            if (A[i].ws_bytes() > 0 && (!workspace || workspace_bytes < A[i].ws_bytes())) return WQD_ESPACE;
+        }
+        for (int i = 0; i < nparts; i++) {
+            rc = aq_gemm_launch(A[i], nwg[i], w, static_cast<const uint16_t *>(x) + r0[i] * ldx, rm[i], ldx,
+                                y + r0[i] * ldy, ldy, ws ? ws + kCntRegion : nullptr, static_cast<hipStream_t>(stream));
+            if (rc != WQD_OK) return rc;
+        }
+        return WQD_OK;
     }
     Plan P = plan_single(fmt, N, K, M, cus);
     if (P.ws_bytes() > 0 && (!workspace || workspace_bytes < P.ws_bytes())) return WQD_ESPACE;
@@ -1027,7 +1067,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.nwg = int32_t(G.nwg);
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
-            rc = launch_aq(M, G.rw, AP, st, G.bi);
+            rc = launch_aq(G.m ? G.m : M, G.rw, AP, st, G.bi);
             if (rc != WQD_OK) return rc;
             if ((rc = mark(1)) != WQD_OK) return rc;
             li++;

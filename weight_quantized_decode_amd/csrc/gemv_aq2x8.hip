@@ -25,7 +25,8 @@
 // M = 2, one table for both rows: dword (b*256 + c)*64 + g holds the fp16 pair (T_b,g[c] of row 0,
 //   of row 1), 128 KiB, so it is single-buffered (a barrier, the build, a barrier per slice); the
 //   same two lookups per 8 weights give both rows' terms.
-// M = 3..8 (and batch-invariant calls), direct decode: the codebooks sit in LDS, each lane decodes
+// M = 3..8 (and batch-invariant calls), direct decode (at M = 3 and 4 the host runs row parts on
+//   the table kernels instead): the codebooks sit in LDS, each lane decodes
 //   its group's 8 rows (two 16-byte LDS reads and one packed fp16 add per row) and multiplies them
 //   with each activation row; the 8 row sums are reduced across lanes per tile.
 //
