@@ -58,7 +58,7 @@ def test_config_full_size(cfg, M):
     run_config(cfg, M, W.WQD_PERSISTENT)
 
 
-@pytest.mark.parametrize("cfg,M", [(2, 1), (5, 2)])
+@pytest.mark.parametrize("cfg,M", [(2, 1), (5, 2), (5, 3)])
 def test_config_ordered_mode(cfg, M):
     note(f"config {cfg} M={M} ordered")
     run_config(cfg, M, W.WQD_ORDERED)
