@@ -52,7 +52,7 @@ def run_config(cfg, M, mode, layers=None):
     return worst
 
 
-@pytest.mark.parametrize("cfg,M", [(1, 1), (2, 1), (4, 1), (4, 8), (5, 1), (5, 2), (5, 4), (5, 8), (6, 1), (6, 8)])
+@pytest.mark.parametrize("cfg,M", [(1, 1), (2, 1), (4, 1), (4, 8), (5, 1), (5, 2), (5, 4), (5, 6), (5, 8), (6, 1), (6, 8)])
 def test_config_full_size(cfg, M):
     note(f"config {cfg} M={M} persistent")
     run_config(cfg, M, W.WQD_PERSISTENT)

@@ -383,17 +383,23 @@ static int64_t aq_nwg(int64_t M, int cus) {
     return int64_t(cus) * (fn ? resident_per_cu(reinterpret_cast<const void *>(fn), aq_waves(int(M)) * 64) : 1);
 }
 
-// AQ2X8 at M = 3 and 4 runs as two row parts on the lookup-table kernels, rows 0-1 (M = 2) and
-// the rest (M = 1 or 2), one launch each: they read the weights twice, against one pass of the
-// direct decode, and still take about 0.9 of its time on the 70B MLP (M = 3: 129 against 143 us
-// per step; M = 4: 146 against 162).  Batch-invariant calls keep the direct decode at every M.
-static int aq_row_parts(int64_t M, bool bi, int64_t (&r0)[2], int64_t (&rm)[2]) {
-    if (!bi && (M == 3 || M == 4)) {
-        r0[0] = 0, rm[0] = 2, r0[1] = 2, rm[1] = M - 2;
-        return 2;
+// AQ2X8 at M = 3 and 4 runs as row parts on the lookup-table kernels: rows 0-1 at M = 2 and the
+// rest at M = 1 or 2, one launch each.  They read the weights once per part, against one pass of
+// the direct decode, and still take about 0.9 of its time on the 70B MLP (per step, M = 3: 129
+// against 143 us; M = 4: 146 against 162).  Three parts lose: M = 5 took 203 against 195 us, M = 6
+// 217 against 215.  Batch-invariant calls keep the direct decode at every M.
+constexpr int kMaxAqParts = 2;
+static int aq_row_parts(int64_t M, bool bi, int64_t (&r0)[kMaxAqParts], int64_t (&rm)[kMaxAqParts]) {
+    if (bi || M < 3 || M > 2 * kMaxAqParts) {
+        r0[0] = 0, rm[0] = M;
+        return 1;
     }
-    r0[0] = 0, rm[0] = M;
-    return 1;
+    int n = 0;
+    for (int64_t r = 0; r < M; r += 2, n++) {
+        r0[n] = r;
+        rm[n] = (M - r >= 2) ? 2 : 1;
+    }
+    return n;
 }
 
 struct AqPlan {
@@ -736,7 +742,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
     }
     if (has_aq) {
         // AQ2X8 projections: one launch per row part, every workgroup taking one piece of each
-        int64_t r0[2], rm[2];
+        int64_t r0[kMaxAqParts], rm[kMaxAqParts];
         const int nparts = aq_row_parts(M, bi, r0, rm);
         for (int part_i = 0; part_i < nparts; part_i++) {
             const int64_t Mp = rm[part_i];
@@ -787,7 +793,7 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
 
     SP.off_descs = 0;
     SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
-    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count * 2, 256);  // (two row parts)
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count * kMaxAqParts, 256);  // (row parts)
     SP.off_cnt = SP.off_ctr + 256;
     int64_t cnt_all = 0;
     for (int i = 0; i < count; i++) {
@@ -837,7 +843,7 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     if (fmt == AQ2X8) {
         // the row parts run one after the other on the stream and share the partial slots
-        int64_t r0[2], rm[2], need = 0;
+        int64_t r0[kMaxAqParts], rm[kMaxAqParts], need = 0;
         const int nparts = aq_row_parts(M, false, r0, rm);
         for (int i = 0; i < nparts; i++) {
             AqPlan A = plan_aq(N, K, rm[i], aq_nwg(rm[i], device_cus()));
@@ -860,10 +866,10 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
     if (fmt == AQ2X8) {
         // row parts (M = 3, 4) run one after the other and share the partial slots: each launch
         // leaves them cleared
-        int64_t r0[2], rm[2];
+        int64_t r0[kMaxAqParts], rm[kMaxAqParts];
         const int nparts = aq_row_parts(M, false, r0, rm);
-        AqPlan A[2];
-        int64_t nwg[2];
+        AqPlan A[kMaxAqParts];
+        int64_t nwg[kMaxAqParts];
         for (int i = 0; i < nparts; i++) {
             nwg[i] = aq_nwg(rm[i], cus);
             A[i] = plan_aq(N, K, rm[i], nwg[i]);
