@@ -103,7 +103,8 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
  * at zero again, so it can be reused by later calls on the same stream (calls that overlap in
  * time must not share a workspace).  When K is split, the wave that finishes the last K-slice of
  * a 64-row group adds the slices' partial sums in ascending order, so results are the same bits
- * from run to run. */
+ * from run to run.  AQ2X8 at M = 3 and 4 is two launches (activation rows 0-1, then the rest) on
+ * the lookup-table kernels; every other call is one launch. */
 WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
                      int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
@@ -177,7 +178,8 @@ enum {
                            pointer and ldx) share one launch, at most 4 entries per launch and a
                            gate/up pair never split (q/k/v in one launch, gate/up in one); runs
                            follow one another in list order, so a later run may read what an
-                           earlier one wrote.  AQ2X8 entries launch one at a time.  Entries of
+                           earlier one wrote.  AQ2X8 entries launch one at a time (at M = 3
+                           and 4, two launches: rows 0-1, then the rest).  Entries of
                            one run must not write the same y elements. */
 };
 
@@ -226,8 +228,9 @@ WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64
 /* Profiling variant: the same work as wqd_run_projections, with hipEvent_t events[2i] recorded
  * on the stream just before the i-th kernel launch of the call and events[2i+1] just after it.
  * Launch order in WQD_PERSISTENT mode: the int8 quantizers (WQD_INT8_ACTIVATIONS), the CB4+CB8
- * launch if both formats are present, then one launch per remaining format (ascending format id);
- * in the other modes, list order (a segment's quantizers first).
+ * launch if both formats are present, then one launch per remaining format (ascending format id;
+ * AQ2X8 at M = 3 and 4: one per row part, rows 0-1 first); in the other modes, list order (a
+ * segment's quantizers first).
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,
