@@ -306,3 +306,16 @@ def test_size_limits(fmt):
                             None, 0, None) == W.WQD_ESHAPE
     assert W.lib().wqd_gemm(fmt, 64, W.WQD_MAX_K + kb, FAKE, FAKE, 1, W.WQD_MAX_K + kb, FAKE, 64,
                             None, 0, None) == W.WQD_ESHAPE
+
+
+def test_aq2x8_row_part_launch_counts():
+    """AQ2X8 at M = 3 and 4 runs as two launches (rows 0-1, then the rest) on the table kernels;
+    other M, and batch-invariant calls, take one launch per AQ2X8 group."""
+    L = W.lib()
+    X = FAKE + (1 << 40)
+    arr = _fake_list([(I.CB4, 64, 64, E0, X), (I.AQ2X8, 128, 1024, E0, X), (I.AQ2X8, 64, 512, E0, X)])
+    n = len(arr)
+    for M, aq in ((1, 1), (2, 1), (3, 2), (4, 2), (5, 1), (8, 1)):
+        assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT) == 1 + aq, M       # CB4 + AQ2X8
+        assert L.wqd_stack_launches(arr, n, M, W.WQD_ORDERED) == 1 + 2 * aq, M      # one entry each
+        assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT | W.WQD_BATCH_INVARIANT) == 2, M
