@@ -109,6 +109,19 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
                      int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): wqd_gemm without a workspace argument.  The split-K counters and
+ * partial sums live in a file-scope device array of WQD_NOALLOC_MAX_BYTES bytes, one copy per GPU,
+ * held from the first call on that GPU until the process ends.  The first call on a device looks
+ * the array's address up and clears it with a kernel on `stream`; every call leaves its counters
+ * at zero again.  The call allocates nothing (no hipMalloc, no allocating library routine).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made.  Arguments and results as wqd_gemm; WQD_ESPACE when the
+ * shape needs more than WQD_NOALLOC_MAX_BYTES (wqd_gemm_workspace_bytes() gives the need). */
+#define WQD_NOALLOC_MAX_BYTES (16ll << 20)
+WQD_API int wqd_gemm_noalloc(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
+                             int64_t ldx, float *y, int64_t ldy, void *stream);
+
 /* ---------------------------------------------------------------- TQ2 with int8 activations */
 
 /* Device workspace wqd_gemm_i8 needs (always > 0): the quantized activations and wqd_gemm's

@@ -319,3 +319,15 @@ def test_aq2x8_row_part_launch_counts():
         assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT) == 1 + aq, M       # CB4 + AQ2X8
         assert L.wqd_stack_launches(arr, n, M, W.WQD_ORDERED) == 1 + 2 * aq, M      # one entry each
         assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT | W.WQD_BATCH_INVARIANT) == 2, M
+
+
+def test_gemm_noalloc_rejects_shapes_beyond_the_scratch():
+    # an 8-row CB8 call over 2^20 rows with split K needs more than the scratch array holds: the
+    # call is refused before any HIP call (the pointers are never read)
+    N, K, M = 1 << 20, 4096, 8
+    need = W.wqd_gemm_workspace_bytes(I.CB8, N, K, M)
+    assert need > W.WQD_NOALLOC_MAX_BYTES
+    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, 256, 256, M, K, 256, N, None) == W.WQD_ESPACE
+    # argument errors come first, as for wqd_gemm
+    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, None, 256, M, K, 256, N, None) == W.WQD_EINVAL
+    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, 256, 256, 9, K, 256, N, None) == W.WQD_ESHAPE

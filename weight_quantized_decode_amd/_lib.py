@@ -30,7 +30,9 @@ EXPORTED = [
     "wqd_gemm", "wqd_dequant_f32", "wqd_stack_workspace_bytes", "wqd_stack_setup",
     "wqd_run_projections", "wqd_run_projections_timed", "wqd_stack_launches", "wqd_stream_check",
     "wqd_last_hip_error", "wqd_status_str", "wqd_gemm_i8_workspace_bytes", "wqd_gemm_i8", "wqd_quantize_i8",
+    "wqd_gemm_noalloc",
 ]
+WQD_NOALLOC_MAX_BYTES = 16 << 20
 
 
 class WqdError(RuntimeError):
@@ -65,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "wqd_prepare_host": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, i64, vp, i64]),
             "wqd_gemm_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
             "wqd_gemm": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
+            "wqd_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp]),
             "wqd_dequant_f32": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp]),
             "wqd_gemm_i8_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
             "wqd_gemm_i8": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
@@ -139,6 +142,13 @@ def wqd_gemm(fmt: int, N: int, K: int, w, x, y, workspace=None, stream=None) -> 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("wqd_gemm", lib().wqd_gemm(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
                                       _dptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wqd_gemm_noalloc(fmt: int, N: int, K: int, w, x, y, stream=None) -> None:
+    """wqd_gemm without a workspace: the library's per-GPU scratch array serves as one."""
+    M = x.shape[0]
+    _check("wqd_gemm_noalloc", lib().wqd_gemm_noalloc(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y),
+                                                      y.stride(0), _stream(stream)))
 
 
 def wqd_gemm_i8_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/wqd.h"
@@ -857,10 +858,13 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     return P.ws_bytes();
 }
 
-WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
+}  // extern "C"
+
+// One projection on a caller-provided (or the file-scope scratch) workspace: the body of wqd_gemm
+// and wqd_gemm_noalloc.  The arguments are checked by the caller.
+static int gemm_impl(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
                      float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
-    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
-    if (rc != WQD_OK) return rc;
+    int rc = WQD_OK;
     const int cus = device_cus();
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     if (fmt == AQ2X8) {
@@ -887,6 +891,72 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
     int *cnt = reinterpret_cast<int *>(ws);
     float *part = ws ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr;
     return gemm_launch(P, w, x, M, ldx, y, ldy, cnt, part, static_cast<hipStream_t>(stream), cus);
+}
+
+// ------------------------------------------------------------------------------------------
+// Scratch of wqd_gemm_noalloc: the split-K counters and partial sums of one call, in a file-scope
+// device array (one copy per GPU, held until the process ends) instead of a caller workspace.
+// Host code never passes the array's name to a kernel: on the host it is a stand-in symbol, not a
+// device address.  The device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that pointer is used afterwards.
+// ------------------------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = WQD_NOALLOC_MAX_BYTES;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4 *p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of the scratch array on the current device.  The first call on a device looks
+// the address up and clears the array with a fill kernel on `st` (the counters must start at
+// zero; every later call leaves them at zero again).
+static int scratch_on_device(hipStream_t st, uint8_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return WQD_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!p) return hip_fail(hipErrorInvalidSymbol);
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, st, static_cast<uint4 *>(p), kScratchBytes / 16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return WQD_OK;
+}
+
+extern "C" {
+
+WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
+                     float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
+    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+    if (rc != WQD_OK) return rc;
+    return gemm_impl(fmt, N, K, w, x, M, ldx, y, ldy, workspace, workspace_bytes, stream);
+}
+
+WQD_API int wqd_gemm_noalloc(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
+                             float *y, int64_t ldy, void *stream) {
+    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+    if (rc != WQD_OK) return rc;
+    const int64_t need = wqd_gemm_workspace_bytes(fmt, N, K, M);
+    if (need < 0) return int(need);
+    if (need > kScratchBytes) return WQD_ESPACE;
+    uint8_t *ws = nullptr;
+    if (need > 0) {
+        rc = scratch_on_device(static_cast<hipStream_t>(stream), &ws);
+        if (rc != WQD_OK) return rc;
+    }
+    return gemm_impl(fmt, N, K, w, x, M, ldx, y, ldy, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 // Workspace of wqd_gemm_i8: [wqd_gemm's counters and partials][q: M x K bytes][a: M x K/128 fp32]
