@@ -103,8 +103,10 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
  * at zero again, so it can be reused by later calls on the same stream (calls that overlap in
  * time must not share a workspace).  When K is split, the wave that finishes the last K-slice of
  * a 64-row group adds the slices' partial sums in ascending order, so results are the same bits
- * from run to run.  AQ2X8 at M = 3 and 4 is two launches (activation rows 0-1, then the rest) on
- * the lookup-table kernels; every other call is one launch. */
+ * from run to run.  Every call is one launch.  AQ2X8 forms its group sums in fp32 at every M:
+ * fp32 lookup tables of the activations at M = 1, exact fp16 products of codebook entries summed
+ * in fp32 on the matrix cores at M > 1; its K-splits are added in split order by the wave that
+ * finishes last. */
 WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
                      int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
                      void *stream);
@@ -191,9 +193,8 @@ enum {
                            pointer and ldx) share one launch, at most 4 entries per launch and a
                            gate/up pair never split (q/k/v in one launch, gate/up in one); runs
                            follow one another in list order, so a later run may read what an
-                           earlier one wrote.  AQ2X8 entries launch one at a time (at M = 3
-                           and 4, two launches: rows 0-1, then the rest).  Entries of
-                           one run must not write the same y elements. */
+                           earlier one wrote.  AQ2X8 entries launch one at a time.  Entries
+                           of one run must not write the same y elements. */
 };
 
 /* Flag OR-ed into a mode: batch-invariant results (trapetum "Benchmarks", November update: a
@@ -202,9 +203,9 @@ enum {
  * made with row m alone (M = 1), for every M <= 8, in every mode and whatever else the list
  * holds: every projection is sliced the same way at every M, and every M runs the same per-row
  * instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
- * A verify of 9..16 rows is two calls.  AQ2X8 entries then use the direct decode at every M
- * (their M = 1 lookup-table kernel rounds differently), one workgroup per CU and one row block per
- * wave.  Results differ in rounding (within the bound) from calls without the flag. */
+ * A verify of 9..16 rows is two calls.  AQ2X8 entries then take the matrix-core kernel at every M
+ * (the M = 1 lookup-table kernel rounds differently), with pieces planned for every CU whatever
+ * the list.  Results differ in rounding (within the bound) from calls without the flag. */
 enum { WQD_BATCH_INVARIANT = 0x10 };
 
 /* Flag OR-ed into a mode: the TQ2 entries of the list multiply int8-quantized activations, as
@@ -241,9 +242,8 @@ WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64
 /* Profiling variant: the same work as wqd_run_projections, with hipEvent_t events[2i] recorded
  * on the stream just before the i-th kernel launch of the call and events[2i+1] just after it.
  * Launch order in WQD_PERSISTENT mode: the int8 quantizers (WQD_INT8_ACTIVATIONS), the CB4+CB8
- * launch if both formats are present, then one launch per remaining format (ascending format id;
- * AQ2X8 at M = 3 and 4: one per row part, rows 0-1 first); in the other modes, list order (a
- * segment's quantizers first).
+ * launch if both formats are present, then one launch per remaining format (ascending format
+ * id); in the other modes, list order (a segment's quantizers first).
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,

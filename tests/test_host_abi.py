@@ -71,22 +71,22 @@ def test_prepare_keeps_canonical_byte_order_for_byte_formats(fmt, N, K):
 
 @pytest.mark.parametrize("N,K", [(70, 1000), (64, 512), (8, 8), (130, 8 * 200)])
 def test_prepare_tiles_aq2x8_codes(N, K):
-    # AQ2X8 codes go to tiles of 8 rows x 64 groups, slice-major: the 16 bytes of lane l in tile
-    # (r8, s) are (c0, c1) of rows 8*r8..8*r8+7 for group 64*s + l.  Rebuild the canonical [N][G][2] code array
-    # from the tiles, and check the padding (rows >= N, groups >= G) is zero; scales and codebooks
-    # are copied verbatim.
+    # AQ2X8 codes go to tiles of 16 rows x 32 groups, slice-major: the 16 bytes of lane 32h + g in
+    # tile (b16, s) are (c0, c1) of rows 16*b16 + 8h .. + 7 for group 32*s + g.  Rebuild the
+    # canonical [N][G][2] code array from the tiles, and check the padding (rows >= N, groups >= G)
+    # is zero; scales and codebooks are copied verbatim.
     canon = I.gen_weight(I.AQ2X8, N, K, (5, I.AQ2X8))
     prep = W.wqd_prepare_host(I.AQ2X8, N, K, canon)
     G = K // 8
-    KS = (G + 63) // 64
+    KS = (G + 31) // 32
     RG = (N + 63) // 64
     Npad = RG * 64
-    tiles = prep[:Npad // 8 * KS * 1024].reshape(KS, Npad // 8, 64, 8, 2)  # [s][r8][lane][row][c]
-    codes = tiles.transpose(1, 3, 0, 2, 4).reshape(Npad, KS * 64, 2)        # [n][g][c]
+    tiles = prep[:Npad // 16 * KS * 1024].reshape(KS, Npad // 16, 2, 32, 8, 2)  # [s][b16][h][g][row][c]
+    codes = tiles.transpose(1, 2, 4, 0, 3, 5).reshape(Npad, KS * 32, 2)        # [n][group][c]
     want = canon[8192 + 2 * N:].reshape(N, G, 2)
     assert np.array_equal(codes[:N, :G], want)
     assert np.all(codes[N:] == 0) and np.all(codes[:, G:] == 0)
-    off_s = (Npad // 8 * KS * 1024 + 255) // 256 * 256
+    off_s = (Npad // 16 * KS * 1024 + 255) // 256 * 256
     assert np.array_equal(prep[off_s:off_s + 2 * N], canon[8192:8192 + 2 * N])
     off_c = (off_s + 2 * Npad + 255) // 256 * 256
     assert np.array_equal(prep[off_c:off_c + 8192], canon[:8192])
@@ -308,16 +308,16 @@ def test_size_limits(fmt):
                             None, 0, None) == W.WQD_ESHAPE
 
 
-def test_aq2x8_row_part_launch_counts():
-    """AQ2X8 at M = 3 and 4 runs as two launches (rows 0-1, then the rest) on the table kernels;
-    other M, and batch-invariant calls, take one launch per AQ2X8 group."""
+def test_aq2x8_launch_counts():
+    """The AQ2X8 entries of a segment share one launch at every M (the lookup-table kernel at
+    M = 1, the matrix-core kernel above and in batch-invariant lists)."""
     L = W.lib()
     X = FAKE + (1 << 40)
     arr = _fake_list([(I.CB4, 64, 64, E0, X), (I.AQ2X8, 128, 1024, E0, X), (I.AQ2X8, 64, 512, E0, X)])
     n = len(arr)
-    for M, aq in ((1, 1), (2, 1), (3, 2), (4, 2), (5, 1), (8, 1)):
-        assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT) == 1 + aq, M       # CB4 + AQ2X8
-        assert L.wqd_stack_launches(arr, n, M, W.WQD_ORDERED) == 1 + 2 * aq, M      # one entry each
+    for M in range(1, 9):
+        assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT) == 2, M       # CB4 + AQ2X8
+        assert L.wqd_stack_launches(arr, n, M, W.WQD_ORDERED) == 3, M          # one entry each
         assert L.wqd_stack_launches(arr, n, M, W.WQD_PERSISTENT | W.WQD_BATCH_INVARIANT) == 2, M
 
 

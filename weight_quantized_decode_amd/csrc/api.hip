@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, La
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= L.N * L.G) return;
     const int64_t n = i / L.G, g = i - n * L.G;
-    const uint8_t *t = w + ((g / 64 * (L.Npad / 8) + n / 8) * 64 + g % 64) * 16 + 2 * (n % 8);
+    const int64_t lane = ((n % 16) / 8) * 32 + g % 32;
+    const uint8_t *t = w + ((g / 32 * (L.Npad / 16) + n / 16) * 64 + lane) * 16 + 2 * (n % 8);
     const uint32_t c0 = t[0], c1 = t[1];
     const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
     const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
@@ -174,20 +175,6 @@ static GemvFn pick_gemv(int mask, int M, bool epi = false, bool bi = false) {
     return nullptr;
 }
 
-// Resident workgroups per CU of a kernel (queried once per kernel and device).  The persistent
-// grid never exceeds what is resident at once, so every workgroup starts immediately.
-static int resident_per_cu(const void *fn, int threads) {
-    struct Entry { const void *fn; int dev; int n; };
-    static thread_local std::vector<Entry> cache;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    for (const Entry &e : cache)
-        if (e.fn == fn && e.dev == dev) return e.n;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 1) n = 1;
-    cache.push_back({fn, dev, n});
-    return n;
-}
 // The row kernels are compiled for WQD_WG_PER_CU resident workgroups per CU (see gemv_impl.h).
 static int resident_per_cu(GemvFn fn) { return fn ? WQD_WG_PER_CU : 1; }
 
@@ -371,69 +358,49 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
 }
 
 // ------------------------------------------------------------------------------------------
-// AQ2X8 planning.  A projection's RB x KS tiles (8-row blocks x 64-group slices) are cut into
-// a x b pieces (row chunks of nrb <= 16*RW blocks, K-splits of ns slices); every workgroup of the
-// launch takes one piece of each projection (piece j on workgroup (j + off) % nwg).  The cost
-// model per piece, in tile loads (KiB): ns * (nrb + table build) plus a fixed charge for a
-// K-split (its partial round trip); the shape with the cheapest busiest workgroup wins.
+// AQ2X8 planning.  A projection's RB x KS tiles (16-row blocks x 32-group slices) are cut into
+// a x b pieces (row chunks of nrb <= 16*RW blocks, K-splits of ns slices), dealt over the nw
+// workgroups that serve the projection.  Cost model per piece, in tile loads (KiB): ns * (nrb +
+// slice setup) plus a fixed charge for a K-split (its partial round trip); the shape whose
+// busiest workgroup is cheapest wins.  M = 1 runs the lookup-table kernel; M > 1 and every
+// batch-invariant call run the matrix-core kernel.
 // ------------------------------------------------------------------------------------------
-static int aq_rw_max(int64_t M) { return M == 1 ? WQD_AQ1_RW_MAX : M == 2 ? 4 : M <= 4 ? 2 : 1; }  // (M > 4, RW 2: spills)
-
-static int64_t aq_nwg(int64_t M, int cus) {
-    AqFn fn = aq_fn(int(M), aq_rw_max(M));
-    return int64_t(cus) * (fn ? resident_per_cu(reinterpret_cast<const void *>(fn), aq_waves(int(M)) * 64) : 1);
-}
-
-// AQ2X8 at M = 3 and 4 runs as row parts on the lookup-table kernels: rows 0-1 at M = 2 and the
-// rest at M = 1 or 2, one launch each.  They read the weights once per part, against one pass of
-// the direct decode, and still take about 0.9 of its time on the 70B MLP (per step, M = 3: 129
-// against 143 us; M = 4: 146 against 162).  Three parts lose: M = 5 took 203 against 195 us, M = 6
-// 217 against 215.  Batch-invariant calls keep the direct decode at every M.
-constexpr int kMaxAqParts = 2;
-static int aq_row_parts(int64_t M, bool bi, int64_t (&r0)[kMaxAqParts], int64_t (&rm)[kMaxAqParts]) {
-    if (bi || M < 3 || M > 2 * kMaxAqParts) {
-        r0[0] = 0, rm[0] = M;
-        return 1;
-    }
-    int n = 0;
-    for (int64_t r = 0; r < M; r += 2, n++) {
-        r0[n] = r;
-        rm[n] = (M - r >= 2) ? 2 : 1;
-    }
-    return n;
-}
+static bool aq_lut(int64_t M, bool bi) { return M == 1 && !bi; }
 
 struct AqPlan {
     Layout L;
-    int64_t RB = 0, a = 1, b = 1, nrb = 1, ns = 1, RW = 1;
-    int64_t part_bytes = 0;  // M * b * Npad tagged 8-byte slots when b > 1 (256-byte aligned)
-    // wqd_gemm workspace: [kCntRegion bytes, unused by AQ2X8][partials]
+    bool lut = false;
+    int64_t RB = 0, a = 1, b = 1, nrb = 1, ns = 1;
+    int64_t cnt_bytes = 0;   // a * kAqWaves arrival counters when b > 1 (256-byte aligned)
+    int64_t part_bytes = 0;  // M * b * Npad fp32 partials when b > 1 (256-byte aligned)
+    int64_t tiles() const { return RB * L.KS; }
+    // wqd_gemm workspace: [kCntRegion bytes of counters][partials]
     int64_t ws_bytes() const { return b > 1 ? kCntRegion + part_bytes : 0; }
 };
 
-// bi: the batch-invariant plan (direct decode, one row block per wave per slice, and the caller
-// passes a workgroup count that does not depend on M), so the pieces do not depend on M.
-static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg, bool bi = false) {
+static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
     AqPlan A;
     A.L = make_layout(AQ2X8, N, K);
     if (!A.L.ok) return A;
-    const int64_t RB = (N + 7) / 8, KS = A.L.KS, rwmax = bi ? 1 : aq_rw_max(M), W = aq_waves(int(M));
-    // a slice's table (M = 1; M = 2: twice the matrix work, not overlapped) or staging (M > 2)
-    const int64_t build = bi ? 2 : M == 1 ? WQD_AQ_BUILD_CHARGE : M == 2 ? 2 * WQD_AQ_BUILD_CHARGE : 2;
-    const int64_t split_charge = WQD_AQ_SPLIT_CHARGE;
-    if (nwg < 1) nwg = 1;
+    A.lut = lut;
+    const int64_t RB = (N + 15) / 16, KS = A.L.KS;
+    const int64_t per = int64_t(kAqWaves) * (lut ? kAqLutRW : kAqMmaRW);  // most row blocks per piece
+    const int64_t bmax = lut ? kAqLutMaxSplits : kAqMmaMaxSplits;
+    const int64_t setup = lut ? WQD_AQ_BUILD_CHARGE : 2;  // table build / activation staging
+    if (nw < 1) nw = 1;
     double best = 1e300;
-    for (int64_t b = 1; b <= KS && b <= WQD_AQ_MAX_SPLITS; b++) {
+    for (int64_t b = 1; b <= KS && b <= bmax; b++) {
         const int64_t ns = (KS + b - 1) / b;
         if ((KS + ns - 1) / ns != b) continue;  // same split as a smaller b
-        int64_t a = nwg / b;
-        if (a > (RB + W - 1) / W) a = (RB + W - 1) / W;    // at least one block per wave...
-        if (a < (RB + W * rwmax - 1) / (W * rwmax)) a = (RB + W * rwmax - 1) / (W * rwmax);  // ...at most RW
+        int64_t a = nw / b;
+        if (a < (RB + per - 1) / per) a = (RB + per - 1) / per;
+        if (a > RB) a = RB;
         if (a < 1) a = 1;
         const int64_t nrb = (RB + a - 1) / a;
         a = (RB + nrb - 1) / nrb;
-        const int64_t rounds = (a * b + nwg - 1) / nwg;
-        const double cost = double(rounds) * double(ns * (nrb + build) + (b > 1 ? split_charge : 0));
+        if (b > 1 && a * kAqWaves * 4 > kCntRegion) continue;  // the counters fit their region
+        const int64_t rounds = (a * b + nw - 1) / nw;
+        const double cost = double(rounds) * double(ns * (nrb + setup) + (b > 1 ? WQD_AQ_SPLIT_CHARGE : 0));
         if (cost < best) {
             best = cost;
             A.a = a;
@@ -443,14 +410,13 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nwg, bool bi = fa
         }
     }
     A.RB = RB;
-    A.RW = 1;  // M = 1 kernels exist for RW = 1, 2, 4 and 8 (two passes of 4); M > 1 for 1, 2
-    while (A.RW * W < A.nrb) A.RW *= 2;
-    A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 8, 256) : 0;
+    A.cnt_bytes = A.b > 1 ? align_up(A.a * kAqWaves * 4, 256) : 0;
+    A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 4, 256) : 0;
     return A;
 }
 
 static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
-                           void *part, int64_t off) {
+                           void *part, void *cnt, int64_t off, int64_t nw) {
     AqDesc D;
     memset(&D, 0, sizeof(D));
     const uint8_t *base = static_cast<const uint8_t *>(w);
@@ -459,7 +425,8 @@ static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_
     D.cbk = reinterpret_cast<const uint16_t *>(base + A.L.off_cbk);
     D.x = static_cast<const uint16_t *>(x);
     D.y = y;
-    D.part = A.b > 1 ? static_cast<uint64_t *>(part) : nullptr;
+    D.part = A.b > 1 ? static_cast<float *>(part) : nullptr;
+    D.cnt = A.b > 1 ? static_cast<int *>(cnt) : nullptr;
     D.ldx = ldx;
     D.ldy = ldy;
     D.N = int32_t(A.L.N);
@@ -473,27 +440,72 @@ static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_
     D.ns = int32_t(A.ns);
     D.npieces = int32_t(A.a * A.b);
     D.off = int32_t(off);
+    D.nw = int32_t(nw);
     return D;
 }
 
-static int launch_aq(int64_t M, int64_t RW, const AqParams &AP, hipStream_t st, bool bi = false) {
-    AqFn fn = aq_fn(int(M), int(RW), bi);
+static int launch_aq(int64_t M, bool lut, const AqParams &AP, hipStream_t st) {
+    AqFn fn = aq_fn(int(M), lut);
     if (!fn) return WQD_EINVAL;
-    hipLaunchKernelGGL(fn, dim3(unsigned(AP.nwg)), dim3(aq_waves(int(M)) * 64), 0, st, AP);
+    hipLaunchKernelGGL(fn, dim3(unsigned(AP.nwg)), dim3(kAqWaves * 64), 0, st, AP);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
 
-// One AQ2X8 projection alone, on a workspace whose partial region starts at `part`.
-static int aq_gemm_launch(const AqPlan &A, int64_t nwg, const void *w, const void *x, int64_t M, int64_t ldx,
-                          float *y, int64_t ldy, void *part, hipStream_t st) {
+// Workgroups of an AQ2X8 launch over projections with these plans (one per CU at most, none idle)
+// and the share of each projection: the lookup-table kernel deals every projection's pieces over
+// all workgroups (each starting where the previous one stopped); the matrix-core kernel gives
+// each projection a contiguous range of workgroups in proportion to its tiles, so a workgroup
+// loads the 16 LDS copies of one projection's codebooks once.
+struct AqShare {
+    int64_t off = 0, nw = 1;
+};
+static int64_t aq_assign(const std::vector<AqPlan> &plans, int cus, bool lut, std::vector<AqShare> &share) {
+    share.assign(plans.size(), AqShare());
+    int64_t pieces = 0, tiles = 0;
+    for (const AqPlan &A : plans) {
+        pieces += A.a * A.b;
+        tiles += A.tiles();
+    }
+    int64_t nwg = pieces < cus ? pieces : cus;
+    if (nwg < 1) nwg = 1;
+    if (lut) {
+        int64_t off = 0;
+        for (size_t k = 0; k < plans.size(); k++) {
+            share[k].off = off % nwg;
+            share[k].nw = nwg;
+            off += plans[k].a * plans[k].b;
+        }
+        return nwg;
+    }
+    int64_t start = 0;
+    for (size_t k = 0; k < plans.size(); k++) {
+        int64_t nw = tiles > 0 ? (plans[k].tiles() * nwg + tiles / 2) / tiles : 1;
+        if (nw < 1) nw = 1;
+        if (nw > nwg) nw = nwg;
+        if (nw > plans[k].a * plans[k].b) nw = plans[k].a * plans[k].b;
+        share[k].off = start % nwg;
+        share[k].nw = nw;
+        start += nw;
+    }
+    return nwg;
+}
+
+// One AQ2X8 projection alone, on a workspace of counters then partials.
+static int aq_gemm_launch(int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx, float *y,
+                          int64_t ldy, uint8_t *ws, int64_t ws_bytes, hipStream_t st, int cus) {
+    const bool lut = aq_lut(M, false);
+    std::vector<AqPlan> plans(1, plan_aq(N, K, M, cus, lut));
+    if (plans[0].ws_bytes() > 0 && (!ws || ws_bytes < plans[0].ws_bytes())) return WQD_ESPACE;
+    std::vector<AqShare> share;
+    const int64_t nwg = aq_assign(plans, cus, lut, share);
     AqParams AP;
     memset(&AP, 0, sizeof(AP));
-    AP.d0 = make_aq_desc(A, w, x, ldx, y, ldy, part, 0);
+    AP.d0 = make_aq_desc(plans[0], w, x, ldx, y, ldy, ws ? ws + kCntRegion : nullptr, ws, share[0].off, share[0].nw);
     AP.descs = nullptr;
     AP.ndesc = 1;
-    AP.nwg = int32_t(nwg < A.a * A.b ? nwg : A.a * A.b);
-    return launch_aq(M, A.RW, AP, st);
+    AP.nwg = int32_t(nwg);
+    return launch_aq(M, lut, AP, st);
 }
 
 static int check_proj(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
@@ -544,8 +556,8 @@ struct LaunchGroup {
     bool aq = false;           // an AQ2X8 launch
     bool epi = false;          // some descriptor applies an epilogue
     bool bi = false;           // batch-invariant instance
-    int64_t rw = 1, nwg = 0;   // AQ2X8: kernel instance and workgroups
-    int64_t m = 0;             // AQ2X8 row part: its activation rows (0: the call's M)
+    bool lut = false;          // AQ2X8: the lookup-table kernel (else the matrix-core one)
+    int64_t nwg = 0;           // AQ2X8: workgroups
     int xq = -1;               // >= 0: the int8 quantizer launch of StackPlan::xqs[xq]
 };
 
@@ -742,44 +754,41 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         SP.groups.push_back(G);
     }
     if (has_aq) {
-        // AQ2X8 projections: one launch per row part, every workgroup taking one piece of each
-        int64_t r0[kMaxAqParts], rm[kMaxAqParts];
-        const int nparts = aq_row_parts(M, bi, r0, rm);
-        for (int part_i = 0; part_i < nparts; part_i++) {
-            const int64_t Mp = rm[part_i];
-            const int64_t aq_wg = bi ? cus : aq_nwg(Mp, cus);  // (batch-invariant: one workgroup per CU at every M)
-            LaunchGroup G;
-            G.mask = fmt_bit(AQ2X8);
-            G.aq = true;
-            G.bi = bi;
-            G.m = Mp;
-            G.first = int(SP.aqdescs.size());
-            std::vector<AqPlan> plans;
-            std::vector<int> idx;
-            int64_t total_pieces = 0;
-            for (int i = b; i < e; i++) {
-                if (p[i].fmt != AQ2X8) continue;
-                plans.push_back(plan_aq(p[i].N, p[i].K, Mp, aq_wg, bi));
-                idx.push_back(i);
-                total_pieces += plans.back().a * plans.back().b;
-            }
-            G.nwg = total_pieces < aq_wg ? total_pieces : aq_wg;  // no idle workgroups
-            int64_t off = 0;
-            for (size_t k = 0; k < plans.size(); k++) {
-                const AqPlan &A = plans[k];
-                const wqd_proj &q = p[idx[k]];
-                void *part = base ? static_cast<void *>(base + part_off) : nullptr;
-                part_off += A.part_bytes;
-                SP.needs_ws |= A.b > 1;
-                const uint16_t *xr = static_cast<const uint16_t *>(q.x) + r0[part_i] * q.ldx;
-                float *yr = q.y + r0[part_i] * q.ldy;
-                SP.aqdescs.push_back(make_aq_desc(A, q.w, xr, q.ldx, yr, q.ldy, part, off % G.nwg));
-                off += A.a * A.b;
-                if (A.RW > G.rw) G.rw = A.RW;
-            }
-            G.count = int(plans.size());
-            SP.groups.push_back(G);
+        // AQ2X8 projections: one launch over all of them (batch-invariant lists plan every
+        // projection as if it had every CU, so the pieces do not depend on M or on the list)
+        const bool lut = aq_lut(M, bi);
+        LaunchGroup G;
+        G.mask = fmt_bit(AQ2X8);
+        G.aq = true;
+        G.bi = bi;
+        G.lut = lut;
+        G.first = int(SP.aqdescs.size());
+        std::vector<AqPlan> plans;
+        std::vector<int> idx;
+        for (int i = b; i < e; i++) {
+            if (p[i].fmt != AQ2X8) continue;
+            plans.push_back(plan_aq(p[i].N, p[i].K, M, cus, lut));
+            idx.push_back(i);
         }
+        std::vector<AqShare> share;
+        G.nwg = aq_assign(plans, cus, lut, share);
+        if (!lut && !bi) {
+            // the matrix-core kernel: each projection re-planned for the workgroups it gets
+            for (size_t k = 0; k < plans.size(); k++) plans[k] = plan_aq(p[idx[k]].N, p[idx[k]].K, M, share[k].nw, lut);
+            G.nwg = aq_assign(plans, cus, lut, share);
+        }
+        for (size_t k = 0; k < plans.size(); k++) {
+            const AqPlan &A = plans[k];
+            const wqd_proj &q = p[idx[k]];
+            void *part = base ? static_cast<void *>(base + part_off) : nullptr;
+            void *cnt = base ? static_cast<void *>(base + cnt_off) : nullptr;
+            part_off += A.part_bytes;
+            cnt_off += A.cnt_bytes;
+            SP.needs_ws |= A.b > 1;
+            SP.aqdescs.push_back(make_aq_desc(A, q.w, q.x, q.ldx, q.y, q.ldy, part, cnt, share[k].off, share[k].nw));
+        }
+        G.count = int(plans.size());
+        SP.groups.push_back(G);
     }
 }
 
@@ -794,12 +803,13 @@ static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mod
 
     SP.off_descs = 0;
     SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
-    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count * kMaxAqParts, 256);  // (row parts)
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
     SP.off_cnt = SP.off_ctr + 256;
     int64_t cnt_all = 0;
     for (int i = 0; i < count; i++) {
-        if (p[i].fmt == AQ2X8 || p[i].epi == WQD_EPI_SILU_UP) continue;
-        cnt_all += align_up(make_layout(p[i].fmt, p[i].N, p[i].K).RG * 4, 256);
+        if (p[i].epi == WQD_EPI_SILU_UP) continue;
+        // (an AQ2X8 plan keeps its counters within kCntRegion bytes)
+        cnt_all += p[i].fmt == AQ2X8 ? kCntRegion : align_up(make_layout(p[i].fmt, p[i].N, p[i].K).RG * 4, 256);
     }
     SP.cnt_bytes = cnt_all > kCntRegion ? cnt_all : kCntRegion;
     // int8 activations: one region per distinct TQ2 activation (the same layout in every mode,
@@ -843,15 +853,9 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     if (k_multiple(fmt) == 0) return WQD_EINVAL;
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     if (fmt == AQ2X8) {
-        // the row parts run one after the other on the stream and share the partial slots
-        int64_t r0[kMaxAqParts], rm[kMaxAqParts], need = 0;
-        const int nparts = aq_row_parts(M, false, r0, rm);
-        for (int i = 0; i < nparts; i++) {
-            AqPlan A = plan_aq(N, K, rm[i], aq_nwg(rm[i], device_cus()));
-            if (!A.L.ok) return WQD_ESHAPE;
-            if (A.ws_bytes() > need) need = A.ws_bytes();
-        }
-        return need;
+        AqPlan A = plan_aq(N, K, M, device_cus(), aq_lut(M, false));
+        if (!A.L.ok) return WQD_ESHAPE;
+        return A.ws_bytes();
     }
     Plan P = plan_single(fmt, N, K, M, device_cus());
     if (!P.L.ok) return WQD_ESHAPE;
@@ -864,28 +868,10 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
 // and wqd_gemm_noalloc.  The arguments are checked by the caller.
 static int gemm_impl(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
                      float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
-    int rc = WQD_OK;
     const int cus = device_cus();
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    if (fmt == AQ2X8) {
-        // row parts (M = 3, 4) run one after the other and share the partial slots: each launch
-        // leaves them cleared
-        int64_t r0[kMaxAqParts], rm[kMaxAqParts];
-        const int nparts = aq_row_parts(M, false, r0, rm);
-        AqPlan A[kMaxAqParts];
-        int64_t nwg[kMaxAqParts];
-        for (int i = 0; i < nparts; i++) {
-            nwg[i] = aq_nwg(rm[i], cus);
-            A[i] = plan_aq(N, K, rm[i], nwg[i]);
-            if (A[i].ws_bytes() > 0 && (!workspace || workspace_bytes < A[i].ws_bytes())) return WQD_ESPACE;
-        }
-        for (int i = 0; i < nparts; i++) {
-            rc = aq_gemm_launch(A[i], nwg[i], w, static_cast<const uint16_t *>(x) + r0[i] * ldx, rm[i], ldx,
-                                y + r0[i] * ldy, ldy, ws ? ws + kCntRegion : nullptr, static_cast<hipStream_t>(stream));
-            if (rc != WQD_OK) return rc;
-        }
-        return WQD_OK;
-    }
+    if (fmt == AQ2X8)
+        return aq_gemm_launch(N, K, w, x, M, ldx, y, ldy, ws, workspace_bytes, static_cast<hipStream_t>(stream), cus);
     Plan P = plan_single(fmt, N, K, M, cus);
     if (P.ws_bytes() > 0 && (!workspace || workspace_bytes < P.ws_bytes())) return WQD_ESPACE;
     int *cnt = reinterpret_cast<int *>(ws);
@@ -1143,7 +1129,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.nwg = int32_t(G.nwg);
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
-            rc = launch_aq(G.m ? G.m : M, G.rw, AP, st, G.bi);
+            rc = launch_aq(M, G.lut, AP, st);
             if (rc != WQD_OK) return rc;
             if ((rc = mark(1)) != WQD_OK) return rc;
             li++;

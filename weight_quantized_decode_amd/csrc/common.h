@@ -137,38 +137,25 @@ constexpr int fmt_bit(int fmt) { return 1 << fmt; }
 constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 
 // ------------------------------------------------------------------------------------------
-// AQ2X8 (its own kernel, on the transposed tile layout): a projection's (8-row block x K-slice)
-// tiles are cut into a x b rectangular pieces, a row chunks of nrb blocks times b K-splits of ns
-// slices.  Piece j = split * a + chunk runs on workgroup (j + off) % nwg (and j + nwg, ... when
-// there are more pieces than workgroups).  With b > 1 each piece stores one tagged partial per
-// row, and at the end of their work the b workgroups of a chunk each add the b partials of a
-// share (1/b) of its rows.
+// AQ2X8 (kernels of their own, on the 16-row x 32-group tile layout of layout.h).  A projection's
+// (16-row block x 32-group slice) tiles are cut into a x b rectangular pieces: a row chunks of
+// nrb blocks times b K-splits of ns slices.  Piece j = split * a + chunk runs on workgroup
+// wb + (j mod nw) of the launch, where wb = off and nw of the projection say which workgroups
+// serve it.  Wave w of a workgroup owns row blocks RW*w .. RW*w + RW-1 of every piece it runs.
+// With b > 1 each piece stores fp32 partial sums per row and counts itself done, per wave slot,
+// on its row chunk; the wave that arrives last adds the b partials in split order.
 // ------------------------------------------------------------------------------------------
-// Waves per AQ2X8 workgroup (one workgroup per CU at M = 1, whose table fills the LDS): 8 or 16
-// for M = 1 (WQD_AQ1_WAVES), 16 for M > 1.  A piece has at most waves * RW row blocks, 64 at
-// M = 1.
-#ifndef WQD_AQ1_WAVES
-#define WQD_AQ1_WAVES 16
-#endif
-__host__ __device__ constexpr int aq_waves(int M) { return M == 1 ? WQD_AQ1_WAVES : 16; }
-#ifndef WQD_AQ1_RW_MAX
-#define WQD_AQ1_RW_MAX 8  // most 8-row blocks per wave per slice at M = 1 (8: two passes of 4)
-#endif
-// AQ2X8 planner charges, in tile loads: building a slice's table (M = 1) and a K-split's
-// partial round trip.
+constexpr int kAqWaves = 16;        // waves per AQ2X8 workgroup (one workgroup per CU)
+constexpr int kAqLutMaxSplits = 32; // most K-splits of a lookup-table (M = 1) projection
+constexpr int kAqMmaMaxSplits = 8;  // most K-splits of a matrix-core projection
+constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-table kernel
+constexpr int kAqMmaRW = 2;         // row blocks per wave per slice, matrix-core kernel
 #ifndef WQD_AQ_BUILD_CHARGE
-#define WQD_AQ_BUILD_CHARGE 16
-#endif
-#ifndef WQD_AQ_MAX_SPLITS
-#define WQD_AQ_MAX_SPLITS 64  // most K-splits of an AQ2X8 projection
+#define WQD_AQ_BUILD_CHARGE 8       // planner charge of a slice's table build, in tile loads
 #endif
 #ifndef WQD_AQ_SPLIT_CHARGE
-#define WQD_AQ_SPLIT_CHARGE 32
+#define WQD_AQ_SPLIT_CHARGE 32      // planner charge of a K-split (partial round trip), in tiles
 #endif
-// Waves per SIMD an AQ2X8 instance is compiled for (its VGPR budget).
-__host__ __device__ constexpr int aq_waves_per_simd(int M) { return M == 1 ? WQD_AQ1_WAVES / 4 : 4; }
-constexpr uint32_t kAqTag = 0x7FA5A5A5u;     // high word of a written partial slot (an sNaN,
-                                             // which no float arithmetic produces)
 
 struct AqDesc {
     const uint8_t *codes;     // tile plane
@@ -176,13 +163,14 @@ struct AqDesc {
     const uint16_t *cbk;      // codebooks C[2][256][8], fp16
     const uint16_t *x;        // activations, M rows of ldx fp16
     float *y;                 // output, M rows of ldy fp32
-    uint64_t *part;           // [M][b][Npad] tagged partials when b > 1
+    float *part;              // [M][b][Npad] partial sums when b > 1
+    int *cnt;                 // [a][kAqWaves] arrival counters when b > 1 (zero between calls)
     int64_t ldx, ldy;
-    int32_t N, G, KS, RB;     // rows, groups, K-slices, 8-row blocks holding rows < N
+    int32_t N, G, KS, RB;     // rows, groups, 32-group slices, 16-row blocks holding rows < N
     int32_t Npad;
     int32_t a, b, nrb, ns;    // pieces: a row chunks of nrb blocks x b splits of ns slices
-    int32_t npieces, off;     // a * b pieces; piece j runs on workgroup (j + off) % nwg
-    int32_t pad_;
+    int32_t npieces;          // a * b
+    int32_t off, nw;          // workgroups off .. off + nw - 1 (mod the launch's) serve the pieces
 };
 
 struct AqParams {
@@ -193,9 +181,9 @@ struct AqParams {
 };
 
 typedef void (*AqFn)(AqParams);
-// AQ2X8 kernel for M activation rows with RW 8-row blocks per wave per K-slice (M = 1: 2, 4 or
-// 8; M > 1: 1 or 2); bi: the batch-invariant instance (direct decode at every M, RW = 1).
-AqFn aq_fn(int M, int RW, bool bi = false);
+// AQ2X8 kernel instance: the lookup-table kernel (M = 1, lut) or the matrix-core kernel for M
+// activation rows (1 <= M <= 8; every batch-invariant call takes it).
+AqFn aq_fn(int M, bool lut);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies

@@ -1,40 +1,45 @@
-// AQ2X8 dequantize-and-multiply kernels (gfx950), on the transposed tile layout of layout.h: one
-// wavefront lane per group of 8 weights, and 8 rows per 16-byte lane load.
+// AQ2X8 dequantize-and-multiply kernels (gfx950) on the tile layout of layout.h: a tile is 16 rows
+// x 32 groups of 8 weights, and lane 32h + g holds the code pairs (c0, c1) of rows 8h..8h+7 of
+// group g.
 //
 // The weights of row n, group g are s_n * (C_0[c0] + C_1[c1]) with two 8-bit codes into two
-// codebooks of 256 fp16 8-vectors (trapetum "Benchmarks", the additive vector-quantization GEMV
-// section), so
+// codebooks of 256 fp16 8-vectors (trapetum "Benchmarks", "Additive vector-quantization GEMV
+// (AQLM-style, 2-bit)"), so
 //     y_n = s_n * sum_g ( T_0,g[c0(n,g)] + T_1,g[c1(n,g)] ),   T_b,g[c] = sum_j C_b[c][j] x[8g+j]:
-// a per-group lookup table built from the activations, after which only the codes are read.
+// a per-group lookup table built from the activations, after which only the codes are read.  The
+// same page keeps such group sums in f32 (its 1x16 kernel moved to f32 after fp16 group sums
+// drifted from the dequantized weights), and so do both kernels here: no intermediate value is
+// rounded to fp16.
 //
-// M = 1, lookup tables:
-//   * For one K-slice of 64 groups the workgroup builds T in LDS as dword (c*64 + g) holding the
-//     pair (T_0,g[c], T_1,g[c]) in fp16: 64 KiB.  T is the product C_b (256 x 8) . X (8 x 64),
-//     X[j][g] = x[8g+j], on the 4x4x4 matrix core: with 4 codebook rows broadcast as the A
-//     operand and each lane's own group activations as B, one pair of MFMAs (k = 0..3, 4..7)
-//     leaves T[c][g = lane] for 4 codes in 4 registers of lane g (exact fp16 products, fp32
-//     sums), already in table order.  Each wave builds 256/W codes of both codebooks.
-//   * Two tables alternate: the table of the next slice is built while the current one is read,
-//     with one workgroup barrier per slice.
-//   * Lane g reads only bank g, so the lookups never conflict: two LDS reads per 8 weights (the
-//     addresses made by one v_perm each from the code bytes) and one v_fma_mix that adds the low
-//     fp16 half of one word to the high half of the other in fp32.
-//   * The 64 lanes' terms of a row are summed by a transposed butterfly in a fixed order: per tile
-//     the permlane32 and permlane16 swap stages fold 8 rows x 64 lanes into 2 values per lane,
-//     which accumulate over the slices of a piece; the DPP stages finish the sum once per piece.
-// M = 2, one table for both rows: dword (b*256 + c)*64 + g holds the fp16 pair (T_b,g[c] of row 0,
-//   of row 1), 128 KiB, so it is single-buffered (a barrier, the build, a barrier per slice); the
-//   same two lookups per 8 weights give both rows' terms.
-// M = 3..8 (and batch-invariant calls), direct decode (at M = 3 and 4 the host runs row parts on
-//   the table kernels instead): the codebooks sit in LDS, each lane decodes
-//   its group's 8 rows (two 16-byte LDS reads and one packed fp16 add per row) and multiplies them
-//   with each activation row; the 8 row sums are reduced across lanes per tile.
+// Lookup-table kernel (M = 1):
+//   * For one slice of 32 groups the workgroup builds T in LDS, fp32, at dword c*64 + b*32 + g:
+//     64 KiB.  Two tables alternate: the table of the next slice is built while the current one
+//     is read, with one workgroup barrier per slice.
+//   * The build is T_b = C_b (256 x 8) . X (8 x 32), X[j][g] = x[8g+j]: one 32x32x8 matrix-core
+//     product per wave (16 waves: codebook w/8, codes 32(w%8)..+31), whose 16 result registers
+//     per lane are written as 16 dwords (exact fp16 products, fp32 sums).
+//   * Per row of a tile, lane 32h + g reads T_h[c_h] and T_(1-h)[c_(1-h)] of its group: in one LDS
+//     instruction the lanes of half 0 read codebook-0 entries (columns 0..31) and the lanes of
+//     half 1 codebook-1 entries (columns 32..63), so no two lanes meet in a bank.  Each address is
+//     one v_perm of the code word with a per-lane byte selector.  The two fp32 entries are added to
+//     the lane's 8 row sums, which are reduced over the 32 lanes of a half once per piece.
+// Matrix-core kernel (M = 1..8; every batch-invariant call takes it):
+//   * y = x W^T on the 16x16x32 fp16 matrix core: A = 16 activation rows (rows past M repeat row
+//     M-1 and are never stored) x 32 k (4 groups), B = 32 k x 16 weight rows, whose operand in
+//     lane 16q + n is the 8 fp16 values of codebook entry C_b[c_b(n, 4t + q)].  The two codebooks
+//     are two products into the same fp32 accumulators: every product is exact, every sum fp32.
+//   * The codebooks sit in LDS in 16 copies, entry e of copy j at ((b*256 + e)*16 + j)*16 bytes:
+//     lane 16q + n gathers from copy n, so the 16 lanes of one LDS pass hit 16 different 16-byte
+//     bank groups.
+//   * A tile goes through the wave's LDS staging area, from which each lane reads the 8 code pairs
+//     it needs (row n, groups 4t + q), 2 bytes each.  The activations of a slice are staged in
+//     LDS (double-buffered, one barrier per slice).
 //
-// Work: see AqDesc.  A workgroup walks its pieces in order, slice by slice; the loads of the next
-// slice (of the same or the next piece) are in flight while a slice is processed.  With b > 1
-// K-splits a piece stores one tagged 64-bit partial per row (no fence: a slot is either still zero or holds
-// the tag and the value), and once all of its own pieces are done each of the b workgroups of a
-// chunk adds the b partials, in split order, of its share of the chunk's rows.
+// Work (AqDesc): a workgroup walks its pieces in order, slice by slice; the tile loads of the next
+// two slices are in flight while a slice is processed.  Pieces with b > 1 store fp32 partials.
+// Once all of its pieces are done, each wave counts its slot of every split piece done, and the
+// wave that arrives last adds that slot's partials in split order: no workgroup ever waits for
+// another, and results are the same bits from run to run.
 #include <stddef.h>
 
 #include "gemv_impl.h"
@@ -43,7 +48,10 @@ namespace wqd {
 namespace {
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int W = kAqWaves;
 
 __device__ __forceinline__ float f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t u32(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -57,31 +65,27 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppRor8 = 0x128;         // row_ror:8 (lane i <-> i^8 within 16)
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
 
-// Sum over the 64 lanes of v[r] for each of 8 rows r, in a fixed order, in two stages.
-// fold_rows8: lanes l, l^32 and l^16 -> two values per lane, w[j] holding row j + 2*bit4 + 4*bit5
-// of the lane (summed over its 4 lanes {l, l^16, l^32, l^48}).
-__device__ __forceinline__ void fold_rows8(const float (&v)[8], float (&w)[2]) {
+// Sum over the 32 lanes of each half (lanes 32h .. 32h+31) of v[r], r < 8, in a fixed order (a
+// transposed butterfly).  On return lane l holds the sum of row (l >> 2) & 7 of its half.
+__device__ __forceinline__ float reduce_half8(const float (&v)[8], int lane) {
     float u[4];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {  // lanes l, l^32: row r in lanes 0-31, row r+4 in lanes 32-63
-        const auto s = __builtin_amdgcn_permlane32_swap(u32(v[r]), u32(v[r + 4]), false, false);
+    for (int r = 0; r < 4; r++) {  // lanes l, l^16: row r + 4*bit4
+        const auto s = __builtin_amdgcn_permlane16_swap(u32(v[r]), u32(v[r + 4]), false, false);
         u[r] = f32(s[0]) + f32(s[1]);
     }
+    const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+    float w[2];
 #pragma unroll
-    for (int r = 0; r < 2; r++) {  // lanes l, l^16: row r + 2*bit4 + 4*bit5
-        const auto s = __builtin_amdgcn_permlane16_swap(u32(u[r]), u32(u[r + 2]), false, false);
-        w[r] = f32(s[0]) + f32(s[1]);
+    for (int r = 0; r < 2; r++) {  // lanes l, l^8: row r + 2*bit3 + 4*bit4
+        const float keep = b3 ? u[r + 2] : u[r], give = b3 ? u[r] : u[r + 2];
+        w[r] = keep + dpp<kDppRor8>(give);
     }
-}
-// finish_rows8: the rest of the sum (lanes l^8, then the 8 lanes of an octet).  On return lanes
-// 8r..8r+7 all hold the sum of row r.
-__device__ __forceinline__ float finish_rows8(const float (&w)[2], int lane) {
-    const float x0 = w[0] + dpp<kDppRor8>(w[0]);  // lanes l, l^8
-    const float x1 = w[1] + dpp<kDppRor8>(w[1]);
-    float z = (lane & 8) ? x1 : x0;               // row bit3 + 2*bit4 + 4*bit5
-    z = z + dpp<kDppXor1>(z);
+    // lanes i, 7-i within 8 (bit 2 differs): row bit2 + 2*bit3 + 4*bit4
+    const float keep = b2 ? w[1] : w[0], give = b2 ? w[0] : w[1];
+    float z = keep + dpp<kDppHalfMirror>(give);
+    z = z + dpp<kDppXor1>(z);  // the 4 lanes of a quad hold the same row
     z = z + dpp<kDppXor2>(z);
-    z = z + dpp<kDppHalfMirror>(z);
     return z;
 }
 
@@ -98,8 +102,7 @@ __device__ __forceinline__ T load_uniform(const T *p) {
 }
 
 // Descriptor p, read with scalar loads either from the table or, for a single projection, from
-// the kernel argument itself (AqParams::d0 sits at the start of the kernarg segment).  Choosing
-// between two pointers rather than two structs keeps the descriptor out of scratch memory.
+// the kernel argument itself (AqParams::d0 sits at the start of the kernarg segment).
 __device__ __forceinline__ AqDesc get_desc(const AqParams &P, int p) {
     static_assert(offsetof(AqParams, d0) == 0, "d0 leads the kernel arguments");
     p = min(max(p, 0), P.ndesc - 1);  // never read outside the table
@@ -112,9 +115,10 @@ __device__ __forceinline__ AqDesc get_desc(const AqParams &P, int p) {
 struct Piece {
     int p;          // projection; == ndesc past the end of the list
     int j;          // piece index within the projection
-    int rb0, rb1;   // 8-row blocks [rb0, rb1)
-    int s0, s1;     // K-slices [s0, s1)
-    int split;
+    int nw;         // workgroups serving the projection (piece stride)
+    int chunk, split;
+    int rb0, rb1;   // 16-row blocks [rb0, rb1)
+    int s0, s1;     // 32-group slices [s0, s1)
 };
 
 // The first piece of this workgroup at or after (projection p, piece j); j < 0: start of p.
@@ -124,14 +128,16 @@ __device__ __forceinline__ Piece find_piece(const AqParams &P, int wg, int p, in
         if (j < 0) {
             j = (wg - D.off) % P.nwg;
             if (j < 0) j += P.nwg;
+            if (j >= D.nw) j = D.npieces;  // not one of the projection's workgroups
         }
         if (j < D.npieces) {
             Piece q;
             q.p = p;
             q.j = j;
+            q.nw = D.nw;
             q.split = j / D.a;
-            const int chunk = j - q.split * D.a;
-            q.rb0 = chunk * D.nrb;
+            q.chunk = j - q.split * D.a;
+            q.rb0 = q.chunk * D.nrb;
             q.rb1 = min(D.RB, q.rb0 + D.nrb);
             q.s0 = q.split * D.ns;
             q.s1 = min(D.KS, q.s0 + D.ns);
@@ -143,501 +149,281 @@ __device__ __forceinline__ Piece find_piece(const AqParams &P, int wg, int p, in
     Piece q;
     q.p = P.ndesc;
     q.j = 0;
-    q.rb0 = q.rb1 = q.s0 = q.s1 = q.split = 0;
+    q.nw = 1;
+    q.chunk = q.split = q.rb0 = q.rb1 = q.s0 = q.s1 = 0;
     return q;
 }
 __device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Piece &q) {
-    return find_piece(P, wg, q.p, q.j + P.nwg);
+    return find_piece(P, wg, q.p, q.j + q.nw);
 }
 
-// Row block (from the piece's first) of tile i of wave wid in pass `pass` of a slice: a pass covers
-// W * RW consecutive row blocks, RW consecutive ones per wave (each wave's tiles of a slice are
-// one contiguous run of RW KiB; wave-interleaved tiles measured 2.5% slower on the 70B MLP).
-template <int RW, int W>
-__device__ __forceinline__ int tile_rb(int wid, int i, int pass) {
-    return RW * (wid + W * pass) + i;
-}
-
-// Tile loader running ahead of the processing.  It walks units (piece, slice, pass): each slice
-// of a piece is read in NP passes of RW tiles per wave (tile_rb), so one table serves
-// NP * W * RW row blocks.
-template <int RW, int W, int NP>
+// Tile loader running ahead of the processing: one unit is one slice of the current piece; wave
+// wid loads row blocks rb0 + RW*wid .. + RW-1 of it.
+template <int RW>
 struct Loader {
-    const uint8_t *base;   // code plane (wave-uniform; the lane's 16 bytes are added at the load)
-    int64_t s_stride;      // bytes between slices (R8 = Npad/8 KiB)
+    const uint8_t *base;   // code plane (the lane's 16 bytes are added at the load)
+    int64_t s_stride;      // bytes between slices (Npad/16 KiB)
     int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
     int rb0, rb1;          // the piece's row blocks
     int wv;                // this wave
-    const uint16_t *x, *cbk;  // operands of the slice's table / activation stage
+    const uint16_t *x, *cbk;
     int64_t ldx;
     int G;
-    Piece q;  // current piece
-    int s, pass;
+    Piece q;               // current piece
+    int s;                 // current slice
     bool done;
 
-    // (the next piece is looked up only when this one ends: at the start of the kernel, one
-    // descriptor read stands before the first loads instead of two)
-    __device__ __forceinline__ void setup(const AqParams &P, const Piece n, int wg, int wid, int lane) {
+    __device__ __forceinline__ void setup(const AqParams &P, const Piece n, int wid) {
         q = n;
         s = n.s0;
-        pass = 0;
         const AqDesc D = get_desc(P, n.p);
         base = D.codes;
-        s_stride = int64_t(D.Npad / 8) * 1024;
+        s_stride = int64_t(D.Npad / 16) * 1024;
         x = D.x;
         cbk = D.cbk;
         ldx = D.ldx;
         G = D.G;
         s_max = D.KS - 1;
-        rb_max = D.Npad / 8 - 1;
+        rb_max = D.Npad / 16 - 1;
         rb0 = n.rb0;
-        wv = wid;
         rb1 = n.rb1;
+        wv = wid;
     }
-    // A missing tile (past the piece, or past the end of the list) still takes its place in the
-    // ring (every load stays unconditional): it reads 1 KiB of the codebooks, which the table
-    // build keeps in L2, instead of HBM.
+    // A missing tile (past the piece, or past the end of the work) still takes its place in the
+    // ring, so every load stays unconditional: it reads 1 KiB of the codebooks instead.
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        const int r = rb0 + tile_rb<RW, W>(wv, i, pass);
+        const int r = rb0 + RW * wv + i;
         return (done || r >= rb1) ? reinterpret_cast<const uint8_t *>(cbk)
                                   : base + int64_t(min(s, s_max)) * s_stride + int64_t(min(r, rb_max)) * 1024;
     }
-    // After the tiles of a unit: step to the next pass, slice or piece.
-    __device__ __forceinline__ void step(const AqParams &P, int wg, int wid, int lane) {
+    __device__ __forceinline__ void step(const AqParams &P, int wg, int wid) {
         if (done) return;
-        if (++pass < NP) return;
-        pass = 0;
         if (++s < q.s1) return;
         const Piece qn = next_piece(P, wg, q);
         if (qn.p >= P.ndesc) {
             done = true;
             s = q.s1 - 1;
         } else {
-            setup(P, qn, wg, wid, lane);
+            setup(P, qn, wid);
         }
     }
 };
 
-constexpr int kSpinMax = 1 << 22;   // polls of a missing partial before giving up (NaN result)
-constexpr int kFinLoads = 8;        // partial loads in flight per row in the finalize (32 measured slower)
+template <int RW>
+__device__ __forceinline__ void load_tiles(const Loader<RW> &ld, u32x4 (&t)[RW], int lane) {
+#pragma unroll
+    for (int i = 0; i < RW; i++)
+        t[i] = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)(ld.addr(i) + lane * 16));
+}
+template <int RW>
+__device__ __forceinline__ void settle_tiles(u32x4 (&t)[RW]) {
+#pragma unroll
+    for (int i = 0; i < RW; i++) __asm__ volatile("" ::"v"(t[i]));
+}
 
-// Adds the b tagged partials of rows of the pieces this workgroup ran, then scales and writes y
-// and clears the slots.  The rows of a row chunk are shared out over its b splits: the workgroup
-// that ran split t finalizes rows [t*R/b, (t+1)*R/b) of the chunk's R rows.  A row takes L lanes
-// (L = b/8 rounded up to a power of two): lane j of the row loads partials 8j..8j+7 in one round
-// and adds them in split order, then the L lane sums are combined in a fixed tree.  The shares of
-// all of the workgroup's pieces are finalized at once: each share takes whole waves (its rows x L
-// lanes, rounded up to 64), numbered over the pieces in order, and wave w takes numbers w, w + W,
-// ..., so the partial loads of the pieces are in flight together rather than one memory round
-// trip per piece.  Runs after all of the workgroup's own pieces; a partial not yet written is
-// polled again (bounded), and its writer never waits on another workgroup, so the wait ends.
-template <int M, int W>
-__device__ __forceinline__ void finalize(const AqParams &P, int wg, int wid, int lane) {
-    int first = 0;  // first wave number of the piece's share
-    for (Piece q = find_piece(P, wg, 0, -1); q.p < P.ndesc; q = next_piece(P, wg, q)) {
-        const AqDesc D = get_desc(P, q.p);
-        if (D.b == 1) continue;
-        int L = 1;
-        while (L * kFinLoads < D.b) L *= 2;  // (b <= 64 keeps L <= 8)
-        const int r0 = q.rb0 * 8, R = min((q.rb1 - q.rb0) * 8, D.N - r0);
-        const int lo = r0 + (R * q.split) / D.b, hi = r0 + (R * (q.split + 1)) / D.b;
-        const int nw = ((hi - lo) * L + 63) / 64;  // waves of this share
-        const int sub = lane & (L - 1);            // this lane's group of partials
-        const int t0 = sub * kFinLoads;
-        // wave numbers [first, first + nw) are this share's; wave wid takes those = wid mod W
-        for (int v = first + ((wid - first) % W + W) % W; v < first + nw; v += W) {
-            const int k = ((v - first) * 64 + lane) / L;  // row of the share (L lanes per row)
-            const bool live = k < hi - lo;                // (every lane still takes the combine)
-            const int row = lo + min(k, hi - lo - 1);
-            const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
+// ------------------------------------------------------------------------------------------
+// Split pieces: arrival and the sum of the partials.
+// ------------------------------------------------------------------------------------------
+
+// Adds the b partials (in split order) of this wave's rows of piece q, scales them and writes y,
+// then clears the wave's counter.  Items (activation row m, row block i, row rr) are taken by the
+// lanes in turn; every partial load of the wave is in flight at once (at most BMAX per item).
+template <int M, int RW, int BMAX>
+__device__ __forceinline__ void add_splits(const AqDesc &D, const Piece &q, int wid, int lane) {
+    constexpr int ITEMS = M * RW * 16;
+    constexpr int NI = (ITEMS + 63) / 64;
+    float v[NI][BMAX];
+    int rowv[NI], mv[NI];
+    bool live[NI];
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                uint64_t *slot = D.part + (int64_t(m) * D.b) * D.Npad + row;
-                uint64_t v8[kFinLoads];
+    for (int it = 0; it < NI; it++) {
+        const int item = lane + 64 * it;
+        const int m = item / (RW * 16), rem = item - m * (RW * 16);
+        const int rb = q.rb0 + RW * wid + rem / 16, row = 16 * rb + (rem & 15);
+        live[it] = item < ITEMS && rb < q.rb1 && row < D.N;
+        rowv[it] = live[it] ? row : 0;
+        mv[it] = live[it] ? m : 0;
 #pragma unroll
-                for (int j = 0; j < kFinLoads; j++)
-                    v8[j] = (live && t0 + j < D.b) ? __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                                   : (uint64_t(kAqTag) << 32);
-                float sum = 0.f;
-                int ok = 1;
+        for (int j = 0; j < BMAX; j++)
+            v[it][j] = __hip_atomic_load(as_global(D.part + (int64_t(mv[it]) * D.b + min(j, D.b - 1)) * D.Npad + rowv[it]),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
-                for (int j = 0; j < kFinLoads; j++) {
-                    int spins = 0;
-                    while (uint32_t(v8[j] >> 32) != kAqTag && spins < kSpinMax) {
-                        __builtin_amdgcn_s_sleep(2);
-                        v8[j] = __hip_atomic_load(as_global(slot + int64_t(t0 + j) * D.Npad), __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-                        spins++;
-                    }
-                    ok &= uint32_t(v8[j] >> 32) == kAqTag;
-                    if (t0 + j < D.b) sum += f32(uint32_t(v8[j]));  // split order
-                }
-                // combine the L lanes of the row: pairs, then pairs of pairs (a fixed order)
-                for (int o = 1; o < L; o <<= 1) {
-                    sum += __shfl_xor(sum, o);
-                    ok &= __shfl_xor(ok, o);
-                }
-                if (live && sub == 0) gst(D.y + int64_t(m) * D.ldy + row, ok ? sum * sc : __builtin_nanf(""));
-                if (live)
-                    for (int j = 0; j < kFinLoads && t0 + j < D.b; j++)
-                        __hip_atomic_store(as_global(slot + int64_t(t0 + j) * D.Npad), uint64_t(0), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; it < NI; it++) {
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < BMAX; j++)
+            if (j < D.b) sum += v[it][j];
+        if (live[it]) {
+            const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + rowv[it]));
+            gst(D.y + int64_t(mv[it]) * D.ldy + rowv[it], sum * sc);
+        }
+    }
+    if (lane == 0) __hip_atomic_store(as_global(D.cnt + q.chunk * W + wid), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After all of the workgroup's pieces: the wave counts its slot of each split piece done (up to 8
+// atomics in flight at once) and adds the partials of the slots where it arrived last.  The
+// partial stores of the pieces have completed before the counts are taken.
+template <int M, int RW, int BMAX>
+__device__ __forceinline__ void finish(const AqParams &P, int wg, int wid, int lane) {
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    Piece q = find_piece(P, wg, 0, -1);
+    while (q.p < P.ndesc) {
+        const Piece q0 = q;
+        int old[8];
+        int n = 0;
+        static_for<8>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            old[k] = -1;
+            while (q.p < P.ndesc && get_desc(P, q.p).b == 1) q = next_piece(P, wg, q);
+            if (q.p < P.ndesc) {
+                const AqDesc D = get_desc(P, q.p);
+                int o = 0;
+                if (lane == 0)
+                    o = __hip_atomic_fetch_add(as_global(D.cnt + q.chunk * W + wid), 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                old[k] = o;
+                n++;
+                q = next_piece(P, wg, q);
             }
-        }
-        first += nw;
+        });
+        Piece r = q0;
+        static_for<8>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if (k < n) {
+                while (get_desc(P, r.p).b == 1) r = next_piece(P, wg, r);
+                const AqDesc D = get_desc(P, r.p);
+                if (__builtin_amdgcn_readfirstlane(old[k]) == D.b - 1) add_splits<M, RW, BMAX>(D, r, wid, lane);
+                r = next_piece(P, wg, r);
+            }
+        });
+        while (q.p < P.ndesc && get_desc(P, q.p).b == 1) q = next_piece(P, wg, q);
     }
 }
 
-template <int M, bool LUT>
-struct LdsWords {
-    static constexpr int value = LUT ? 2 * 256 * 64 : 2048 + 256 * M;
+// ------------------------------------------------------------------------------------------
+// Lookup-table kernel, M = 1.  RW: 16-row blocks per wave per slice (a piece has at most W*RW).
+// One workgroup per CU (the two tables take 128 KiB of LDS), 4 waves per SIMD.
+// ------------------------------------------------------------------------------------------
+struct LutOps {
+    u32x2 A;   // this wave's codebook rows (A operand of the table build)
+    u32x2 B;   // the slice's activations of this lane's group (B operand)
+    int gval;  // groups of the slice inside K
 };
 
-// ------------------------------------------------------------------------------------------
-// The kernel.  RW: 8-row blocks per wave per slice (a piece has at most W * RW of them).
-//
-// Pipeline: the tiles (RW per wave) and operands of the next two slices are in flight while a
-// slice is processed.  At the start of a slice the wave waits for that slice's loads (the oldest
-// it has in flight), then issues the loads of the slice two ahead, then builds the table and
-// processes.  With W * RW = 64 row blocks a workgroup keeps about 128 KiB in flight.
-// ------------------------------------------------------------------------------------------
-
-// Per-slice operands of the table build (M = 1: activation pairs of the two 32-group blocks and
-// this wave's two codebook rows) or of the stage (M > 1: one activation row, a codebook part).
-struct SliceOps {
-    u32x2 B[2], A[2];
-    u32x2 B1[2];  // M = 2 tables: the second activation row's halves
-    u32x4 X, C;
-    int gval;  // groups of the slice inside K (M = 1: the table masks the rest)
-};
-
-// fp32 T_0 (low half of d0) + T_1 (high half of d1), both fp16 table entries.
-__device__ __forceinline__ float add_lo_hi(uint32_t d0, uint32_t d1) {
-    float r;
-    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
-    return r;
-}
-// fp32 sums of the low halves and of the high halves of two fp16 pairs.
-__device__ __forceinline__ float add_lo_lo(uint32_t d0, uint32_t d1) {
-    float r;
-    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
-    return r;
-}
-__device__ __forceinline__ float add_hi_hi(uint32_t d0, uint32_t d1) {
-    float r;
-    __asm__("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(d0), "v"(d1));
-    return r;
-}
-// fp16 pair (a, b), round to nearest even.
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
-}
-
-// M = 1: the 128 KiB table allows one workgroup per CU, i.e. 2 waves per SIMD, so each wave may
-// use 256 VGPRs (the compiler would otherwise aim for more waves than can ever be resident).
-// BI: the batch-invariant instance, which takes the direct decode at every M (M = 1 included), so
-// that a row's arithmetic does not depend on M.
-template <int M, int RW, int NP, bool BI = false>
-__global__ __launch_bounds__(aq_waves(M) * 64) __attribute__((amdgpu_waves_per_eu(1, aq_waves_per_simd(M))))
-void aq_kernel(AqParams P) {
-    constexpr int W = aq_waves(M);  // waves per workgroup
-    constexpr bool LUT = (M <= 2 && !BI);  // lookup tables (else the direct decode)
-    constexpr bool LUT2 = LUT && M == 2;   // one table of both activation rows, single-buffered
-    __shared__ uint32_t lds[LdsWords<M, LUT>::value];
+template <int RW>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_lut_kernel(AqParams P) {
+    __shared__ uint32_t lds[2 * 256 * 64];
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int wg = blockIdx.x;
+    const int h = lane >> 5, g = lane & 31;
 
     Piece pp = find_piece(P, wg, 0, -1);  // piece being processed
     if (pp.p >= P.ndesc) return;          // no work for this workgroup (same for all its waves)
     int ps = pp.s0;                       // slice being processed
+    AqDesc pd = get_desc(P, pp.p);
 
-    AqDesc pd = get_desc(P, pp.p);        // its descriptor
-
-    Loader<RW, W, NP> ld;
-    static_assert(LUT || NP == 1, "passes share a lookup table (M = 1)");
+    Loader<RW> ld;
     ld.done = false;
-    ld.setup(P, pp, wg, wid, lane);
+    ld.setup(P, pp, wid);
 
-    // M = 1 table share of this wave: NQ quads of codes (4NQ codes from 4NQ*wid) of both
-    // codebooks.  Its MFMA A operands hold 4NQ blocks (codebook, quad, k-half) of 4 codebook
-    // rows: block n = 16r + b sits in lanes 4b..4b+3 of A[r], as codebook n / 2NQ, quad
-    // (n % 2NQ) / 2, k-half n % 2.
-    constexpr int NQ = 64 / W;
-    static_assert(!LUT || (4 * NQ <= 32 && W * NQ == 64), "the A operands hold the wave's blocks");
+    // LDS byte address of a lookup: (tb << 16) | (code << 8) | (b << 7) | (g << 2), b the codebook.
+    // Byte 0 and byte 2 come from lk, byte 1 is the code byte the selector picks from the word:
+    // word t holds (c0, c1) of rows 2t and 2t+1.
+    const uint32_t lkA0 = (uint32_t(g) << 2) | (uint32_t(h) << 7);
+    const uint32_t lkB0 = (uint32_t(g) << 2) | (uint32_t(1 - h) << 7);
+    const uint32_t selA[2] = {0x0c020000u | ((4u + h) << 8), 0x0c020000u | ((6u + h) << 8)};
+    const uint32_t selB[2] = {0x0c020000u | ((5u - h) << 8), 0x0c020000u | ((7u - h) << 8)};
 
-    // Issue the loads of the loader's slice: operands first, then the RW tiles; step the loader.
-    // Every load is unconditional with a clamped address (a load under a lane condition makes
-    // the compiler wait for it at once); groups past G are zeroed where the operands are used.
-    auto load_slice = [&](u32x4 (&t)[RW], SliceOps &o) __attribute__((always_inline)) {
-        if constexpr (LUT) {
-            o.gval = ld.G - ld.s * 64;
-            const int g = min(ld.s * 64 + lane, ld.G - 1);  // lane = group
+    auto load_slice = [&](u32x4 (&t)[RW], LutOps &o) __attribute__((always_inline)) {
+        const int cb = wid >> 3, code = 32 * (wid & 7) + g;
+        o.A = gld<u32x2>(ld.cbk + (int64_t(cb) * 256 + code) * 8 + 4 * h);
+        o.gval = ld.G - ld.s * 32;
+        const int gi = min(ld.s * 32 + g, ld.G - 1);
+        o.B = gld<u32x2>(ld.x + int64_t(gi) * 8 + 4 * h);
+        load_tiles(ld, t, lane);
+        ld.step(P, wg, wid);
+    };
+    auto settle_ops = [&](LutOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.A), "v"(o.B)); };
+
+    // The table of a slice into buffer tb: wave w computes T_(w/8)[32(w%8) .. +31][g = 0..31].
+    auto build = [&](const LutOps &o, int tb) __attribute__((always_inline)) {
+        const u32x2 B = g < o.gval ? o.B : u32x2{0u, 0u};  // groups past K read as zero
+        f32x16 z;
 #pragma unroll
-            for (int h = 0; h < 2; h++) o.B[h] = gld<u32x2>(ld.x + int64_t(g) * 8 + 4 * h);
-            if constexpr (LUT2) {
+        for (int v = 0; v < 16; v++) z[v] = 0.f;
+        const f32x16 D = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A), __builtin_bit_cast(h4, B), z, 0, 0, 0);
+        uint32_t *tab = lds + tb * (256 * 64) + (wid >> 3) * 32 + g;
 #pragma unroll
-                for (int h = 0; h < 2; h++) o.B1[h] = gld<u32x2>(ld.x + ld.ldx + int64_t(g) * 8 + 4 * h);
+        for (int v = 0; v < 16; v++) {  // register v of lane l: code row 8(v/4) + 4(l/32) + v%4
+            const int code = 32 * (wid & 7) + 8 * (v >> 2) + 4 * h + (v & 3);
+            tab[code * 64] = u32(D[v]);
+        }
+    };
+
+    float acc[RW][8];
+#pragma unroll
+    for (int i = 0; i < RW; i++)
+#pragma unroll
+        for (int r = 0; r < 8; r++) acc[i][r] = 0.f;
+
+    // One tile: the 8 rows of this lane's half, its group.
+    auto process = [&](const u32x4 &v, float (&a)[8], uint32_t lkA, uint32_t lkB) __attribute__((always_inline)) {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                const uint32_t ea = lds_word(lds, __builtin_amdgcn_perm(w4[t], lkA, selA[p]));
+                const uint32_t eb = lds_word(lds, __builtin_amdgcn_perm(w4[t], lkB, selB[p]));
+                a[2 * t + p] += f32(ea);
+                a[2 * t + p] += f32(eb);
             }
-#pragma unroll
-            for (int r = 0; r < (4 * NQ + 15) / 16; r++) {
-                const int n = min(16 * r + (lane >> 2), 4 * NQ - 1);
-                const int cb = n / (2 * NQ), quad = (n % (2 * NQ)) / 2, half = n % 2;
-                const int code = wid * 4 * NQ + 4 * quad + (lane & 3);
-                o.A[r] = gld<u32x2>(ld.cbk + (int64_t(cb) * 256 + code) * 8 + 4 * half);
-            }
-        } else {
-            const int g = min(ld.s * 64 + lane, ld.G - 1);
-            o.X = gld<u32x4>(ld.x + int64_t(min(wid, M - 1)) * ld.ldx + int64_t(g) * 8);
-            o.C = gld<u32x4>(reinterpret_cast<const uint8_t *>(ld.cbk) + (threadIdx.x & 511) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < RW; i++) {  // uniform tile base + the lane's 16 bytes
-#if WQD_NT_CODES
-            t[i] = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)(ld.addr(i) + lane * 16));
-#else
-            t[i] = gld<u32x4>(ld.addr(i) + lane * 16);
-#endif
-        }
-        ld.step(P, wg, wid, lane);
-    };
-    // Wait for a slice's tiles and operands: an empty asm statement that reads them.
-    auto settle_tiles = [&](u32x4 (&t)[RW]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < RW; i++) __asm__ volatile("" ::"v"(t[i]));
-    };
-    auto settle_ops = [&](SliceOps &o) __attribute__((always_inline)) {
-        if constexpr (LUT) {
-            __asm__ volatile("" ::"v"(o.B[0]), "v"(o.B[1]), "v"(o.A[0]), "v"(o.A[1]));
-            if constexpr (LUT2) __asm__ volatile("" ::"v"(o.B1[0]), "v"(o.B1[1]));
-        } else {
-            __asm__ volatile("" ::"v"(o.X), "v"(o.C));
         }
     };
 
-    // per row block and activation row: two folded row sums (see fold_rows8), finished once per
-    // piece
-    constexpr int NACC = 2 * M;
-    float acc[NP][RW][NACC];
-#pragma unroll
-    for (int p = 0; p < NP; p++)
-#pragma unroll
-        for (int i = 0; i < RW; i++)
-#pragma unroll
-            for (int r = 0; r < NACC; r++) acc[p][i][r] = 0.f;
-
-    int tb = 0;   // M = 1: table buffer of the slice being processed
-
-    // Piece epilogue: row sums -> y (b == 1) or this split's tagged partial slots.
+    // Piece epilogue: row sums -> y (b == 1) or this split's partials.
     auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
 #pragma unroll
-        for (int pi = 0; pi < NP * RW; pi++) {
-            const int p = pi / RW, i = pi % RW;
-            const int rb = q.rb0 + tile_rb<RW, W>(wid, i, p);
-            const int row = rb * 8 + (lane >> 3);
-            const bool ok = (lane & 7) == 0 && rb < q.rb1 && row < D.N && q.split < D.b;
-#pragma unroll
-            for (int m = 0; m < M; m++) {
-                const float w2[2] = {acc[p][i][2 * m], acc[p][i][2 * m + 1]};
-                const float z = finish_rows8(w2, lane);
-                if (ok) {
+        for (int i = 0; i < RW; i++) {
+            const int rb = q.rb0 + RW * wid + i;
+            if (rb < q.rb1) {
+                const float z = reduce_half8(acc[i], lane);
+                const int row = 16 * rb + 8 * h + ((lane >> 2) & 7);
+                if ((lane & 3) == 0 && row < D.N) {
                     if (D.b == 1) {
-                        // (the scale is loaded here, not ahead: an early load's result would be
-                        // waited for behind every tile in flight)
                         const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
-                        gst(D.y + int64_t(m) * D.ldy + row, z * sc);
+                        gst(D.y + row, z * sc);
                     } else {
-                        const uint64_t v = (uint64_t(kAqTag) << 32) | u32(z);
-                        __hip_atomic_store(as_global(D.part + (int64_t(m) * D.b + q.split) * D.Npad + row), v, __ATOMIC_RELAXED,
+                        __hip_atomic_store(as_global(D.part + int64_t(q.split) * D.Npad + row), z, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
 #pragma unroll
-            for (int r = 0; r < NACC; r++) acc[p][i][r] = 0.f;
+            for (int r = 0; r < 8; r++) acc[i][r] = 0.f;
         }
     };
 
-    // M = 1: build the table of a slice (its operands o) into table buffer tb.
-    auto build_table = [&](const SliceOps &o, int tb) __attribute__((always_inline)) {
-        const bool in = lane < o.gval;  // groups past K read as zero
-        const u32x2 B0 = in ? o.B[0] : u32x2{0u, 0u}, B1 = in ? o.B[1] : u32x2{0u, 0u};
-        uint32_t *tab = lds + tb * (256 * 64);
-        if constexpr (LUT2) {
-            // dword (cb*256 + c)*64 + g holds (T_cb[c] for row 0, for row 1) of group g
-            const u32x2 R0 = in ? o.B1[0] : u32x2{0u, 0u}, R1 = in ? o.B1[1] : u32x2{0u, 0u};
-            static_for<NQ>([&](auto qc) {
-                constexpr int q = decltype(qc)::value;
-                static_for<2>([&](auto cc) {
-                    constexpr int cb = decltype(cc)::value;
-                    constexpr int n0 = cb * 2 * NQ + 2 * q, n1 = n0 + 1;
-                    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const f32x4 D0 = mfma_xw<n1 % 16>(o.A[n1 / 16], B1, mfma_xw<n0 % 16>(o.A[n0 / 16], B0, z));
-                    const f32x4 D1 = mfma_xw<n1 % 16>(o.A[n1 / 16], R1, mfma_xw<n0 % 16>(o.A[n0 / 16], R0, z));
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        tab[(cb * 256 + wid * 4 * NQ + 4 * q + i) * 64 + lane] = pack_h2(D0[i], D1[i]);
-                });
-            });
-            return;
-        }
-        static_for<NQ>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            f32x4 D[2];
-            static_for<2>([&](auto cc) {
-                constexpr int cb = decltype(cc)::value;
-                constexpr int n0 = cb * 2 * NQ + 2 * q, n1 = n0 + 1;  // k-halves 0 and 1
-                const f32x4 d = mfma_xw<n0 % 16>(o.A[n0 / 16], B0, f32x4{0.f, 0.f, 0.f, 0.f});
-                D[cb] = mfma_xw<n1 % 16>(o.A[n1 / 16], B1, d);
-            });
-            // register i of lane g: T_b[code 4NQ*wid + 4q + i][group g]
-#pragma unroll
-            for (int i = 0; i < 4; i++) tab[(wid * 4 * NQ + 4 * q + i) * 64 + lane] = pack_h2(D[0][i], D[1][i]);
-        });
-    };
-
-    // M > 1: stage the activations of a slice.
-    auto slice_start = [&](const SliceOps &o) __attribute__((always_inline)) {
-        const int G = pd.G;
-        if constexpr (LUT) {
-        } else {
-            const bool in = ps * 64 + lane < G;
-            const u32x4 X = in ? o.X : u32x4{0u, 0u, 0u, 0u};
-            lds_barrier();  // every wave is done with the previous stage
-            u32x4 *cbl = reinterpret_cast<u32x4 *>(lds);
-            u32x4 *xl = cbl + 512;
-            if (threadIdx.x < 512) cbl[threadIdx.x] = o.C;
-            if (wid < M) xl[wid * 64 + lane] = X;  // (waves >= M loaded a copy of row M-1)
-            lds_barrier();
-        }
-    };
-
-    // One tile: this lane's group for 8 rows of row block i (M = 1: lk selects the table).
-    auto process = [&](const u32x4 &v, float (&a)[NACC], uint32_t lk) __attribute__((always_inline)) {
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (LUT2) {
-            // codebook 0 entries in table half 0, codebook 1 in half 1 (byte 2 of the address);
-            // each dword gives the term of both activation rows
-            const uint32_t lk1 = lk | 0x10000u;
-            float v0[8], v1[8];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const uint32_t d0 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk, 0x0c020400u));
-                const uint32_t d1 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk1, 0x0c020500u));
-                const uint32_t d2 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk, 0x0c020600u));
-                const uint32_t d3 = lds_word(lds, __builtin_amdgcn_perm(w4[t], lk1, 0x0c020700u));
-                v0[2 * t] = add_lo_lo(d0, d1);
-                v1[2 * t] = add_hi_hi(d0, d1);
-                v0[2 * t + 1] = add_lo_lo(d2, d3);
-                v1[2 * t + 1] = add_hi_hi(d2, d3);
-            }
-            float w[2];
-            fold_rows8(v0, w);
-            a[0] += w[0];
-            a[1] += w[1];
-            fold_rows8(v1, w);
-            a[2] += w[0];
-            a[3] += w[1];
-        } else if constexpr (LUT) {
-            float v[8];
-#pragma unroll
-            for (int t = 0; t < 4; t++) {  // word t: (c0, c1) of rows 2t and 2t+1
-                // address (tb*256 + c)*256 + 4*lane: byte 0 from lk, byte 1 the code, byte 2 tb
-                const uint32_t a0 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020400u);
-                const uint32_t a1 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020500u);
-                const uint32_t a2 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020600u);
-                const uint32_t a3 = __builtin_amdgcn_perm(w4[t], lk, 0x0c020700u);
-                v[2 * t] = add_lo_hi(lds_word(lds, a0), lds_word(lds, a1));
-                v[2 * t + 1] = add_lo_hi(lds_word(lds, a2), lds_word(lds, a3));
-            }
-            float w[2];
-            fold_rows8(v, w);
-            a[0] += w[0];
-            a[1] += w[1];
-        } else {
-            // decode the 8 rows of this lane's group once, then take the activation rows one at a
-            // time (staged in LDS), folding each row's 64 lane terms to two per lane
-            const u32x4 *cbl = reinterpret_cast<const u32x4 *>(lds);
-            const u32x4 *xl = cbl + 512;
-            uint32_t wv[8][4];
-#pragma unroll
-            for (int r = 0; r < 8; r++) {
-                const uint32_t c0 = (w4[r >> 1] >> (16 * (r & 1))) & 0xFFu;
-                const uint32_t c1 = (w4[r >> 1] >> (16 * (r & 1) + 8)) & 0xFFu;
-                const u32x4 E0 = cbl[c0], E1 = cbl[256 + c1];
-                const uint32_t e0[4] = {E0.x, E0.y, E0.z, E0.w}, e1[4] = {E1.x, E1.y, E1.z, E1.w};
-#pragma unroll
-                for (int k = 0; k < 4; k++) wv[r][k] = __builtin_bit_cast(uint32_t, as_h2(e0[k]) + as_h2(e1[k]));
-            }
-#pragma unroll
-            for (int m = 0; m < M; m++) {
-                const u32x4 X = xl[m * 64 + lane];
-                const uint32_t xw[4] = {X.x, X.y, X.z, X.w};
-                float val[8];
-#pragma unroll
-                for (int r = 0; r < 8; r++) {
-                    float sm = 0.f;
-#pragma unroll
-                    for (int k = 0; k < 4; k++) sm = dot2(wv[r][k], xw[k], sm);
-                    val[r] = sm;
-                }
-                float w2[2];
-                fold_rows8(val, w2);
-                a[2 * m] += w2[0];
-                a[2 * m + 1] += w2[1];
-            }
-        }
-    };
-
-    // One slice: wait for it, prefetch the one two ahead, build, process, advance.  Returns true
-    // after the last slice of the last piece.
-    // M = 1: the operands of the slice after it (oa) are waited for too, and its table is built
-    // into the other buffer before this slice's lookups; the barrier at the end makes it
-    // complete for every wave and frees this slice's table for the slice after next.
-    // A unit is one pass over a slice; the table of the next slice is built (and the barrier
-    // taken) in the last pass.
-    auto step = [&](auto pc, u32x4 (&cur)[RW], SliceOps &oc, SliceOps &oa, u32x4 (&nxt)[RW], SliceOps &on) __attribute__((always_inline)) -> bool {
-        constexpr int pass = decltype(pc)::value;
-        constexpr bool last = pass == NP - 1;
+    int tb = 0;  // table of the slice being processed
+    // One slice: wait for its tiles and the next slice's table operands, issue the loads of the
+    // slice two ahead, build the next table into the other buffer, look up this slice, barrier.
+    auto step = [&](u32x4 (&cur)[RW], LutOps &on, u32x4 (&nxt)[RW], LutOps &onew) __attribute__((always_inline)) -> bool {
         settle_tiles(cur);
-        if constexpr (LUT2) {
-            if constexpr (pass == 0) settle_ops(oc);
-        } else if constexpr (LUT) {
-            if constexpr (last) settle_ops(oa);
-        } else {
-            settle_ops(oc);
-        }
-        load_slice(nxt, on);
-        auto lookups = [&](uint32_t lk) __attribute__((always_inline)) {
+        settle_ops(on);
+        load_slice(nxt, onew);
+        build(on, tb ^ 1);
+        const uint32_t lkA = lkA0 | (uint32_t(tb) << 16), lkB = lkB0 | (uint32_t(tb) << 16);
 #pragma unroll
-            for (int i = 0; i < RW; i++) {
-                // (the ring slots past the piece's end hold no tile)
-                if (pp.rb0 + tile_rb<RW, W>(wid, i, pass) < pp.rb1) process(cur[i], acc[pass][i], lk);
-                // one tile at a time: hoisting the address math of every tile blows the register budget
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        if constexpr (LUT2) {
-            if constexpr (pass == 0) {  // the slice's table replaces the previous slice's
-                lds_barrier();          // every wave is done with the previous table
-                build_table(oc, 0);
-                lds_barrier();          // the table is complete
-            }
-            lookups(uint32_t(lane) << 2);
-        } else if constexpr (LUT) {
-            if constexpr (last) build_table(oa, tb ^ 1);
-            lookups((uint32_t(lane) << 2) | (uint32_t(tb) << 16));
-            if constexpr (last) {
-                lds_barrier();
-                tb ^= 1;
-            }
-        } else {
-            slice_start(oc);
-            lookups(0);
+        for (int i = 0; i < RW; i++) {
+            if (pp.rb0 + RW * wid + i < pp.rb1) process(cur[i], acc[i], lkA, lkB);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (!last) return false;
+        lds_barrier();
+        tb ^= 1;
         if (++ps < pp.s1) return false;
         epilogue(pp, pd);
         const Piece pn = next_piece(P, wg, pp);
@@ -648,67 +434,206 @@ void aq_kernel(AqParams P) {
         return false;
     };
 
-    // Three slice buffers: while slice s is processed, slices s+1 and s+2 are in flight.
     u32x4 buf0[RW], buf1[RW], buf2[RW];
-    SliceOps ops0, ops1, ops2;
+    LutOps ops0, ops1, ops2;
     load_slice(buf0, ops0);
     load_slice(buf1, ops1);
-    if constexpr (LUT && !LUT2) {  // the first table (M = 2: built by the first slice's step)
-        settle_ops(ops0);
-        build_table(ops0, 0);
-        lds_barrier();
-    }
-    // (the ring has 3 buffers and a slice NP passes: 3 * NP steps per round)
+    settle_ops(ops0);
+    build(ops0, 0);
+    lds_barrier();
     while (true) {
-        if (step(Int<0>{}, buf0, ops0, ops1, buf2, ops2)) break;
-        if (step(Int<1 % NP>{}, buf1, ops1, ops2, buf0, ops0)) break;
-        if (step(Int<2 % NP>{}, buf2, ops2, ops0, buf1, ops1)) break;
-        if constexpr (NP == 2) {
-            if (step(Int<1>{}, buf0, ops0, ops1, buf2, ops2)) break;
-            if (step(Int<0>{}, buf1, ops1, ops2, buf0, ops0)) break;
-            if (step(Int<1>{}, buf2, ops2, ops0, buf1, ops1)) break;
-        }
+        if (step(buf0, ops1, buf2, ops2)) break;
+        if (step(buf1, ops2, buf0, ops0)) break;
+        if (step(buf2, ops0, buf1, ops1)) break;
     }
-    finalize<M, W>(P, wg, wid, lane);
+    finish<1, RW, kAqLutMaxSplits>(P, wg, wid, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// Matrix-core kernel, M activation rows.  RW: 16-row blocks per wave per slice.
+// ------------------------------------------------------------------------------------------
+constexpr int kCbBytes = 2 * 256 * 16 * 16;  // 16 copies of the two codebooks
+constexpr int kStageBytes = 2 * 544;         // per wave: a tile, half h at h*544 (padded)
+constexpr int kXRow = 33 * 16;               // staged activations: one row of a slice (padded)
+
+template <int M>
+struct MmaLds {
+    static constexpr int off_stage = kCbBytes;
+    static constexpr int off_x = kCbBytes + W * kStageBytes;
+    static constexpr int xbuf = M * kXRow;
+    static constexpr int bytes = off_x + 2 * xbuf;
+};
+
+struct MmaOps {
+    u32x4 X;   // this thread's 8 activations of the slice (row t/32, group t%32), t < 32M
+    int gval;  // groups of the slice inside K
+};
+
+template <int M, int RW>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_mma_kernel(AqParams P) {
+    using L = MmaLds<M>;
+    static_assert(L::bytes <= 160 * 1024, "LDS of one workgroup");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
+
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wg = blockIdx.x;
+    const int n = lane & 15, q4 = lane >> 4;     // MMA operand lane: row (weight or activation), k-block
+    const int th = lane >> 5, tg = lane & 31;    // tile lane: half, group
+
+    Piece pp = find_piece(P, wg, 0, -1);
+    if (pp.p >= P.ndesc) return;
+    int ps = pp.s0;
+    AqDesc pd = get_desc(P, pp.p);
+
+    Loader<RW> ld;
+    ld.done = false;
+    ld.setup(P, pp, wid);
+
+    const int xt = min(int(threadIdx.x), 32 * M - 1);
+    auto load_slice = [&](u32x4 (&t)[RW], MmaOps &o) __attribute__((always_inline)) {
+        o.gval = ld.G - ld.s * 32;
+        const int gi = min(ld.s * 32 + (xt & 31), ld.G - 1);
+        o.X = gld<u32x4>(ld.x + int64_t(xt >> 5) * ld.ldx + int64_t(gi) * 8);
+        load_tiles(ld, t, lane);
+        ld.step(P, wg, wid);
+    };
+    auto settle_ops = [&](MmaOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.X)); };
+    auto stage_x = [&](const MmaOps &o, int xb) __attribute__((always_inline)) {
+        if (threadIdx.x < 32 * M) {
+            const bool in = int(threadIdx.x & 31) < o.gval;
+            *reinterpret_cast<u32x4 *>(lds + L::off_x + xb * L::xbuf + (threadIdx.x >> 5) * kXRow + (threadIdx.x & 31) * 16) =
+                in ? o.X : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // The projection's codebooks into the 16 copies (all loads first, then the writes).
+    auto codebooks = [&](const uint16_t *cbk) __attribute__((always_inline)) {
+        u32x4 e[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) e[k] = gld<u32x4>(cbk + ((threadIdx.x + k * W * 64) >> 4) * 8);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const int idx = threadIdx.x + k * W * 64;  // entry idx >> 4, copy idx & 15
+            *reinterpret_cast<u32x4 *>(lds + (idx >> 4) * 256 + (idx & 15) * 16) = e[k];
+        }
+    };
+
+    f32x4 Dacc[RW][2];
+#pragma unroll
+    for (int i = 0; i < RW; i++)
+#pragma unroll
+        for (int c = 0; c < 2; c++) Dacc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint8_t *stage = lds + L::off_stage + wid * kStageBytes;
+    const uint8_t *code_src = stage + (n >> 3) * 544 + q4 * 16 + 2 * (n & 7);
+    const uint32_t lkc = (1u << 16) | (uint32_t(n) << 4);
+    // One tile into accumulators D: transpose the codes through the staging area, then 8 steps of
+    // 4 groups, each two products (codebook 0, codebook 1).
+    auto mma_tile = [&](const u32x4 &v, const u32x4 (&A)[8], f32x4 (&D)[2]) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4 *>(stage + th * 544 + tg * 16) = v;
+        uint32_t cp[8];
+#pragma unroll
+        for (int t = 0; t < 8; t++) cp[t] = *reinterpret_cast<const uint16_t *>(code_src + t * 64);
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const uint32_t a0 = __builtin_amdgcn_perm(cp[t], lkc, 0x0c0c0400u);  // (c0 << 8) | (n << 4)
+            const uint32_t a1 = __builtin_amdgcn_perm(cp[t], lkc, 0x0c020500u);  // 64 KiB + (c1 << 8) | (n << 4)
+            const u32x4 B0 = *reinterpret_cast<const u32x4 *>(lds + a0);
+            const u32x4 B1 = *reinterpret_cast<const u32x4 *>(lds + a1);
+            const h8 Ah = __builtin_bit_cast(h8, A[t]);
+            D[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, B0), D[t & 1], 0, 0, 0);
+            D[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, B1), D[t & 1], 0, 0, 0);
+        }
+    };
+
+    // Piece epilogue: register v of lane 16q + n is activation row 4q + v of weight row n.
+    auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RW; i++) {
+            const int rb = q.rb0 + RW * wid + i;
+            const int row = 16 * rb + n;
+            if (rb < q.rb1 && row < D.N) {
+                const float sc = D.b == 1 ? half_bits_to_float(gld<uint16_t>(D.rscale + row)) : 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const int m = 4 * q4 + v;
+                    const float s = Dacc[i][0][v] + Dacc[i][1][v];
+                    if (m < M) {
+                        if (D.b == 1)
+                            gst(D.y + int64_t(m) * D.ldy + row, s * sc);
+                        else
+                            __hip_atomic_store(as_global(D.part + (int64_t(m) * D.b + q.split) * D.Npad + row), s,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; c++) Dacc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    int xb = 0;  // activation buffer of the slice being processed
+    auto step = [&](u32x4 (&cur)[RW], MmaOps &on, u32x4 (&nxt)[RW], MmaOps &onew) __attribute__((always_inline)) -> bool {
+        settle_tiles(cur);
+        settle_ops(on);
+        load_slice(nxt, onew);
+        stage_x(on, xb ^ 1);
+        u32x4 A[8];  // lane 16q + m: activation row min(m, M-1), groups 4t + q of the slice
+        const uint8_t *xs = lds + L::off_x + xb * L::xbuf + min(n, M - 1) * kXRow + q4 * 16;
+#pragma unroll
+        for (int t = 0; t < 8; t++) A[t] = *reinterpret_cast<const u32x4 *>(xs + t * 64);
+#pragma unroll
+        for (int i = 0; i < RW; i++) {
+            if (pp.rb0 + RW * wid + i < pp.rb1) mma_tile(cur[i], A, Dacc[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_barrier();
+        xb ^= 1;
+        if (++ps < pp.s1) return false;
+        epilogue(pp, pd);
+        const Piece pn = next_piece(P, wg, pp);
+        if (pn.p >= P.ndesc) return true;
+        const bool newcb = pn.p != pp.p && get_desc(P, pn.p).cbk != pd.cbk;
+        pp = pn;
+        ps = pp.s0;
+        pd = get_desc(P, pp.p);
+        if (newcb) {  // every wave is past its lookups of the old codebooks (the barrier above)
+            codebooks(pd.cbk);
+            lds_barrier();
+        }
+        return false;
+    };
+
+    u32x4 buf0[RW], buf1[RW], buf2[RW];
+    MmaOps ops0, ops1, ops2;
+    codebooks(pd.cbk);
+    load_slice(buf0, ops0);
+    load_slice(buf1, ops1);
+    settle_ops(ops0);
+    stage_x(ops0, 0);
+    lds_barrier();
+    while (true) {
+        if (step(buf0, ops1, buf2, ops2)) break;
+        if (step(buf1, ops2, buf0, ops0)) break;
+        if (step(buf2, ops0, buf1, ops1)) break;
+    }
+    finish<M, RW, kAqMmaMaxSplits>(P, wg, wid, lane);
 }
 
 }  // namespace
 
-AqFn aq_fn(int M, int RW, bool bi) {
-    if (bi) {  // one row block per wave per slice at every M
-        switch (M) {
-        case 1: return aq_kernel<1, 1, 1, true>;
-        case 2: return aq_kernel<2, 1, 1, true>;
-        case 3: return aq_kernel<3, 1, 1, true>;
-        case 4: return aq_kernel<4, 1, 1, true>;
-        case 5: return aq_kernel<5, 1, 1, true>;
-        case 6: return aq_kernel<6, 1, 1, true>;
-        case 7: return aq_kernel<7, 1, 1, true>;
-        case 8: return aq_kernel<8, 1, 1, true>;
-        }
-        return nullptr;
-    }
-#define WQD_AQ_CASE(m)                                   \
-    case m:                                              \
-        return RW == 1 ? aq_kernel<m, 1, 1> : aq_kernel<m, 2, 1>;
+AqFn aq_fn(int M, bool lut) {
+    if (lut) return M == 1 ? aq_lut_kernel<kAqLutRW> : nullptr;
     switch (M) {
-    case 1:  // RW: row blocks per wave per slice; 8 = two passes of 4
-        if (RW <= 1) return aq_kernel<1, 1, 1>;
-        if (RW == 2) return aq_kernel<1, 2, 1>;
-        if (RW == 4) return aq_kernel<1, 4, 1>;
-        return aq_kernel<1, 4, 2>;
-    case 2:  // lookup tables: RW 4 = two passes of 2
-        if (RW <= 1) return aq_kernel<2, 1, 1>;
-        if (RW == 2) return aq_kernel<2, 2, 1>;
-        return aq_kernel<2, 2, 2>;
-        WQD_AQ_CASE(3)
-        WQD_AQ_CASE(4)
-        WQD_AQ_CASE(5)
-        WQD_AQ_CASE(6)
-        WQD_AQ_CASE(7)
-        WQD_AQ_CASE(8)
+    case 1: return aq_mma_kernel<1, kAqMmaRW>;
+    case 2: return aq_mma_kernel<2, kAqMmaRW>;
+    case 3: return aq_mma_kernel<3, kAqMmaRW>;
+    case 4: return aq_mma_kernel<4, kAqMmaRW>;
+    case 5: return aq_mma_kernel<5, kAqMmaRW>;
+    case 6: return aq_mma_kernel<6, kAqMmaRW>;
+    case 7: return aq_mma_kernel<7, kAqMmaRW>;
+    case 8: return aq_mma_kernel<8, kAqMmaRW>;
     }
-#undef WQD_AQ_CASE
     return nullptr;
 }
 

@@ -30,13 +30,13 @@
 //   AQ1X16 chunk = 8 groups of 8 weights, 64 weights: the 8 little-endian 16-bit codes in
 //         canonical order.
 //   AQ2X8 is tiled the other way round (one lane per group of 8 weights, not per row): tiles of
-//         8 rows x 64 groups.  With G = K/8 groups, KS = ceil(G/64) slices of 64 groups,
-//         R8 = Npad/8 row blocks and row block r8 = n/8, the tile (r8, s) sits at
-//         ((s*R8 + r8)*64 + lane)*16, lane = group g % 64 of slice s = g / 64, and its 16 bytes
-//         are (c0, c1) of rows 8*r8 + 0..7 of that group, row by row.  One wavefront load reads
-//         one tile (1 KiB); the tiles of consecutive row blocks of one slice are contiguous.
-//         Groups past G and rows past N are zero.  C = 8*KS, so the plane still holds RG*C*1024
-//         bytes.
+//         16 rows x 32 groups.  With G = K/8 groups, KS = ceil(G/32) slices of 32 groups,
+//         R16 = Npad/16 row blocks and row block b16 = n/16, the tile (b16, s) sits at
+//         ((s*R16 + b16)*64 + lane)*16 with lane = 32*h + g: g = group % 32 of slice s = group / 32,
+//         h = (n % 16) / 8, and its 16 bytes are (c0, c1) of rows 16*b16 + 8*h + 0..7 of that
+//         group, row by row.  One wavefront load reads one tile (1 KiB); the tiles of consecutive
+//         row blocks of one slice are contiguous.  Groups past G and rows past N are zero.
+//         C = 4*KS, so the plane still holds RG*C*1024 bytes.
 #pragma once
 #include <stdint.h>
 
@@ -64,7 +64,7 @@ struct Layout {
     int64_t weights_per_chunk = 0;
     int64_t blocks = 0;       // scale blocks per row (Q4_0, TQ2)
     int64_t Q = 0;            // quads of blocks per row (Q4_0, TQ2)
-    int64_t G = 0, KS = 0;    // AQ2X8: groups of 8 weights per row, slices of 64 groups
+    int64_t G = 0, KS = 0;    // AQ2X8: groups of 8 weights per row, slices of 32 groups
     int64_t off_scales = 0, off_cbk = 0, total = 0;
     bool ok = false;
 };
@@ -105,8 +105,8 @@ inline Layout make_layout(int fmt, int64_t N, int64_t K) {
     L.C_full = K / L.weights_per_chunk;
     if (fmt == AQ2X8) {
         L.G = K / 8;
-        L.KS = (L.G + 63) / 64;
-        L.C = 8 * L.KS;
+        L.KS = (L.G + 31) / 32;
+        L.C = 4 * L.KS;
         L.C_full = L.C;
     }
     L.Q = (L.blocks + 3) / 4;

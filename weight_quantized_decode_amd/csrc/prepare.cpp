@@ -90,13 +90,14 @@ void prep_bytes(const Layout &L, const uint8_t *row_codes, uint8_t *dst) {
     }
 }
 
-// AQ2X8: canonical rows of (c0, c1) pairs -> transposed 8-row x 64-group tiles (layout.h).
+// AQ2X8: canonical rows of (c0, c1) pairs -> transposed 16-row x 32-group tiles (layout.h).
 void prep_aq2x8(const Layout &L, const uint8_t *row_codes, uint8_t *dst) {
+    const int64_t R16 = L.Npad / 16;
     for (int64_t n = 0; n < L.N; n++) {
         const uint8_t *row = row_codes + n * L.G * 2;
-        const int64_t r8 = n / 8, r = n % 8;
+        const int64_t b16 = n / 16, h = (n % 16) / 8, r = n % 8;
         for (int64_t g = 0; g < L.G; g++) {
-            uint8_t *t = dst + ((g / 64 * (L.Npad / 8) + r8) * 64 + g % 64) * kChunkBytes + 2 * r;
+            uint8_t *t = dst + ((g / 32 * R16 + b16) * 64 + 32 * h + g % 32) * kChunkBytes + 2 * r;
             t[0] = row[2 * g];
             t[1] = row[2 * g + 1];
         }
