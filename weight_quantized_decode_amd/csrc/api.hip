@@ -371,7 +371,7 @@ struct AqPlan {
     Layout L;
     bool lut = false;
     int64_t RB = 0, a = 1, b = 1, nrb = 1, ns = 1;
-    int64_t cnt_bytes = 0;   // a * kAqWaves arrival counters when b > 1 (256-byte aligned)
+    int64_t cnt_bytes = 0;   // a arrival counters, kAqCntStride ints apart, when b > 1 (256-byte aligned)
     int64_t part_bytes = 0;  // M * b * Npad fp32 partials when b > 1 (256-byte aligned)
     int64_t tiles() const { return RB * L.KS; }
     // wqd_gemm workspace: [kCntRegion bytes of counters][partials]
@@ -398,7 +398,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
         if (a < 1) a = 1;
         const int64_t nrb = (RB + a - 1) / a;
         a = (RB + nrb - 1) / nrb;
-        if (b > 1 && a * kAqWaves * 4 > kCntRegion) continue;  // the counters fit their region
+        if (b > 1 && a * kAqCntStride * 4 > kCntRegion) continue;  // the counters fit their region
         const int64_t rounds = (a * b + nw - 1) / nw;
         const double cost = double(rounds) * double(ns * (nrb + setup) + (b > 1 ? WQD_AQ_SPLIT_CHARGE : 0));
         if (cost < best) {
@@ -410,7 +410,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
         }
     }
     A.RB = RB;
-    A.cnt_bytes = A.b > 1 ? align_up(A.a * kAqWaves * 4, 256) : 0;
+    A.cnt_bytes = A.b > 1 ? align_up(A.a * kAqCntStride * 4, 256) : 0;
     A.part_bytes = A.b > 1 ? align_up(M * A.b * A.L.Npad * 4, 256) : 0;
     return A;
 }

@@ -141,15 +141,17 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 // (16-row block x 32-group slice) tiles are cut into a x b rectangular pieces: a row chunks of
 // nrb blocks times b K-splits of ns slices.  Piece j = split * a + chunk runs on workgroup
 // wb + (j mod nw) of the launch, where wb = off and nw of the projection say which workgroups
-// serve it.  Wave w of a workgroup owns row blocks RW*w .. RW*w + RW-1 of every piece it runs.
-// With b > 1 each piece stores fp32 partial sums per row and counts itself done, per wave slot,
-// on its row chunk; the wave that arrives last adds the b partials in split order.
+// serve it.  Wave w of a workgroup owns row blocks w, w + 16, .. (RW of them) of every piece.
+// With b > 1 each piece stores fp32 partial sums per row and counts itself done on its row chunk
+// (one counter per chunk, each on a 128-byte line of its own); the workgroup that arrives last
+// adds the b partials in split order.
 // ------------------------------------------------------------------------------------------
 constexpr int kAqWaves = 16;        // waves per AQ2X8 workgroup (one workgroup per CU)
 constexpr int kAqLutMaxSplits = 32; // most K-splits of a lookup-table (M = 1) projection
 constexpr int kAqMmaMaxSplits = 8;  // most K-splits of a matrix-core projection
 constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-table kernel
 constexpr int kAqMmaRW = 2;         // row blocks per wave per slice, matrix-core kernel
+constexpr int kAqCntStride = 32;    // ints between the arrival counters of two row chunks
 #ifndef WQD_AQ_BUILD_CHARGE
 #define WQD_AQ_BUILD_CHARGE 8       // planner charge of a slice's table build, in tile loads
 #endif
@@ -164,7 +166,8 @@ struct AqDesc {
     const uint16_t *x;        // activations, M rows of ldx fp16
     float *y;                 // output, M rows of ldy fp32
     float *part;              // [M][b][Npad] partial sums when b > 1
-    int *cnt;                 // [a][kAqWaves] arrival counters when b > 1 (zero between calls)
+    int *cnt;                 // arrival counter of chunk c at cnt[c * kAqCntStride] when b > 1
+                              // (zero between calls)
     int64_t ldx, ldy;
     int32_t N, G, KS, RB;     // rows, groups, 32-group slices, 16-row blocks holding rows < N
     int32_t Npad;

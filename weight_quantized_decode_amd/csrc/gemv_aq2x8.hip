@@ -21,8 +21,9 @@
 //   * Per row of a tile, lane 32h + g reads T_h[c_h] and T_(1-h)[c_(1-h)] of its group: in one LDS
 //     instruction the lanes of half 0 read codebook-0 entries (columns 0..31) and the lanes of
 //     half 1 codebook-1 entries (columns 32..63), so no two lanes meet in a bank.  Each address is
-//     one v_perm of the code word with a per-lane byte selector.  The two fp32 entries are added to
-//     the lane's 8 row sums, which are reduced over the 32 lanes of a half once per piece.
+//     one v_perm of the code word with a per-lane byte selector.  The two fp32 entries of each of
+//     the lane's 8 rows are added, folded with the lane 16 apart (4 sums per lane) and accumulated;
+//     the rest of the sum over the 32 lanes of a half is taken once per piece.
 // Matrix-core kernel (M = 1..8; every batch-invariant call takes it):
 //   * y = x W^T on the 16x16x32 fp16 matrix core: A = 16 activation rows (rows past M repeat row
 //     M-1 and are never stored) x 32 k (4 groups), B = 32 k x 16 weight rows, whose operand in
@@ -37,9 +38,9 @@
 //
 // Work (AqDesc): a workgroup walks its pieces in order, slice by slice; the tile loads of the next
 // two slices are in flight while a slice is processed.  Pieces with b > 1 store fp32 partials.
-// Once all of its pieces are done, each wave counts its slot of every split piece done, and the
-// wave that arrives last adds that slot's partials in split order: no workgroup ever waits for
-// another, and results are the same bits from run to run.
+// Once all of its pieces are done, the workgroup counts each split piece done on its row chunk,
+// and the workgroup that arrives last adds the chunk's partials in split order: no workgroup ever
+// waits for another, and results are the same bits from run to run.
 #include <stddef.h>
 
 #include "gemv_impl.h"
@@ -52,6 +53,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int W = kAqWaves;
+#ifndef WQD_AQ_LUT_RING
+#define WQD_AQ_LUT_RING 3  // unit buffers of the lookup-table kernel's load ring
+#endif
 
 __device__ __forceinline__ float f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t u32(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -65,15 +69,17 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppRor8 = 0x128;         // row_ror:8 (lane i <-> i^8 within 16)
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
 
-// Sum over the 32 lanes of each half (lanes 32h .. 32h+31) of v[r], r < 8, in a fixed order (a
-// transposed butterfly).  On return lane l holds the sum of row (l >> 2) & 7 of its half.
-__device__ __forceinline__ float reduce_half8(const float (&v)[8], int lane) {
-    float u[4];
+// Sums over the 32 lanes of each half (lanes 32h .. 32h+31) of v[r], r < 8, in a fixed order (a
+// transposed butterfly), in two parts.  fold16: lanes l and l^16, leaving row r + 4*bit4 in u[r],
+// r < 4.  finish_half4: the rest; on return lane l holds the sum of row (l >> 2) & 7 of its half.
+__device__ __forceinline__ void fold16(const float (&v)[8], float (&u)[4]) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {  // lanes l, l^16: row r + 4*bit4
+    for (int r = 0; r < 4; r++) {
         const auto s = __builtin_amdgcn_permlane16_swap(u32(v[r]), u32(v[r + 4]), false, false);
         u[r] = f32(s[0]) + f32(s[1]);
     }
+}
+__device__ __forceinline__ float finish_half4(const float (&u)[4], int lane) {
     const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
     float w[2];
 #pragma unroll
@@ -157,8 +163,12 @@ __device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Pie
     return find_piece(P, wg, q.p, q.j + q.nw);
 }
 
+// Row block (from the piece's first) of tile i of wave wid: the waves take turns, so a piece of
+// fewer than W*RW row blocks leaves every wave with a nearly equal share.
+__device__ __forceinline__ int tile_rb(int wid, int i) { return wid + W * i; }
+
 // Tile loader running ahead of the processing: one unit is one slice of the current piece; wave
-// wid loads row blocks rb0 + RW*wid .. + RW-1 of it.
+// wid loads row blocks rb0 + tile_rb(wid, i), i < RW, of it.
 template <int RW>
 struct Loader {
     const uint8_t *base;   // code plane (the lane's 16 bytes are added at the load)
@@ -192,7 +202,7 @@ struct Loader {
     // A missing tile (past the piece, or past the end of the work) still takes its place in the
     // ring, so every load stays unconditional: it reads 1 KiB of the codebooks instead.
     __device__ __forceinline__ const uint8_t *addr(int i) const {
-        const int r = rb0 + RW * wv + i;
+        const int r = rb0 + tile_rb(wv, i);
         return (done || r >= rb1) ? reinterpret_cast<const uint8_t *>(cbk)
                                   : base + int64_t(min(s, s_max)) * s_stride + int64_t(min(r, rb_max)) * 1024;
     }
@@ -225,26 +235,27 @@ __device__ __forceinline__ void settle_tiles(u32x4 (&t)[RW]) {
 // Split pieces: arrival and the sum of the partials.
 // ------------------------------------------------------------------------------------------
 
-// Adds the b partials (in split order) of this wave's rows of piece q, scales them and writes y,
-// then clears the wave's counter.  Items (activation row m, row block i, row rr) are taken by the
-// lanes in turn; every partial load of the wave is in flight at once (at most BMAX per item).
-template <int M, int RW, int BMAX>
-__device__ __forceinline__ void add_splits(const AqDesc &D, const Piece &q, int wid, int lane) {
-    constexpr int ITEMS = M * RW * 16;
-    constexpr int NI = (ITEMS + 63) / 64;
-    float v[NI][BMAX];
+// Adds the b partials (in split order) of every row of piece q's row chunk, scales them and writes
+// y, then clears the chunk's counter.  Items (activation row m, row of the chunk) are taken by the
+// workgroup's threads in turn.  NL >= b loads per item, unconditional (indices past b - 1 repeat
+// the last split and are not added), so every load of a thread is in flight at once.
+template <int M, int RW, int NL>
+__device__ __forceinline__ void add_splits_n(const AqDesc &D, const Piece &q) {
+    constexpr int ROWS = W * RW * 16;  // most rows of a chunk
+    constexpr int NI = (M * ROWS + W * 64 - 1) / (W * 64);
+    const int r0 = 16 * q.rb0, nrows = min(16 * q.rb1, D.N) - r0;
+    float v[NI][NL];
     int rowv[NI], mv[NI];
     bool live[NI];
 #pragma unroll
     for (int it = 0; it < NI; it++) {
-        const int item = lane + 64 * it;
-        const int m = item / (RW * 16), rem = item - m * (RW * 16);
-        const int rb = q.rb0 + RW * wid + rem / 16, row = 16 * rb + (rem & 15);
-        live[it] = item < ITEMS && rb < q.rb1 && row < D.N;
-        rowv[it] = live[it] ? row : 0;
+        const int item = int(threadIdx.x) + W * 64 * it;
+        const int m = item / ROWS, rr = item - m * ROWS;
+        live[it] = m < M && rr < nrows;
+        rowv[it] = live[it] ? r0 + rr : 0;
         mv[it] = live[it] ? m : 0;
 #pragma unroll
-        for (int j = 0; j < BMAX; j++)
+        for (int j = 0; j < NL; j++)
             v[it][j] = __hip_atomic_load(as_global(D.part + (int64_t(mv[it]) * D.b + min(j, D.b - 1)) * D.Npad + rowv[it]),
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -252,53 +263,103 @@ __device__ __forceinline__ void add_splits(const AqDesc &D, const Piece &q, int 
     for (int it = 0; it < NI; it++) {
         float sum = 0.f;
 #pragma unroll
-        for (int j = 0; j < BMAX; j++)
+        for (int j = 0; j < NL; j++)
             if (j < D.b) sum += v[it][j];
         if (live[it]) {
             const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + rowv[it]));
             gst(D.y + int64_t(mv[it]) * D.ldy + rowv[it], sum * sc);
         }
     }
-    if (lane == 0) __hip_atomic_store(as_global(D.cnt + q.chunk * W + wid), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(as_global(D.cnt + q.chunk * kAqCntStride), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int M, int RW, int BMAX>
+__device__ __forceinline__ void add_splits(const AqDesc &D, const Piece &q) {
+    if (BMAX <= 8 || D.b <= 8) add_splits_n<M, RW, 8>(D, q);
+    else if (BMAX <= 16 || D.b <= 16) add_splits_n<M, RW, (BMAX < 16 ? BMAX : 16)>(D, q);
+    else if (BMAX <= 24 || D.b <= 24) add_splits_n<M, RW, (BMAX < 24 ? BMAX : 24)>(D, q);
+    else add_splits_n<M, RW, BMAX>(D, q);
 }
 
-// After all of the workgroup's pieces: the wave counts its slot of each split piece done (up to 8
-// atomics in flight at once) and adds the partials of the slots where it arrived last.  The
-// partial stores of the pieces have completed before the counts are taken.
+// The split pieces a workgroup ran, recorded in LDS at the end of each (the finish reads them
+// per lane instead of walking the piece list again, which is scalar-unit work for every wave).
+constexpr int kAqMaxRec = 64;
+struct AqRec {
+    int *cnt;      // the piece's chunk counter
+    int32_t b;     // its splits
+    int32_t p, j;  // projection and piece index
+    int32_t pad_;
+};
+__device__ __forceinline__ void record_piece(AqRec *rec, int &nrec, const Piece &q, const AqDesc &D, int wid, int lane) {
+    if (D.b == 1) return;
+    if (nrec < kAqMaxRec && wid == 0 && lane == 0) {
+        AqRec r;
+        r.cnt = D.cnt + q.chunk * kAqCntStride;
+        r.b = D.b;
+        r.p = q.p;
+        r.j = q.j;
+        r.pad_ = 0;
+        rec[nrec] = r;
+    }
+    nrec++;
+}
+
+// After all of the workgroup's pieces: once every wave's partial stores have completed, the
+// workgroup counts each of its split pieces done on the piece's row chunk (lane k of wave 0 takes
+// the k-th, so the atomics are one instruction), and where it arrived last it adds the chunk's
+// partials.  `rec` holds the nrec pieces record_piece kept (at most kAqMaxRec; past that the piece
+// list is walked again), `flags` 64 ints of LDS.
 template <int M, int RW, int BMAX>
-__device__ __forceinline__ void finish(const AqParams &P, int wg, int wid, int lane) {
+__device__ __forceinline__ void finish(const AqParams &P, int wg, int wid, int lane, const AqRec *rec, int nrec,
+                                       int *flags) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // every wave's partials are stored (and the records written)
+    if (nrec <= kAqMaxRec) {
+        if (wid == 0) {
+            int last = 0;
+            if (lane < nrec) {
+                const AqRec r = rec[lane];
+                last = __hip_atomic_fetch_add(as_global(r.cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == r.b - 1;
+            }
+            flags[lane] = last;
+        }
+        lds_barrier();
+        for (int k = 0; k < nrec; k++) {
+            if (!__builtin_amdgcn_readfirstlane(flags[k])) continue;
+            const int p = __builtin_amdgcn_readfirstlane(rec[k].p), j = __builtin_amdgcn_readfirstlane(rec[k].j);
+            const Piece q = find_piece(P, wg, p, j);
+            add_splits<M, RW, BMAX>(get_desc(P, q.p), q);
+        }
+        return;
+    }
     Piece q = find_piece(P, wg, 0, -1);
     while (q.p < P.ndesc) {
         const Piece q0 = q;
-        int old[8];
-        int n = 0;
-        static_for<8>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            old[k] = -1;
-            while (q.p < P.ndesc && get_desc(P, q.p).b == 1) q = next_piece(P, wg, q);
-            if (q.p < P.ndesc) {
-                const AqDesc D = get_desc(P, q.p);
-                int o = 0;
-                if (lane == 0)
-                    o = __hip_atomic_fetch_add(as_global(D.cnt + q.chunk * W + wid), 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                old[k] = o;
-                n++;
-                q = next_piece(P, wg, q);
+        int *cnt = nullptr;  // lane k: the k-th split piece's counter and split count
+        int bk = 0, n = 0;
+        for (; q.p < P.ndesc && n < 64; q = next_piece(P, wg, q)) {
+            const AqDesc D = get_desc(P, q.p);
+            if (D.b == 1) continue;
+            if (lane == n) {
+                cnt = D.cnt + q.chunk * kAqCntStride;
+                bk = D.b;
             }
-        });
-        Piece r = q0;
-        static_for<8>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            if (k < n) {
-                while (get_desc(P, r.p).b == 1) r = next_piece(P, wg, r);
-                const AqDesc D = get_desc(P, r.p);
-                if (__builtin_amdgcn_readfirstlane(old[k]) == D.b - 1) add_splits<M, RW, BMAX>(D, r, wid, lane);
-                r = next_piece(P, wg, r);
-            }
-        });
-        while (q.p < P.ndesc && get_desc(P, q.p).b == 1) q = next_piece(P, wg, q);
+            n++;
+        }
+        if (wid == 0) {
+            int last = 0;
+            if (lane < n) last = __hip_atomic_fetch_add(as_global(cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == bk - 1;
+            flags[lane] = last;
+        }
+        lds_barrier();
+        int k = 0;
+        for (Piece r = q0; k < n; r = next_piece(P, wg, r)) {
+            const AqDesc D = get_desc(P, r.p);
+            if (D.b == 1) continue;
+            if (__builtin_amdgcn_readfirstlane(flags[k])) add_splits<M, RW, BMAX>(D, r);
+            k++;
+        }
+        lds_barrier();  // flags are read before the next round overwrites them
     }
 }
 
@@ -312,9 +373,11 @@ struct LutOps {
     int gval;  // groups of the slice inside K
 };
 
-template <int RW>
+template <int RW, int R>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_lut_kernel(AqParams P) {
     __shared__ uint32_t lds[2 * 256 * 64];
+    __shared__ AqRec recs[kAqMaxRec];
+    int nrec = 0;
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -364,34 +427,51 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     };
 
-    float acc[RW][8];
+    // per row block: the lane's 8 row sums folded over lanes l, l^16 (fold16)
+    float acc[RW][4];
 #pragma unroll
     for (int i = 0; i < RW; i++)
 #pragma unroll
-        for (int r = 0; r < 8; r++) acc[i][r] = 0.f;
+        for (int r = 0; r < 4; r++) acc[i][r] = 0.f;
 
-    // One tile: the 8 rows of this lane's half, its group.
-    auto process = [&](const u32x4 &v, float (&a)[8], uint32_t lkA, uint32_t lkB) __attribute__((always_inline)) {
+    // One tile: the 8 rows of this lane's half, its group.  The 16 lookups go out as two groups of
+    // 8 (rows 0, 1, 4, 5, then rows 2, 3, 6, 7); the second group's addresses are tied to the first
+    // lookup's result, so at most 15 LDS reads are outstanding and every wait is counted exactly.
+    auto process = [&](const u32x4 &v, float (&a)[4], uint32_t lkA, uint32_t lkB) __attribute__((always_inline)) {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t e[2][8];
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
+        for (int q = 0; q < 2; q++) {
+            uint32_t ad[8];
 #pragma unroll
-            for (int p = 0; p < 2; p++) {
-                const uint32_t ea = lds_word(lds, __builtin_amdgcn_perm(w4[t], lkA, selA[p]));
-                const uint32_t eb = lds_word(lds, __builtin_amdgcn_perm(w4[t], lkB, selB[p]));
-                a[2 * t + p] += f32(ea);
-                a[2 * t + p] += f32(eb);
+            for (int k = 0; k < 4; k++) {  // row r = (k & 1) + 2q + 4(k >> 1) is word r/2, parity r%2
+                const int r = (k & 1) + 2 * q + 4 * (k >> 1);
+                ad[2 * k] = __builtin_amdgcn_perm(w4[r >> 1], lkA, selA[r & 1]);
+                ad[2 * k + 1] = __builtin_amdgcn_perm(w4[r >> 1], lkB, selB[r & 1]);
             }
+            if (q == 1)
+                __asm__ volatile("" : "+v"(ad[0]), "+v"(ad[1]), "+v"(ad[2]), "+v"(ad[3]), "+v"(ad[4]), "+v"(ad[5]),
+                                 "+v"(ad[6]), "+v"(ad[7]) : "v"(e[0][0]));
+#pragma unroll
+            for (int k = 0; k < 8; k++) e[q][k] = lds_word(lds, ad[k]);
         }
+        float r8[8], u[4];
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+#pragma unroll
+            for (int k = 0; k < 4; k++) r8[(k & 1) + 2 * q + 4 * (k >> 1)] = f32(e[q][2 * k]) + f32(e[q][2 * k + 1]);
+        fold16(r8, u);
+#pragma unroll
+        for (int r = 0; r < 4; r++) a[r] += u[r];
     };
 
     // Piece epilogue: row sums -> y (b == 1) or this split's partials.
     auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            const int rb = q.rb0 + RW * wid + i;
+            const int rb = q.rb0 + tile_rb(wid, i);
             if (rb < q.rb1) {
-                const float z = reduce_half8(acc[i], lane);
+                const float z = finish_half4(acc[i], lane);
                 const int row = 16 * rb + 8 * h + ((lane >> 2) & 7);
                 if ((lane & 3) == 0 && row < D.N) {
                     if (D.b == 1) {
@@ -404,7 +484,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 8; r++) acc[i][r] = 0.f;
+            for (int r = 0; r < 4; r++) acc[i][r] = 0.f;
         }
     };
 
@@ -415,17 +495,21 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         settle_tiles(cur);
         settle_ops(on);
         load_slice(nxt, onew);
+        // (no scalar load may be pending during the build and lookups: the LDS waits are then
+        // counted exactly instead of draining every lookup in flight)
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         build(on, tb ^ 1);
         const uint32_t lkA = lkA0 | (uint32_t(tb) << 16), lkB = lkB0 | (uint32_t(tb) << 16);
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            if (pp.rb0 + RW * wid + i < pp.rb1) process(cur[i], acc[i], lkA, lkB);
+            if (pp.rb0 + tile_rb(wid, i) < pp.rb1) process(cur[i], acc[i], lkA, lkB);
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         tb ^= 1;
         if (++ps < pp.s1) return false;
         epilogue(pp, pd);
+        record_piece(recs, nrec, pp, pd, wid, lane);
         const Piece pn = next_piece(P, wg, pp);
         if (pn.p >= P.ndesc) return true;
         pp = pn;
@@ -434,19 +518,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         return false;
     };
 
-    u32x4 buf0[RW], buf1[RW], buf2[RW];
-    LutOps ops0, ops1, ops2;
-    load_slice(buf0, ops0);
-    load_slice(buf1, ops1);
-    settle_ops(ops0);
-    build(ops0, 0);
+    // R unit buffers: while unit s is processed, units s+1 .. s+R-2 are in flight, and the loads of
+    // unit s+R-1 go into the buffer unit s-1 freed.
+    u32x4 buf[R][RW];
+    LutOps ops[R];
+    static_for<R - 1>([&](auto kc) { load_slice(buf[decltype(kc)::value], ops[decltype(kc)::value]); });
+    settle_ops(ops[0]);
+    build(ops[0], 0);
     lds_barrier();
-    while (true) {
-        if (step(buf0, ops1, buf2, ops2)) break;
-        if (step(buf1, ops2, buf0, ops0)) break;
-        if (step(buf2, ops0, buf1, ops1)) break;
+    bool fin = false;
+    while (!fin) {
+        static_for<R>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if (!fin) fin = step(buf[k], ops[(k + 1) % R], buf[(k + R - 1) % R], ops[(k + R - 1) % R]);
+        });
     }
-    finish<1, RW, kAqLutMaxSplits>(P, wg, wid, lane);
+    finish<1, RW, kAqLutMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -472,8 +559,10 @@ struct MmaOps {
 template <int M, int RW>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_mma_kernel(AqParams P) {
     using L = MmaLds<M>;
-    static_assert(L::bytes <= 160 * 1024, "LDS of one workgroup");
+    static_assert(L::bytes + kAqMaxRec * sizeof(AqRec) <= 160 * 1024, "LDS of one workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
+    __shared__ AqRec recs[kAqMaxRec];
+    int nrec = 0;
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -550,7 +639,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            const int rb = q.rb0 + RW * wid + i;
+            const int rb = q.rb0 + tile_rb(wid, i);
             const int row = 16 * rb + n;
             if (rb < q.rb1 && row < D.N) {
                 const float sc = D.b == 1 ? half_bits_to_float(gld<uint16_t>(D.rscale + row)) : 0.f;
@@ -584,13 +673,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         for (int t = 0; t < 8; t++) A[t] = *reinterpret_cast<const u32x4 *>(xs + t * 64);
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            if (pp.rb0 + RW * wid + i < pp.rb1) mma_tile(cur[i], A, Dacc[i]);
+            if (pp.rb0 + tile_rb(wid, i) < pp.rb1) mma_tile(cur[i], A, Dacc[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         xb ^= 1;
         if (++ps < pp.s1) return false;
         epilogue(pp, pd);
+        record_piece(recs, nrec, pp, pd, wid, lane);
         const Piece pn = next_piece(P, wg, pp);
         if (pn.p >= P.ndesc) return true;
         const bool newcb = pn.p != pp.p && get_desc(P, pn.p).cbk != pd.cbk;
@@ -617,13 +707,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         if (step(buf1, ops2, buf0, ops0)) break;
         if (step(buf2, ops0, buf1, ops1)) break;
     }
-    finish<M, RW, kAqMmaMaxSplits>(P, wg, wid, lane);
+    finish<M, RW, kAqMmaMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
 }
 
 }  // namespace
 
 AqFn aq_fn(int M, bool lut) {
-    if (lut) return M == 1 ? aq_lut_kernel<kAqLutRW> : nullptr;
+    if (lut) return M == 1 ? aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING> : nullptr;
     switch (M) {
     case 1: return aq_mma_kernel<1, kAqMmaRW>;
     case 2: return aq_mma_kernel<2, kAqMmaRW>;
