@@ -1,7 +1,11 @@
 """Helpers of the GPU tests: seeded weights uploaded in the prepared layout, and the parity bar."""
+import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
+
+import oracle
 
 from weight_quantized_decode_amd import _lib as W
 from weight_quantized_decode_amd import inputs as I
@@ -65,3 +69,34 @@ def check_parity(y_gpu, y_ref, a_ref, what=""):
         raise AssertionError(f"{what}: {bad.sum()} outputs outside the bound; first {idx.tolist()}: "
                              f"gpu {y[tuple(idx[0])]} ref {y_ref[tuple(idx[0])]} bound {bound[tuple(idx[0])]}")
     return float(np.max(err / (a_ref + 1e-30)))
+
+
+_POOL = None
+
+
+def oracle_gemm_all(fmt, N, K, canon, x_bits, rows=None):
+    """The oracle's (y, sum |x*w|) on every row (or the given rows), the rows cut into one range per
+    host thread (the oracle's C entry point releases the GIL)."""
+    global _POOL
+    T = max(1, len(os.sched_getaffinity(0)))
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(T)
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    parts = [r for r in np.array_split(rows, T) if r.size]
+    res = list(_POOL.map(lambda r: oracle.gemm_f64(fmt, N, K, canon, x_bits, rows=r), parts))
+    return np.concatenate([y for y, _ in res], axis=1), np.concatenate([a for _, a in res], axis=1)
+
+
+def aq2x8_cancelling(canon, N, K, key, rel=1e-3):
+    """AQ2x8 canonical bytes whose two codebooks nearly cancel, C1[c] = fp16(-C0[c] * (1 + rel*n)) with
+    n ~ N(0,1), and c1 = c0 in every group: each weight is about `rel` times the entries it is the
+    sum of.  A path that rounds a per-group sum of products to fp16 before the two codebooks'
+    terms meet makes errors of about 2^-12 of the terms, far above 2e-3 * sum |x*w| here."""
+    canon = np.array(canon, dtype=np.uint8, copy=True)
+    C = canon[:8192].view("<u2").astype(np.uint16).view(np.float16).astype(np.float64).reshape(2, 256, 8)
+    g = I.rng(*[int(k) for k in key], 30)
+    C1 = -C[0] * (1.0 + rel * g.standard_normal((256, 8)))
+    canon[4096:8192] = I.f16_bits(C1).astype("<u2").view(np.uint8).reshape(-1)
+    codes = canon[8192 + 2 * N:].reshape(N, K // 8, 2)
+    codes[:, :, 1] = codes[:, :, 0]
+    return canon

@@ -14,7 +14,7 @@ import oracle
 from weight_quantized_decode_amd import _lib as W
 from weight_quantized_decode_amd import inputs as I
 
-from gpu_util import check_parity, new_y, note, run_gemm, upload_weight, upload_x, workspace
+from gpu_util import aq2x8_cancelling, check_parity, new_y, note, run_gemm, upload_weight, upload_x, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def test_dequant_bit_exact_with_subnormal_scales():
 
 
 @pytest.mark.parametrize("fmt,N,K", SMALL)
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemm_parity_small(fmt, N, K, M):
     note(f"gemm fmt={fmt} N={N} K={K} M={M}")
     canon = I.gen_weight(fmt, N, K, (14, fmt, N, K))
@@ -108,23 +108,94 @@ def test_gemm_deterministic(fmt):
 
 
 @pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
-def test_gemm_one_hot_and_zero_activations(fmt):
-    # One-hot x returns a column of the dequantized matrix: exactly for the formats whose weights
-    # are exact in fp16 arithmetic; for AQ2x8 the kernel adds the two fp16 codebook entries in
-    # fp16 (one rounding, relative error <= 2^-11) before the fp32 product.  Zero x returns zero.
-    import torch
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemm_one_hot_and_zero_activations(fmt, M):
+    # One-hot x returns a column of the dequantized matrix.  The weights of Q4_0, CB4, CB8, TQ2 and
+    # AQ1X16 are exact in fp32, so the column is exact.  An AQ2x8 weight is s * (C0 + C1): the
+    # kernels form C0 + C1 in fp32 (the one nonzero lookup-table term or product of each codebook,
+    # added once) and scale it once, which is exactly the debug dequant's fp32(fp32(C0 + C1) * s):
+    # equal bits, and within two fp32 roundings of the exact weight.  Zero x returns zero.
+    # (M = 1 takes the lookup-table kernel, M = 2 the matrix-core one; row 1 is zero.)
     N, K = 128, 512
-    note(f"gemm one-hot fmt={fmt}")
+    note(f"gemm one-hot fmt={fmt} M={M}")
     canon = I.gen_weight(fmt, N, K, (17, fmt))
     w = upload_weight(fmt, N, K, canon)
     k = 301
-    x = np.zeros((2, K), dtype=np.uint16)
+    x = np.zeros((M, K), dtype=np.uint16)
     x[0, k] = 0x3C00  # 1.0
-    y = run_gemm(fmt, N, K, w, upload_x(x), 2).cpu().numpy()
+    y = run_gemm(fmt, N, K, w, upload_x(x), M).cpu().numpy()
     W64 = oracle.decode_f64(fmt, N, K, canon)
-    assert np.all(y[1] == 0.0)
-    rtol = 2.0 ** -11 + 2.0 ** -23 if fmt == I.AQ2X8 else 1e-7
+    if M > 1:
+        assert np.all(y[1:] == 0.0)
+    rtol = 2.0 ** -23 + 2.0 ** -46 if fmt == I.AQ2X8 else 1e-7
     assert np.all(np.abs(y[0] - W64[:, k]) <= rtol * np.abs(W64[:, k]))
+    if fmt == I.AQ2X8:
+        dq = oracle.dequant_f32(fmt, N, K, canon)[:, k]
+        assert np.array_equal(y[0].view(np.uint32), dq.view(np.uint32))
+    yz = run_gemm(fmt, N, K, w, upload_x(np.zeros((M, K), dtype=np.uint16)), M).cpu().numpy()
+    assert np.all(yz == 0.0)
+
+
+@pytest.mark.parametrize("N,K", [(200, 1000), (129, 8192)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_aq2x8_cancelling_codebooks(N, K, M):
+    # Codebooks with C1 ~ -C0 and c1 = c0 everywhere: every weight is about 1e-3 of the entries
+    # it is the sum of, so the bound 2e-3 * sum |x*w| is about 2e-6 of the group sums the kernels
+    # form.  fp16 rounding of those sums (about 2^-12 of them) fails it; fp32 sums pass.
+    note(f"aq2x8 cancelling N={N} K={K} M={M}")
+    canon = aq2x8_cancelling(I.gen_weight(I.AQ2X8, N, K, (19, N, K)), N, K, (19, N, K))
+    x = I.gen_x(M, K, (19, N, K, M))
+    w = upload_weight(I.AQ2X8, N, K, canon)
+    y = run_gemm(I.AQ2X8, N, K, w, upload_x(x), M)
+    yref, aref = oracle.gemm_f64(I.AQ2X8, N, K, canon, x)
+    check_parity(y.cpu().numpy(), yref, aref, f"cancelling N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_aq2x8_cancelling_codebooks_batch_invariant(M):
+    # the same inputs through the batch-invariant list path (the matrix-core kernel at every M)
+    N, K = 129, 8192
+    note(f"aq2x8 cancelling batch-invariant M={M}")
+    canon = aq2x8_cancelling(I.gen_weight(I.AQ2X8, N, K, (20,)), N, K, (20,))
+    x = I.gen_x(M, K, (20, M))
+    y = new_y(M, N)
+    dev = [dict(fmt=I.AQ2X8, N=N, K=K, w=upload_weight(I.AQ2X8, N, K, canon), x=upload_x(x), y=y)]
+    arr = W.make_proj_array(dev)
+    ws = workspace(W.wqd_stack_workspace_bytes(arr, M))
+    W.wqd_run_projections(arr, M, W.WQD_ORDERED | W.WQD_BATCH_INVARIANT, ws)
+    W.wqd_stream_check()
+    yref, aref = oracle.gemm_f64(I.AQ2X8, N, K, canon, x)
+    check_parity(y.cpu().numpy(), yref, aref, f"cancelling batch-invariant M={M}")
+
+
+TQ2_CODE3 = [(130, 1280), (70, 17408)]
+
+
+@pytest.mark.parametrize("N,K", TQ2_CODE3)
+def test_tq2_code3_dequant_bit_exact(N, K):
+    # code 3 decodes to +2d ("Anatomy of a PQ2_0 block"); the workloads never draw it
+    import torch
+    note(f"tq2 code 3 dequant N={N} K={K}")
+    canon = I.gen_weight(I.TQ2, N, K, (21, N, K), tq2_code3=0.1)
+    w = upload_weight(I.TQ2, N, K, canon)
+    out = torch.full((N, K), float("nan"), dtype=torch.float32, device="cuda")
+    W.wqd_dequant_f32(I.TQ2, N, K, w, out)
+    W.wqd_stream_check()
+    ref = oracle.dequant_f32(I.TQ2, N, K, canon)
+    assert (ref > 0).any() and np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K", TQ2_CODE3)
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_tq2_code3_gemm_parity(N, K, M):
+    # M = 1: the vector-ALU decode (fp16-subnormal fields); M > 1: the exact-fp16 matrix-core decode
+    note(f"tq2 code 3 gemm N={N} K={K} M={M}")
+    canon = I.gen_weight(I.TQ2, N, K, (22, N, K), tq2_code3=0.1)
+    x = I.gen_x(M, K, (22, N, K, M))
+    w = upload_weight(I.TQ2, N, K, canon)
+    y = run_gemm(I.TQ2, N, K, w, upload_x(x), M)
+    yref, aref = oracle.gemm_f64(I.TQ2, N, K, canon, x)
+    check_parity(y.cpu().numpy(), yref, aref, f"tq2 code 3 N={N} K={K} M={M}")
 
 
 @pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])

@@ -39,11 +39,13 @@ def test_quantizer_bit_exact(K, M):
     assert np.array_equal(s.cpu().numpy(), sr)
 
 
+@pytest.mark.parametrize("code3", [0.0, 0.1])
 @pytest.mark.parametrize("M", [1, 3, 8])
 @pytest.mark.parametrize("N,K", SHAPES)
-def test_int8_gemm_parity(N, K, M):
-    note(f"tq2 int8 gemm N={N} K={K} M={M}")
-    canon = I.gen_weight(I.TQ2, N, K, (91, N, K))
+def test_int8_gemm_parity(N, K, M, code3):
+    # code3 > 0: blocks holding code 3 (+2d, "Anatomy of a PQ2_0 block"), which the workloads never draw
+    note(f"tq2 int8 gemm N={N} K={K} M={M} code3={code3}")
+    canon = I.gen_weight(I.TQ2, N, K, (91, N, K), tq2_code3=code3)
     xb = I.gen_x(M, K, (91, N, K, M))
     w = upload_weight(I.TQ2, N, K, canon)
     y = new_y(M, N, ldy=N + 2)

@@ -14,9 +14,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FMTS = [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16]
 
 
-def declared_symbols():
-    text = open(os.path.join(ROOT, "include", "wqd.h")).read()
-    return sorted(set(re.findall(r"WQD_API\s+[\w\s\*]+?\b(wqd_\w+)\s*\(", text)))
+def declared_symbols(header="wqd.h", api="WQD_API"):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    return sorted(set(re.findall(api + r"\s+[\w\s\*]+?\b(wqd_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -26,6 +26,21 @@ def test_library_exports_every_declared_symbol():
     for s in syms:
         assert hasattr(L, s), s
     assert sorted(W.EXPORTED) == syms
+
+
+def test_probe_library_exports_every_declared_symbol():
+    # the read-only stream probe the bench times beside the kernels (include/wqd_probe.h)
+    import ctypes
+    syms = declared_symbols("wqd_probe.h", "WQD_PROBE_API")
+    assert syms == ["wqd_probe_read"]
+    L = ctypes.CDLL(os.path.join(ROOT, "weight_quantized_decode_amd", "libwqd_probe.so"))
+    for s in syms:
+        assert hasattr(L, s), s
+    L.wqd_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    # bad arguments are refused before any HIP call
+    assert L.wqd_probe_read(None, 16384, 256, 0, None) == -1
+    assert L.wqd_probe_read(256, 1000, 256, 0, None) == -1
+    assert L.wqd_probe_read(257, 16384, 256, 0, None) == -1
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -72,13 +72,14 @@ def _check(fmt: int, N: int, K: int) -> None:
 
 
 def gen_weight(fmt: int, N: int, K: int, key: Sequence[int], *, cb_sigma: float = 0.02,
-               scale_sigma: float | None = None) -> np.ndarray:
+               scale_sigma: float | None = None, tq2_code3: float = 0.0) -> np.ndarray:
     """Canonical bytes (uint8 array) of one random packed weight matrix.
 
     Distributions follow the workloads: Q4_0 codes uniform over 16 values and
     d = fp16(|N(0,1)|*0.01); CB4/CB8 centroids sorted fp16(N(0, cb_sigma)) with
     uniform codes; TQ2 codes 0/1/2 with probabilities .25/.5/.25 (code 3 never
-    drawn) and d = fp16(|N(0,1)|*0.02); AQ2x8 codebooks fp16(N(0,0.01)),
+    drawn, unless tq2_code3 > 0: then code 3 takes that share of the code-2 draws) and
+    d = fp16(|N(0,1)|*0.02); AQ2x8 codebooks fp16(N(0,0.01)),
     uniform 8-bit codes and row scales fp16(U(0.5,1.5)); AQ1x16 one codebook
     fp16(N(0,0.014)) (about the spread of a sum of two AQ2x8 entries), uniform
     16-bit codes and row scales fp16(U(0.5,1.5)).
@@ -105,8 +106,12 @@ def gen_weight(fmt: int, N: int, K: int, key: Sequence[int], *, cb_sigma: float 
         sig = 0.02 if scale_sigma is None else scale_sigma
         nb = K // 128
         d = f16_bits(np.abs(rng(*key, 0).standard_normal((N, nb))) * sig)
-        crumbs = rng(*key, 1).choice(np.array([0, 1, 2], dtype=np.uint8), size=(N, nb, 32, 4),
-                                     p=[0.25, 0.5, 0.25])
+        if tq2_code3 > 0:
+            crumbs = rng(*key, 1).choice(np.array([0, 1, 2, 3], dtype=np.uint8), size=(N, nb, 32, 4),
+                                         p=[0.25, 0.5, 0.25 - tq2_code3, tq2_code3])
+        else:
+            crumbs = rng(*key, 1).choice(np.array([0, 1, 2], dtype=np.uint8), size=(N, nb, 32, 4),
+                                         p=[0.25, 0.5, 0.25])
         qs = (crumbs[..., 0] | (crumbs[..., 1] << 2) | (crumbs[..., 2] << 4) | (crumbs[..., 3] << 6)).astype(np.uint8)
         blk = np.empty((N, nb, 34), dtype=np.uint8)
         blk[:, :, 0:2] = d.astype("<u2").view(np.uint8).reshape(N, nb, 2)
