@@ -43,9 +43,12 @@
  *   K must be a multiple of 32 (Q4_0), 2 (CB4), 1 (CB8), 128 (TQ2) or 8 (AQ2X8, AQ1X16).
  *
  * Prepared (device) layout: the same bytes re-laid once at load time into planes ("prepared
- * weights": a contiguous code plane, then the scale plane, then codebooks), built by
- * wqd_prepare_host and uploaded by the caller.  Its size is wqd_prepared_bytes(); it must be
- * 16-byte aligned on the device.
+ * weights": a code plane, then the scale plane, then codebooks), built by wqd_prepare_host and
+ * uploaded by the caller.  Its size is wqd_prepared_bytes(); it must be 16-byte aligned on the
+ * device.  wqd_bind turns a prepared buffer into a wqd_weight view (one pointer per plane), and
+ * every compute entry point takes that view (the ternary page's prepared-weight planes, "Anatomy
+ * of a PQ2_0 block"; trapetum "Benchmarks", "Per-layer PyTorch op speedup vs torch dense fp16": the
+ * per-projection op that replaces torch.mv takes such a weight and a short activation row).
  */
 #ifndef WQD_H
 #define WQD_H
@@ -89,17 +92,42 @@ WQD_API int64_t wqd_prepared_bytes(int fmt, int64_t N, int64_t K);
 WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonical_host,
                              int64_t canonical_bytes, void *prepared_host, int64_t prepared_bytes);
 
+/* ---------------------------------------------------------------- bound weights */
+
+/* A prepared weight matrix of one format, as plane pointers (device memory owned by the caller;
+ * the planes need not be contiguous).  Fields:
+ *   fmt, N, K          format and shape (N, K <= 2^30; K a whole number of blocks or groups);
+ *   codes              the code plane (16-byte aligned);
+ *   scales             Q4_0 / TQ2 block scales (8-byte aligned), AQ2X8 / AQ1X16 row scales
+ *                      (2-byte aligned); NULL for CB4, CB8;
+ *   codebooks          CB4 16 / CB8 256 entries (2-byte aligned), AQ2X8 C[2][256][8] / AQ1X16
+ *                      C[65536][8] (16-byte aligned); NULL for Q4_0, TQ2;
+ *   code_row_bytes     packed code bytes per row: K/2 (Q4_0, CB4), K (CB8), K/4 (TQ2, AQ2X8, AQ1X16);
+ *   scale_row_elems    scales per row: K/32 (Q4_0), K/128 (TQ2), 1 (AQ2X8, AQ1X16), 0 (CB4, CB8).
+ * Calls check every field and return WQD_EINVAL (missing plane, unknown format), WQD_ESHAPE
+ * (shape, or row sizes that do not match it) or WQD_EALIGN before any HIP call. */
+typedef struct {
+    int32_t fmt, N, K, pad;
+    const void *codes, *scales, *codebooks;
+    int64_t code_row_bytes, scale_row_elems;
+} wqd_weight;
+
+/* Fill *out with the planes of a prepared buffer (wqd_prepared_bytes(fmt, N, K) bytes, 16-byte
+ * aligned, laid out by wqd_prepare_host).  Pure host arithmetic: `prepared` is not read.  Errors:
+ * WQD_EINVAL (NULL argument, unknown format), WQD_ESHAPE, WQD_EALIGN. */
+WQD_API int wqd_bind(int fmt, int64_t N, int64_t K, const void *prepared, wqd_weight *out);
+
 /* ---------------------------------------------------------------- one projection */
 
-/* Device workspace wqd_gemm needs for this shape, in bytes (0 = none): one counter per 64-row
- * group and the split-K partial sums. */
-WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
+/* Device workspace wqd_gemm needs for this weight and M, in bytes (0 = none): split-K counters and
+ * partial sums.  Or a negative wqd_status. */
+WQD_API int64_t wqd_workspace_bytes(const wqd_weight *w, int64_t M);
 
-/* y[m*ldy + n] = sum_k x[m*ldx + k] * W[n][k] for 1 <= M <= 8, enqueued on `stream`.
- * w: prepared weights (wqd_prepared_bytes(fmt, N, K) bytes, 16-byte aligned).
+/* y[m*ldy + n] = sum_k x[m*ldx + k] * W[n][k] for 1 <= M <= 8 (N, K and W from the view w),
+ * enqueued on `stream`.
  * x: M rows of K fp16 values, ldx >= K and even, 4-byte aligned.  y: M rows of N fp32, ldy >= N.
- * workspace: at least wqd_gemm_workspace_bytes(fmt, N, K, M) bytes of device memory (may be NULL
- * when that is 0).  It must be zero-filled before its first use; every call leaves its counters
+ * workspace: at least wqd_workspace_bytes(w, M) bytes of device memory (may be NULL when that is
+ * 0).  It must be zero-filled before its first use; every call leaves its counters
  * at zero again, so it can be reused by later calls on the same stream (calls that overlap in
  * time must not share a workspace).  When K is split, the wave that finishes the last K-slice of
  * a 64-row group adds the slices' partial sums in ascending order, so results are the same bits
@@ -107,9 +135,8 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
  * fp32 lookup tables of the activations at M = 1, exact fp16 products of codebook entries summed
  * in fp32 on the matrix cores at M > 1; its K-splits are added in split order by the wave that
  * finishes last. */
-WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
-                     int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
-                     void *stream);
+WQD_API int wqd_gemm(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                     void *workspace, int64_t workspace_bytes, void *stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): wqd_gemm without a workspace argument.  The split-K counters and
@@ -119,16 +146,16 @@ WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x
  * at zero again.  The call allocates nothing (no hipMalloc, no allocating library routine).  All
  * calls on one GPU share the array: calls that overlap in time on one GPU (other streams, other
  * threads) race and must not be made.  Arguments and results as wqd_gemm; WQD_ESPACE when the
- * shape needs more than WQD_NOALLOC_MAX_BYTES (wqd_gemm_workspace_bytes() gives the need). */
+ * shape needs more than WQD_NOALLOC_MAX_BYTES (wqd_workspace_bytes() gives the need). */
 #define WQD_NOALLOC_MAX_BYTES (16ll << 20)
-WQD_API int wqd_gemm_noalloc(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
-                             int64_t ldx, float *y, int64_t ldy, void *stream);
+WQD_API int wqd_gemm_noalloc(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y,
+                             int64_t ldy, void *stream);
 
 /* ---------------------------------------------------------------- TQ2 with int8 activations */
 
 /* Device workspace wqd_gemm_i8 needs (always > 0): the quantized activations and wqd_gemm's
- * counters and partial sums.  fmt must be WQD_TQ2 (WQD_EINVAL otherwise). */
-WQD_API int64_t wqd_gemm_i8_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M);
+ * counters and partial sums.  w must be a WQD_TQ2 weight (WQD_EINVAL otherwise). */
+WQD_API int64_t wqd_gemm_i8_workspace_bytes(const wqd_weight *w, int64_t M);
 
 /* The TQ2 projection with int8 activations ("Making a ternary reasoning model fast in vLLM", "Why
  * small integers are a good fit"): each 128-element block of each row of x is quantized to int8,
@@ -136,12 +163,11 @@ WQD_API int64_t wqd_gemm_i8_workspace_bytes(int fmt, int64_t N, int64_t K, int64
  * block), then y[m][n] = sum_b d_b * a[m][b] * sum_{k in b} (code_k - 1) * q[m][k] with exact
  * integer block sums (v_dot4_i32_i8) and fp32 accumulation over blocks.  Two launches: the
  * quantizer, then the product.  Lossy against wqd_gemm: each activation moves by at most a/2, so
- * |y_i8 - y| <= sum_k |w[n][k]| * a(k) / 2.  Arguments as wqd_gemm (fmt must be WQD_TQ2, so K is a
- * multiple of 128); the workspace (256-byte aligned, at least wqd_gemm_i8_workspace_bytes) is
- * required and must be zero-filled before its first use, like wqd_gemm's. */
-WQD_API int wqd_gemm_i8(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
-                        int64_t ldx, float *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
-                        void *stream);
+ * |y_i8 - y| <= sum_k |w[n][k]| * a(k) / 2.  Arguments as wqd_gemm (w must be WQD_TQ2); the
+ * workspace (256-byte aligned, at least wqd_gemm_i8_workspace_bytes) is required and must be
+ * zero-filled before its first use, like wqd_gemm's. */
+WQD_API int wqd_gemm_i8(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Inspection of the quantizer wqd_gemm_i8 runs first: q[m*K + k] (int8, natural order), a[m*(K/128)
  * + b] (fp32) and qsum[m*(K/128) + b] (int32, the block's sum of q) for M <= 8 rows of x, K a
@@ -152,7 +178,7 @@ WQD_API int wqd_quantize_i8(const void *x, int64_t M, int64_t K, int64_t ldx, in
 /* Debug decode: out[n*K + k] = dequantized weight in fp32, bit-exact: the exact value for Q4_0,
  * CB4, CB8, TQ2 and AQ1X16 (all representable in fp32); for AQ2X8 fp32(fp32(C0 + C1) * s) with
  * round-to-nearest-even after the add and after the product. */
-WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream);
+WQD_API int wqd_dequant_f32(const wqd_weight *w, float *out, void *stream);
 
 /* ---------------------------------------------------------------- layer / stack */
 
@@ -173,13 +199,13 @@ typedef enum {
 } wqd_epilogue;
 
 typedef struct {
-    int32_t fmt;
-    int32_t epi;      /* wqd_epilogue */
-    int64_t N, K;
-    const void *w;    /* prepared weights */
-    const void *x;    /* fp16 activations, M rows of ldx */
+    const wqd_weight *w; /* bound weights (format and shape come from the view); host memory, read
+                            during the call only */
+    int32_t epi;         /* wqd_epilogue */
+    int32_t pad;
+    const void *x;       /* fp16 activations, M rows of ldx */
     int64_t ldx;
-    float *y;         /* fp32 outputs, M rows of ldy */
+    float *y;            /* fp32 outputs, M rows of ldy */
     int64_t ldy;
 } wqd_proj;
 

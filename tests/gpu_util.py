@@ -22,9 +22,10 @@ def note(msg: str) -> None:
 
 
 def upload_weight(fmt, N, K, canon):
+    """The prepared weights on the device, bound (a Weight view that keeps its buffer alive)."""
     import torch
     prep = W.wqd_prepare_host(fmt, N, K, canon)
-    return torch.from_numpy(prep).to("cuda")
+    return W.wqd_bind(fmt, N, K, torch.from_numpy(prep).to("cuda"))
 
 
 def upload_x(x_bits, ldx=None):
@@ -50,11 +51,10 @@ def workspace(nbytes):
     return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device="cuda")
 
 
-def run_gemm(fmt, N, K, w, x_dev, M, y=None, stream=None):
-    import torch
-    y = new_y(M, N) if y is None else y
-    ws = workspace(W.wqd_gemm_workspace_bytes(fmt, N, K, M))
-    W.wqd_gemm(fmt, N, K, w, x_dev, y, ws, stream)
+def run_gemm(w, x_dev, M, y=None, stream=None):
+    y = new_y(M, w.N) if y is None else y
+    ws = workspace(W.wqd_workspace_bytes(w, M))
+    W.wqd_gemm(w, x_dev, y, ws, stream)
     W.wqd_stream_check(stream)
     return y
 

@@ -35,7 +35,7 @@ def test_dequant_bit_exact(fmt, N, K):
     canon = I.gen_weight(fmt, N, K, (11, fmt, N, K))
     w = upload_weight(fmt, N, K, canon)
     out = torch.full((N, K), float("nan"), dtype=torch.float32, device="cuda")
-    W.wqd_dequant_f32(fmt, N, K, w, out)
+    W.wqd_dequant_f32(w, out)
     W.wqd_stream_check()
     got = out.cpu().numpy()
     ref = oracle.dequant_f32(fmt, N, K, canon)
@@ -50,7 +50,7 @@ def test_dequant_bit_exact_with_subnormal_scales():
         canon = I.gen_weight(fmt, N, K, (12, fmt), scale_sigma=2.0 ** -16)
         w = upload_weight(fmt, N, K, canon)
         out = torch.empty((N, K), dtype=torch.float32, device="cuda")
-        W.wqd_dequant_f32(fmt, N, K, w, out)
+        W.wqd_dequant_f32(w, out)
         W.wqd_stream_check()
         ref = oracle.dequant_f32(fmt, N, K, canon)
         assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
@@ -61,7 +61,7 @@ def test_dequant_bit_exact_with_subnormal_scales():
     canon = np.concatenate([C.view(np.uint8), canon[8192:]])
     w = upload_weight(I.AQ2X8, N, K, canon)
     out = torch.empty((N, K), dtype=torch.float32, device="cuda")
-    W.wqd_dequant_f32(I.AQ2X8, N, K, w, out)
+    W.wqd_dequant_f32(w, out)
     W.wqd_stream_check()
     ref = oracle.dequant_f32(I.AQ2X8, N, K, canon)
     assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
@@ -74,7 +74,7 @@ def test_gemm_parity_small(fmt, N, K, M):
     canon = I.gen_weight(fmt, N, K, (14, fmt, N, K))
     x = I.gen_x(M, K, (14, fmt, N, K, M))
     w = upload_weight(fmt, N, K, canon)
-    y = run_gemm(fmt, N, K, w, upload_x(x), M)
+    y = run_gemm(w, upload_x(x), M)
     yref, aref = oracle.gemm_f64(fmt, N, K, canon, x)
     check_parity(y.cpu().numpy(), yref, aref, f"fmt={fmt} N={N} K={K} M={M}")
 
@@ -88,7 +88,7 @@ def test_gemm_strided_x_and_y(fmt):
     w = upload_weight(fmt, N, K, canon)
     xd = upload_x(x, ldx=K + 40)
     y = new_y(M, N, ldy=N + 10, fill=-7.0)
-    run_gemm(fmt, N, K, w, xd, M, y=y)
+    run_gemm(w, xd, M, y=y)
     full = y.as_strided((M, N + 10), (N + 10, 1)).cpu().numpy()
     assert np.all(full[:, N:] == -7.0)  # padding of y untouched
     yref, aref = oracle.gemm_f64(fmt, N, K, canon, x)
@@ -102,8 +102,8 @@ def test_gemm_deterministic(fmt):
     canon = I.gen_weight(fmt, N, K, (16, fmt))
     x = upload_x(I.gen_x(M, K, (16, fmt)))
     w = upload_weight(fmt, N, K, canon)
-    a = run_gemm(fmt, N, K, w, x, M).cpu().numpy()
-    b = run_gemm(fmt, N, K, w, x, M).cpu().numpy()
+    a = run_gemm(w, x, M).cpu().numpy()
+    b = run_gemm(w, x, M).cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
@@ -123,7 +123,7 @@ def test_gemm_one_hot_and_zero_activations(fmt, M):
     k = 301
     x = np.zeros((M, K), dtype=np.uint16)
     x[0, k] = 0x3C00  # 1.0
-    y = run_gemm(fmt, N, K, w, upload_x(x), M).cpu().numpy()
+    y = run_gemm(w, upload_x(x), M).cpu().numpy()
     W64 = oracle.decode_f64(fmt, N, K, canon)
     if M > 1:
         assert np.all(y[1:] == 0.0)
@@ -132,7 +132,7 @@ def test_gemm_one_hot_and_zero_activations(fmt, M):
     if fmt == I.AQ2X8:
         dq = oracle.dequant_f32(fmt, N, K, canon)[:, k]
         assert np.array_equal(y[0].view(np.uint32), dq.view(np.uint32))
-    yz = run_gemm(fmt, N, K, w, upload_x(np.zeros((M, K), dtype=np.uint16)), M).cpu().numpy()
+    yz = run_gemm(w, upload_x(np.zeros((M, K), dtype=np.uint16)), M).cpu().numpy()
     assert np.all(yz == 0.0)
 
 
@@ -146,7 +146,7 @@ def test_aq2x8_cancelling_codebooks(N, K, M):
     canon = aq2x8_cancelling(I.gen_weight(I.AQ2X8, N, K, (19, N, K)), N, K, (19, N, K))
     x = I.gen_x(M, K, (19, N, K, M))
     w = upload_weight(I.AQ2X8, N, K, canon)
-    y = run_gemm(I.AQ2X8, N, K, w, upload_x(x), M)
+    y = run_gemm(w, upload_x(x), M)
     yref, aref = oracle.gemm_f64(I.AQ2X8, N, K, canon, x)
     check_parity(y.cpu().numpy(), yref, aref, f"cancelling N={N} K={K} M={M}")
 
@@ -179,7 +179,7 @@ def test_tq2_code3_dequant_bit_exact(N, K):
     canon = I.gen_weight(I.TQ2, N, K, (21, N, K), tq2_code3=0.1)
     w = upload_weight(I.TQ2, N, K, canon)
     out = torch.full((N, K), float("nan"), dtype=torch.float32, device="cuda")
-    W.wqd_dequant_f32(I.TQ2, N, K, w, out)
+    W.wqd_dequant_f32(w, out)
     W.wqd_stream_check()
     ref = oracle.dequant_f32(I.TQ2, N, K, canon)
     assert (ref > 0).any() and np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
@@ -193,7 +193,7 @@ def test_tq2_code3_gemm_parity(N, K, M):
     canon = I.gen_weight(I.TQ2, N, K, (22, N, K), tq2_code3=0.1)
     x = I.gen_x(M, K, (22, N, K, M))
     w = upload_weight(I.TQ2, N, K, canon)
-    y = run_gemm(I.TQ2, N, K, w, upload_x(x), M)
+    y = run_gemm(w, upload_x(x), M)
     yref, aref = oracle.gemm_f64(I.TQ2, N, K, canon, x)
     check_parity(y.cpu().numpy(), yref, aref, f"tq2 code 3 N={N} K={K} M={M}")
 
@@ -205,14 +205,15 @@ def test_workspace_reuse_leaves_counters_zero(fmt):
     import torch
     note(f"workspace reuse fmt={fmt}")
     shapes = [(300, 2048, 2), (130, 1024, 1), (300, 2048, 3)]
-    need = max(W.wqd_gemm_workspace_bytes(fmt, N, K, M) for N, K, M in shapes)
+    ws_ = [upload_weight(fmt, N, K, I.gen_weight(fmt, N, K, (18, fmt, i))) for i, (N, K, M) in enumerate(shapes)]
+    need = max(W.wqd_workspace_bytes(w, M) for w, (N, K, M) in zip(ws_, shapes))
     ws = workspace(need)
     for i, (N, K, M) in enumerate(shapes):
         canon = I.gen_weight(fmt, N, K, (18, fmt, i))
         x = I.gen_x(M, K, (18, fmt, i))
-        w = upload_weight(fmt, N, K, canon)
+        w = ws_[i]
         y = new_y(M, N)
-        W.wqd_gemm(fmt, N, K, w, upload_x(x), y, ws)
+        W.wqd_gemm(w, upload_x(x), y, ws)
         W.wqd_stream_check()
         yref, aref = oracle.gemm_f64(fmt, N, K, canon, x)
         check_parity(y.cpu().numpy(), yref, aref, f"reuse fmt={fmt} call {i}")

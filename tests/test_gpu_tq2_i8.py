@@ -49,8 +49,8 @@ def test_int8_gemm_parity(N, K, M, code3):
     xb = I.gen_x(M, K, (91, N, K, M))
     w = upload_weight(I.TQ2, N, K, canon)
     y = new_y(M, N, ldy=N + 2)
-    ws = workspace(W.wqd_gemm_i8_workspace_bytes(I.TQ2, N, K, M))
-    W.wqd_gemm_i8(I.TQ2, N, K, w, upload_x(xb), y, ws)
+    ws = workspace(W.wqd_gemm_i8_workspace_bytes(w, M))
+    W.wqd_gemm_i8(w, upload_x(xb), y, ws)
     W.wqd_stream_check()
     got = y.cpu().numpy().astype(np.float64)
     q, a, _ = oracle.quantize_x_i8(xb)
@@ -74,11 +74,11 @@ def test_int8_gemm_repeats_bits_and_reuses_its_workspace():
     canon = I.gen_weight(I.TQ2, N, K, (92, 0))
     xb = I.gen_x(M, K, (92, 1))
     w, x = upload_weight(I.TQ2, N, K, canon), upload_x(xb)
-    ws = workspace(W.wqd_gemm_i8_workspace_bytes(I.TQ2, N, K, M))
+    ws = workspace(W.wqd_gemm_i8_workspace_bytes(w, M))
     outs = []
     for _ in range(2):
         y = new_y(M, N)
-        W.wqd_gemm_i8(I.TQ2, N, K, w, x, y, ws)
+        W.wqd_gemm_i8(w, x, y, ws)
         W.wqd_stream_check()
         outs.append(y.cpu().numpy())
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))

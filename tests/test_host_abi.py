@@ -1,5 +1,6 @@
 """Host-side checks of libwqd (no GPU needed): exported symbols, byte counts, the prepared
 layout's re-lay of the canonical bytes, and argument validation before any HIP call."""
+import ctypes
 import os
 import re
 
@@ -148,51 +149,124 @@ def test_prepare_rejects_bad_arguments():
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
 
 
-@pytest.mark.parametrize("args,status", [
-    ((9, 64, 64, FAKE, FAKE, 1, 64, FAKE, 64), W.WQD_EINVAL),          # unknown format
-    ((1, 64, 48, FAKE, FAKE, 1, 64, FAKE, 64), W.WQD_ESHAPE),          # K not whole blocks
-    ((1, 64, 64, FAKE, FAKE, 0, 64, FAKE, 64), W.WQD_ESHAPE),          # M = 0
-    ((1, 64, 64, FAKE, FAKE, 9, 64, FAKE, 64), W.WQD_ESHAPE),          # M = 9
-    ((1, 64, 64, FAKE, FAKE, 1, 32, FAKE, 64), W.WQD_ESHAPE),          # ldx < K
-    ((1, 64, 64, FAKE, FAKE, 1, 64, FAKE, 10), W.WQD_ESHAPE),          # ldy < N
-    ((1, 64, 64, FAKE + 8, FAKE, 1, 64, FAKE, 64), W.WQD_EALIGN),      # w not 16-byte aligned
-    ((1, 64, 64, FAKE, FAKE + 2, 1, 64, FAKE, 64), W.WQD_EALIGN),      # x not 4-byte aligned
-    ((1, 64, 64, FAKE, FAKE, 1, 65, FAKE, 64), W.WQD_EALIGN),          # odd ldx
-    ((1, 64, 64, None, FAKE, 1, 64, FAKE, 64), W.WQD_EINVAL),          # null weight
+def _view(fmt, N, K, base=FAKE):
+    """A bound view of a never-dereferenced prepared buffer at base."""
+    return W.wqd_bind(fmt, N, K, base)
+
+
+def test_bind_sets_the_planes_of_each_format():
+    for fmt in (I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16):
+        N, K = 96, 1024
+        v = _view(fmt, N, K).view
+        assert (v.fmt, v.N, v.K, v.codes) == (fmt, N, K, FAKE)
+        has_scales = fmt in (I.Q4_0, I.TQ2, I.AQ2X8, I.AQ1X16)
+        has_cbk = fmt in (I.CB4, I.CB8, I.AQ2X8, I.AQ1X16)
+        assert (v.scales is not None) == has_scales and (v.codebooks is not None) == has_cbk
+        # every plane lies inside the prepared buffer
+        end = FAKE + W.wqd_prepared_bytes(fmt, N, K)
+        for p in (v.scales, v.codebooks):
+            assert p is None or FAKE < p < end
+        assert v.scale_row_elems == {I.Q4_0: K // 32, I.TQ2: K // 128, I.AQ2X8: 1, I.AQ1X16: 1}.get(fmt, 0)
+        assert v.code_row_bytes == {I.Q4_0: K // 2, I.CB4: K // 2, I.CB8: K}.get(fmt, K // 4)
+
+
+def test_bind_errors():
+    L, v = W.lib(), W.wqd_weight()
+    assert L.wqd_bind(9, 64, 64, FAKE, ctypes.byref(v)) == W.WQD_EINVAL     # unknown format
+    assert L.wqd_bind(1, 64, 48, FAKE, ctypes.byref(v)) == W.WQD_ESHAPE     # K not whole blocks
+    assert L.wqd_bind(1, 0, 64, FAKE, ctypes.byref(v)) == W.WQD_ESHAPE      # N = 0
+    assert L.wqd_bind(1, 64, 64, None, ctypes.byref(v)) == W.WQD_EINVAL     # null buffer
+    assert L.wqd_bind(1, 64, 64, FAKE, None) == W.WQD_EINVAL                # null view
+    assert L.wqd_bind(1, 64, 64, FAKE + 8, ctypes.byref(v)) == W.WQD_EALIGN  # buffer not 16-byte aligned
+
+
+def _edited(base_fmt, **fields):
+    w = _view(base_fmt, 64, 64)
+    for k, val in fields.items():
+        setattr(w.view, k, val)
+    return w
+
+
+@pytest.mark.parametrize("spec,x,M,ldx,y,ldy,status", [
+    ((1, dict(fmt=9)), FAKE, 1, 64, FAKE, 64, W.WQD_EINVAL),                 # unknown format
+    ((1, dict(K=48)), FAKE, 1, 64, FAKE, 64, W.WQD_ESHAPE),                  # K not whole blocks
+    ((1, dict(K=128)), FAKE, 1, 128, FAKE, 64, W.WQD_ESHAPE),                # row sizes of another K
+    ((1, dict(scale_row_elems=1)), FAKE, 1, 64, FAKE, 64, W.WQD_ESHAPE),     # scale rows disagree
+    ((1, {}), FAKE, 0, 64, FAKE, 64, W.WQD_ESHAPE),                  # M = 0
+    ((1, {}), FAKE, 9, 64, FAKE, 64, W.WQD_ESHAPE),                  # M = 9
+    ((1, {}), FAKE, 1, 32, FAKE, 64, W.WQD_ESHAPE),                  # ldx < K
+    ((1, {}), FAKE, 1, 64, FAKE, 10, W.WQD_ESHAPE),                  # ldy < N
+    ((1, dict(codes=FAKE + 8)), FAKE, 1, 64, FAKE, 64, W.WQD_EALIGN),        # codes not 16-byte aligned
+    ((1, dict(scales=FAKE + 4100)), FAKE, 1, 64, FAKE, 64, W.WQD_EALIGN),    # Q4_0 scales not 8-byte aligned
+    ((5, dict(codebooks=FAKE + 8)), FAKE, 1, 64, FAKE, 64, W.WQD_EALIGN),    # AQ2X8 codebooks not 16-byte aligned
+    ((1, {}), FAKE + 2, 1, 64, FAKE, 64, W.WQD_EALIGN),              # x not 4-byte aligned
+    ((1, {}), FAKE, 1, 65, FAKE, 64, W.WQD_EALIGN),                  # odd ldx
+    ((1, dict(codes=None)), FAKE, 1, 64, FAKE, 64, W.WQD_EINVAL),            # null codes
+    ((1, dict(scales=None)), FAKE, 1, 64, FAKE, 64, W.WQD_EINVAL),           # Q4_0 without scales
+    ((2, dict(codebooks=None)), FAKE, 1, 64, FAKE, 64, W.WQD_EINVAL),        # CB4 without a codebook
+    ((1, {}), None, 1, 64, FAKE, 64, W.WQD_EINVAL),                  # null x
 ])
-def test_gemm_argument_errors_before_any_launch(args, status):
-    fmt, N, K, w, x, M, ldx, y, ldy = args
-    assert W.lib().wqd_gemm(fmt, N, K, w, x, M, ldx, y, ldy, None, 0, None) == status
+def test_gemm_argument_errors_before_any_launch(spec, x, M, ldx, y, ldy, status):
+    w = _edited(spec[0], **spec[1])
+    L = W.lib()
+    assert L.wqd_gemm(w.ref(), x, M, ldx, y, ldy, None, 0, None) == status
+    assert L.wqd_gemm_noalloc(w.ref(), x, M, ldx, y, ldy, None) == status
+
+
+def test_gemm_null_view():
+    L = W.lib()
+    assert L.wqd_gemm(None, FAKE, 1, 64, FAKE, 64, None, 0, None) == W.WQD_EINVAL
+    assert L.wqd_workspace_bytes(None, 1) == W.WQD_EINVAL
+    assert L.wqd_dequant_f32(None, FAKE, None) == W.WQD_EINVAL
+
+
+def test_workspace_bytes_rules():
+    w = _view(I.Q4_0, 64, 32768)
+    assert W.wqd_workspace_bytes(w, 1) > 0                       # long K: split, needs counters
+    assert W.lib().wqd_workspace_bytes(w.ref(), 0) == W.WQD_ESHAPE
+    assert W.lib().wqd_workspace_bytes(w.ref(), 9) == W.WQD_ESHAPE
+    assert W.lib().wqd_workspace_bytes(_edited(1, fmt=9).ref(), 1) == W.WQD_EINVAL
 
 
 def test_gemm_workspace_too_small_is_reported():
     # one 64-row group with a long K: its K is split, so it needs counters and partials
-    need = W.wqd_gemm_workspace_bytes(I.Q4_0, 64, 32768, 1)
+    w = _view(I.Q4_0, 64, 32768)
+    need = W.wqd_workspace_bytes(w, 1)
     assert need > 0
-    assert W.lib().wqd_gemm(I.Q4_0, 64, 32768, FAKE, FAKE, 1, 32768, FAKE, 64, FAKE, need - 4,
-                            None) == W.WQD_ESPACE
+    assert W.lib().wqd_gemm(w.ref(), FAKE, 1, 32768, FAKE, 64, FAKE, need - 4, None) == W.WQD_ESPACE
+
+
+def _list(entries):
+    """wqd_proj array of (fmt, N, K, epi, x) entries on never-dereferenced pointers."""
+    arr = (W.wqd_proj * len(entries))()
+    keep = []
+    for i, (fmt, N, K, epi, x) in enumerate(entries):
+        w = _view(fmt, N, K, FAKE + (i << 26))
+        keep.append(w)
+        arr[i].w = ctypes.pointer(w.view)
+        arr[i].epi, arr[i].x, arr[i].ldx = epi, x, K
+        arr[i].y, arr[i].ldy = FAKE + (i << 26) + (1 << 25), N
+    arr._keep = keep
+    return arr
+
+
+_fake_list = _list
 
 
 def test_run_projections_rejects_bad_mode_and_lists():
-    arr = (W.wqd_proj * 1)()
-    arr[0].fmt, arr[0].N, arr[0].K = I.CB4, 64, 64
-    arr[0].w, arr[0].x, arr[0].y, arr[0].ldx, arr[0].ldy = FAKE, FAKE, FAKE, 64, 64
+    arr = _list([(I.CB4, 64, 64, W.WQD_EPI_NONE, FAKE)])
     L = W.lib()
     assert L.wqd_run_projections(arr, 1, 1, 7, FAKE, 1 << 20, None) == W.WQD_EINVAL
     assert L.wqd_run_projections(arr, 1, 0, 0, FAKE, 1 << 20, None) == W.WQD_ESHAPE
     arr[0].epi = 7  # no such epilogue
     assert L.wqd_run_projections(arr, 1, 1, 0, FAKE, 1 << 20, None) == W.WQD_EINVAL
     assert L.wqd_stack_workspace_bytes(arr, 1, 1) == W.WQD_EINVAL
-
-
-def _fake_list(entries):
-    """wqd_proj array of (fmt, N, K, epi, x) entries on never-dereferenced pointers."""
-    arr = (W.wqd_proj * len(entries))()
-    for i, (fmt, N, K, epi, x) in enumerate(entries):
-        arr[i].fmt, arr[i].N, arr[i].K, arr[i].epi = fmt, N, K, epi
-        arr[i].w, arr[i].x, arr[i].ldx = FAKE + (i << 24), x, K
-        arr[i].y, arr[i].ldy = FAKE + (i << 24) + (1 << 23), N
-    return arr
+    arr[0].epi = W.WQD_EPI_NONE
+    arr[0].w = None  # an entry without a weight view
+    assert L.wqd_stack_workspace_bytes(arr, 1, 1) == W.WQD_EINVAL
+    bad = _edited(I.CB4, codes=FAKE + 4)  # a view that fails its own checks
+    arr[0].w = ctypes.pointer(bad.view)
+    assert L.wqd_stack_workspace_bytes(arr, 1, 1) == W.WQD_EALIGN
 
 
 G, U, A, E0 = W.WQD_EPI_SILU_GATE, W.WQD_EPI_SILU_UP, W.WQD_EPI_ADD, W.WQD_EPI_NONE
@@ -282,12 +356,13 @@ def test_batch_invariant_flag_rules():
 
 def test_int8_entry_point_rules():
     L = W.lib()
-    assert L.wqd_gemm_i8_workspace_bytes(I.CB4, 64, 1024, 1) == W.WQD_EINVAL  # TQ2 only
-    assert L.wqd_gemm_i8_workspace_bytes(I.TQ2, 64, 1024, 1) > 0
-    assert L.wqd_gemm_i8(I.TQ2, 64, 1024, FAKE, FAKE, 1, 1024, FAKE, 64, None, 0, None) == W.WQD_EINVAL
-    need = L.wqd_gemm_i8_workspace_bytes(I.TQ2, 64, 1024, 1)
-    assert L.wqd_gemm_i8(I.TQ2, 64, 1024, FAKE, FAKE, 1, 1024, FAKE, 64, FAKE, need - 1, None) == W.WQD_ESPACE
-    assert L.wqd_gemm_i8(I.TQ2, 64, 1000, FAKE, FAKE, 1, 1024, FAKE, 64, FAKE, need, None) == W.WQD_ESHAPE
+    cb, tq = _view(I.CB4, 64, 1024), _view(I.TQ2, 64, 1024)
+    assert L.wqd_gemm_i8_workspace_bytes(cb.ref(), 1) == W.WQD_EINVAL  # TQ2 only
+    assert L.wqd_gemm_i8_workspace_bytes(tq.ref(), 1) > 0
+    assert L.wqd_gemm_i8(tq.ref(), FAKE, 1, 1024, FAKE, 64, None, 0, None) == W.WQD_EINVAL
+    need = L.wqd_gemm_i8_workspace_bytes(tq.ref(), 1)
+    assert L.wqd_gemm_i8(tq.ref(), FAKE, 1, 1024, FAKE, 64, FAKE, need - 1, None) == W.WQD_ESPACE
+    assert L.wqd_gemm_i8(tq.ref(), FAKE, 1, 1000, FAKE, 64, FAKE, need, None) == W.WQD_ESHAPE
     assert L.wqd_quantize_i8(FAKE, 1, 100, 128, FAKE, FAKE, FAKE, None) == W.WQD_ESHAPE
     assert L.wqd_quantize_i8(None, 1, 128, 128, FAKE, FAKE, FAKE, None) == W.WQD_EINVAL
 
@@ -317,10 +392,12 @@ def test_size_limits(fmt):
     assert W.lib().wqd_prepared_bytes(fmt, W.WQD_MAX_N + 1, 1024) == W.WQD_ESHAPE
     assert W.lib().wqd_prepared_bytes(fmt, 64, W.WQD_MAX_K + kb) == W.WQD_ESHAPE
     assert W.lib().wqd_canonical_bytes(fmt, 64, W.WQD_MAX_K + kb) == W.WQD_ESHAPE
-    assert W.lib().wqd_gemm(fmt, W.WQD_MAX_N + 1, 1024, FAKE, FAKE, 1, 1024, FAKE, W.WQD_MAX_N + 1,
-                            None, 0, None) == W.WQD_ESHAPE
-    assert W.lib().wqd_gemm(fmt, 64, W.WQD_MAX_K + kb, FAKE, FAKE, 1, W.WQD_MAX_K + kb, FAKE, 64,
-                            None, 0, None) == W.WQD_ESHAPE
+    v = W.wqd_weight()
+    assert W.lib().wqd_bind(fmt, W.WQD_MAX_N + 1, 1024, FAKE, ctypes.byref(v)) == W.WQD_ESHAPE
+    assert W.lib().wqd_bind(fmt, 64, W.WQD_MAX_K + kb, FAKE, ctypes.byref(v)) == W.WQD_ESHAPE
+    big = _view(fmt, W.WQD_MAX_N, 1024)
+    big.view.N = W.WQD_MAX_N + 1  # a hand-edited view past the limit
+    assert W.lib().wqd_gemm(big.ref(), FAKE, 1, 1024, FAKE, W.WQD_MAX_N + 1, None, 0, None) == W.WQD_ESHAPE
 
 
 def test_aq2x8_launch_counts():
@@ -340,9 +417,10 @@ def test_gemm_noalloc_rejects_shapes_beyond_the_scratch():
     # an 8-row CB8 call over 2^20 rows with split K needs more than the scratch array holds: the
     # call is refused before any HIP call (the pointers are never read)
     N, K, M = 1 << 20, 4096, 8
-    need = W.wqd_gemm_workspace_bytes(I.CB8, N, K, M)
+    w = _view(I.CB8, N, K, 256)
+    need = W.wqd_workspace_bytes(w, M)
     assert need > W.WQD_NOALLOC_MAX_BYTES
-    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, 256, 256, M, K, 256, N, None) == W.WQD_ESPACE
+    assert W.lib().wqd_gemm_noalloc(w.ref(), 256, M, K, 256, N, None) == W.WQD_ESPACE
     # argument errors come first, as for wqd_gemm
-    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, None, 256, M, K, 256, N, None) == W.WQD_EINVAL
-    assert W.lib().wqd_gemm_noalloc(I.CB8, N, K, 256, 256, 9, K, 256, N, None) == W.WQD_ESHAPE
+    assert W.lib().wqd_gemm_noalloc(w.ref(), None, M, K, 256, N, None) == W.WQD_EINVAL
+    assert W.lib().wqd_gemm_noalloc(w.ref(), 256, 9, K, 256, N, None) == W.WQD_ESHAPE

@@ -20,18 +20,17 @@ CALLS = [(4096, 11008, 3), (1000, 11008, 1)]
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_noalloc_matches_gemm_two_calls(fmt):
-    for N, K, M in CALLS:
-        assert 0 < W.wqd_gemm_workspace_bytes(fmt, N, K, M) <= W.WQD_NOALLOC_MAX_BYTES
     for i, (N, K, M) in enumerate(CALLS):
         note(f"noalloc fmt={fmt} call {i} N={N} K={K} M={M}")
         canon = I.gen_weight(fmt, N, K, (40, fmt, i))
         x = I.gen_x(M, K, (40, fmt, i))
         w = upload_weight(fmt, N, K, canon)
+        assert 0 < W.wqd_workspace_bytes(w, M) <= W.WQD_NOALLOC_MAX_BYTES
         xd = upload_x(x)
         y_ref = new_y(M, N)
-        W.wqd_gemm(fmt, N, K, w, xd, y_ref, workspace(W.wqd_gemm_workspace_bytes(fmt, N, K, M)))
+        W.wqd_gemm(w, xd, y_ref, workspace(W.wqd_workspace_bytes(w, M)))
         y = new_y(M, N)
-        W.wqd_gemm_noalloc(fmt, N, K, w, xd, y)
+        W.wqd_gemm_noalloc(w, xd, y)
         W.wqd_stream_check()
         a, b = y.cpu().numpy(), y_ref.cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"fmt={fmt} call {i}"

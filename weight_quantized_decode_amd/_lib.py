@@ -26,7 +26,7 @@ WQD_MAX_N = 1 << 30
 WQD_MAX_K = 1 << 30
 
 EXPORTED = [
-    "wqd_canonical_bytes", "wqd_prepared_bytes", "wqd_prepare_host", "wqd_gemm_workspace_bytes",
+    "wqd_canonical_bytes", "wqd_prepared_bytes", "wqd_prepare_host", "wqd_bind", "wqd_workspace_bytes",
     "wqd_gemm", "wqd_dequant_f32", "wqd_stack_workspace_bytes", "wqd_stack_setup",
     "wqd_run_projections", "wqd_run_projections_timed", "wqd_stack_launches", "wqd_stream_check",
     "wqd_last_hip_error", "wqd_status_str", "wqd_gemm_i8_workspace_bytes", "wqd_gemm_i8", "wqd_quantize_i8",
@@ -44,10 +44,38 @@ class WqdError(RuntimeError):
         super().__init__(f"{fn} failed with status {status}: {msg}")
 
 
+class wqd_weight(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("codebooks", ctypes.c_void_p),
+                ("code_row_bytes", ctypes.c_int64), ("scale_row_elems", ctypes.c_int64)]
+
+
 class wqd_proj(ctypes.Structure):
-    _fields_ = [("fmt", ctypes.c_int32), ("epi", ctypes.c_int32), ("N", ctypes.c_int64),
-                ("K", ctypes.c_int64), ("w", ctypes.c_void_p), ("x", ctypes.c_void_p),
-                ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+    _fields_ = [("w", ctypes.POINTER(wqd_weight)), ("epi", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+class Weight:
+    """A bound wqd_weight view and the device buffer it points into (kept alive with it)."""
+
+    def __init__(self, view: wqd_weight, buf=None):
+        self.view = view
+        self.buf = buf
+
+    @property
+    def fmt(self) -> int:
+        return self.view.fmt
+
+    @property
+    def N(self) -> int:
+        return self.view.N
+
+    @property
+    def K(self) -> int:
+        return self.view.K
+
+    def ref(self):
+        return ctypes.byref(self.view)
 
 
 _lib = None
@@ -65,12 +93,13 @@ def lib() -> ctypes.CDLL:
             "wqd_canonical_bytes": (i64, [ctypes.c_int, i64, i64]),
             "wqd_prepared_bytes": (i64, [ctypes.c_int, i64, i64]),
             "wqd_prepare_host": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, i64, vp, i64]),
-            "wqd_gemm_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
-            "wqd_gemm": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
-            "wqd_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp]),
-            "wqd_dequant_f32": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp]),
-            "wqd_gemm_i8_workspace_bytes": (i64, [ctypes.c_int, i64, i64, i64]),
-            "wqd_gemm_i8": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, i64, i64, vp, i64, vp, i64, vp]),
+            "wqd_bind": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, ctypes.POINTER(wqd_weight)]),
+            "wqd_workspace_bytes": (i64, [ctypes.POINTER(wqd_weight), i64]),
+            "wqd_gemm": (ctypes.c_int, [ctypes.POINTER(wqd_weight), vp, i64, i64, vp, i64, vp, i64, vp]),
+            "wqd_gemm_noalloc": (ctypes.c_int, [ctypes.POINTER(wqd_weight), vp, i64, i64, vp, i64, vp]),
+            "wqd_dequant_f32": (ctypes.c_int, [ctypes.POINTER(wqd_weight), vp, vp]),
+            "wqd_gemm_i8_workspace_bytes": (i64, [ctypes.POINTER(wqd_weight), i64]),
+            "wqd_gemm_i8": (ctypes.c_int, [ctypes.POINTER(wqd_weight), vp, i64, i64, vp, i64, vp, i64, vp]),
             "wqd_quantize_i8": (ctypes.c_int, [vp, i64, i64, i64, vp, vp, vp, vp]),
             "wqd_stack_workspace_bytes": (i64, [ctypes.POINTER(wqd_proj), i32, i64]),
             "wqd_stack_setup": (ctypes.c_int, [ctypes.POINTER(wqd_proj), i32, i64, i32, vp, i64, vp]),
@@ -130,36 +159,46 @@ def wqd_prepare_host(fmt: int, N: int, K: int, canonical: np.ndarray) -> np.ndar
     return out
 
 
+# ------------------------------------------------------------------------- bound weights
+
+def wqd_bind(fmt: int, N: int, K: int, prepared) -> Weight:
+    """The plane view of a prepared weight buffer (a device tensor, or a raw address)."""
+    view = wqd_weight()
+    addr = prepared if isinstance(prepared, int) else _dptr(prepared)
+    _check("wqd_bind", lib().wqd_bind(fmt, N, K, addr, ctypes.byref(view)))
+    return Weight(view, None if isinstance(prepared, int) else prepared)
+
+
 # ------------------------------------------------------------------------- one projection
 
-def wqd_gemm_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
-    return _check("wqd_gemm_workspace_bytes", lib().wqd_gemm_workspace_bytes(fmt, N, K, M))
+def wqd_workspace_bytes(w: Weight, M: int) -> int:
+    return _check("wqd_workspace_bytes", lib().wqd_workspace_bytes(w.ref(), M))
 
 
-def wqd_gemm(fmt: int, N: int, K: int, w, x, y, workspace=None, stream=None) -> None:
+def wqd_gemm(w: Weight, x, y, workspace=None, stream=None) -> None:
     """y[M, N] (fp32) = x[M, K] (fp16) times the dequantized W[N, K]; x and y may have row strides."""
     M = x.shape[0]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("wqd_gemm", lib().wqd_gemm(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
-                                      _dptr(workspace), ws_bytes, _stream(stream)))
+    _check("wqd_gemm", lib().wqd_gemm(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0), _dptr(workspace),
+                                      ws_bytes, _stream(stream)))
 
 
-def wqd_gemm_noalloc(fmt: int, N: int, K: int, w, x, y, stream=None) -> None:
+def wqd_gemm_noalloc(w: Weight, x, y, stream=None) -> None:
     """wqd_gemm without a workspace: the library's per-GPU scratch array serves as one."""
     M = x.shape[0]
-    _check("wqd_gemm_noalloc", lib().wqd_gemm_noalloc(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y),
-                                                      y.stride(0), _stream(stream)))
+    _check("wqd_gemm_noalloc", lib().wqd_gemm_noalloc(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
+                                                      _stream(stream)))
 
 
-def wqd_gemm_i8_workspace_bytes(fmt: int, N: int, K: int, M: int) -> int:
-    return _check("wqd_gemm_i8_workspace_bytes", lib().wqd_gemm_i8_workspace_bytes(fmt, N, K, M))
+def wqd_gemm_i8_workspace_bytes(w: Weight, M: int) -> int:
+    return _check("wqd_gemm_i8_workspace_bytes", lib().wqd_gemm_i8_workspace_bytes(w.ref(), M))
 
 
-def wqd_gemm_i8(fmt: int, N: int, K: int, w, x, y, workspace, stream=None) -> None:
+def wqd_gemm_i8(w: Weight, x, y, workspace, stream=None) -> None:
     """TQ2 times int8-quantized x (quantized inside the call); x and y may have row strides."""
     M = x.shape[0]
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("wqd_gemm_i8", lib().wqd_gemm_i8(fmt, N, K, _dptr(w), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
+    _check("wqd_gemm_i8", lib().wqd_gemm_i8(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
                                             _dptr(workspace), ws_bytes, _stream(stream)))
 
 
@@ -170,28 +209,32 @@ def wqd_quantize_i8(x, q, a, qsum, stream=None) -> None:
                                                     _stream(stream)))
 
 
-def wqd_dequant_f32(fmt: int, N: int, K: int, w, out, stream=None) -> None:
-    _check("wqd_dequant_f32", lib().wqd_dequant_f32(fmt, N, K, _dptr(w), _dptr(out), _stream(stream)))
+def wqd_dequant_f32(w: Weight, out, stream=None) -> None:
+    _check("wqd_dequant_f32", lib().wqd_dequant_f32(w.ref(), _dptr(out), _stream(stream)))
 
 
 # ------------------------------------------------------------------------- layer / stack
 
 def make_proj_array(projs: Sequence[dict]):
-    """projs: dicts with fmt, N, K, w, x, y (torch tensors) and optionally epi (a WQD_EPI_*
-    value; y may be None for a WQD_EPI_SILU_UP entry); returns a ctypes array of wqd_proj.
-    The array holds raw device pointers: the caller keeps the tensors alive while it is used."""
+    """projs: dicts with w (a Weight, or a prepared device tensor together with fmt, N and K), x, y
+    (torch tensors) and optionally epi (a WQD_EPI_* value; y may be None for a WQD_EPI_SILU_UP
+    entry); returns a ctypes array of wqd_proj.  The array holds raw device pointers and keeps the
+    weight views alive; the caller keeps the tensors alive while it is used."""
     arr = (wqd_proj * len(projs))()
+    keep = []
     for i, p in enumerate(projs):
-        arr[i].fmt = p["fmt"]
+        w = p["w"]
+        if not isinstance(w, Weight):
+            w = wqd_bind(p["fmt"], p["N"], p["K"], w)
+        keep.append(w)
+        arr[i].w = ctypes.pointer(w.view)
         arr[i].epi = p.get("epi", WQD_EPI_NONE)
-        arr[i].N = p["N"]
-        arr[i].K = p["K"]
-        arr[i].w = p["w"].data_ptr()
         arr[i].x = p["x"].data_ptr()
         arr[i].ldx = p["x"].stride(0)
         y = p.get("y")
         arr[i].y = None if y is None else y.data_ptr()
         arr[i].ldy = 0 if y is None else y.stride(0)
+    arr._keep = keep
     return arr
 
 

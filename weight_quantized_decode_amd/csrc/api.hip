@@ -18,7 +18,8 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 
 // Debug decode of the prepared layout to dense fp32, one thread per (row, chunk).
 template <int FMT>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, Layout L, float *out) {
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, const uint8_t *scales, const uint16_t *cbk,
+                                                      Layout L, float *out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= L.N * L.C) return;
     const int64_t n = i / L.C, c = i - n * L.C;
@@ -26,10 +27,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, Layout L
     const uint4 v = *reinterpret_cast<const uint4 *>(w + ((g * L.C + c) * 64 + r) * 16);
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
     float *orow = out + n * L.K;
-    const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
     if constexpr (FMT == Q4_0 || FMT == TQ2) {
         const int64_t b = (FMT == Q4_0) ? c : c / 2;
-        const uint16_t dh = reinterpret_cast<const uint16_t *>(w + L.off_scales)[((g * L.Q + b / 4) * 64 + r) * 4 + b % 4];
+        const uint16_t dh = reinterpret_cast<const uint16_t *>(scales)[((g * L.Q + b / 4) * 64 + r) * 4 + b % 4];
         const float d = half_bits_to_float(dh);
         for (int t = 0; t < 4; t++) {
             if constexpr (FMT == Q4_0) {
@@ -64,29 +64,29 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *w, Layout L
 
 // Debug decode of AQ1X16, one thread per (row, group of 8 weights): fp16 scale times fp16 entry
 // (exact in fp32).
-__global__ __launch_bounds__(256) void dequant_aq1x16_kernel(const uint8_t *w, Layout L, float *out) {
+__global__ __launch_bounds__(256) void dequant_aq1x16_kernel(const uint8_t *w, const uint16_t *rscale,
+                                                             const uint16_t *cbk, Layout L, float *out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= L.N * (L.K / 8)) return;
     const int64_t G = L.K / 8;
     const int64_t n = i / G, g = i - n * G;
     const int64_t g64 = n / 64, r = n % 64, c = g / 8;
     const uint16_t code = reinterpret_cast<const uint16_t *>(w + ((g64 * L.C + c) * 64 + r) * 16)[g % 8];
-    const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
-    const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
+    const float s = half_bits_to_float(rscale[n]);
     float *o = out + n * L.K + g * 8;
     for (int j = 0; j < 8; j++) o[j] = __fmul_rn(half_bits_to_float(cbk[(int64_t)code * 8 + j]), s);
 }
 
 // Debug decode of the AQ2X8 tile layout, one thread per (row, group of 8 weights).
-__global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, Layout L, float *out) {
+__global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, const uint16_t *rscale,
+                                                            const uint16_t *cbk, Layout L, float *out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= L.N * L.G) return;
     const int64_t n = i / L.G, g = i - n * L.G;
     const int64_t lane = ((n % 16) / 8) * 32 + g % 32;
     const uint8_t *t = w + ((g / 32 * (L.Npad / 16) + n / 16) * 64 + lane) * 16 + 2 * (n % 8);
     const uint32_t c0 = t[0], c1 = t[1];
-    const uint16_t *cbk = reinterpret_cast<const uint16_t *>(w + L.off_cbk);
-    const float s = half_bits_to_float(reinterpret_cast<const uint16_t *>(w + L.off_scales)[n]);
+    const float s = half_bits_to_float(rscale[n]);
     float *o = out + n * L.K + g * 8;
     for (int j = 0; j < 8; j++) {
         const float e0 = half_bits_to_float(cbk[(0 * 256 + c0) * 8 + j]);
@@ -311,14 +311,13 @@ static Plan plan_single(int fmt, int64_t N, int64_t K, int64_t M, int cus) {
     return P;
 }
 
-static Desc make_desc(const Plan &P, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
+static Desc make_desc(const Plan &P, const wqd_weight *w, const void *x, int64_t ldx, float *y, int64_t ldy,
                       float *part, int *cnt) {
     Desc D;
     memset(&D, 0, sizeof(D));
-    const uint8_t *base = static_cast<const uint8_t *>(w);
-    D.codes = base;
-    D.scales = base + P.L.off_scales;
-    D.cbk = reinterpret_cast<const uint16_t *>(base + P.L.off_cbk);
+    D.codes = static_cast<const uint8_t *>(w->codes);
+    D.scales = static_cast<const uint8_t *>(w->scales);
+    D.cbk = static_cast<const uint16_t *>(w->codebooks);
     D.x = static_cast<const uint16_t *>(x);
     D.y = y;
     D.part = P.S > 1 ? part : nullptr;
@@ -415,14 +414,13 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
     return A;
 }
 
-static AqDesc make_aq_desc(const AqPlan &A, const void *w, const void *x, int64_t ldx, float *y, int64_t ldy,
+static AqDesc make_aq_desc(const AqPlan &A, const wqd_weight *w, const void *x, int64_t ldx, float *y, int64_t ldy,
                            void *part, void *cnt, int64_t off, int64_t nw) {
     AqDesc D;
     memset(&D, 0, sizeof(D));
-    const uint8_t *base = static_cast<const uint8_t *>(w);
-    D.codes = base;
-    D.rscale = reinterpret_cast<const uint16_t *>(base + A.L.off_scales);
-    D.cbk = reinterpret_cast<const uint16_t *>(base + A.L.off_cbk);
+    D.codes = static_cast<const uint8_t *>(w->codes);
+    D.rscale = static_cast<const uint16_t *>(w->scales);
+    D.cbk = static_cast<const uint16_t *>(w->codebooks);
     D.x = static_cast<const uint16_t *>(x);
     D.y = y;
     D.part = A.b > 1 ? static_cast<float *>(part) : nullptr;
@@ -492,7 +490,7 @@ static int64_t aq_assign(const std::vector<AqPlan> &plans, int cus, bool lut, st
 }
 
 // One AQ2X8 projection alone, on a workspace of counters then partials.
-static int aq_gemm_launch(int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx, float *y,
+static int aq_gemm_launch(int64_t N, int64_t K, const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y,
                           int64_t ldy, uint8_t *ws, int64_t ws_bytes, hipStream_t st, int cus) {
     const bool lut = aq_lut(M, false);
     std::vector<AqPlan> plans(1, plan_aq(N, K, M, cus, lut));
@@ -508,19 +506,47 @@ static int aq_gemm_launch(int64_t N, int64_t K, const void *w, const void *x, in
     return launch_aq(M, lut, AP, st);
 }
 
-static int check_proj(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M,
-                      int64_t ldx, const float *y, int64_t ldy) {
-    if (k_multiple(fmt) == 0 || !w || !x || !y) return WQD_EINVAL;
-    Layout L = make_layout(fmt, N, K);
-    if (!L.ok || M < 1 || M > WQD_MAX_M || ldx < K || ldy < N) return WQD_ESHAPE;
-    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(x) & 3) ||
-        (reinterpret_cast<uintptr_t>(y) & 3) || (ldx & 1))
-        return WQD_EALIGN;
+// Scales per row of each format's prepared scale plane (0: none) and its plane alignment.
+static int64_t scale_row_elems(int fmt, int64_t K) {
+    switch (fmt) {
+    case Q4_0: return K / 32;
+    case TQ2: return K / 128;
+    case AQ2X8:
+    case AQ1X16: return 1;
+    default: return 0;
+    }
+}
+
+// A bound weight view: known format, shape inside the limits, the planes this format reads
+// present and aligned for the kernels' loads, and row sizes that agree with the shape.
+static int check_weight(const wqd_weight *w) {
+    if (!w || k_multiple(w->fmt) == 0) return WQD_EINVAL;
+    const int fmt = w->fmt;
+    Layout L = make_layout(fmt, w->N, w->K);
+    if (!L.ok) return WQD_ESHAPE;
+    if (w->code_row_bytes != L.row_code_bytes || w->scale_row_elems != scale_row_elems(fmt, w->K)) return WQD_ESHAPE;
+    const bool has_scales = fmt == Q4_0 || fmt == TQ2 || fmt == AQ2X8 || fmt == AQ1X16;
+    const bool has_cbk = fmt == CB4 || fmt == CB8 || fmt == AQ2X8 || fmt == AQ1X16;
+    if (!w->codes || (has_scales && !w->scales) || (has_cbk && !w->codebooks)) return WQD_EINVAL;
+    const uintptr_t c = reinterpret_cast<uintptr_t>(w->codes), sc = reinterpret_cast<uintptr_t>(w->scales),
+                    cb = reinterpret_cast<uintptr_t>(w->codebooks);
+    if (c & 15) return WQD_EALIGN;
+    if (has_scales && (sc & ((fmt == Q4_0 || fmt == TQ2) ? 7 : 1))) return WQD_EALIGN;
+    if (has_cbk && (cb & ((fmt == AQ2X8 || fmt == AQ1X16) ? 15 : 1))) return WQD_EALIGN;
+    return WQD_OK;
+}
+
+static int check_proj(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, const float *y, int64_t ldy) {
+    int rc = check_weight(w);
+    if (rc != WQD_OK) return rc;
+    if (!x || !y) return WQD_EINVAL;
+    if (M < 1 || M > WQD_MAX_M || ldx < w->K || ldy < w->N) return WQD_ESHAPE;
+    if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3) || (ldx & 1)) return WQD_EALIGN;
     return WQD_OK;
 }
 
 // One projection onto the stream, with its slice counters and partials.
-static int gemm_launch(const Plan &P, const void *w, const void *x, int64_t M, int64_t ldx, float *y,
+static int gemm_launch(const Plan &P, const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y,
                        int64_t ldy, int *cnt, float *part, hipStream_t st, int cus) {
     GemvParams GP;
     memset(&GP, 0, sizeof(GP));
@@ -581,17 +607,48 @@ struct StackPlan {
     int64_t total() const { return off_part + part_bytes; }
 };
 
+// A list entry with its weight view's format and shape copied out (views validated first).
+struct Proj {
+    int32_t fmt, epi;
+    int64_t N, K;
+    const wqd_weight *w;
+    const void *x;
+    int64_t ldx;
+    float *y;
+    int64_t ldy;
+};
+
+static int to_projs(const wqd_proj *p, int32_t count, std::vector<Proj> &out) {
+    if (!p || count < 1) return WQD_EINVAL;
+    out.resize(size_t(count));
+    for (int i = 0; i < count; i++) {
+        const int rc = check_weight(p[i].w);
+        if (rc != WQD_OK) return rc;
+        Proj &q = out[size_t(i)];
+        q.fmt = p[i].w->fmt;
+        q.epi = p[i].epi;
+        q.N = p[i].w->N;
+        q.K = p[i].w->K;
+        q.w = p[i].w;
+        q.x = p[i].x;
+        q.ldx = p[i].ldx;
+        q.y = p[i].y;
+        q.ldy = p[i].ldy;
+    }
+    return WQD_OK;
+}
+
 // Entries, with the epilogue rules: a WQD_EPI_SILU_GATE entry is followed by its
 // WQD_EPI_SILU_UP entry (same format and N; the pair writes the gate entry's y), and AQ2X8
 // entries take no epilogue.
-static int check_list(const wqd_proj *p, int32_t count, int64_t M) {
+static int check_list(const Proj *p, int32_t count, int64_t M) {
     if (!p || count < 1) return WQD_EINVAL;
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
     for (int i = 0; i < count; i++) {
-        const wqd_proj &q = p[i];
+        const Proj &q = p[i];
         if (q.epi < WQD_EPI_NONE || q.epi > WQD_EPI_SILU_UP) return WQD_EINVAL;
         if (q.epi != WQD_EPI_NONE && q.fmt == AQ2X8) return WQD_EINVAL;
-        const wqd_proj *out = &q;
+        const Proj *out = &q;
         if (q.epi == WQD_EPI_SILU_GATE) {
             if (i + 1 >= count || p[i + 1].epi != WQD_EPI_SILU_UP || p[i + 1].fmt != q.fmt || p[i + 1].N != q.N)
                 return WQD_EINVAL;
@@ -599,17 +656,17 @@ static int check_list(const wqd_proj *p, int32_t count, int64_t M) {
             if (i == 0 || p[i - 1].epi != WQD_EPI_SILU_GATE) return WQD_EINVAL;
             out = &p[i - 1];
         }
-        const int rc = check_proj(q.fmt, q.N, q.K, q.w, q.x, M, q.ldx, out->y, out->ldy);
+        const int rc = check_proj(q.w, q.x, M, q.ldx, out->y, out->ldy);
         if (rc != WQD_OK) return rc;
     }
     return WQD_OK;
 }
 
-static bool fuse_with(const wqd_proj &a, const wqd_proj &b) {
+static bool fuse_with(const Proj &a, const Proj &b) {
     return a.fmt == b.fmt && a.fmt != AQ2X8 && a.x == b.x && a.ldx == b.ldx;
 }
 
-static void list_segments(const wqd_proj *p, int count, int mode, std::vector<std::pair<int, int>> &seg) {
+static void list_segments(const Proj *p, int count, int mode, std::vector<std::pair<int, int>> &seg) {
     seg.clear();
     if (mode == WQD_PERSISTENT) {
         seg.push_back({0, count});
@@ -633,13 +690,13 @@ static void list_segments(const wqd_proj *p, int count, int mode, std::vector<st
 // Plans the launches of entries [b, e) onto counters from cnt_off and partials from part_off
 // (offsets into the workspace at `base`, which may be null when only sizes are wanted).
 // The index in SP.xqs of entry q's quantized activation (int8 lists, TQ2 entries), or -1.
-static int xq_of(const StackPlan &SP, const wqd_proj &q) {
+static int xq_of(const StackPlan &SP, const Proj &q) {
     for (size_t k = 0; k < SP.xqs.size(); k++)
         if (SP.xqs[k].x == q.x && SP.xqs[k].ldx == q.ldx && SP.xqs[k].K == q.K) return int(k);
     return -1;
 }
 
-static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, bool bi, bool i8, uint8_t *base,
+static void plan_segment(const Proj *p, int b, int e, int64_t M, int mode, bool bi, bool i8, uint8_t *base,
                          int64_t &cnt_off, int64_t &part_off, StackPlan &SP, int cus) {
     // kernel format of entry i: TQ2 entries of an int8 list run the int8 product
     auto kfmt = [&](int i) { return (i8 && p[i].fmt == TQ2) ? TQ2I8 : p[i].fmt; };
@@ -692,7 +749,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
             return WQD_BI_CW > 0 ? plan_ws(f, N, K, M, WQD_BI_CW) : plan_cs(f, N, K, M, WQD_BI_CS);
         };
         // int8 activations of a TQ2 entry: the descriptor reads q, a and the sums of q
-        auto to_i8 = [&](Desc &D, const wqd_proj &q) {
+        auto to_i8 = [&](Desc &D, const Proj &q) {
             if (D.fmt != TQ2 || !i8) return;
             const XQ &xq = SP.xqs[xq_of(SP, q)];
             D.fmt = TQ2I8;
@@ -709,12 +766,12 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         for (int fmt = 1; fmt <= TQ2I8; fmt++) {
             if (!(mask & fmt_bit(fmt))) continue;
             for (int i = b; i < e; i++) {
-                const wqd_proj &q = p[i];
+                const Proj &q = p[i];
                 if (kfmt(i) != fmt || q.epi == WQD_EPI_SILU_UP) continue;
                 const Plan P = plan_of(fmt, q.N, q.K);
                 if (q.epi == WQD_EPI_SILU_GATE) {
                     // gate and up share one slice counter per row group and one partial array
-                    const wqd_proj &r = p[i + 1];
+                    const Proj &r = p[i + 1];
                     const Plan U = plan_of(fmt, r.N, r.K);
                     const int64_t S_all = P.S + U.S;
                     int *cnt = base ? reinterpret_cast<int *>(base + cnt_off) : nullptr;
@@ -779,7 +836,7 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
         }
         for (size_t k = 0; k < plans.size(); k++) {
             const AqPlan &A = plans[k];
-            const wqd_proj &q = p[idx[k]];
+            const Proj &q = p[idx[k]];
             void *part = base ? static_cast<void *>(base + part_off) : nullptr;
             void *cnt = base ? static_cast<void *>(base + cnt_off) : nullptr;
             part_off += A.part_bytes;
@@ -792,13 +849,17 @@ static void plan_segment(const wqd_proj *p, int b, int e, int64_t M, int mode, b
     }
 }
 
-static int build_stack_plan(const wqd_proj *p, int32_t count, int64_t M, int mode_flags, void *ws, StackPlan &SP,
+static int build_stack_plan(const wqd_proj *pub, int32_t count, int64_t M, int mode_flags, void *ws, StackPlan &SP,
                             int cus) {
+    std::vector<Proj> list;
+    int rc = to_projs(pub, count, list);
+    if (rc != WQD_OK) return rc;
+    const Proj *p = list.data();
     const bool bi = (mode_flags & WQD_BATCH_INVARIANT) != 0;
     const bool i8 = (mode_flags & WQD_INT8_ACTIVATIONS) != 0;
     const int mode = mode_flags & ~(WQD_BATCH_INVARIANT | WQD_INT8_ACTIVATIONS);
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
-    int rc = check_list(p, count, M);
+    rc = check_list(p, count, M);
     if (rc != WQD_OK) return rc;
 
     SP.off_descs = 0;
@@ -849,9 +910,7 @@ using namespace wqd;
 
 extern "C" {
 
-WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M) {
-    if (k_multiple(fmt) == 0) return WQD_EINVAL;
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+static int64_t workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M) {
     if (fmt == AQ2X8) {
         AqPlan A = plan_aq(N, K, M, device_cus(), aq_lut(M, false));
         if (!A.L.ok) return WQD_ESHAPE;
@@ -862,17 +921,25 @@ WQD_API int64_t wqd_gemm_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t 
     return P.ws_bytes();
 }
 
+WQD_API int64_t wqd_workspace_bytes(const wqd_weight *w, int64_t M) {
+    const int rc = check_weight(w);
+    if (rc != WQD_OK) return rc;
+    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+    return workspace_bytes(w->fmt, w->N, w->K, M);
+}
+
 }  // extern "C"
 
 // One projection on a caller-provided (or the file-scope scratch) workspace: the body of wqd_gemm
 // and wqd_gemm_noalloc.  The arguments are checked by the caller.
-static int gemm_impl(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
-                     float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
+static int gemm_impl(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                     void *workspace, int64_t workspace_bytes, void *stream) {
     const int cus = device_cus();
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    if (fmt == AQ2X8)
-        return aq_gemm_launch(N, K, w, x, M, ldx, y, ldy, ws, workspace_bytes, static_cast<hipStream_t>(stream), cus);
-    Plan P = plan_single(fmt, N, K, M, cus);
+    if (w->fmt == AQ2X8)
+        return aq_gemm_launch(w->N, w->K, w, x, M, ldx, y, ldy, ws, workspace_bytes, static_cast<hipStream_t>(stream),
+                              cus);
+    Plan P = plan_single(w->fmt, w->N, w->K, M, cus);
     if (P.ws_bytes() > 0 && (!workspace || workspace_bytes < P.ws_bytes())) return WQD_ESPACE;
     int *cnt = reinterpret_cast<int *>(ws);
     float *part = ws ? reinterpret_cast<float *>(ws + kCntRegion) : nullptr;
@@ -923,18 +990,18 @@ static int scratch_on_device(hipStream_t st, uint8_t **out) {
 
 extern "C" {
 
-WQD_API int wqd_gemm(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
-                     float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
-    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+WQD_API int wqd_gemm(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy, void *workspace,
+                     int64_t workspace_bytes, void *stream) {
+    int rc = check_proj(w, x, M, ldx, y, ldy);
     if (rc != WQD_OK) return rc;
-    return gemm_impl(fmt, N, K, w, x, M, ldx, y, ldy, workspace, workspace_bytes, stream);
+    return gemm_impl(w, x, M, ldx, y, ldy, workspace, workspace_bytes, stream);
 }
 
-WQD_API int wqd_gemm_noalloc(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
-                             float *y, int64_t ldy, void *stream) {
-    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+WQD_API int wqd_gemm_noalloc(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                             void *stream) {
+    int rc = check_proj(w, x, M, ldx, y, ldy);
     if (rc != WQD_OK) return rc;
-    const int64_t need = wqd_gemm_workspace_bytes(fmt, N, K, M);
+    const int64_t need = workspace_bytes(w->fmt, w->N, w->K, M);
     if (need < 0) return int(need);
     if (need > kScratchBytes) return WQD_ESPACE;
     uint8_t *ws = nullptr;
@@ -942,7 +1009,7 @@ WQD_API int wqd_gemm_noalloc(int fmt, int64_t N, int64_t K, const void *w, const
         rc = scratch_on_device(static_cast<hipStream_t>(stream), &ws);
         if (rc != WQD_OK) return rc;
     }
-    return gemm_impl(fmt, N, K, w, x, M, ldx, y, ldy, ws, need > 0 ? kScratchBytes : 0, stream);
+    return gemm_impl(w, x, M, ldx, y, ldy, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 // Workspace of wqd_gemm_i8: [wqd_gemm's counters and partials][q: M x K bytes][a: M x K/128 fp32]
@@ -959,19 +1026,21 @@ static I8Ws i8_workspace(const Plan &P, int64_t M, int64_t K) {
     return w;
 }
 
-WQD_API int64_t wqd_gemm_i8_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t M) {
-    if (fmt != TQ2) return WQD_EINVAL;
+WQD_API int64_t wqd_gemm_i8_workspace_bytes(const wqd_weight *w, int64_t M) {
+    const int rc = check_weight(w);
+    if (rc != WQD_OK) return rc;
+    if (w->fmt != TQ2) return WQD_EINVAL;
     if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
-    Plan P = plan_single(TQ2, N, K, M, device_cus());
-    if (!P.L.ok) return WQD_ESHAPE;
-    return i8_workspace(P, M, K).total;
+    Plan P = plan_single(TQ2, w->N, w->K, M, device_cus());
+    return i8_workspace(P, M, w->K).total;
 }
 
-WQD_API int wqd_gemm_i8(int fmt, int64_t N, int64_t K, const void *w, const void *x, int64_t M, int64_t ldx,
-                        float *y, int64_t ldy, void *workspace, int64_t workspace_bytes, void *stream) {
-    if (fmt != TQ2) return WQD_EINVAL;
-    int rc = check_proj(fmt, N, K, w, x, M, ldx, y, ldy);
+WQD_API int wqd_gemm_i8(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
+                        void *workspace, int64_t workspace_bytes, void *stream) {
+    int rc = check_proj(w, x, M, ldx, y, ldy);
     if (rc != WQD_OK) return rc;
+    if (w->fmt != TQ2) return WQD_EINVAL;
+    const int64_t N = w->N, K = w->K;
     const int cus = device_cus();
     Plan P = plan_single(TQ2, N, K, M, cus);
     const I8Ws iw = i8_workspace(P, M, K);
@@ -1016,22 +1085,26 @@ WQD_API int wqd_quantize_i8(const void *x, int64_t M, int64_t K, int64_t ldx, in
     return e == hipSuccess ? WQD_OK : hip_fail(e);
 }
 
-WQD_API int wqd_dequant_f32(int fmt, int64_t N, int64_t K, const void *w, float *out, void *stream) {
-    if (k_multiple(fmt) == 0 || !w || !out) return WQD_EINVAL;
-    Layout L = make_layout(fmt, N, K);
-    if (!L.ok) return WQD_ESHAPE;
-    if (reinterpret_cast<uintptr_t>(w) & 15) return WQD_EALIGN;
+WQD_API int wqd_dequant_f32(const wqd_weight *w, float *out, void *stream) {
+    int rc = check_weight(w);
+    if (rc != WQD_OK) return rc;
+    if (!out) return WQD_EINVAL;
+    const int fmt = w->fmt;
+    Layout L = make_layout(fmt, w->N, w->K);
     const int64_t threads = (fmt == AQ2X8) ? L.N * L.G : (fmt == AQ1X16) ? L.N * (L.K / 8) : L.N * L.C;
     const unsigned blocks = unsigned((threads + 255) / 256);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const uint8_t *wc = static_cast<const uint8_t *>(w->codes);
+    const uint8_t *sc = static_cast<const uint8_t *>(w->scales);
+    const uint16_t *cb = static_cast<const uint16_t *>(w->codebooks);
+    const uint16_t *rs = static_cast<const uint16_t *>(w->scales);
     switch (fmt) {
-    case Q4_0: hipLaunchKernelGGL(dequant_kernel<Q4_0>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case CB4: hipLaunchKernelGGL(dequant_kernel<CB4>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case CB8: hipLaunchKernelGGL(dequant_kernel<CB8>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case TQ2: hipLaunchKernelGGL(dequant_kernel<TQ2>, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case AQ2X8: hipLaunchKernelGGL(dequant_aq2x8_kernel, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
-    case AQ1X16: hipLaunchKernelGGL(dequant_aq1x16_kernel, dim3(blocks), dim3(256), 0, st, wb, L, out); break;
+    case Q4_0: hipLaunchKernelGGL(dequant_kernel<Q4_0>, dim3(blocks), dim3(256), 0, st, wc, sc, cb, L, out); break;
+    case CB4: hipLaunchKernelGGL(dequant_kernel<CB4>, dim3(blocks), dim3(256), 0, st, wc, sc, cb, L, out); break;
+    case CB8: hipLaunchKernelGGL(dequant_kernel<CB8>, dim3(blocks), dim3(256), 0, st, wc, sc, cb, L, out); break;
+    case TQ2: hipLaunchKernelGGL(dequant_kernel<TQ2>, dim3(blocks), dim3(256), 0, st, wc, sc, cb, L, out); break;
+    case AQ2X8: hipLaunchKernelGGL(dequant_aq2x8_kernel, dim3(blocks), dim3(256), 0, st, wc, rs, cb, L, out); break;
+    case AQ1X16: hipLaunchKernelGGL(dequant_aq1x16_kernel, dim3(blocks), dim3(256), 0, st, wc, rs, cb, L, out); break;
     }
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? WQD_OK : hip_fail(e);

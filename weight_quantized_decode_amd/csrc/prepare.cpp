@@ -158,6 +158,28 @@ WQD_API int wqd_prepare_host(int fmt, int64_t N, int64_t K, const void *canonica
     return WQD_OK;
 }
 
+WQD_API int wqd_bind(int fmt, int64_t N, int64_t K, const void *prepared, wqd_weight *out) {
+    if (k_multiple(fmt) == 0 || !prepared || !out) return WQD_EINVAL;
+    Layout L = make_layout(fmt, N, K);
+    if (!L.ok) return WQD_ESHAPE;
+    if (reinterpret_cast<uintptr_t>(prepared) & 15) return WQD_EALIGN;
+    const uint8_t *base = static_cast<const uint8_t *>(prepared);
+    const bool has_scales = fmt == Q4_0 || fmt == TQ2 || fmt == AQ2X8 || fmt == AQ1X16;
+    const bool has_cbk = fmt == CB4 || fmt == CB8 || fmt == AQ2X8 || fmt == AQ1X16;
+    wqd_weight w;
+    memset(&w, 0, sizeof(w));
+    w.fmt = fmt;
+    w.N = int32_t(N);
+    w.K = int32_t(K);
+    w.codes = base;
+    w.scales = has_scales ? base + L.off_scales : nullptr;
+    w.codebooks = has_cbk ? base + L.off_cbk : nullptr;
+    w.code_row_bytes = L.row_code_bytes;
+    w.scale_row_elems = fmt == Q4_0 ? K / 32 : fmt == TQ2 ? K / 128 : (fmt == AQ2X8 || fmt == AQ1X16) ? 1 : 0;
+    *out = w;
+    return WQD_OK;
+}
+
 WQD_API const char *wqd_status_str(int status) {
     switch (status) {
     case WQD_OK: return "ok";
