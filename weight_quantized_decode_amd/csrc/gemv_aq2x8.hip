@@ -167,63 +167,73 @@ __device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Pie
 // fewer than W*RW row blocks leaves every wave with a nearly equal share.
 __device__ __forceinline__ int tile_rb(int wid, int i) { return wid + W * i; }
 
-// Tile loader running ahead of the processing: one unit is one slice of the current piece; wave
-// wid loads row blocks rb0 + tile_rb(wid, i), i < RW, of it.
+// Load cursor, running ahead of the processing: where this wave's tiles of the next slice to load
+// are, and that slice's activations and codebooks.  Going from one slice to the next only adds a
+// stride to each address; the piece arithmetic runs once per piece.  A missing tile (past the
+// piece's row blocks, or past the end of the work) still takes its place in the load ring, so every
+// load stays unconditional: it reads 1 KiB of the codebooks instead, with a stride of 0.
 template <int RW>
-struct Loader {
-    const uint8_t *base;   // code plane (the lane's 16 bytes are added at the load)
-    int64_t s_stride;      // bytes between slices (Npad/16 KiB)
-    int s_max, rb_max;     // last slice and row block of the plane (tile addresses stay inside)
-    int rb0, rb1;          // the piece's row blocks
-    int wv;                // this wave
-    const uint16_t *x, *cbk;
-    int64_t ldx;
-    int G;
-    Piece q;               // current piece
-    int s;                 // current slice
+struct Cursor {
+    const uint8_t *ta[RW];  // per lane: its 16 bytes of tile i of the next slice
+    int64_t tstr[RW];       // bytes from one slice of tile i to the next (0 for a missing tile)
+    const uint8_t *cbk;     // the projection's codebooks
+    const uint8_t *xp;      // x of the next slice (bytes from row 0)
+    int64_t ldx;            // bytes between activation rows
+    int gl;                 // groups of the projection from the next slice on
+    int left;               // slices of the piece after the next one
+    int p, j, nw;           // the piece (to find the next)
     bool done;
 
-    __device__ __forceinline__ void setup(const AqParams &P, const Piece n, int wid) {
-        q = n;
-        s = n.s0;
+    __device__ __forceinline__ void setup(const AqParams &P, const Piece &n, int wid, int lane) {
         const AqDesc D = get_desc(P, n.p);
-        base = D.codes;
-        s_stride = int64_t(D.Npad / 16) * 1024;
-        x = D.x;
-        cbk = D.cbk;
-        ldx = D.ldx;
-        G = D.G;
-        s_max = D.KS - 1;
-        rb_max = D.Npad / 16 - 1;
-        rb0 = n.rb0;
-        rb1 = n.rb1;
-        wv = wid;
+        const int64_t stride = int64_t(D.Npad / 16) * 1024;
+        cbk = reinterpret_cast<const uint8_t *>(D.cbk);
+        xp = reinterpret_cast<const uint8_t *>(D.x) + int64_t(n.s0) * 512;
+        ldx = D.ldx * 2;
+        gl = D.G - 32 * n.s0;
+        left = n.s1 - n.s0 - 1;
+        p = n.p;
+        j = n.j;
+        nw = n.nw;
+        done = false;
+        const uint8_t *t0 = D.codes + int64_t(n.s0) * stride + int64_t(n.rb0 + wid) * 1024 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < RW; i++) {
+            const bool valid = n.rb0 + tile_rb(wid, i) < n.rb1;
+            ta[i] = valid ? t0 + i * (W * 1024) : cbk + lane * 16;
+            tstr[i] = valid ? stride : 0;
+        }
     }
-    // A missing tile (past the piece, or past the end of the work) still takes its place in the
-    // ring, so every load stays unconditional: it reads 1 KiB of the codebooks instead.
-    __device__ __forceinline__ const uint8_t *addr(int i) const {
-        const int r = rb0 + tile_rb(wv, i);
-        return (done || r >= rb1) ? reinterpret_cast<const uint8_t *>(cbk)
-                                  : base + int64_t(min(s, s_max)) * s_stride + int64_t(min(r, rb_max)) * 1024;
-    }
-    __device__ __forceinline__ void step(const AqParams &P, int wg, int wid) {
+    // To the next slice: the piece's next, else the first of the workgroup's next piece.
+    __device__ __forceinline__ void advance(const AqParams &P, int wg, int wid, int lane) {
         if (done) return;
-        if (++s < q.s1) return;
-        const Piece qn = next_piece(P, wg, q);
-        if (qn.p >= P.ndesc) {
-            done = true;
-            s = q.s1 - 1;
-        } else {
-            setup(P, qn, wid);
+        if (left > 0) {
+            left--;
+#pragma unroll
+            for (int i = 0; i < RW; i++) ta[i] += tstr[i];
+            xp += 512;
+            gl -= 32;
+            return;
+        }
+        const Piece n = find_piece(P, wg, p, j + nw);
+        if (n.p < P.ndesc) {
+            setup(P, n, wid, lane);
+            return;
+        }
+        done = true;  // the activation and codebook loads keep the last slice's (in bounds)
+#pragma unroll
+        for (int i = 0; i < RW; i++) {
+            ta[i] = cbk + lane * 16;
+            tstr[i] = 0;
         }
     }
 };
 
 template <int RW>
-__device__ __forceinline__ void load_tiles(const Loader<RW> &ld, u32x4 (&t)[RW], int lane) {
+__device__ __forceinline__ void load_tiles(const Cursor<RW> &c, u32x4 (&t)[RW]) {
 #pragma unroll
     for (int i = 0; i < RW; i++)
-        t[i] = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)(ld.addr(i) + lane * 16));
+        t[i] = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)c.ta[i]);
 }
 template <int RW>
 __device__ __forceinline__ void settle_tiles(u32x4 (&t)[RW]) {
@@ -387,11 +397,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     Piece pp = find_piece(P, wg, 0, -1);  // piece being processed
     if (pp.p >= P.ndesc) return;          // no work for this workgroup (same for all its waves)
     int ps = pp.s0;                       // slice being processed
-    AqDesc pd = get_desc(P, pp.p);
+    int rows_w = pp.rb1 - pp.rb0 - wid;   // tile i of this wave is in the piece when 16 i < rows_w
 
-    Loader<RW> ld;
-    ld.done = false;
-    ld.setup(P, pp, wid);
+    Cursor<RW> ld;
+    ld.setup(P, pp, wid, lane);
 
     // LDS byte address of a lookup: (tb << 16) | (code << 8) | (b << 7) | (g << 2), b the codebook.
     // Byte 0 and byte 2 come from lk, byte 1 is the code byte the selector picks from the word:
@@ -401,14 +410,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const uint32_t selA[2] = {0x0c020000u | ((4u + h) << 8), 0x0c020000u | ((6u + h) << 8)};
     const uint32_t selB[2] = {0x0c020000u | ((5u - h) << 8), 0x0c020000u | ((7u - h) << 8)};
 
+    // the build operands: this wave's codebook rows (codebook wid/8, codes 32(wid%8) + g), and
+    // the 8 activations of group g (groups past K clamp to the last, then read as zero)
+    const uint32_t aoff = ((wid >> 3) * 256 + 32 * (wid & 7) + g) * 16 + 8 * h;
     auto load_slice = [&](u32x4 (&t)[RW], LutOps &o) __attribute__((always_inline)) {
-        const int cb = wid >> 3, code = 32 * (wid & 7) + g;
-        o.A = gld<u32x2>(ld.cbk + (int64_t(cb) * 256 + code) * 8 + 4 * h);
-        o.gval = ld.G - ld.s * 32;
-        const int gi = min(ld.s * 32 + g, ld.G - 1);
-        o.B = gld<u32x2>(ld.x + int64_t(gi) * 8 + 4 * h);
-        load_tiles(ld, t, lane);
-        ld.step(P, wg, wid);
+        o.A = gld<u32x2>(ld.cbk + aoff);
+        o.gval = ld.gl;
+        o.B = gld<u32x2>(ld.xp + min(g, ld.gl - 1) * 16 + 8 * h);
+        load_tiles(ld, t);
+        ld.advance(P, wg, wid, lane);
     };
     auto settle_ops = [&](LutOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.A), "v"(o.B)); };
 
@@ -470,7 +480,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
         for (int i = 0; i < RW; i++) {
             const int rb = q.rb0 + tile_rb(wid, i);
-            if (rb < q.rb1) {
+            if (W * i < rows_w) {
                 const float z = finish_half4(acc[i], lane);
                 const int row = 16 * rb + 8 * h + ((lane >> 2) & 7);
                 if ((lane & 3) == 0 && row < D.N) {
@@ -488,13 +498,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     };
 
-    int tb = 0;  // table of the slice being processed
-    // One slice: wait for its tiles and the next slice's table operands, issue the loads of the
-    // slice two ahead, build the next table into the other buffer, look up this slice, barrier.
-    auto step = [&](u32x4 (&cur)[RW], LutOps &on, u32x4 (&nxt)[RW], LutOps &onew) __attribute__((always_inline)) -> bool {
+    int tb = 0;         // table of the slice being processed
+    bool fin = false;   // every piece is done (the remaining steps of the ring's round are empty)
+    // One slice: issue the loads of the slice two ahead (into the buffers the previous slice
+    // left), wait for this slice's tiles and the next slice's table operands, build the next table
+    // into the other buffer, look up this slice, barrier.  The loads and waits come first and on
+    // every path, the same in every step, so that the waits of the ring are counted exactly.
+    auto step = [&](u32x4 (&cur)[RW], LutOps &on, u32x4 (&nxt)[RW], LutOps &onew) __attribute__((always_inline)) {
+        load_slice(nxt, onew);
         settle_tiles(cur);
         settle_ops(on);
-        load_slice(nxt, onew);
+        if (fin) return;
         // (no scalar load may be pending during the build and lookups: the LDS waits are then
         // counted exactly instead of draining every lookup in flight)
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -502,37 +516,36 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         const uint32_t lkA = lkA0 | (uint32_t(tb) << 16), lkB = lkB0 | (uint32_t(tb) << 16);
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            if (pp.rb0 + tile_rb(wid, i) < pp.rb1) process(cur[i], acc[i], lkA, lkB);
+            if (W * i < rows_w) process(cur[i], acc[i], lkA, lkB);
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         tb ^= 1;
-        if (++ps < pp.s1) return false;
+        if (++ps < pp.s1) return;
+        const AqDesc pd = get_desc(P, pp.p);
         epilogue(pp, pd);
         record_piece(recs, nrec, pp, pd, wid, lane);
-        const Piece pn = next_piece(P, wg, pp);
-        if (pn.p >= P.ndesc) return true;
-        pp = pn;
+        pp = next_piece(P, wg, pp);
+        fin = pp.p >= P.ndesc;
         ps = pp.s0;
-        pd = get_desc(P, pp.p);
-        return false;
+        rows_w = pp.rb1 - pp.rb0 - wid;
     };
 
     // R unit buffers: while unit s is processed, units s+1 .. s+R-2 are in flight, and the loads of
     // unit s+R-1 go into the buffer unit s-1 freed.
-    u32x4 buf[R][RW];
-    LutOps ops[R];
-    static_for<R - 1>([&](auto kc) { load_slice(buf[decltype(kc)::value], ops[decltype(kc)::value]); });
-    settle_ops(ops[0]);
-    build(ops[0], 0);
+    static_assert(R == 3, "three unit buffers");
+    u32x4 buf0[RW], buf1[RW], buf2[RW];
+    LutOps ops0, ops1, ops2;
+    load_slice(buf0, ops0);
+    load_slice(buf1, ops1);
+    settle_ops(ops0);
+    build(ops0, 0);
     lds_barrier();
-    bool fin = false;
-    while (!fin) {
-        static_for<R>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            if (!fin) fin = step(buf[k], ops[(k + 1) % R], buf[(k + R - 1) % R], ops[(k + R - 1) % R]);
-        });
-    }
+    do {
+        step(buf0, ops1, buf2, ops2);
+        step(buf1, ops2, buf0, ops0);
+        step(buf2, ops0, buf1, ops1);
+    } while (!fin);
     finish<1, RW, kAqLutMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
 }
 
@@ -573,19 +586,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     Piece pp = find_piece(P, wg, 0, -1);
     if (pp.p >= P.ndesc) return;
     int ps = pp.s0;
-    AqDesc pd = get_desc(P, pp.p);
+    int rows_w = pp.rb1 - pp.rb0 - wid;  // tile i of this wave is in the piece when 16 i < rows_w
+    const uint16_t *pcbk = get_desc(P, pp.p).cbk;  // codebooks in LDS
 
-    Loader<RW> ld;
-    ld.done = false;
-    ld.setup(P, pp, wid);
+    Cursor<RW> ld;
+    ld.setup(P, pp, wid, lane);
 
+    // thread t < 32M stages the 8 activations of row t/32, group t%32 of a slice
     const int xt = min(int(threadIdx.x), 32 * M - 1);
     auto load_slice = [&](u32x4 (&t)[RW], MmaOps &o) __attribute__((always_inline)) {
-        o.gval = ld.G - ld.s * 32;
-        const int gi = min(ld.s * 32 + (xt & 31), ld.G - 1);
-        o.X = gld<u32x4>(ld.x + int64_t(xt >> 5) * ld.ldx + int64_t(gi) * 8);
-        load_tiles(ld, t, lane);
-        ld.step(P, wg, wid);
+        o.gval = ld.gl;
+        o.X = gld<u32x4>(ld.xp + (xt >> 5) * ld.ldx + min(xt & 31, ld.gl - 1) * 16);
+        load_tiles(ld, t);
+        ld.advance(P, wg, wid, lane);
     };
     auto settle_ops = [&](MmaOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.X)); };
     auto stage_x = [&](const MmaOps &o, int xb) __attribute__((always_inline)) {
@@ -641,7 +654,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         for (int i = 0; i < RW; i++) {
             const int rb = q.rb0 + tile_rb(wid, i);
             const int row = 16 * rb + n;
-            if (rb < q.rb1 && row < D.N) {
+            if (W * i < rows_w && row < D.N) {
                 const float sc = D.b == 1 ? half_bits_to_float(gld<uint16_t>(D.rscale + row)) : 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
@@ -661,11 +674,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     };
 
-    int xb = 0;  // activation buffer of the slice being processed
-    auto step = [&](u32x4 (&cur)[RW], MmaOps &on, u32x4 (&nxt)[RW], MmaOps &onew) __attribute__((always_inline)) -> bool {
+    int xb = 0;         // activation buffer of the slice being processed
+    bool fin = false;   // every piece is done (the remaining steps of the ring's round are empty)
+    // One slice: the loads of the slice two ahead, the waits for this slice's tiles and the next
+    // slice's activations (first and on every path, as in the lookup-table kernel), the next
+    // slice's activations into LDS, the products of this slice, barrier.
+    auto step = [&](u32x4 (&cur)[RW], MmaOps &on, u32x4 (&nxt)[RW], MmaOps &onew) __attribute__((always_inline)) {
+        load_slice(nxt, onew);
         settle_tiles(cur);
         settle_ops(on);
-        load_slice(nxt, onew);
+        if (fin) return;
         stage_x(on, xb ^ 1);
         u32x4 A[8];  // lane 16q + m: activation row min(m, M-1), groups 4t + q of the slice
         const uint8_t *xs = lds + L::off_x + xb * L::xbuf + min(n, M - 1) * kXRow + q4 * 16;
@@ -673,40 +691,41 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         for (int t = 0; t < 8; t++) A[t] = *reinterpret_cast<const u32x4 *>(xs + t * 64);
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            if (pp.rb0 + tile_rb(wid, i) < pp.rb1) mma_tile(cur[i], A, Dacc[i]);
+            if (W * i < rows_w) mma_tile(cur[i], A, Dacc[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
         xb ^= 1;
-        if (++ps < pp.s1) return false;
+        if (++ps < pp.s1) return;
+        const AqDesc pd = get_desc(P, pp.p);
         epilogue(pp, pd);
         record_piece(recs, nrec, pp, pd, wid, lane);
-        const Piece pn = next_piece(P, wg, pp);
-        if (pn.p >= P.ndesc) return true;
-        const bool newcb = pn.p != pp.p && get_desc(P, pn.p).cbk != pd.cbk;
-        pp = pn;
+        pp = next_piece(P, wg, pp);
+        fin = pp.p >= P.ndesc;
         ps = pp.s0;
-        pd = get_desc(P, pp.p);
-        if (newcb) {  // every wave is past its lookups of the old codebooks (the barrier above)
-            codebooks(pd.cbk);
+        rows_w = pp.rb1 - pp.rb0 - wid;
+        if (fin) return;
+        const uint16_t *ncbk = get_desc(P, pp.p).cbk;
+        if (ncbk != pcbk) {  // every wave is past its lookups of the old codebooks (the barrier above)
+            pcbk = ncbk;
+            codebooks(pcbk);
             lds_barrier();
         }
-        return false;
     };
 
     u32x4 buf0[RW], buf1[RW], buf2[RW];
     MmaOps ops0, ops1, ops2;
-    codebooks(pd.cbk);
+    codebooks(pcbk);
     load_slice(buf0, ops0);
     load_slice(buf1, ops1);
     settle_ops(ops0);
     stage_x(ops0, 0);
     lds_barrier();
-    while (true) {
-        if (step(buf0, ops1, buf2, ops2)) break;
-        if (step(buf1, ops2, buf0, ops0)) break;
-        if (step(buf2, ops0, buf1, ops1)) break;
-    }
+    do {
+        step(buf0, ops1, buf2, ops2);
+        step(buf1, ops2, buf0, ops0);
+        step(buf2, ops0, buf1, ops1);
+    } while (!fin);
     finish<M, RW, kAqMmaMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
 }
 
