@@ -442,8 +442,16 @@ static AqDesc make_aq_desc(const AqPlan &A, const wqd_weight *w, const void *x, 
     return D;
 }
 
-static int launch_aq(int64_t M, bool lut, const AqParams &AP, hipStream_t st) {
-    AqFn fn = aq_fn(int(M), lut);
+// Whether the record form of the AQ2X8 kernels may run these descriptors: a bound on the pieces
+// one workgroup serves (the sum over projections of ceil(npieces / nw)) within the record count.
+static bool aq_rec(const AqDesc *d, int64_t n, bool lut) {
+    int64_t pieces = 0;
+    for (int64_t i = 0; i < n; i++) pieces += (int64_t(d[i].npieces) + d[i].nw - 1) / d[i].nw;
+    return pieces <= (lut ? kAqLutRecs : kAqMmaRecs);
+}
+
+static int launch_aq(int64_t M, bool lut, bool rec, const AqParams &AP, hipStream_t st) {
+    AqFn fn = aq_fn(int(M), lut, rec);
     if (!fn) return WQD_EINVAL;
     hipLaunchKernelGGL(fn, dim3(unsigned(AP.nwg)), dim3(kAqWaves * 64), 0, st, AP);
     hipError_t e = hipGetLastError();
@@ -503,7 +511,7 @@ static int aq_gemm_launch(int64_t N, int64_t K, const wqd_weight *w, const void 
     AP.descs = nullptr;
     AP.ndesc = 1;
     AP.nwg = int32_t(nwg);
-    return launch_aq(M, lut, AP, st);
+    return launch_aq(M, lut, aq_rec(&AP.d0, 1, lut), AP, st);
 }
 
 // Scales per row of each format's prepared scale plane (0: none) and its plane alignment.
@@ -1202,7 +1210,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.nwg = int32_t(G.nwg);
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
-            rc = launch_aq(M, G.lut, AP, st);
+            rc = launch_aq(M, G.lut, aq_rec(&SP.aqdescs[G.first], G.count, G.lut), AP, st);
             if (rc != WQD_OK) return rc;
             if ((rc = mark(1)) != WQD_OK) return rc;
             li++;

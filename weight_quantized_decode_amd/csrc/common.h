@@ -152,6 +152,8 @@ constexpr int kAqMmaMaxSplits = 8;  // most K-splits of a matrix-core projection
 constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-table kernel
 constexpr int kAqMmaRW = 2;         // row blocks per wave per slice, matrix-core kernel
 constexpr int kAqCntStride = 32;    // ints between the arrival counters of two row chunks
+constexpr int kAqLutRecs = 64;      // most pieces per workgroup kept as LDS records, lookup-table kernel
+constexpr int kAqMmaRecs = 40;      // the same, matrix-core kernel (its LDS holds the codebook copies)
 #ifndef WQD_AQ_BUILD_CHARGE
 #define WQD_AQ_BUILD_CHARGE 8       // planner charge of a slice's table build, in tile loads
 #endif
@@ -185,8 +187,10 @@ struct AqParams {
 
 typedef void (*AqFn)(AqParams);
 // AQ2X8 kernel instance: the lookup-table kernel (M = 1, lut) or the matrix-core kernel for M
-// activation rows (1 <= M <= 8; every batch-invariant call takes it).
-AqFn aq_fn(int M, bool lut);
+// activation rows (1 <= M <= 8; every batch-invariant call takes it).  rec: the form that keeps
+// each workgroup's pieces as LDS records, valid when no workgroup serves more than kAqLutRecs
+// (lut) or kAqMmaRecs pieces; the other form walks the descriptors.
+AqFn aq_fn(int M, bool lut, bool rec);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies

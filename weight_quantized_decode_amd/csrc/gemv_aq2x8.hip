@@ -37,7 +37,9 @@
 //     LDS (double-buffered, one barrier per slice).
 //
 // Work (AqDesc): a workgroup walks its pieces in order, slice by slice; the tile loads of the next
-// two slices are in flight while a slice is processed.  Pieces with b > 1 store fp32 partials.
+// two slices are in flight while a slice is processed.  When a workgroup serves few pieces (the
+// usual case: one piece of each projection), wave 0 writes all of them as LDS records at the start,
+// so moving to the next piece is an LDS read; otherwise every wave walks the descriptors.  Pieces with b > 1 store fp32 partials.
 // Once all of its pieces are done, the workgroup counts each split piece done on its row chunk,
 // and the workgroup that arrives last adds the chunk's partials in split order: no workgroup ever
 // waits for another, and results are the same bits from run to run.
@@ -117,7 +119,7 @@ __device__ __forceinline__ AqDesc get_desc(const AqParams &P, int p) {
     return load_uniform(d);
 }
 
-// A piece of this workgroup's work list (wave-uniform).
+// A piece of this workgroup's work list (wave-uniform), as the descriptor defines it.
 struct Piece {
     int p;          // projection; == ndesc past the end of the list
     int j;          // piece index within the projection
@@ -127,28 +129,32 @@ struct Piece {
     int s0, s1;     // 32-group slices [s0, s1)
 };
 
+__device__ __forceinline__ Piece piece_of(const AqDesc &D, int p, int j) {
+    Piece q;
+    q.p = p;
+    q.j = j;
+    q.nw = D.nw;
+    q.split = j / D.a;
+    q.chunk = j - q.split * D.a;
+    q.rb0 = q.chunk * D.nrb;
+    q.rb1 = min(D.RB, q.rb0 + D.nrb);
+    q.s0 = q.split * D.ns;
+    q.s1 = min(D.KS, q.s0 + D.ns);
+    return q;
+}
+
 // The first piece of this workgroup at or after (projection p, piece j); j < 0: start of p.
+// Workgroup wg serves pieces j = (wg - off) mod nwg, then every nw-th, of each projection whose
+// workgroups it is among (0 <= off < nwg).
 __device__ __forceinline__ Piece find_piece(const AqParams &P, int wg, int p, int j) {
     while (p < P.ndesc) {
         const AqDesc D = get_desc(P, p);
         if (j < 0) {
-            j = (wg - D.off) % P.nwg;
+            j = wg - D.off;
             if (j < 0) j += P.nwg;
             if (j >= D.nw) j = D.npieces;  // not one of the projection's workgroups
         }
-        if (j < D.npieces) {
-            Piece q;
-            q.p = p;
-            q.j = j;
-            q.nw = D.nw;
-            q.split = j / D.a;
-            q.chunk = j - q.split * D.a;
-            q.rb0 = q.chunk * D.nrb;
-            q.rb1 = min(D.RB, q.rb0 + D.nrb);
-            q.s0 = q.split * D.ns;
-            q.s1 = min(D.KS, q.s0 + D.ns);
-            return q;
-        }
+        if (j < D.npieces) return piece_of(D, p, j);
         p++;
         j = -1;
     }
@@ -159,8 +165,164 @@ __device__ __forceinline__ Piece find_piece(const AqParams &P, int wg, int p, in
     q.chunk = q.split = q.rb0 = q.rb1 = q.s0 = q.s1 = 0;
     return q;
 }
-__device__ __forceinline__ Piece next_piece(const AqParams &P, int wg, const Piece &q) {
-    return find_piece(P, wg, q.p, q.j + q.nw);
+
+// Everything the kernels use of one piece: its row blocks and slices, and the fields of its
+// projection that the loads, the epilogue and the split sum read.
+struct PieceRec {
+    const uint8_t *codes;    // tile plane
+    const uint8_t *x;        // activations (row 0)
+    const uint8_t *cbk;      // codebooks
+    float *y;                // output (row 0)
+    float *part;             // partials [M][b][Npad] when b > 1
+    const uint16_t *rscale;  // row scales
+    int *cnt;                // the piece's row-chunk arrival counter when b > 1
+    int64_t ldx;             // bytes between activation rows
+    int64_t ldy;             // elements between output rows
+    int32_t rb0, rb1, s0, s1;
+    int32_t N, Npad, G, b;
+    int32_t split, pad[5];
+};
+static_assert(sizeof(PieceRec) == 128, "record of 8 x 16 bytes");
+
+__device__ __forceinline__ PieceRec make_rec(const Piece &q, const AqDesc &D) {
+    PieceRec r;
+    r.codes = D.codes;
+    r.x = reinterpret_cast<const uint8_t *>(D.x);
+    r.cbk = reinterpret_cast<const uint8_t *>(D.cbk);
+    r.y = D.y;
+    r.part = D.part;
+    r.rscale = D.rscale;
+    r.cnt = D.b > 1 ? D.cnt + q.chunk * kAqCntStride : nullptr;
+    r.ldx = D.ldx * 2;
+    r.ldy = D.ldy;
+    r.rb0 = q.rb0;
+    r.rb1 = q.rb1;
+    r.s0 = q.s0;
+    r.s1 = q.s1;
+    r.N = D.N;
+    r.Npad = D.Npad;
+    r.G = D.G;
+    r.b = D.b;
+    r.split = q.split;
+#pragma unroll
+    for (int i = 0; i < 5; i++) r.pad[i] = 0;
+    return r;
+}
+
+// A record in LDS, read by every lane of a wave at the same address (broadcast), made uniform.
+__device__ __forceinline__ PieceRec read_rec(const PieceRec *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+    uint32_t w[32];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const u32x4 v = q[i];
+        w[4 * i] = __builtin_amdgcn_readfirstlane(v.x);
+        w[4 * i + 1] = __builtin_amdgcn_readfirstlane(v.y);
+        w[4 * i + 2] = __builtin_amdgcn_readfirstlane(v.z);
+        w[4 * i + 3] = __builtin_amdgcn_readfirstlane(v.w);
+    }
+    PieceRec r;
+    __builtin_memcpy(&r, w, sizeof(r));
+    return r;
+}
+
+// The workgroup's piece records, in walk order (projection, then piece index), built once by wave
+// 0 at the start: lane l takes projection base + l, counts the pieces this workgroup serves of it,
+// and writes their records after those of the lanes before it.  Returns the number of pieces (the
+// host launches this form only when a bound on it, the sum over projections of
+// ceil(npieces / nw), is at most CAP).
+template <int CAP>
+__device__ int build_recs(const AqParams &P, int wg, int lane, PieceRec *recs) {
+    int total = 0;
+    for (int base = 0; base < P.ndesc; base += 64) {
+        const int p = min(base + lane, P.ndesc - 1);
+        AqDesc D;
+        if (P.descs) {  // lane p's descriptor from the table
+            uint32_t w[sizeof(AqDesc) / 4];
+#pragma unroll
+            for (unsigned i = 0; i < sizeof(AqDesc) / 4; i++)
+                w[i] = gld<uint32_t>(reinterpret_cast<const uint32_t *>(P.descs + p) + i);
+            __builtin_memcpy(&D, w, sizeof(D));
+        } else {  // the single projection of the kernel arguments
+            D = get_desc(P, 0);
+        }
+        int j0 = wg - D.off;
+        if (j0 < 0) j0 += P.nwg;
+        const int cnt = (base + lane < P.ndesc && j0 < D.nw && j0 < D.npieces) ? (D.npieces - j0 + D.nw - 1) / D.nw : 0;
+        int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        const int first = total + incl - cnt;
+        for (int r = 0; r < cnt && first + r < CAP; r++) recs[first + r] = make_rec(piece_of(D, p, j0 + r * D.nw), D);
+        total += __shfl(incl, 63, 64);
+    }
+    return total;
+}
+
+// Where a walk over the workgroup's pieces stands: record k (records in LDS), or piece (p, j) of
+// the list (walking the descriptors).
+struct PiecePos {
+    int k, p, j, nw;
+};
+template <bool REC>
+struct Pieces {
+    const AqParams &P;
+    int wg;
+    const PieceRec *recs;  // REC: the records
+    int n;                 // REC: their number
+
+    __device__ __forceinline__ bool first(PiecePos &pos, PieceRec &r) const {
+        if constexpr (REC) {
+            pos.k = 0;
+            if (n < 1) return false;
+            r = read_rec(recs);
+            return true;
+        } else {
+            return walk_to(find_piece(P, wg, 0, -1), pos, r);
+        }
+    }
+    __device__ __forceinline__ bool next(PiecePos &pos, PieceRec &r) const {
+        if constexpr (REC) {
+            if (++pos.k >= n) return false;
+            r = read_rec(recs + pos.k);
+            return true;
+        } else {
+            return walk_to(find_piece(P, wg, pos.p, pos.j + pos.nw), pos, r);
+        }
+    }
+    // The record of the piece at pos (again).
+    __device__ __forceinline__ PieceRec at(const PiecePos &pos) const {
+        if constexpr (REC) {
+            return read_rec(recs + pos.k);
+        } else {
+            const AqDesc D = get_desc(P, pos.p);
+            return make_rec(piece_of(D, pos.p, pos.j), D);
+        }
+    }
+    __device__ __forceinline__ bool walk_to(const Piece &q, PiecePos &pos, PieceRec &r) const {
+        if (q.p >= P.ndesc) return false;
+        pos.p = q.p;
+        pos.j = q.j;
+        pos.nw = q.nw;
+        r = make_rec(q, get_desc(P, q.p));
+        return true;
+    }
+};
+
+// At the start: wave 0 builds the records (REC), every wave then sees them.  `nshared` is an int
+// of LDS.
+template <bool REC, int CAP>
+__device__ __forceinline__ int start_pieces(const AqParams &P, int wg, int wid, int lane, PieceRec *recs, int *nshared) {
+    if constexpr (!REC) return 0;
+    if (wid == 0) {
+        const int t = build_recs<CAP>(P, wg, lane, recs);
+        if (lane == 0) *nshared = t;
+    }
+    lds_barrier();
+    return min(__builtin_amdgcn_readfirstlane(*nshared), CAP);
 }
 
 // Row block (from the piece's first) of tile i of wave wid: the waves take turns, so a piece of
@@ -169,10 +331,10 @@ __device__ __forceinline__ int tile_rb(int wid, int i) { return wid + W * i; }
 
 // Load cursor, running ahead of the processing: where this wave's tiles of the next slice to load
 // are, and that slice's activations and codebooks.  Going from one slice to the next only adds a
-// stride to each address; the piece arithmetic runs once per piece.  A missing tile (past the
+// stride to each address; the piece bookkeeping runs once per piece.  A missing tile (past the
 // piece's row blocks, or past the end of the work) still takes its place in the load ring, so every
 // load stays unconditional: it reads 1 KiB of the codebooks instead, with a stride of 0.
-template <int RW>
+template <int RW, bool REC>
 struct Cursor {
     const uint8_t *ta[RW];  // per lane: its 16 bytes of tile i of the next slice
     int64_t tstr[RW];       // bytes from one slice of tile i to the next (0 for a missing tile)
@@ -181,31 +343,27 @@ struct Cursor {
     int64_t ldx;            // bytes between activation rows
     int gl;                 // groups of the projection from the next slice on
     int left;               // slices of the piece after the next one
-    int p, j, nw;           // the piece (to find the next)
+    PiecePos pos;
     bool done;
 
-    __device__ __forceinline__ void setup(const AqParams &P, const Piece &n, int wid, int lane) {
-        const AqDesc D = get_desc(P, n.p);
-        const int64_t stride = int64_t(D.Npad / 16) * 1024;
-        cbk = reinterpret_cast<const uint8_t *>(D.cbk);
-        xp = reinterpret_cast<const uint8_t *>(D.x) + int64_t(n.s0) * 512;
-        ldx = D.ldx * 2;
-        gl = D.G - 32 * n.s0;
-        left = n.s1 - n.s0 - 1;
-        p = n.p;
-        j = n.j;
-        nw = n.nw;
+    __device__ __forceinline__ void setup(const PieceRec &r, int wid, int lane) {
+        const int64_t stride = int64_t(r.Npad / 16) * 1024;
+        cbk = r.cbk;
+        xp = r.x + int64_t(r.s0) * 512;
+        ldx = r.ldx;
+        gl = r.G - 32 * r.s0;
+        left = r.s1 - r.s0 - 1;
         done = false;
-        const uint8_t *t0 = D.codes + int64_t(n.s0) * stride + int64_t(n.rb0 + wid) * 1024 + lane * 16;
+        const uint8_t *t0 = r.codes + int64_t(r.s0) * stride + int64_t(r.rb0 + wid) * 1024 + lane * 16;
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            const bool valid = n.rb0 + tile_rb(wid, i) < n.rb1;
+            const bool valid = r.rb0 + tile_rb(wid, i) < r.rb1;
             ta[i] = valid ? t0 + i * (W * 1024) : cbk + lane * 16;
             tstr[i] = valid ? stride : 0;
         }
     }
     // To the next slice: the piece's next, else the first of the workgroup's next piece.
-    __device__ __forceinline__ void advance(const AqParams &P, int wg, int wid, int lane) {
+    __device__ __forceinline__ void advance(const Pieces<REC> &pcs, int wid, int lane) {
         if (done) return;
         if (left > 0) {
             left--;
@@ -215,9 +373,9 @@ struct Cursor {
             gl -= 32;
             return;
         }
-        const Piece n = find_piece(P, wg, p, j + nw);
-        if (n.p < P.ndesc) {
-            setup(P, n, wid, lane);
+        PieceRec r;
+        if (pcs.next(pos, r)) {
+            setup(r, wid, lane);
             return;
         }
         done = true;  // the activation and codebook loads keep the last slice's (in bounds)
@@ -229,8 +387,8 @@ struct Cursor {
     }
 };
 
-template <int RW>
-__device__ __forceinline__ void load_tiles(const Cursor<RW> &c, u32x4 (&t)[RW]) {
+template <int RW, bool REC>
+__device__ __forceinline__ void load_tiles(const Cursor<RW, REC> &c, u32x4 (&t)[RW]) {
 #pragma unroll
     for (int i = 0; i < RW; i++)
         t[i] = __builtin_nontemporal_load((const u32x4 __attribute__((address_space(1))) *)(uintptr_t)c.ta[i]);
@@ -245,15 +403,15 @@ __device__ __forceinline__ void settle_tiles(u32x4 (&t)[RW]) {
 // Split pieces: arrival and the sum of the partials.
 // ------------------------------------------------------------------------------------------
 
-// Adds the b partials (in split order) of every row of piece q's row chunk, scales them and writes
+// Adds the b partials (in split order) of every row of piece r's row chunk, scales them and writes
 // y, then clears the chunk's counter.  Items (activation row m, row of the chunk) are taken by the
 // workgroup's threads in turn.  NL >= b loads per item, unconditional (indices past b - 1 repeat
 // the last split and are not added), so every load of a thread is in flight at once.
 template <int M, int RW, int NL>
-__device__ __forceinline__ void add_splits_n(const AqDesc &D, const Piece &q) {
+__device__ __forceinline__ void add_splits_n(const PieceRec &r) {
     constexpr int ROWS = W * RW * 16;  // most rows of a chunk
     constexpr int NI = (M * ROWS + W * 64 - 1) / (W * 64);
-    const int r0 = 16 * q.rb0, nrows = min(16 * q.rb1, D.N) - r0;
+    const int r0 = 16 * r.rb0, nrows = min(16 * r.rb1, r.N) - r0;
     float v[NI][NL];
     int rowv[NI], mv[NI];
     bool live[NI];
@@ -266,7 +424,7 @@ __device__ __forceinline__ void add_splits_n(const AqDesc &D, const Piece &q) {
         mv[it] = live[it] ? m : 0;
 #pragma unroll
         for (int j = 0; j < NL; j++)
-            v[it][j] = __hip_atomic_load(as_global(D.part + (int64_t(mv[it]) * D.b + min(j, D.b - 1)) * D.Npad + rowv[it]),
+            v[it][j] = __hip_atomic_load(as_global(r.part + (int64_t(mv[it]) * r.b + min(j, r.b - 1)) * r.Npad + rowv[it]),
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
@@ -274,108 +432,157 @@ __device__ __forceinline__ void add_splits_n(const AqDesc &D, const Piece &q) {
         float sum = 0.f;
 #pragma unroll
         for (int j = 0; j < NL; j++)
-            if (j < D.b) sum += v[it][j];
+            if (j < r.b) sum += v[it][j];
         if (live[it]) {
-            const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + rowv[it]));
-            gst(D.y + int64_t(mv[it]) * D.ldy + rowv[it], sum * sc);
+            const float sc = half_bits_to_float(gld<uint16_t>(r.rscale + rowv[it]));
+            gst(r.y + int64_t(mv[it]) * r.ldy + rowv[it], sum * sc);
         }
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(as_global(D.cnt + q.chunk * kAqCntStride), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(as_global(r.cnt), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <int M, int RW, int BMAX>
-__device__ __forceinline__ void add_splits(const AqDesc &D, const Piece &q) {
-    if (BMAX <= 8 || D.b <= 8) add_splits_n<M, RW, 8>(D, q);
-    else if (BMAX <= 16 || D.b <= 16) add_splits_n<M, RW, (BMAX < 16 ? BMAX : 16)>(D, q);
-    else if (BMAX <= 24 || D.b <= 24) add_splits_n<M, RW, (BMAX < 24 ? BMAX : 24)>(D, q);
-    else add_splits_n<M, RW, BMAX>(D, q);
+__device__ __forceinline__ void add_splits(const PieceRec &r) {
+    if (BMAX <= 8 || r.b <= 8) add_splits_n<M, RW, 8>(r);
+    else if (BMAX <= 16 || r.b <= 16) add_splits_n<M, RW, (BMAX < 16 ? BMAX : 16)>(r);
+    else if (BMAX <= 24 || r.b <= 24) add_splits_n<M, RW, (BMAX < 24 ? BMAX : 24)>(r);
+    else add_splits_n<M, RW, BMAX>(r);
 }
 
-// The split pieces a workgroup ran, recorded in LDS at the end of each (the finish reads them
-// per lane instead of walking the piece list again, which is scalar-unit work for every wave).
-constexpr int kAqMaxRec = 64;
-struct AqRec {
-    int *cnt;      // the piece's chunk counter
-    int32_t b;     // its splits
-    int32_t p, j;  // projection and piece index
-    int32_t pad_;
-};
-__device__ __forceinline__ void record_piece(AqRec *rec, int &nrec, const Piece &q, const AqDesc &D, int wid, int lane) {
-    if (D.b == 1) return;
-    if (nrec < kAqMaxRec && wid == 0 && lane == 0) {
-        AqRec r;
-        r.cnt = D.cnt + q.chunk * kAqCntStride;
-        r.b = D.b;
-        r.p = q.p;
-        r.j = q.j;
-        r.pad_ = 0;
-        rec[nrec] = r;
+// The record form's split sums: the nc chunks whose records fl[0..nc) name (this workgroup
+// arrived last on each; their split counts b <= NL), summed together.  An item is (chunk,
+// activation row m, row of the chunk); each thread takes G items per round, NL loads each
+// (unconditional, so that all are in flight at once), and issues every load of the round before
+// the first sum, so a round costs one trip to memory however many chunks it covers.  Items past a
+// chunk's rows load its first row instead and are not stored.
+template <int M, int RW, int NL, int G>
+__device__ __forceinline__ void add_splits_g(const PieceRec *recs, const int *fl, int nc) {
+    constexpr int ROWS = W * RW * 16;              // most rows of a chunk
+    const int per = M * ROWS, total = nc * per;
+    for (int base = 0; base < total; base += G * W * 64) {
+        float v[G][NL];
+        float *yp[G];
+        const uint16_t *sp[G];
+        int bb[G];
+        bool live[G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            const int item = base + g * W * 64 + int(threadIdx.x);
+            const int c = min(item / per, nc - 1), rem = item - (item / per) * per;
+            const int m = rem / ROWS, rr = rem - m * ROWS;
+            const PieceRec *rp = recs + fl[c];
+            const int b = rp->b, r0 = 16 * rp->rb0, nrows = min(16 * rp->rb1, rp->N) - r0;
+            live[g] = item < total && rr < nrows;
+            const int row = r0 + (live[g] ? rr : 0), mm = live[g] ? m : 0;
+            const float *part = rp->part + int64_t(mm) * b * rp->Npad + row;
+#pragma unroll
+            for (int j = 0; j < NL; j++)  // (unconditional: indices past b - 1 repeat the last split)
+                v[g][j] = __hip_atomic_load(as_global(part + int64_t(min(j, b - 1)) * rp->Npad), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+            yp[g] = rp->y + int64_t(mm) * rp->ldy + row;
+            sp[g] = rp->rscale + row;
+            bb[g] = b;
+        }
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+            if (!live[g]) continue;
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < NL; j++)
+                if (j < bb[g]) sum += v[g][j];
+            gst(yp[g], sum * half_bits_to_float(gld<uint16_t>(sp[g])));
+        }
     }
-    nrec++;
+    if (int(threadIdx.x) < nc) __hip_atomic_store(as_global(recs[fl[threadIdx.x]].cnt), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// G: as many items per thread as the chunks need (each thread then holds G x NL loads), at most
+// what the registers allow.
+template <int M, int RW, int NL>
+__device__ __forceinline__ void add_splits_recs(const PieceRec *recs, const int *fl, int nc) {
+    constexpr int GMAX = NL >= 24 ? 2 : (48 / NL > 4 ? 4 : 48 / NL);
+    const int need = (nc * M * W * RW * 16 + W * 64 - 1) / (W * 64);  // items per thread for one round
+    if (need <= 1 || GMAX == 1) add_splits_g<M, RW, NL, 1>(recs, fl, nc);
+    else if (need <= 2 || GMAX == 2) add_splits_g<M, RW, NL, (GMAX < 2 ? GMAX : 2)>(recs, fl, nc);
+    else if (need <= 3 || GMAX == 3) add_splits_g<M, RW, NL, (GMAX < 3 ? GMAX : 3)>(recs, fl, nc);
+    else add_splits_g<M, RW, NL, GMAX>(recs, fl, nc);
 }
 
 // After all of the workgroup's pieces: once every wave's partial stores have completed, the
 // workgroup counts each of its split pieces done on the piece's row chunk (lane k of wave 0 takes
-// the k-th, so the atomics are one instruction), and where it arrived last it adds the chunk's
-// partials.  `rec` holds the nrec pieces record_piece kept (at most kAqMaxRec; past that the piece
-// list is walked again), `flags` 64 ints of LDS.
-template <int M, int RW, int BMAX>
-__device__ __forceinline__ void finish(const AqParams &P, int wg, int wid, int lane, const AqRec *rec, int nrec,
-                                       int *flags) {
+// the k-th, so the atomics are one instruction per 64 pieces), and where it arrived last it adds
+// the chunk's partials.  `flags`: 260 ints of LDS.
+template <int M, int RW, int BMAX, bool REC>
+__device__ __forceinline__ void finish(const Pieces<REC> &pcs, int wid, int lane, int *flags) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();  // every wave's partials are stored (and the records written)
-    if (nrec <= kAqMaxRec) {
+    lds_barrier();  // every wave's partials are stored
+    if constexpr (REC) {  // at most 64 records
         if (wid == 0) {
-            int last = 0;
-            if (lane < nrec) {
-                const AqRec r = rec[lane];
-                last = __hip_atomic_fetch_add(as_global(r.cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == r.b - 1;
+            int last = 0, b = 0;
+            if (lane < pcs.n) {
+                const PieceRec *rp = pcs.recs + lane;
+                b = rp->b;
+                int *cnt = rp->cnt;
+                if (b > 1) last = __hip_atomic_fetch_add(as_global(cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == b - 1;
             }
-            flags[lane] = last;
+            // the chunks this workgroup finishes, by split-count class (b <= 8, 16, 24, more), in
+            // record order: the count of class c at flags[c], its list at flags[4 + 64 c ..]
+            const int cls = b <= 8 ? 0 : b <= 16 ? 1 : b <= 24 ? 2 : 3;
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const uint64_t mask = __ballot(last && cls == c);
+                const int pos = __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
+                if (last && cls == c) flags[4 + 64 * c + pos] = lane;
+                if (lane == 0) flags[c] = __popcll(mask);
+            }
         }
         lds_barrier();
-        for (int k = 0; k < nrec; k++) {
-            if (!__builtin_amdgcn_readfirstlane(flags[k])) continue;
-            const int p = __builtin_amdgcn_readfirstlane(rec[k].p), j = __builtin_amdgcn_readfirstlane(rec[k].j);
-            const Piece q = find_piece(P, wg, p, j);
-            add_splits<M, RW, BMAX>(get_desc(P, q.p), q);
-        }
+        int nc[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) nc[c] = __builtin_amdgcn_readfirstlane(flags[c]);
+        if (nc[0]) add_splits_recs<M, RW, 8>(pcs.recs, flags + 4, nc[0]);
+        if (BMAX > 8 && nc[1]) add_splits_recs<M, RW, (BMAX < 16 ? BMAX : 16)>(pcs.recs, flags + 4 + 64, nc[1]);
+        if (BMAX > 16 && nc[2]) add_splits_recs<M, RW, (BMAX < 24 ? BMAX : 24)>(pcs.recs, flags + 4 + 128, nc[2]);
+        if (BMAX > 24 && nc[3]) add_splits_recs<M, RW, BMAX>(pcs.recs, flags + 4 + 192, nc[3]);
         return;
-    }
-    Piece q = find_piece(P, wg, 0, -1);
-    while (q.p < P.ndesc) {
-        const Piece q0 = q;
-        int *cnt = nullptr;  // lane k: the k-th split piece's counter and split count
-        int bk = 0, n = 0;
-        for (; q.p < P.ndesc && n < 64; q = next_piece(P, wg, q)) {
-            const AqDesc D = get_desc(P, q.p);
-            if (D.b == 1) continue;
-            if (lane == n) {
-                cnt = D.cnt + q.chunk * kAqCntStride;
-                bk = D.b;
+    } else {
+        PiecePos pos;
+        PieceRec r;
+        bool more = pcs.first(pos, r);
+        while (more) {
+            const PiecePos pos0 = pos;
+            int *cnt = nullptr;  // lane k: the k-th split piece's counter and split count
+            int bk = 0, n = 0;
+            for (; more && n < 64; more = pcs.next(pos, r)) {
+                if (r.b == 1) continue;
+                if (lane == n) {
+                    cnt = r.cnt;
+                    bk = r.b;
+                }
+                n++;
             }
-            n++;
+            if (wid == 0) {
+                int last = 0;
+                if (lane < n) last = __hip_atomic_fetch_add(as_global(cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == bk - 1;
+                flags[lane] = last;
+            }
+            lds_barrier();
+            PiecePos q = pos0;
+            PieceRec rq = pcs.at(q);
+            for (int k = 0; k < n; ) {
+                if (rq.b > 1) {
+                    if (__builtin_amdgcn_readfirstlane(flags[k])) add_splits<M, RW, BMAX>(rq);
+                    k++;
+                }
+                if (k < n) pcs.next(q, rq);
+            }
+            lds_barrier();  // flags are read before the next round overwrites them
         }
-        if (wid == 0) {
-            int last = 0;
-            if (lane < n) last = __hip_atomic_fetch_add(as_global(cnt), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == bk - 1;
-            flags[lane] = last;
-        }
-        lds_barrier();
-        int k = 0;
-        for (Piece r = q0; k < n; r = next_piece(P, wg, r)) {
-            const AqDesc D = get_desc(P, r.p);
-            if (D.b == 1) continue;
-            if (__builtin_amdgcn_readfirstlane(flags[k])) add_splits<M, RW, BMAX>(D, r);
-            k++;
-        }
-        lds_barrier();  // flags are read before the next round overwrites them
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // Lookup-table kernel, M = 1.  RW: 16-row blocks per wave per slice (a piece has at most W*RW).
-// One workgroup per CU (the two tables take 128 KiB of LDS), 4 waves per SIMD.
+// One workgroup per CU (the two tables take 128 KiB of LDS), 4 waves per SIMD.  REC: the
+// workgroup's pieces as LDS records (at most kAqLutRecs), else walked from the descriptors.
 // ------------------------------------------------------------------------------------------
 struct LutOps {
     u32x2 A;   // this wave's codebook rows (A operand of the table build)
@@ -383,24 +590,28 @@ struct LutOps {
     int gval;  // groups of the slice inside K
 };
 
-template <int RW, int R>
+template <int RW, int R, bool REC>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_lut_kernel(AqParams P) {
     __shared__ uint32_t lds[2 * 256 * 64];
-    __shared__ AqRec recs[kAqMaxRec];
-    int nrec = 0;
+    __shared__ PieceRec recs[REC ? kAqLutRecs : 1];
+    __shared__ int nshared;
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int wg = blockIdx.x;
     const int h = lane >> 5, g = lane & 31;
 
-    Piece pp = find_piece(P, wg, 0, -1);  // piece being processed
-    if (pp.p >= P.ndesc) return;          // no work for this workgroup (same for all its waves)
-    int ps = pp.s0;                       // slice being processed
-    int rows_w = pp.rb1 - pp.rb0 - wid;   // tile i of this wave is in the piece when 16 i < rows_w
+    const int nrecs = start_pieces<REC, kAqLutRecs>(P, wg, wid, lane, recs, &nshared);
+    const Pieces<REC> pcs{P, wg, recs, nrecs};
+    PiecePos pos;  // piece being processed
+    PieceRec pr;
+    if (!pcs.first(pos, pr)) return;  // no work for this workgroup (same for all its waves)
+    int ps = pr.s0, ps_end = pr.s1;   // slice being processed, end of the piece's slices
+    int rows_w = pr.rb1 - pr.rb0 - wid;  // tile i of this wave is in the piece when 16 i < rows_w
 
-    Cursor<RW> ld;
-    ld.setup(P, pp, wid, lane);
+    Cursor<RW, REC> ld;
+    ld.pos = pos;
+    ld.setup(pr, wid, lane);
 
     // LDS byte address of a lookup: (tb << 16) | (code << 8) | (b << 7) | (g << 2), b the codebook.
     // Byte 0 and byte 2 come from lk, byte 1 is the code byte the selector picks from the word:
@@ -413,12 +624,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     // the build operands: this wave's codebook rows (codebook wid/8, codes 32(wid%8) + g), and
     // the 8 activations of group g (groups past K clamp to the last, then read as zero)
     const uint32_t aoff = ((wid >> 3) * 256 + 32 * (wid & 7) + g) * 16 + 8 * h;
-    auto load_slice = [&](u32x4 (&t)[RW], LutOps &o) __attribute__((always_inline)) {
+    auto load_ops = [&](LutOps &o) __attribute__((always_inline)) {
         o.A = gld<u32x2>(ld.cbk + aoff);
         o.gval = ld.gl;
         o.B = gld<u32x2>(ld.xp + min(g, ld.gl - 1) * 16 + 8 * h);
+    };
+    auto load_slice = [&](u32x4 (&t)[RW], LutOps &o) __attribute__((always_inline)) {
+        load_ops(o);
         load_tiles(ld, t);
-        ld.advance(P, wg, wid, lane);
+        ld.advance(pcs, wid, lane);
     };
     auto settle_ops = [&](LutOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.A), "v"(o.B)); };
 
@@ -476,25 +690,25 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     };
 
     // Piece epilogue: row sums -> y (b == 1) or this split's partials.
-    auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
+    auto epilogue = [&](const PieceRec &r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            const int rb = q.rb0 + tile_rb(wid, i);
+            const int rb = r.rb0 + tile_rb(wid, i);
             if (W * i < rows_w) {
                 const float z = finish_half4(acc[i], lane);
                 const int row = 16 * rb + 8 * h + ((lane >> 2) & 7);
-                if ((lane & 3) == 0 && row < D.N) {
-                    if (D.b == 1) {
-                        const float sc = half_bits_to_float(gld<uint16_t>(D.rscale + row));
-                        gst(D.y + row, z * sc);
+                if ((lane & 3) == 0 && row < r.N) {
+                    if (r.b == 1) {
+                        const float sc = half_bits_to_float(gld<uint16_t>(r.rscale + row));
+                        gst(r.y + row, z * sc);
                     } else {
-                        __hip_atomic_store(as_global(D.part + int64_t(q.split) * D.Npad + row), z, __ATOMIC_RELAXED,
+                        __hip_atomic_store(as_global(r.part + int64_t(r.split) * r.Npad + row), z, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; r++) acc[i][r] = 0.f;
+            for (int q = 0; q < 4; q++) acc[i][q] = 0.f;
         }
     };
 
@@ -521,22 +735,29 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
         lds_barrier();
         tb ^= 1;
-        if (++ps < pp.s1) return;
-        const AqDesc pd = get_desc(P, pp.p);
-        epilogue(pp, pd);
-        record_piece(recs, nrec, pp, pd, wid, lane);
-        pp = next_piece(P, wg, pp);
-        fin = pp.p >= P.ndesc;
-        ps = pp.s0;
-        rows_w = pp.rb1 - pp.rb0 - wid;
+        if (++ps < ps_end) return;
+        epilogue(pcs.at(pos));
+        PieceRec r;
+        if (!pcs.next(pos, r)) {
+            fin = true;
+            return;
+        }
+        ps = r.s0;
+        ps_end = r.s1;
+        rows_w = r.rb1 - r.rb0 - wid;
     };
 
     // R unit buffers: while unit s is processed, units s+1 .. s+R-2 are in flight, and the loads of
     // unit s+R-1 go into the buffer unit s-1 freed.
+    // At the start every wave issues the first table's operands before any tile load (the
+    // barrier between), so the first build does not wait behind the workgroup's first tiles.
     static_assert(R == 3, "three unit buffers");
     u32x4 buf0[RW], buf1[RW], buf2[RW];
     LutOps ops0, ops1, ops2;
-    load_slice(buf0, ops0);
+    load_ops(ops0);
+    __builtin_amdgcn_s_barrier();
+    load_tiles(ld, buf0);
+    ld.advance(pcs, wid, lane);
     load_slice(buf1, ops1);
     settle_ops(ops0);
     build(ops0, 0);
@@ -546,11 +767,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         step(buf1, ops2, buf0, ops0);
         step(buf2, ops0, buf1, ops1);
     } while (!fin);
-    finish<1, RW, kAqLutMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
+    finish<1, RW, kAqLutMaxSplits, REC>(pcs, wid, lane, reinterpret_cast<int *>(lds));
 }
 
 // ------------------------------------------------------------------------------------------
-// Matrix-core kernel, M activation rows.  RW: 16-row blocks per wave per slice.
+// Matrix-core kernel, M activation rows.  RW: 16-row blocks per wave per slice.  REC as above
+// (at most kAqMmaRecs records).
 // ------------------------------------------------------------------------------------------
 constexpr int kCbBytes = 2 * 256 * 16 * 16;  // 16 copies of the two codebooks
 constexpr int kStageBytes = 2 * 544;         // per wave: a tile, half h at h*544 (padded)
@@ -569,13 +791,13 @@ struct MmaOps {
     int gval;  // groups of the slice inside K
 };
 
-template <int M, int RW>
+template <int M, int RW, bool REC>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_mma_kernel(AqParams P) {
     using L = MmaLds<M>;
-    static_assert(L::bytes + kAqMaxRec * sizeof(AqRec) <= 160 * 1024, "LDS of one workgroup");
+    static_assert(L::bytes + (REC ? kAqMmaRecs : 1) * sizeof(PieceRec) + 16 <= 160 * 1024, "LDS of one workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t lds[L::bytes];
-    __shared__ AqRec recs[kAqMaxRec];
-    int nrec = 0;
+    __shared__ PieceRec recs[REC ? kAqMmaRecs : 1];
+    __shared__ int nshared;
 
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -583,14 +805,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int n = lane & 15, q4 = lane >> 4;     // MMA operand lane: row (weight or activation), k-block
     const int th = lane >> 5, tg = lane & 31;    // tile lane: half, group
 
-    Piece pp = find_piece(P, wg, 0, -1);
-    if (pp.p >= P.ndesc) return;
-    int ps = pp.s0;
-    int rows_w = pp.rb1 - pp.rb0 - wid;  // tile i of this wave is in the piece when 16 i < rows_w
-    const uint16_t *pcbk = get_desc(P, pp.p).cbk;  // codebooks in LDS
+    const int nrecs = start_pieces<REC, kAqMmaRecs>(P, wg, wid, lane, recs, &nshared);
+    const Pieces<REC> pcs{P, wg, recs, nrecs};
+    PiecePos pos;
+    PieceRec pr;
+    if (!pcs.first(pos, pr)) return;
+    int ps = pr.s0, ps_end = pr.s1;
+    int rows_w = pr.rb1 - pr.rb0 - wid;  // tile i of this wave is in the piece when 16 i < rows_w
+    const uint8_t *pcbk = pr.cbk;        // codebooks in LDS
 
-    Cursor<RW> ld;
-    ld.setup(P, pp, wid, lane);
+    Cursor<RW, REC> ld;
+    ld.pos = pos;
+    ld.setup(pr, wid, lane);
 
     // thread t < 32M stages the 8 activations of row t/32, group t%32 of a slice
     const int xt = min(int(threadIdx.x), 32 * M - 1);
@@ -598,7 +824,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         o.gval = ld.gl;
         o.X = gld<u32x4>(ld.xp + (xt >> 5) * ld.ldx + min(xt & 31, ld.gl - 1) * 16);
         load_tiles(ld, t);
-        ld.advance(P, wg, wid, lane);
+        ld.advance(pcs, wid, lane);
     };
     auto settle_ops = [&](MmaOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.X)); };
     auto stage_x = [&](const MmaOps &o, int xb) __attribute__((always_inline)) {
@@ -609,10 +835,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     };
     // The projection's codebooks into the 16 copies (all loads first, then the writes).
-    auto codebooks = [&](const uint16_t *cbk) __attribute__((always_inline)) {
+    auto codebooks = [&](const uint8_t *cbk) __attribute__((always_inline)) {
         u32x4 e[8];
 #pragma unroll
-        for (int k = 0; k < 8; k++) e[k] = gld<u32x4>(cbk + ((threadIdx.x + k * W * 64) >> 4) * 8);
+        for (int k = 0; k < 8; k++) e[k] = gld<u32x4>(cbk + ((threadIdx.x + k * W * 64) >> 4) * 16);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const int idx = threadIdx.x + k * W * 64;  // entry idx >> 4, copy idx & 15
@@ -649,22 +875,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     };
 
     // Piece epilogue: register v of lane 16q + n is activation row 4q + v of weight row n.
-    auto epilogue = [&](const Piece &q, const AqDesc &D) __attribute__((always_inline)) {
+    auto epilogue = [&](const PieceRec &r) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < RW; i++) {
-            const int rb = q.rb0 + tile_rb(wid, i);
+            const int rb = r.rb0 + tile_rb(wid, i);
             const int row = 16 * rb + n;
-            if (W * i < rows_w && row < D.N) {
-                const float sc = D.b == 1 ? half_bits_to_float(gld<uint16_t>(D.rscale + row)) : 0.f;
+            if (W * i < rows_w && row < r.N) {
+                const float sc = r.b == 1 ? half_bits_to_float(gld<uint16_t>(r.rscale + row)) : 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; v++) {
                     const int m = 4 * q4 + v;
                     const float s = Dacc[i][0][v] + Dacc[i][1][v];
                     if (m < M) {
-                        if (D.b == 1)
-                            gst(D.y + int64_t(m) * D.ldy + row, s * sc);
+                        if (r.b == 1)
+                            gst(r.y + int64_t(m) * r.ldy + row, s * sc);
                         else
-                            __hip_atomic_store(as_global(D.part + (int64_t(m) * D.b + q.split) * D.Npad + row), s,
+                            __hip_atomic_store(as_global(r.part + (int64_t(m) * r.b + r.split) * r.Npad + row), s,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
@@ -696,18 +922,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
         lds_barrier();
         xb ^= 1;
-        if (++ps < pp.s1) return;
-        const AqDesc pd = get_desc(P, pp.p);
-        epilogue(pp, pd);
-        record_piece(recs, nrec, pp, pd, wid, lane);
-        pp = next_piece(P, wg, pp);
-        fin = pp.p >= P.ndesc;
-        ps = pp.s0;
-        rows_w = pp.rb1 - pp.rb0 - wid;
-        if (fin) return;
-        const uint16_t *ncbk = get_desc(P, pp.p).cbk;
-        if (ncbk != pcbk) {  // every wave is past its lookups of the old codebooks (the barrier above)
-            pcbk = ncbk;
+        if (++ps < ps_end) return;
+        epilogue(pcs.at(pos));
+        PieceRec r;
+        if (!pcs.next(pos, r)) {
+            fin = true;
+            return;
+        }
+        ps = r.s0;
+        ps_end = r.s1;
+        rows_w = r.rb1 - r.rb0 - wid;
+        if (r.cbk != pcbk) {  // every wave is past its lookups of the old codebooks (the barrier above)
+            pcbk = r.cbk;
             codebooks(pcbk);
             lds_barrier();
         }
@@ -726,22 +952,25 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         step(buf1, ops2, buf0, ops0);
         step(buf2, ops0, buf1, ops1);
     } while (!fin);
-    finish<M, RW, kAqMmaMaxSplits>(P, wg, wid, lane, recs, nrec, reinterpret_cast<int *>(lds));
+    finish<M, RW, kAqMmaMaxSplits, REC>(pcs, wid, lane, reinterpret_cast<int *>(lds));
 }
 
 }  // namespace
 
-AqFn aq_fn(int M, bool lut) {
-    if (lut) return M == 1 ? aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING> : nullptr;
+AqFn aq_fn(int M, bool lut, bool rec) {
+    if (lut) {
+        if (M != 1) return nullptr;
+        return rec ? aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING, true> : aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING, false>;
+    }
     switch (M) {
-    case 1: return aq_mma_kernel<1, kAqMmaRW>;
-    case 2: return aq_mma_kernel<2, kAqMmaRW>;
-    case 3: return aq_mma_kernel<3, kAqMmaRW>;
-    case 4: return aq_mma_kernel<4, kAqMmaRW>;
-    case 5: return aq_mma_kernel<5, kAqMmaRW>;
-    case 6: return aq_mma_kernel<6, kAqMmaRW>;
-    case 7: return aq_mma_kernel<7, kAqMmaRW>;
-    case 8: return aq_mma_kernel<8, kAqMmaRW>;
+    case 1: return rec ? aq_mma_kernel<1, kAqMmaRW, true> : aq_mma_kernel<1, kAqMmaRW, false>;
+    case 2: return rec ? aq_mma_kernel<2, kAqMmaRW, true> : aq_mma_kernel<2, kAqMmaRW, false>;
+    case 3: return rec ? aq_mma_kernel<3, kAqMmaRW, true> : aq_mma_kernel<3, kAqMmaRW, false>;
+    case 4: return rec ? aq_mma_kernel<4, kAqMmaRW, true> : aq_mma_kernel<4, kAqMmaRW, false>;
+    case 5: return rec ? aq_mma_kernel<5, kAqMmaRW, true> : aq_mma_kernel<5, kAqMmaRW, false>;
+    case 6: return rec ? aq_mma_kernel<6, kAqMmaRW, true> : aq_mma_kernel<6, kAqMmaRW, false>;
+    case 7: return rec ? aq_mma_kernel<7, kAqMmaRW, true> : aq_mma_kernel<7, kAqMmaRW, false>;
+    case 8: return rec ? aq_mma_kernel<8, kAqMmaRW, true> : aq_mma_kernel<8, kAqMmaRW, false>;
     }
     return nullptr;
 }
