@@ -132,9 +132,9 @@ WQD_API int64_t wqd_workspace_bytes(const wqd_weight *w, int64_t M);
  * time must not share a workspace).  When K is split, the wave that finishes the last K-slice of
  * a 64-row group adds the slices' partial sums in ascending order, so results are the same bits
  * from run to run.  Every call is one launch.  AQ2X8 forms its group sums in fp32 at every M:
- * fp32 lookup tables of the activations at M = 1, exact fp16 products of codebook entries summed
- * in fp32 on the matrix cores at M > 1; its K-splits are added in split order by the wave that
- * finishes last. */
+ * fp32 lookup tables of the activations at M = 1 and 2, exact fp16 products of codebook entries
+ * summed in fp32 on the matrix cores at M > 2; its K-splits are added in split order by the
+ * workgroup that finishes last. */
 WQD_API int wqd_gemm(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, float *y, int64_t ldy,
                      void *workspace, int64_t workspace_bytes, void *stream);
 
@@ -230,7 +230,7 @@ enum {
  * holds: every projection is sliced the same way at every M, and every M runs the same per-row
  * instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
  * A verify of 9..16 rows is two calls.  AQ2X8 entries then take the matrix-core kernel at every M
- * (the M = 1 lookup-table kernel rounds differently), with pieces planned for every CU whatever
+ * (the M <= 2 lookup-table kernel rounds differently), with pieces planned for every CU whatever
  * the list.  Results differ in rounding (within the bound) from calls without the flag. */
 enum { WQD_BATCH_INVARIANT = 0x10 };
 

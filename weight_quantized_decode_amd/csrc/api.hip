@@ -361,10 +361,10 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
 // a x b pieces (row chunks of nrb <= 16*RW blocks, K-splits of ns slices), dealt over the nw
 // workgroups that serve the projection.  Cost model per piece, in tile loads (KiB): ns * (nrb +
 // slice setup) plus a fixed charge for a K-split (its partial round trip); the shape whose
-// busiest workgroup is cheapest wins.  M = 1 runs the lookup-table kernel; M > 1 and every
+// busiest workgroup is cheapest wins.  M = 1 and 2 run the lookup-table kernel; M > 2 and every
 // batch-invariant call run the matrix-core kernel.
 // ------------------------------------------------------------------------------------------
-static bool aq_lut(int64_t M, bool bi) { return M == 1 && !bi; }
+static bool aq_lut(int64_t M, bool bi) { return M <= 2 && !bi; }
 
 struct AqPlan {
     Layout L;
@@ -383,7 +383,7 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
     if (!A.L.ok) return A;
     A.lut = lut;
     const int64_t RB = (N + 15) / 16, KS = A.L.KS;
-    const int64_t per = int64_t(kAqWaves) * (lut ? kAqLutRW : kAqMmaRW);  // most row blocks per piece
+    const int64_t per = int64_t(kAqWaves) * (lut ? (M == 1 ? kAqLutRW : kAqLut2RW) : kAqMmaRW);  // most row blocks per piece
     const int64_t bmax = lut ? kAqLutMaxSplits : kAqMmaMaxSplits;
     const int64_t setup = lut ? WQD_AQ_BUILD_CHARGE : 2;  // table build / activation staging
     if (nw < 1) nw = 1;

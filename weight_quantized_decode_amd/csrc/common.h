@@ -149,7 +149,11 @@ constexpr int kMaskCB48 = (1 << CB4) | (1 << CB8);
 constexpr int kAqWaves = 16;        // waves per AQ2X8 workgroup (one workgroup per CU)
 constexpr int kAqLutMaxSplits = 32; // most K-splits of a lookup-table (M = 1) projection
 constexpr int kAqMmaMaxSplits = 8;  // most K-splits of a matrix-core projection
-constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-table kernel
+constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-table kernel (M = 1)
+#ifndef WQD_AQ_LUT2_RW
+#define WQD_AQ_LUT2_RW 2
+#endif
+constexpr int kAqLut2RW = WQD_AQ_LUT2_RW;  // the same at M = 2 (two rows' accumulators)
 constexpr int kAqMmaRW = 2;         // row blocks per wave per slice, matrix-core kernel
 constexpr int kAqCntStride = 32;    // ints between the arrival counters of two row chunks
 constexpr int kAqLutRecs = 64;      // most pieces per workgroup kept as LDS records, lookup-table kernel
@@ -186,7 +190,7 @@ struct AqParams {
 };
 
 typedef void (*AqFn)(AqParams);
-// AQ2X8 kernel instance: the lookup-table kernel (M = 1, lut) or the matrix-core kernel for M
+// AQ2X8 kernel instance: the lookup-table kernel (lut: M = 1 or 2) or the matrix-core kernel for M
 // activation rows (1 <= M <= 8; every batch-invariant call takes it).  rec: the form that keeps
 // each workgroup's pieces as LDS records, valid when no workgroup serves more than kAqLutRecs
 // (lut) or kAqMmaRecs pieces; the other form walks the descriptors.

@@ -580,18 +580,25 @@ __device__ __forceinline__ void finish(const Pieces<REC> &pcs, int wid, int lane
 }
 
 // ------------------------------------------------------------------------------------------
-// Lookup-table kernel, M = 1.  RW: 16-row blocks per wave per slice (a piece has at most W*RW).
-// One workgroup per CU (the two tables take 128 KiB of LDS), 4 waves per SIMD.  REC: the
-// workgroup's pieces as LDS records (at most kAqLutRecs), else walked from the descriptors.
+// Lookup-table kernel, M = 1 or 2 activation rows.  RW: 16-row blocks per wave per slice (a piece
+// has at most W*RW).  One workgroup per CU, 4 waves per SIMD; the tables take 128 KiB of LDS:
+//   M = 1: two tables of one slice (fp32, dword c*64 + b*32 + g), the next slice's built while
+//          the current one is read: one barrier per slice;
+//   M = 2: one table whose entries hold both rows' sums (fp32 pairs, at byte (b << 16) | (c << 8) |
+//          (g << 3)), built and then read: two barriers per slice.
+// REC: the workgroup's pieces as LDS records (at most kAqLutRecs), else walked from the descriptors.
 // ------------------------------------------------------------------------------------------
+template <int M>
 struct LutOps {
-    u32x2 A;   // this wave's codebook rows (A operand of the table build)
-    u32x2 B;   // the slice's activations of this lane's group (B operand)
-    int gval;  // groups of the slice inside K
+    u32x2 A;     // this wave's codebook rows (A operand of the table build)
+    u32x2 B[M];  // the slice's activations of this lane's group, per row (B operands)
+    int gval;    // groups of the slice inside K
 };
 
-template <int RW, int R, bool REC>
+template <int M, int RW, int R, bool REC>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void aq_lut_kernel(AqParams P) {
+    static_assert(M == 1 || M == 2, "one or two activation rows");
+    constexpr bool DB = M == 1;  // double-buffered tables
     __shared__ uint32_t lds[2 * 256 * 64];
     __shared__ PieceRec recs[REC ? kAqLutRecs : 1];
     __shared__ int nshared;
@@ -613,57 +620,80 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     ld.pos = pos;
     ld.setup(pr, wid, lane);
 
-    // LDS byte address of a lookup: (tb << 16) | (code << 8) | (b << 7) | (g << 2), b the codebook.
-    // Byte 0 and byte 2 come from lk, byte 1 is the code byte the selector picks from the word:
-    // word t holds (c0, c1) of rows 2t and 2t+1.
-    const uint32_t lkA0 = (uint32_t(g) << 2) | (uint32_t(h) << 7);
-    const uint32_t lkB0 = (uint32_t(g) << 2) | (uint32_t(1 - h) << 7);
+    // LDS byte address of a lookup: byte 0 and byte 2 come from lk, byte 1 is the code byte the
+    // selector picks from the word (word t holds (c0, c1) of rows 2t and 2t+1).  M = 1: (tb << 16) |
+    // (code << 8) | (b << 7) | (g << 2), tb the table buffer; M = 2: (b << 16) | (code << 8) |
+    // (g << 3).  Lanes of half 0 look up codebook 0 (A) while those of half 1 look up codebook 1,
+    // then the other way round (B), so no two lanes of a pass meet in a bank.
+    const uint32_t lkA0 = DB ? (uint32_t(g) << 2) | (uint32_t(h) << 7) : (uint32_t(g) << 3) | (uint32_t(h) << 16);
+    const uint32_t lkB0 = DB ? (uint32_t(g) << 2) | (uint32_t(1 - h) << 7) : (uint32_t(g) << 3) | (uint32_t(1 - h) << 16);
     const uint32_t selA[2] = {0x0c020000u | ((4u + h) << 8), 0x0c020000u | ((6u + h) << 8)};
     const uint32_t selB[2] = {0x0c020000u | ((5u - h) << 8), 0x0c020000u | ((7u - h) << 8)};
 
     // the build operands: this wave's codebook rows (codebook wid/8, codes 32(wid%8) + g), and
-    // the 8 activations of group g (groups past K clamp to the last, then read as zero)
+    // the 8 activations of group g per row (groups past K clamp to the last, then read as zero)
     const uint32_t aoff = ((wid >> 3) * 256 + 32 * (wid & 7) + g) * 16 + 8 * h;
-    auto load_ops = [&](LutOps &o) __attribute__((always_inline)) {
+    auto load_ops = [&](LutOps<M> &o) __attribute__((always_inline)) {
         o.A = gld<u32x2>(ld.cbk + aoff);
         o.gval = ld.gl;
-        o.B = gld<u32x2>(ld.xp + min(g, ld.gl - 1) * 16 + 8 * h);
+#pragma unroll
+        for (int m = 0; m < M; m++) o.B[m] = gld<u32x2>(ld.xp + m * ld.ldx + min(g, ld.gl - 1) * 16 + 8 * h);
     };
-    auto load_slice = [&](u32x4 (&t)[RW], LutOps &o) __attribute__((always_inline)) {
+    auto load_slice = [&](u32x4 (&t)[RW], LutOps<M> &o) __attribute__((always_inline)) {
         load_ops(o);
         load_tiles(ld, t);
         ld.advance(pcs, wid, lane);
     };
-    auto settle_ops = [&](LutOps &o) __attribute__((always_inline)) { __asm__ volatile("" ::"v"(o.A), "v"(o.B)); };
+    auto settle_ops = [&](LutOps<M> &o) __attribute__((always_inline)) {
+        __asm__ volatile("" ::"v"(o.A));
+#pragma unroll
+        for (int m = 0; m < M; m++) __asm__ volatile("" ::"v"(o.B[m]));
+    };
 
-    // The table of a slice into buffer tb: wave w computes T_(w/8)[32(w%8) .. +31][g = 0..31].
-    auto build = [&](const LutOps &o, int tb) __attribute__((always_inline)) {
-        const u32x2 B = g < o.gval ? o.B : u32x2{0u, 0u};  // groups past K read as zero
+    // The table of a slice (into buffer tb when double-buffered): wave w computes
+    // T_(w/8)[32(w%8) .. +31][g = 0..31], one 32x32x8 product per row.
+    auto build = [&](const LutOps<M> &o, int tb) __attribute__((always_inline)) {
         f32x16 z;
 #pragma unroll
         for (int v = 0; v < 16; v++) z[v] = 0.f;
-        const f32x16 D = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A), __builtin_bit_cast(h4, B), z, 0, 0, 0);
-        uint32_t *tab = lds + tb * (256 * 64) + (wid >> 3) * 32 + g;
+        f32x16 D[M];
 #pragma unroll
-        for (int v = 0; v < 16; v++) {  // register v of lane l: code row 8(v/4) + 4(l/32) + v%4
-            const int code = 32 * (wid & 7) + 8 * (v >> 2) + 4 * h + (v & 3);
-            tab[code * 64] = u32(D[v]);
+        for (int m = 0; m < M; m++) {
+            const u32x2 B = g < o.gval ? o.B[m] : u32x2{0u, 0u};  // groups past K read as zero
+            D[m] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4, o.A), __builtin_bit_cast(h4, B), z, 0, 0, 0);
+        }
+        if constexpr (DB) {
+            uint32_t *tab = lds + tb * (256 * 64) + (wid >> 3) * 32 + g;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {  // register v of lane l: code row 8(v/4) + 4(l/32) + v%4
+                const int code = 32 * (wid & 7) + 8 * (v >> 2) + 4 * h + (v & 3);
+                tab[code * 64] = u32(D[0][v]);
+            }
+        } else {
+            uint8_t *tab = reinterpret_cast<uint8_t *>(lds) + ((wid >> 3) << 16) + (g << 3);
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int code = 32 * (wid & 7) + 8 * (v >> 2) + 4 * h + (v & 3);
+                *reinterpret_cast<u32x2 *>(tab + (code << 8)) = u32x2{u32(D[0][v]), u32(D[M - 1][v])};
+            }
         }
     };
 
-    // per row block: the lane's 8 row sums folded over lanes l, l^16 (fold16)
-    float acc[RW][4];
+    // per row block and activation row: the lane's 8 row sums folded over lanes l, l^16 (fold16)
+    float acc[RW][M][4];
 #pragma unroll
     for (int i = 0; i < RW; i++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) acc[i][r] = 0.f;
+        for (int m = 0; m < M; m++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[i][m][r] = 0.f;
 
     // One tile: the 8 rows of this lane's half, its group.  The 16 lookups go out as two groups of
     // 8 (rows 0, 1, 4, 5, then rows 2, 3, 6, 7); the second group's addresses are tied to the first
     // lookup's result, so at most 15 LDS reads are outstanding and every wait is counted exactly.
-    auto process = [&](const u32x4 &v, float (&a)[4], uint32_t lkA, uint32_t lkB) __attribute__((always_inline)) {
+    auto process = [&](const u32x4 &v, float (&a)[M][4], uint32_t lkA, uint32_t lkB) __attribute__((always_inline)) {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        uint32_t e[2][8];
+        u32x2 e[2][8];  // M = 1: .x only
 #pragma unroll
         for (int q = 0; q < 2; q++) {
             uint32_t ad[8];
@@ -675,18 +705,27 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             }
             if (q == 1)
                 __asm__ volatile("" : "+v"(ad[0]), "+v"(ad[1]), "+v"(ad[2]), "+v"(ad[3]), "+v"(ad[4]), "+v"(ad[5]),
-                                 "+v"(ad[6]), "+v"(ad[7]) : "v"(e[0][0]));
+                                 "+v"(ad[6]), "+v"(ad[7]) : "v"(e[0][0].x));
 #pragma unroll
-            for (int k = 0; k < 8; k++) e[q][k] = lds_word(lds, ad[k]);
+            for (int k = 0; k < 8; k++) {
+                if constexpr (M == 1)
+                    e[q][k].x = lds_word(lds, ad[k]);
+                else
+                    e[q][k] = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(lds) + ad[k]);
+            }
         }
-        float r8[8], u[4];
 #pragma unroll
-        for (int q = 0; q < 2; q++)
+        for (int m = 0; m < M; m++) {
+            float r8[8], u[4];
 #pragma unroll
-            for (int k = 0; k < 4; k++) r8[(k & 1) + 2 * q + 4 * (k >> 1)] = f32(e[q][2 * k]) + f32(e[q][2 * k + 1]);
-        fold16(r8, u);
+            for (int q = 0; q < 2; q++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) a[r] += u[r];
+                for (int k = 0; k < 4; k++)
+                    r8[(k & 1) + 2 * q + 4 * (k >> 1)] = f32(e[q][2 * k][m]) + f32(e[q][2 * k + 1][m]);
+            fold16(r8, u);
+#pragma unroll
+            for (int r = 0; r < 4; r++) a[m][r] += u[r];
+        }
     };
 
     // Piece epilogue: row sums -> y (b == 1) or this split's partials.
@@ -695,39 +734,54 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         for (int i = 0; i < RW; i++) {
             const int rb = r.rb0 + tile_rb(wid, i);
             if (W * i < rows_w) {
-                const float z = finish_half4(acc[i], lane);
                 const int row = 16 * rb + 8 * h + ((lane >> 2) & 7);
-                if ((lane & 3) == 0 && row < r.N) {
-                    if (r.b == 1) {
-                        const float sc = half_bits_to_float(gld<uint16_t>(r.rscale + row));
-                        gst(r.y + row, z * sc);
-                    } else {
-                        __hip_atomic_store(as_global(r.part + int64_t(r.split) * r.Npad + row), z, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                const bool st = (lane & 3) == 0 && row < r.N;
+                const float sc = st && r.b == 1 ? half_bits_to_float(gld<uint16_t>(r.rscale + row)) : 0.f;
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    const float z = finish_half4(acc[i][m], lane);
+                    if (st) {
+                        if (r.b == 1)
+                            gst(r.y + int64_t(m) * r.ldy + row, z * sc);
+                        else
+                            __hip_atomic_store(as_global(r.part + (int64_t(m) * r.b + r.split) * r.Npad + row), z,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; q++) acc[i][q] = 0.f;
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) acc[i][m][q] = 0.f;
         }
     };
 
-    int tb = 0;         // table of the slice being processed
+    int tb = 0;         // table of the slice being processed (double-buffered tables)
     bool fin = false;   // every piece is done (the remaining steps of the ring's round are empty)
     // One slice: issue the loads of the slice two ahead (into the buffers the previous slice
-    // left), wait for this slice's tiles and the next slice's table operands, build the next table
-    // into the other buffer, look up this slice, barrier.  The loads and waits come first and on
-    // every path, the same in every step, so that the waits of the ring are counted exactly.
-    auto step = [&](u32x4 (&cur)[RW], LutOps &on, u32x4 (&nxt)[RW], LutOps &onew) __attribute__((always_inline)) {
+    // left), wait for this slice's tiles and the table operands, then (M = 1) build the next
+    // slice's table into the other buffer and look up this slice, barrier, or (M = 2) build this
+    // slice's table, barrier, look it up, barrier.  The loads and waits come first and on every
+    // path, the same in every step, so that the waits of the ring are counted exactly.
+    auto step = [&](u32x4 (&cur)[RW], LutOps<M> &ocur, LutOps<M> &on, u32x4 (&nxt)[RW], LutOps<M> &onew)
+                    __attribute__((always_inline)) {
         load_slice(nxt, onew);
         settle_tiles(cur);
-        settle_ops(on);
+        if constexpr (DB)
+            settle_ops(on);
+        else
+            settle_ops(ocur);
         if (fin) return;
         // (no scalar load may be pending during the build and lookups: the LDS waits are then
         // counted exactly instead of draining every lookup in flight)
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        build(on, tb ^ 1);
-        const uint32_t lkA = lkA0 | (uint32_t(tb) << 16), lkB = lkB0 | (uint32_t(tb) << 16);
+        if constexpr (DB) {
+            build(on, tb ^ 1);
+        } else {
+            build(ocur, 0);
+            lds_barrier();
+        }
+        const uint32_t lkA = lkA0 | (uint32_t(DB ? tb : 0) << 16), lkB = lkB0 | (uint32_t(DB ? tb : 0) << 16);
 #pragma unroll
         for (int i = 0; i < RW; i++) {
             if (W * i < rows_w) process(cur[i], acc[i], lkA, lkB);
@@ -753,21 +807,23 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     // barrier between), so the first build does not wait behind the workgroup's first tiles.
     static_assert(R == 3, "three unit buffers");
     u32x4 buf0[RW], buf1[RW], buf2[RW];
-    LutOps ops0, ops1, ops2;
+    LutOps<M> ops0, ops1, ops2;
     load_ops(ops0);
     __builtin_amdgcn_s_barrier();
     load_tiles(ld, buf0);
     ld.advance(pcs, wid, lane);
     load_slice(buf1, ops1);
-    settle_ops(ops0);
-    build(ops0, 0);
-    lds_barrier();
+    if constexpr (DB) {
+        settle_ops(ops0);
+        build(ops0, 0);
+        lds_barrier();
+    }
     do {
-        step(buf0, ops1, buf2, ops2);
-        step(buf1, ops2, buf0, ops0);
-        step(buf2, ops0, buf1, ops1);
+        step(buf0, ops0, ops1, buf2, ops2);
+        step(buf1, ops1, ops2, buf0, ops0);
+        step(buf2, ops2, ops0, buf1, ops1);
     } while (!fin);
-    finish<1, RW, kAqLutMaxSplits, REC>(pcs, wid, lane, reinterpret_cast<int *>(lds));
+    finish<M, RW, kAqLutMaxSplits, REC>(pcs, wid, lane, reinterpret_cast<int *>(lds));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -959,8 +1015,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 
 AqFn aq_fn(int M, bool lut, bool rec) {
     if (lut) {
-        if (M != 1) return nullptr;
-        return rec ? aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING, true> : aq_lut_kernel<kAqLutRW, WQD_AQ_LUT_RING, false>;
+        if (M == 1)
+            return rec ? aq_lut_kernel<1, kAqLutRW, WQD_AQ_LUT_RING, true> : aq_lut_kernel<1, kAqLutRW, WQD_AQ_LUT_RING, false>;
+        if (M == 2)
+            return rec ? aq_lut_kernel<2, kAqLut2RW, WQD_AQ_LUT_RING, true> : aq_lut_kernel<2, kAqLut2RW, WQD_AQ_LUT_RING, false>;
+        return nullptr;
     }
     switch (M) {
     case 1: return rec ? aq_mma_kernel<1, kAqMmaRW, true> : aq_mma_kernel<1, kAqMmaRW, false>;
