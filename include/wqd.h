@@ -70,7 +70,9 @@ typedef enum {
                         1..8, ld too small */
     WQD_EALIGN = -3, /* weight not 16-byte aligned, x or y not 4-byte aligned, odd ldx */
     WQD_ESPACE = -4, /* a capacity or workspace argument is smaller than required */
-    WQD_EHIP = -5    /* a HIP call failed; wqd_last_hip_error() gives its hipError_t */
+    WQD_EHIP = -5,   /* a HIP call failed; wqd_last_hip_error() gives its hipError_t */
+    WQD_ESTALE = -6  /* (reported by wqd_stream_check) a WQD_PERSISTENT launch found the workspace's
+                        descriptor table set up for another list, and wrote no output */
 } wqd_status;
 
 enum { WQD_MAX_M = 8 };
@@ -250,10 +252,14 @@ enum { WQD_INT8_ACTIVATIONS = 0x20 };
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs_host, int32_t count, int64_t M);
 
 /* Write the descriptor tables of this projection list for `mode` (WQD_PERSISTENT, optionally
- * with WQD_BATCH_INVARIANT and WQD_INT8_ACTIVATIONS) into the workspace and zero its counters
- * (blocking copies).
- * Must be called once before wqd_run_projections in that mode, and again whenever a pointer or
- * shape in the list changes.  Errors: WQD_EINVAL for another mode. */
+ * with WQD_BATCH_INVARIANT and WQD_INT8_ACTIVATIONS) into the workspace, zero its counters and
+ * stamp the tables with a fingerprint of the list.  Everything is enqueued on `stream` as kernel
+ * launches whose data travel in their arguments (no host synchronization, no memset or copy
+ * node: the call may be captured in a graph).
+ * Must be called before wqd_run_projections in that mode, and again whenever a pointer, shape,
+ * epilogue or mode of the list changes.  A WQD_PERSISTENT call whose list does not match the
+ * stamp (setup not repeated after a change) writes no output: its kernels return at once and
+ * the next wqd_stream_check reports WQD_ESTALE.  Errors: WQD_EINVAL for another mode. */
 WQD_API int wqd_stack_setup(const wqd_proj *projs_host, int32_t count, int64_t M, int32_t mode,
                             void *workspace, int64_t workspace_bytes, void *stream);
 
@@ -280,7 +286,9 @@ WQD_API int wqd_stack_launches(const wqd_proj *projs_host, int32_t count, int64_
 
 /* ---------------------------------------------------------------- errors */
 
-/* Synchronize `stream` and map any pending asynchronous error to WQD_EHIP. */
+/* Synchronize `stream` and map any pending asynchronous error to WQD_EHIP; then WQD_ESTALE if a
+ * WQD_PERSISTENT launch on this device found a stale descriptor table since the last check
+ * (the report is per device, and clears it). */
 WQD_API int wqd_stream_check(void *stream);
 /* hipError_t of the last WQD_EHIP returned on this thread (0 if none). */
 WQD_API int wqd_last_hip_error(void);

@@ -335,7 +335,7 @@ def test_pair_needs_a_workspace():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert W.wqd_status_str(s)
 
 

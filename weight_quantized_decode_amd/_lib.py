@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SO_PATH = os.path.join(_HERE, "libwqd.so")
 
 WQD_Q4_0, WQD_CB4, WQD_CB8, WQD_TQ2, WQD_AQ2X8, WQD_AQ1X16 = 1, 2, 3, 4, 5, 6
-WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP = 0, -1, -2, -3, -4, -5
+WQD_OK, WQD_EINVAL, WQD_ESHAPE, WQD_EALIGN, WQD_ESPACE, WQD_EHIP, WQD_ESTALE = 0, -1, -2, -3, -4, -5, -6
 WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED = 0, 1, 2
 WQD_BATCH_INVARIANT = 0x10
 WQD_INT8_ACTIVATIONS = 0x20

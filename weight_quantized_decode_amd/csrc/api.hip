@@ -2,6 +2,7 @@
 // dequantize-and-multiply kernels live in gemv_<format>.hip (instances of gemv_impl.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <mutex>
@@ -609,6 +610,7 @@ struct StackPlan {
     std::vector<AqDesc> aqdescs;
     std::vector<LaunchGroup> groups;
     std::vector<XQ> xqs;
+    int64_t off_stamp = 0;     // the table's stamp: fingerprint of the list setup wrote it for
     int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_xq = 0, off_part = 0;
     int64_t part_bytes = 0;    // partial bytes this mode uses
     bool needs_ws = false;     // some launch counts slices (split K or a gate/up pair)
@@ -870,8 +872,9 @@ static int build_stack_plan(const wqd_proj *pub, int32_t count, int64_t M, int m
     rc = check_list(p, count, M);
     if (rc != WQD_OK) return rc;
 
-    SP.off_descs = 0;
-    SP.off_aqdescs = align_up(int64_t(sizeof(Desc)) * count, 256);
+    SP.off_stamp = 0;
+    SP.off_descs = 256;
+    SP.off_aqdescs = align_up(SP.off_descs + int64_t(sizeof(Desc)) * count, 256);
     SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
     SP.off_cnt = SP.off_ctr + 256;
     int64_t cnt_all = 0;
@@ -993,6 +996,84 @@ static int scratch_on_device(hipStream_t st, uint8_t **out) {
         g_scratch_ptr[dev] = p;
     }
     *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return WQD_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Descriptor tables of WQD_PERSISTENT lists.  Setup writes them with kernels whose arguments
+// carry the bytes (so nothing on the host has to outlive the call and the call can be captured),
+// then zeroes the counters, then writes the stamp: a fingerprint of the plan.  Every launch from
+// the tables carries the fingerprint of the plan it was called with and checks the stamp first.
+// ------------------------------------------------------------------------------------------
+constexpr int kWriteWords = 960;  // payload dwords per writer launch (arguments stay under 4 KiB)
+struct WriteChunk {
+    uint32_t *dst;
+    int32_t nwords;
+    int32_t pad_;
+    uint32_t w[kWriteWords];
+};
+__global__ __launch_bounds__(256) void write_words_kernel(WriteChunk c) {
+    // the payload is read where it lies, in the kernel-argument segment (indexing the parameter
+    // itself would copy it to scratch first)
+    const cu32p src = (cu32p)((uintptr_t)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(WriteChunk, w));
+    for (int i = int(threadIdx.x); i < c.nwords; i += 256) c.dst[i] = src[i];
+}
+
+static int write_bytes(uint8_t *dst, const void *src, int64_t bytes, hipStream_t st) {
+    const uint8_t *s = static_cast<const uint8_t *>(src);
+    for (int64_t off = 0; off < bytes; off += 4 * kWriteWords) {
+        WriteChunk c;
+        memset(&c, 0, sizeof(c));
+        const int64_t n = bytes - off < 4 * kWriteWords ? bytes - off : 4 * kWriteWords;
+        c.dst = reinterpret_cast<uint32_t *>(dst + off);
+        c.nwords = int32_t((n + 3) / 4);
+        memcpy(c.w, s + off, size_t(n));
+        hipLaunchKernelGGL(write_words_kernel, dim3(1), dim3(256), 0, st, c);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return WQD_OK;
+}
+
+// Fingerprint of a plan: its descriptors (every pointer, shape and piece assignment), the mode
+// and M.  Never 0 (a zero-filled workspace holds no table).
+static uint64_t plan_fingerprint(const StackPlan &SP, int64_t M, int32_t mode) {
+    uint64_t h = 0x243F6A8885A308D3ull ^ uint64_t(M) ^ (uint64_t(uint32_t(mode)) << 32);
+    auto mix = [&](const void *p, size_t n) {
+        const uint8_t *b = static_cast<const uint8_t *>(p);
+        for (size_t i = 0; i + 8 <= n; i += 8) {
+            uint64_t w;
+            memcpy(&w, b + i, 8);
+            h = (h ^ w) * 0x9E3779B97F4A7C15ull;
+            h ^= h >> 29;
+        }
+        for (size_t i = n & ~size_t(7); i < n; i++) h = (h ^ b[i]) * 0x100000001B3ull;
+        h = (h ^ uint64_t(n)) * 0x9E3779B97F4A7C15ull;
+    };
+    mix(SP.descs.data(), sizeof(Desc) * SP.descs.size());
+    mix(SP.aqdescs.data(), sizeof(AqDesc) * SP.aqdescs.size());
+    return h | 1;
+}
+
+// The per-device flag a launch raises when it finds a stale table (a file-scope device variable;
+// its device address comes from hipGetSymbolAddress, once per device with the device current).
+static __device__ int stale_flag;
+static std::mutex g_flag_mu;
+static void *g_flag_ptr[kMaxScratchDevices];
+static int flag_on_device(int **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return WQD_EINVAL;
+    std::lock_guard<std::mutex> lock(g_flag_mu);
+    if (!g_flag_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(stale_flag));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!p) return hip_fail(hipErrorInvalidSymbol);
+        g_flag_ptr[dev] = p;
+    }
+    *out = static_cast<int *>(g_flag_ptr[dev]);
     return WQD_OK;
 }
 
@@ -1145,19 +1226,18 @@ WQD_API int wqd_stack_setup(const wqd_proj *projs, int32_t count, int64_t M, int
     if (workspace_bytes < SP.total()) return WQD_ESPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t *base = static_cast<uint8_t *>(workspace);
-    hipError_t e = hipSuccess;
-    if (!SP.descs.empty())
-        e = hipMemcpyAsync(base + SP.off_descs, SP.descs.data(), sizeof(Desc) * SP.descs.size(),
-                           hipMemcpyHostToDevice, st);
-    if (e == hipSuccess && !SP.aqdescs.empty())
-        e = hipMemcpyAsync(base + SP.off_aqdescs, SP.aqdescs.data(), sizeof(AqDesc) * SP.aqdescs.size(),
-                           hipMemcpyHostToDevice, st);
+    if (!SP.descs.empty() && (rc = write_bytes(base + SP.off_descs, SP.descs.data(), int64_t(sizeof(Desc) * SP.descs.size()), st)) != WQD_OK)
+        return rc;
+    if (!SP.aqdescs.empty() &&
+        (rc = write_bytes(base + SP.off_aqdescs, SP.aqdescs.data(), int64_t(sizeof(AqDesc) * SP.aqdescs.size()), st)) != WQD_OK)
+        return rc;
     // launch-group and slice counters start at 0; every launch leaves them at 0 again
-    std::vector<uint8_t> zeros(size_t(SP.off_part - SP.off_ctr), 0);
-    if (e == hipSuccess)
-        e = hipMemcpyAsync(base + SP.off_ctr, zeros.data(), zeros.size(), hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    return e == hipSuccess ? WQD_OK : hip_fail(e);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<uint4 *>(base + SP.off_ctr),
+                       (SP.off_part - SP.off_ctr) / 16);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+    const uint64_t fp = plan_fingerprint(SP, M, mode);  // last: the tables are complete before it
+    return write_bytes(base + SP.off_stamp, &fp, 8, st);
 }
 
 static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M, int32_t mode,
@@ -1185,6 +1265,11 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     const bool table = persistent;
     const Desc *dtab = table ? reinterpret_cast<const Desc *>(base + SP.off_descs) : nullptr;
     const AqDesc *atab = table ? reinterpret_cast<const AqDesc *>(base + SP.off_aqdescs) : nullptr;
+    // launches from the tables check them against this list
+    const uint64_t *stamp = table ? reinterpret_cast<const uint64_t *>(base + SP.off_stamp) : nullptr;
+    const uint64_t fp = table ? plan_fingerprint(SP, M, mode) : 0;
+    int *stale = nullptr;
+    if (table && (rc = flag_on_device(&stale)) != WQD_OK) return rc;
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
         const LaunchGroup &G = SP.groups[gi];
         if (G.xq >= 0) {
@@ -1208,6 +1293,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.descs = table ? atab + G.first : nullptr;
             AP.ndesc = G.count;
             AP.nwg = int32_t(G.nwg);
+            AP.stamp = stamp;
+            AP.fp = fp;
+            AP.stale = stale;
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
             rc = launch_aq(M, G.lut, aq_rec(&SP.aqdescs[G.first], G.count, G.lut), AP, st);
@@ -1227,6 +1315,9 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
         }
         GP.ndesc = G.count;
         GP.total_wgu = G.total_wgu;
+        GP.stamp = stamp;
+        GP.fp = fp;
+        GP.stale = stale;
         // The dynamic tail pays a barrier, an atomic and a cold load pipeline per unit it hands
         // out: only units of long slices amortize that.  (Launches run one after another, and
         // each leaves its two counters at zero, so they share them.)
@@ -1266,7 +1357,17 @@ WQD_API int wqd_run_projections_timed(const wqd_proj *projs, int32_t count, int6
 WQD_API int wqd_stream_check(void *stream) {
     hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
-    return e == hipSuccess ? WQD_OK : hip_fail(e);
+    if (e != hipSuccess) return hip_fail(e);
+    int *flag = nullptr;
+    int rc = flag_on_device(&flag);
+    if (rc != WQD_OK) return rc;
+    int v = 0;
+    e = hipMemcpy(&v, flag, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e);
+    if (v == 0) return WQD_OK;
+    const int zero = 0;
+    e = hipMemcpy(flag, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    return e == hipSuccess ? WQD_ESTALE : hip_fail(e);
 }
 
 WQD_API int wqd_last_hip_error(void) { return g_last_hip_error; }

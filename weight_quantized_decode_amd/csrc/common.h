@@ -127,6 +127,12 @@ struct GemvParams {
     int *ctr;
     int32_t pool_begin;
     int32_t pad_;
+    // Launches from a descriptor table: the table's stamp and the fingerprint of the list this
+    // launch was planned for; on a mismatch the launch exits without writing y and sets *stale.
+    // stamp == nullptr: no check (descriptors in the kernel arguments).
+    const uint64_t *stamp;
+    uint64_t fp;
+    int *stale;
 };
 
 
@@ -187,6 +193,9 @@ struct AqParams {
     const AqDesc *descs;      // device array (stack)
     int32_t ndesc;
     int32_t nwg;              // workgroups of the launch
+    const uint64_t *stamp;    // as in GemvParams
+    uint64_t fp;
+    int *stale;
 };
 
 typedef void (*AqFn)(AqParams);

@@ -608,6 +608,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int wg = blockIdx.x;
     const int h = lane >> 5, g = lane & 31;
 
+    if (stale_table(P.stamp, P.fp, P.stale)) return;
     const int nrecs = start_pieces<REC, kAqLutRecs>(P, wg, wid, lane, recs, &nshared);
     const Pieces<REC> pcs{P, wg, recs, nrecs};
     PiecePos pos;  // piece being processed
@@ -861,6 +862,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int n = lane & 15, q4 = lane >> 4;     // MMA operand lane: row (weight or activation), k-block
     const int th = lane >> 5, tg = lane & 31;    // tile lane: half, group
 
+    if (stale_table(P.stamp, P.fp, P.stale)) return;
     const int nrecs = start_pieces<REC, kAqMmaRecs>(P, wg, wid, lane, recs, &nshared);
     const Pieces<REC> pcs{P, wg, recs, nrecs};
     PiecePos pos;

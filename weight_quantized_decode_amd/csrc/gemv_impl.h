@@ -85,6 +85,20 @@ template <typename T>
 __device__ __forceinline__ T __attribute__((address_space(1))) *as_global(T *p) {
     return (T __attribute__((address_space(1))) *)(uintptr_t)p;
 }
+// A launch from a descriptor table first compares the table's stamp with the fingerprint of the
+// list it was planned for (a table that setup wrote for another list).  On a mismatch every
+// workgroup returns before touching any output, and workgroup 0 raises *stale.
+__device__ __forceinline__ bool stale_table(const uint64_t *stamp, uint64_t fp, int *stale) {
+    if (!stamp) return false;
+    const cu32p s = (cu32p)(uintptr_t)stamp;
+    const uint64_t v = uint64_t(s[0]) | (uint64_t(s[1]) << 32);
+    if (v == fp) return false;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store((int __attribute__((address_space(1))) *)(uintptr_t)stale, 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 // Workgroup barrier that orders LDS traffic only (global loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -909,6 +923,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWa
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
     __shared__ float red[kWaves * (M < 4 ? M : 4) * 64];  // workgroup-split sums
     __shared__ int next_u;
+    if (stale_table(P.stamp, P.fp, P.stale)) return;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int total = P.total_wgu;

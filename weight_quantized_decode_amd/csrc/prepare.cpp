@@ -188,6 +188,7 @@ WQD_API const char *wqd_status_str(int status) {
     case WQD_EALIGN: return "misaligned pointer or leading dimension";
     case WQD_ESPACE: return "buffer or workspace too small";
     case WQD_EHIP: return "HIP runtime error";
+    case WQD_ESTALE: return "a persistent launch found a descriptor table set up for another list";
     default: return "unknown status";
     }
 }
