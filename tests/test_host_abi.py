@@ -424,3 +424,19 @@ def test_gemm_noalloc_rejects_shapes_beyond_the_scratch():
     # argument errors come first, as for wqd_gemm
     assert W.lib().wqd_gemm_noalloc(w.ref(), None, M, K, 256, N, None) == W.WQD_EINVAL
     assert W.lib().wqd_gemm_noalloc(w.ref(), 256, 9, K, 256, N, None) == W.WQD_ESHAPE
+
+
+def test_binding_checks_tensors_before_any_call():
+    """The Python binding refuses host tensors, wrong dtypes and shapes before it passes a pointer."""
+    import torch
+    w = _view(I.CB4, 64, 64)
+    x_host = torch.zeros((1, 64), dtype=torch.int16)
+    y_host = torch.zeros((1, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        W.wqd_gemm(w, x_host, y_host)
+    with pytest.raises(TypeError):
+        W.wqd_gemm_noalloc(w, x_host, y_host)
+    with pytest.raises(TypeError):
+        W.make_proj_array([dict(w=w, x=x_host, y=y_host)])
+    with pytest.raises(TypeError):
+        W.wqd_bind(I.CB4, 64, 64, torch.zeros(4096, dtype=torch.uint8))  # a host buffer

@@ -132,6 +132,28 @@ def _dptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _mat(t, what: str, rows: Optional[int], cols: int, elem: int, float_ok: bool):
+    """Checks a 2-D device matrix argument: on the GPU, `elem`-byte elements (fp16 bits as int16 or
+    float16, or float32), unit inner stride, the expected shape; returns nothing."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what}: a CUDA tensor is required")
+    ok = {2: (torch.int16, torch.float16), 4: (torch.float32,)}[elem]
+    if t.dtype not in ok:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected one of {ok}")
+    if t.dim() != 2 or t.stride(1) != 1 or t.shape[1] != cols or (rows is not None and t.shape[0] != rows):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} strides {t.stride()}, expected ({rows if rows else 'M'}, {cols}) "
+                         f"with unit inner stride")
+
+
+def _ws(t, what: str = "workspace"):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{what}: a contiguous CUDA tensor is required")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -164,6 +186,14 @@ def wqd_prepare_host(fmt: int, N: int, K: int, canonical: np.ndarray) -> np.ndar
 def wqd_bind(fmt: int, N: int, K: int, prepared) -> Weight:
     """The plane view of a prepared weight buffer (a device tensor, or a raw address)."""
     view = wqd_weight()
+    if not isinstance(prepared, int):
+        import torch
+        if not isinstance(prepared, torch.Tensor) or not prepared.is_cuda or not prepared.is_contiguous():
+            raise TypeError("wqd_bind: a contiguous CUDA tensor (or a raw device address) is required")
+        need = wqd_prepared_bytes(fmt, N, K)
+        if prepared.numel() * prepared.element_size() < need:
+            raise ValueError(f"wqd_bind: buffer of {prepared.numel() * prepared.element_size()} bytes, "
+                             f"the prepared layout takes {need}")
     addr = prepared if isinstance(prepared, int) else _dptr(prepared)
     _check("wqd_bind", lib().wqd_bind(fmt, N, K, addr, ctypes.byref(view)))
     return Weight(view, None if isinstance(prepared, int) else prepared)
@@ -177,7 +207,10 @@ def wqd_workspace_bytes(w: Weight, M: int) -> int:
 
 def wqd_gemm(w: Weight, x, y, workspace=None, stream=None) -> None:
     """y[M, N] (fp32) = x[M, K] (fp16) times the dequantized W[N, K]; x and y may have row strides."""
+    _mat(x, "x", None, w.K, 2, True)
     M = x.shape[0]
+    _mat(y, "y", M, w.N, 4, True)
+    _ws(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("wqd_gemm", lib().wqd_gemm(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0), _dptr(workspace),
                                       ws_bytes, _stream(stream)))
@@ -185,7 +218,9 @@ def wqd_gemm(w: Weight, x, y, workspace=None, stream=None) -> None:
 
 def wqd_gemm_noalloc(w: Weight, x, y, stream=None) -> None:
     """wqd_gemm without a workspace: the library's per-GPU scratch array serves as one."""
+    _mat(x, "x", None, w.K, 2, True)
     M = x.shape[0]
+    _mat(y, "y", M, w.N, 4, True)
     _check("wqd_gemm_noalloc", lib().wqd_gemm_noalloc(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
                                                       _stream(stream)))
 
@@ -196,7 +231,10 @@ def wqd_gemm_i8_workspace_bytes(w: Weight, M: int) -> int:
 
 def wqd_gemm_i8(w: Weight, x, y, workspace, stream=None) -> None:
     """TQ2 times int8-quantized x (quantized inside the call); x and y may have row strides."""
+    _mat(x, "x", None, w.K, 2, True)
     M = x.shape[0]
+    _mat(y, "y", M, w.N, 4, True)
+    _ws(workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("wqd_gemm_i8", lib().wqd_gemm_i8(w.ref(), _dptr(x), M, x.stride(0), _dptr(y), y.stride(0),
                                             _dptr(workspace), ws_bytes, _stream(stream)))
@@ -204,12 +242,22 @@ def wqd_gemm_i8(w: Weight, x, y, workspace, stream=None) -> None:
 
 def wqd_quantize_i8(x, q, a, qsum, stream=None) -> None:
     """q (int8 [M, K]), a (fp32 [M, K/128]) and qsum (int32 [M, K/128]) of fp16 x [M, K]."""
+    import torch
     M, K = x.shape
+    _mat(x, "x", M, K, 2, True)
+    for t, name, dt, n in ((q, "q", torch.int8, M * K), (a, "a", torch.float32, M * (K // 128)),
+                           (qsum, "qsum", torch.int32, M * (K // 128))):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dt or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name}: a contiguous CUDA {dt} tensor of {n} elements is required")
     _check("wqd_quantize_i8", lib().wqd_quantize_i8(_dptr(x), M, K, x.stride(0), _dptr(q), _dptr(a), _dptr(qsum),
                                                     _stream(stream)))
 
 
 def wqd_dequant_f32(w: Weight, out, stream=None) -> None:
+    import torch
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.float32 or \
+            not out.is_contiguous() or out.numel() != w.N * w.K:
+        raise ValueError(f"out: a contiguous CUDA float32 tensor of {w.N} x {w.K} elements is required")
     _check("wqd_dequant_f32", lib().wqd_dequant_f32(w.ref(), _dptr(out), _stream(stream)))
 
 
@@ -229,9 +277,12 @@ def make_proj_array(projs: Sequence[dict]):
         keep.append(w)
         arr[i].w = ctypes.pointer(w.view)
         arr[i].epi = p.get("epi", WQD_EPI_NONE)
+        _mat(p["x"], f"entry {i} x", None, w.K, 2, True)
         arr[i].x = p["x"].data_ptr()
         arr[i].ldx = p["x"].stride(0)
         y = p.get("y")
+        if y is not None:
+            _mat(y, f"entry {i} y", p["x"].shape[0], w.N, 4, True)
         arr[i].y = None if y is None else y.data_ptr()
         arr[i].ldy = 0 if y is None else y.stride(0)
     arr._keep = keep
