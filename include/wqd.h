@@ -76,6 +76,9 @@ typedef enum {
 } wqd_status;
 
 enum { WQD_MAX_M = 8 };
+/* Rows of one batch-invariant list call (WQD_BATCH_INVARIANT without WQD_INT8_ACTIVATIONS): a
+ * verify of up to 16 draft tokens in one pass over the weights. */
+enum { WQD_MAX_M_VERIFY = 16 };
 /* Largest N and K any call accepts (2^30 each): the kernels keep N, K and their chunk counts in
  * 32-bit fields. */
 enum { WQD_MAX_N = 1 << 30, WQD_MAX_K = 1 << 30 };
@@ -228,10 +231,12 @@ enum {
 /* Flag OR-ed into a mode: batch-invariant results (trapetum "Benchmarks", November update: a
  * draft of M tokens verified in one pass whose rows carry, bit for bit, the logits of M decode
  * steps).  With it, row m of a call with M activation rows is bitwise equal to the same call
- * made with row m alone (M = 1), for every M <= 8, in every mode and whatever else the list
- * holds: every projection is sliced the same way at every M, and every M runs the same per-row
- * instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
- * A verify of 9..16 rows is two calls.  AQ2X8 entries then take the matrix-core kernel at every M
+ * made with row m alone (M = 1), for every M <= WQD_MAX_M_VERIFY (16), in every mode and whatever
+ * else the list holds: every projection is sliced the same way at every M, and every M runs the
+ * same per-row instruction sequence (the matrix-core path with one accumulator chain per 4 rows).
+ * A verify of 9..16 rows reads the weights once (one workgroup per CU); its AQ2X8 entries run as
+ * two launches of rows 0..7 and 8.. (the matrix-core kernel takes 8 rows; those weights are read
+ * twice).  WQD_INT8_ACTIVATIONS lists take at most 8 rows.  AQ2X8 entries take the matrix-core kernel at every M
  * (the M <= 2 lookup-table kernel rounds differently), with pieces planned for every CU whatever
  * the list.  Results differ in rounding (within the bound) from calls without the flag. */
 enum { WQD_BATCH_INVARIANT = 0x10 };

@@ -1,6 +1,6 @@
 """Batch-invariant calls (WQD_BATCH_INVARIANT): row m of an M-row call carries the bits of the same
-call made with row m alone, for M = 2..8, in every mode, with epilogues, and whatever else the
-list holds (trapetum "Benchmarks", November update: a verify pass whose rows equal M decode
+call made with row m alone, for M = 2..16 (9..16 rows in one pass over the weights), in every mode,
+with epilogues, and whatever else the list holds (trapetum "Benchmarks", November update: a verify pass whose rows equal M decode
 steps bit for bit).  Every result is also checked against the oracle's bound."""
 import numpy as np
 import pytest
@@ -49,7 +49,7 @@ def _rows_alone(fmt, N, K, w, xb, mode, epi=W.WQD_EPI_NONE, y0=None):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("M", [2, 3, 5, 8])
+@pytest.mark.parametrize("M", [2, 3, 5, 8, 12, 16])
 @pytest.mark.parametrize("fmt,N,K", SHAPES)
 def test_rows_equal_single_row_calls(fmt, N, K, M):
     note(f"batch-invariant fmt={fmt} N={N} K={K} M={M}")
@@ -66,7 +66,7 @@ def test_rows_equal_single_row_calls(fmt, N, K, M):
     check_parity(got, yref, aref, f"batch-invariant fmt={fmt} N={N} K={K} M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 4, 8, 11, 16])
 def test_modes_and_list_contents_do_not_change_bits(M):
     """A mixed list (CB4 + CB8 + Q4_0 + TQ2) gives the same bits in every mode, and each entry's
     bits equal the entry run alone."""
@@ -90,10 +90,11 @@ def test_modes_and_list_contents_do_not_change_bits(M):
         assert np.array_equal(got.view(np.uint32), y.cpu().numpy().view(np.uint32)), f"fmt={f} N={N} alone"
 
 
+@pytest.mark.parametrize("M", [5, 13])
 @pytest.mark.parametrize("mode", list(MODES))
-def test_epilogues_keep_rows_invariant(mode):
+def test_epilogues_keep_rows_invariant(mode, M):
     import torch
-    fmt, N, K, M = I.CB4, 700, 4096, 5
+    fmt, N, K = I.CB4, 700, 4096
     note(f"batch-invariant epilogues mode={mode}")
     cg = I.gen_weight(fmt, N, K, (62, 0))
     cu = I.gen_weight(fmt, N, K, (62, 1))

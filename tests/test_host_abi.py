@@ -440,3 +440,21 @@ def test_binding_checks_tensors_before_any_call():
         W.make_proj_array([dict(w=w, x=x_host, y=y_host)])
     with pytest.raises(TypeError):
         W.wqd_bind(I.CB4, 64, 64, torch.zeros(4096, dtype=torch.uint8))  # a host buffer
+
+
+def test_verify_rows_limits():
+    """Up to 16 rows in batch-invariant lists (one pass); otherwise at most 8; the AQ2X8 entries of a
+    9..16-row verify run as two launches (rows 0..7, 8..)."""
+    L = W.lib()
+    BI, I8 = W.WQD_BATCH_INVARIANT, W.WQD_INT8_ACTIVATIONS
+    X = FAKE + (1 << 40)
+    arr = _list([(I.CB4, 4096, 4096, E0, X), (I.AQ2X8, 1024, 4096, E0, X)])
+    assert L.wqd_stack_launches(arr, 2, 16, W.WQD_PERSISTENT | BI) == 3   # CB4, AQ2X8 rows 0..7, 8..15
+    assert L.wqd_stack_launches(arr, 2, 8, W.WQD_PERSISTENT | BI) == 2
+    assert L.wqd_stack_launches(arr, 2, 12, W.WQD_ORDERED | BI) == 3
+    assert L.wqd_stack_launches(arr, 2, 9, W.WQD_PERSISTENT) == W.WQD_ESHAPE     # not batch-invariant
+    assert L.wqd_stack_launches(arr, 2, 17, W.WQD_PERSISTENT | BI) == W.WQD_ESHAPE
+    tq = _list([(I.TQ2, 256, 1024, E0, X)])
+    assert L.wqd_stack_launches(tq, 1, 9, W.WQD_PERSISTENT | BI | I8) == W.WQD_ESHAPE  # int8: 8 rows
+    assert L.wqd_stack_workspace_bytes(arr, 2, 16) > L.wqd_stack_workspace_bytes(arr, 2, 8) > 0
+    assert L.wqd_stack_workspace_bytes(arr, 2, 17) == W.WQD_ESHAPE

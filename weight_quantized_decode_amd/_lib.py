@@ -22,6 +22,7 @@ WQD_BATCH_INVARIANT = 0x10
 WQD_INT8_ACTIVATIONS = 0x20
 WQD_EPI_NONE, WQD_EPI_ADD, WQD_EPI_SILU_GATE, WQD_EPI_SILU_UP = 0, 1, 2, 3
 WQD_MAX_M = 8
+WQD_MAX_M_VERIFY = 16
 WQD_MAX_N = 1 << 30
 WQD_MAX_K = 1 << 30
 

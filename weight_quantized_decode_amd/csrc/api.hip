@@ -177,12 +177,12 @@ static GemvFn pick_gemv(int mask, int M, bool epi = false, bool bi = false) {
 }
 
 // The row kernels are compiled for WQD_WG_PER_CU resident workgroups per CU (see gemv_impl.h).
-static int resident_per_cu(GemvFn fn) { return fn ? WQD_WG_PER_CU : 1; }
+static int resident_per_cu(GemvFn fn, int64_t M) { return fn ? (M > kMaxM ? 1 : WQD_WG_PER_CU) : 1; }
 
 // Wave slots resident at once for a kernel instance (the persistent grid's capacity).
 static int64_t resident_waves(int mask, int64_t M, int cus) {
     GemvFn fn = pick_gemv(mask, int(M));
-    return int64_t(cus) * (fn ? resident_per_cu(fn) : 1) * kWaves;
+    return int64_t(cus) * resident_per_cu(fn, M) * kWaves;
 }
 
 // Chunks per wave unit for a launch covering `total_cc` chunk-columns (one 1 KiB wave load
@@ -349,7 +349,7 @@ static int launch_gemv(int mask, int M, const GemvParams &GP, hipStream_t st, in
                        bool bi = false) {
     GemvFn fn = pick_gemv(mask, M, epi, bi);
     if (!fn) return WQD_EINVAL;
-    int64_t grid = int64_t(cus) * resident_per_cu(fn);
+    int64_t grid = int64_t(cus) * resident_per_cu(fn, M);
     if (grid > GP.total_wgu) grid = GP.total_wgu;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(fn, dim3(unsigned(grid)), dim3(kThreads), 0, st, GP);
@@ -545,11 +545,12 @@ static int check_weight(const wqd_weight *w) {
     return WQD_OK;
 }
 
-static int check_proj(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, const float *y, int64_t ldy) {
+static int check_proj(const wqd_weight *w, const void *x, int64_t M, int64_t ldx, const float *y, int64_t ldy,
+                      int64_t mmax = WQD_MAX_M) {
     int rc = check_weight(w);
     if (rc != WQD_OK) return rc;
     if (!x || !y) return WQD_EINVAL;
-    if (M < 1 || M > WQD_MAX_M || ldx < w->K || ldy < w->N) return WQD_ESHAPE;
+    if (M < 1 || M > mmax || ldx < w->K || ldy < w->N) return WQD_ESHAPE;
     if ((reinterpret_cast<uintptr_t>(x) & 3) || (reinterpret_cast<uintptr_t>(y) & 3) || (ldx & 1)) return WQD_EALIGN;
     return WQD_OK;
 }
@@ -593,6 +594,7 @@ struct LaunchGroup {
     bool bi = false;           // batch-invariant instance
     bool lut = false;          // AQ2X8: the lookup-table kernel (else the matrix-core one)
     int64_t nwg = 0;           // AQ2X8: workgroups
+    int am = 0;                // AQ2X8: activation rows of the launch when not all (rows 8.. at M > 8)
     int xq = -1;               // >= 0: the int8 quantizer launch of StackPlan::xqs[xq]
 };
 
@@ -651,9 +653,9 @@ static int to_projs(const wqd_proj *p, int32_t count, std::vector<Proj> &out) {
 // Entries, with the epilogue rules: a WQD_EPI_SILU_GATE entry is followed by its
 // WQD_EPI_SILU_UP entry (same format and N; the pair writes the gate entry's y), and AQ2X8
 // entries take no epilogue.
-static int check_list(const Proj *p, int32_t count, int64_t M) {
+static int check_list(const Proj *p, int32_t count, int64_t M, int64_t mmax) {
     if (!p || count < 1) return WQD_EINVAL;
-    if (M < 1 || M > WQD_MAX_M) return WQD_ESHAPE;
+    if (M < 1 || M > mmax) return WQD_ESHAPE;
     for (int i = 0; i < count; i++) {
         const Proj &q = p[i];
         if (q.epi < WQD_EPI_NONE || q.epi > WQD_EPI_SILU_UP) return WQD_EINVAL;
@@ -666,7 +668,7 @@ static int check_list(const Proj *p, int32_t count, int64_t M) {
             if (i == 0 || p[i - 1].epi != WQD_EPI_SILU_GATE) return WQD_EINVAL;
             out = &p[i - 1];
         }
-        const int rc = check_proj(q.w, q.x, M, q.ldx, out->y, out->ldy);
+        const int rc = check_proj(q.w, q.x, M, q.ldx, out->y, out->ldy, mmax);
         if (rc != WQD_OK) return rc;
     }
     return WQD_OK;
@@ -855,7 +857,25 @@ static void plan_segment(const Proj *p, int b, int e, int64_t M, int mode, bool 
             SP.aqdescs.push_back(make_aq_desc(A, q.w, q.x, q.ldx, q.y, q.ldy, part, cnt, share[k].off, share[k].nw));
         }
         G.count = int(plans.size());
-        SP.groups.push_back(G);
+        if (M > kAqMaxMmaM) {
+            // (a batch-invariant verify of 9..16 rows) the matrix-core kernel takes 8 rows: a
+            // second launch runs rows 8.. of the same entries, with the same pieces, on the same
+            // partials and counters (left at zero by the first)
+            G.am = kAqMaxMmaM;
+            SP.groups.push_back(G);
+            LaunchGroup G2 = G;
+            G2.first = int(SP.aqdescs.size());
+            G2.am = int(M) - kAqMaxMmaM;
+            for (int k = 0; k < G.count; k++) {
+                AqDesc D = SP.aqdescs[size_t(G.first + k)];
+                D.x = D.x ? D.x + kAqMaxMmaM * D.ldx : nullptr;
+                D.y = D.y ? D.y + kAqMaxMmaM * D.ldy : nullptr;
+                SP.aqdescs.push_back(D);
+            }
+            SP.groups.push_back(G2);
+        } else {
+            SP.groups.push_back(G);
+        }
     }
 }
 
@@ -869,13 +889,15 @@ static int build_stack_plan(const wqd_proj *pub, int32_t count, int64_t M, int m
     const bool i8 = (mode_flags & WQD_INT8_ACTIVATIONS) != 0;
     const int mode = mode_flags & ~(WQD_BATCH_INVARIANT | WQD_INT8_ACTIVATIONS);
     if (mode != WQD_ORDERED && mode != WQD_PERSISTENT && mode != WQD_FUSED) return WQD_EINVAL;
-    rc = check_list(p, count, M);
+    // a batch-invariant list verifies up to WQD_MAX_M_VERIFY rows in one pass (fp16 activations)
+    rc = check_list(p, count, M, bi && !i8 ? WQD_MAX_M_VERIFY : WQD_MAX_M);
     if (rc != WQD_OK) return rc;
 
     SP.off_stamp = 0;
     SP.off_descs = 256;
     SP.off_aqdescs = align_up(SP.off_descs + int64_t(sizeof(Desc)) * count, 256);
-    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count, 256);
+    // (an AQ2X8 entry of a verify of more than 8 rows has two descriptors, one per launch)
+    SP.off_ctr = align_up(SP.off_aqdescs + int64_t(sizeof(AqDesc)) * count * (M > kAqMaxMmaM ? 2 : 1), 256);
     SP.off_cnt = SP.off_ctr + 256;
     int64_t cnt_all = 0;
     for (int i = 0; i < count; i++) {
@@ -1202,6 +1224,15 @@ WQD_API int wqd_dequant_f32(const wqd_weight *w, float *out, void *stream) {
 WQD_API int64_t wqd_stack_workspace_bytes(const wqd_proj *projs, int32_t count, int64_t M) {
     // enough for every mode
     int64_t need = 0;
+    if (M > WQD_MAX_M) {  // batch-invariant lists only
+        for (int mode : {WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED}) {
+            StackPlan SB;
+            const int rc = build_stack_plan(projs, count, M, mode | WQD_BATCH_INVARIANT, nullptr, SB, device_cus());
+            if (rc != WQD_OK) return rc;
+            if (SB.total() > need) need = SB.total();
+        }
+        return need;
+    }
     for (int mode : {WQD_ORDERED, WQD_PERSISTENT, WQD_FUSED}) {
         StackPlan SP;
         int rc = build_stack_plan(projs, count, M, mode, nullptr, SP, device_cus());
@@ -1298,7 +1329,7 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             AP.stale = stale;
             if (!table && G.count != 1) return WQD_EINVAL;  // (segments hold one AQ2X8 entry)
             if ((rc = mark(0)) != WQD_OK) return rc;
-            rc = launch_aq(M, G.lut, aq_rec(&SP.aqdescs[G.first], G.count, G.lut), AP, st);
+            rc = launch_aq(G.am ? G.am : M, G.lut, aq_rec(&SP.aqdescs[G.first], G.count, G.lut), AP, st);
             if (rc != WQD_OK) return rc;
             if ((rc = mark(1)) != WQD_OK) return rc;
             li++;

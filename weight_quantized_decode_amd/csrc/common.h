@@ -162,6 +162,7 @@ constexpr int kAqLutRW = 4;         // row blocks per wave per slice, lookup-tab
 constexpr int kAqLut2RW = WQD_AQ_LUT2_RW;  // the same at M = 2 (two rows' accumulators)
 constexpr int kAqMmaRW = 2;         // row blocks per wave per slice, matrix-core kernel
 constexpr int kAqCntStride = 32;    // ints between the arrival counters of two row chunks
+constexpr int kAqMaxMmaM = 8;       // activation rows of one matrix-core launch
 constexpr int kAqLutRecs = 64;      // most pieces per workgroup kept as LDS records, lookup-table kernel
 constexpr int kAqMmaRecs = 40;      // the same, matrix-core kernel (its LDS holds the codebook copies)
 #ifndef WQD_AQ_BUILD_CHARGE

@@ -908,8 +908,9 @@ __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, De
 }
 
 // Every instance is compiled for WQD_WG_PER_CU (2) resident 8-wave workgroups per CU, i.e. 4
-// waves per SIMD and at most 128 VGPRs; the launch sizes its persistent grid from the same
-// constant (the runtime occupancy query under-reports kernels without AGPRs).
+// waves per SIMD and at most 128 VGPRs, except the 9..16-row batch-invariant ones (one workgroup
+// per CU, 256 VGPRs); the launch sizes its persistent grid from the same constants (the runtime
+// occupancy query under-reports kernels without AGPRs).
 constexpr int kMinWavesPerEU = WQD_WG_PER_CU * kWaves / 4;
 
 // Persistent kernel over a list of projections whose formats are in MASK.  Workgroup units
@@ -919,7 +920,7 @@ constexpr int kMinWavesPerEU = WQD_WG_PER_CU * kWaves / 4;
 // applies the descriptors' epilogues (lists without any use the instance without that code).
 // BI: the batch-invariant instance (every M on the matrix cores, one chain per quad).
 template <int MASK, int M, bool EPI, bool BI = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU))) void gemv_kernel(GemvParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M > kMaxM ? kThreads / 256 : kMinWavesPerEU))) void gemv_kernel(GemvParams P) {
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
     __shared__ float red[kWaves * (M < 4 ? M : 4) * 64];  // workgroup-split sums
     __shared__ int next_u;
@@ -974,10 +975,31 @@ GemvFn gemv_fn_var(int M) {
     }
     return nullptr;
 }
-// The batch-invariant instances always carry the epilogue code (one set of them per format).
+// Batch-invariant instances for a verify of 9..16 rows in one pass (one workgroup per CU: the
+// four activation quads need up to 256 registers).
 template <int MASK>
+GemvFn gemv_fn_bi_wide(int M) {
+    switch (M) {
+    case 9: return gemv_kernel<MASK, 9, true, true>;
+    case 10: return gemv_kernel<MASK, 10, true, true>;
+    case 11: return gemv_kernel<MASK, 11, true, true>;
+    case 12: return gemv_kernel<MASK, 12, true, true>;
+    case 13: return gemv_kernel<MASK, 13, true, true>;
+    case 14: return gemv_kernel<MASK, 14, true, true>;
+    case 15: return gemv_kernel<MASK, 15, true, true>;
+    case 16: return gemv_kernel<MASK, 16, true, true>;
+    }
+    return nullptr;
+}
+// The batch-invariant instances always carry the epilogue code (one set of them per format).
+// WIDE: with the 9..16-row batch-invariant instances.
+template <int MASK, bool WIDE = true>
 GemvFn gemv_fn(int M, bool epi, bool bi) {
-    if (bi) return gemv_fn_var<MASK, true, true>(M);
+    if (bi) {
+        if (M <= kMaxM) return gemv_fn_var<MASK, true, true>(M);
+        if constexpr (WIDE) return gemv_fn_bi_wide<MASK>(M);
+        return nullptr;
+    }
     return epi ? gemv_fn_var<MASK, true, false>(M) : gemv_fn_var<MASK, false, false>(M);
 }
 

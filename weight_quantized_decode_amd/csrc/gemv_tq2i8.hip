@@ -3,5 +3,5 @@
 #include "gemv_impl.h"
 
 namespace wqd {
-GemvFn gemv_fn_tq2i8(int M, bool epi, bool bi) { return gemv_fn<fmt_bit(TQ2I8)>(M, epi, bi); }
+GemvFn gemv_fn_tq2i8(int M, bool epi, bool bi) { return gemv_fn<fmt_bit(TQ2I8), false>(M, epi, bi); }
 }  // namespace wqd
