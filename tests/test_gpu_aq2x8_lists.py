@@ -4,8 +4,8 @@ A workgroup's pieces are kept as LDS records when their number is small (the 70B
 of each projection per workgroup); a longer list takes the form that walks the descriptors.  Both
 must give the oracle's results: here 70 projections in one persistent launch, so every workgroup
 serves at least 70 pieces (more than either kernel's records), half of them split along K (so the
-split sums walk the list as well, in rounds of 64 pieces), at M = 1 (lookup-table kernel) and
-M = 2 (matrix-core kernel), and the same list in ordered mode.
+split sums walk the list as well, in rounds of 64 pieces), at M = 1 and 2 (the lookup-table
+kernels) and M = 3 (the matrix-core kernel), and the same list in ordered mode.
 """
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(128, 8192), (100, 1000)] * 35  # split along K / ragged N and K, not split
 
 
-@pytest.mark.parametrize("M,mode", [(1, W.WQD_PERSISTENT), (2, W.WQD_PERSISTENT), (1, W.WQD_ORDERED)])
+@pytest.mark.parametrize("M,mode", [(1, W.WQD_PERSISTENT), (2, W.WQD_PERSISTENT), (3, W.WQD_PERSISTENT),
+                                    (1, W.WQD_ORDERED)])
 def test_long_aq2x8_list(M, mode):
     note(f"aq2x8 list of {len(SHAPES)} M={M} mode={mode}")
     xs = {K: I.gen_x(M, K, (71, K)) for K in {k for _, k in SHAPES}}

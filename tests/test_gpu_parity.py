@@ -108,14 +108,15 @@ def test_gemm_deterministic(fmt):
 
 
 @pytest.mark.parametrize("fmt", [I.Q4_0, I.CB4, I.CB8, I.TQ2, I.AQ2X8, I.AQ1X16])
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3])
 def test_gemm_one_hot_and_zero_activations(fmt, M):
     # One-hot x returns a column of the dequantized matrix.  The weights of Q4_0, CB4, CB8, TQ2 and
     # AQ1X16 are exact in fp32, so the column is exact.  An AQ2x8 weight is s * (C0 + C1): the
     # kernels form C0 + C1 in fp32 (the one nonzero lookup-table term or product of each codebook,
     # added once) and scale it once, which is exactly the debug dequant's fp32(fp32(C0 + C1) * s):
     # equal bits, and within two fp32 roundings of the exact weight.  Zero x returns zero.
-    # (M = 1 takes the lookup-table kernel, M = 2 the matrix-core one; row 1 is zero.)
+    # (AQ2x8: M = 1 and 2 take the lookup-table kernels, M = 3 the matrix-core one; rows past 0
+    # are zero.)
     N, K = 128, 512
     note(f"gemm one-hot fmt={fmt} M={M}")
     canon = I.gen_weight(fmt, N, K, (17, fmt))
