@@ -1341,7 +1341,10 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
             GP.descs = dtab + G.first;
         } else {
             if (G.count > kInlineDescs) return WQD_EINVAL;  // (segments are cut to fit)
-            for (int k = 0; k < G.count; k++) GP.d[k] = SP.descs[G.first + k];
+            for (int k = 0; k < G.count; k++) {
+                GP.d[k] = SP.descs[G.first + k];
+                GP.wgu_begin[k] = GP.d[k].wgu_begin;
+            }
             GP.descs = nullptr;
         }
         GP.ndesc = G.count;

@@ -121,6 +121,9 @@ struct GemvParams {
     const Desc *descs;   // device array (stack)
     int32_t ndesc;
     int32_t total_wgu;
+    // first workgroup unit of each inline descriptor (d[i].wgu_begin, here too so that a
+    // workgroup finds its descriptor without a load that depends on another)
+    int32_t wgu_begin[kInlineDescs];
     // Dynamic tail: workgroup units [pool_begin, total_wgu) are taken one at a time from the
     // counter ctr[0] (ctr[1] counts finished workgroups; the last one resets both to 0).
     // ctr == nullptr: static assignment of every unit.

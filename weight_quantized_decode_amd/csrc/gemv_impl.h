@@ -862,9 +862,14 @@ template <int MASK, int M, bool EPI, bool BI>
 __device__ __forceinline__ void run_wgu(const GemvParams &P, int u, int &cur, Desc &D, uint32_t *lds, float *red, int wid,
                                         int lane) {
     // Units are visited in increasing order: search only for the first one, then step forward.
+    // Inline descriptors: their first units are in the kernel arguments beside them.
     const Desc *tab = desc_table(P);
     int p;
-    if (cur < 0) {
+    if (!P.descs) {
+        p = 0;
+#pragma unroll
+        for (int i = 1; i < kInlineDescs; i++) p += (i < P.ndesc && P.wgu_begin[i] <= u) ? 1 : 0;
+    } else if (cur < 0) {
         p = find_proj(tab, P.ndesc, u);
     } else {
         p = cur;
@@ -924,7 +929,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M > kM
     __shared__ uint32_t lds[LdsSizeMask<MASK>::dwords];
     __shared__ float red[kWaves * (M < 4 ? M : 4) * 64];  // workgroup-split sums
     __shared__ int next_u;
-    if (stale_table(P.stamp, P.fp, P.stale)) return;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int total = P.total_wgu;
@@ -936,6 +940,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(M > kM
     const int b = blockIdx.x;
     const int u0 = b * per + min(b, rem);
     const int u1 = u0 + per + (b < rem ? 1 : 0);
+    // (after the arithmetic on the arguments, so that their loads go out with the stamp's
+    // pointer in one round trip: a launch without a table has no stamp to wait for)
+    if (stale_table(P.stamp, P.fp, P.stale)) return;
     int cur = -1;
     Desc D;
     for (int u = u0; u < u1; u++) run_wgu<MASK, M, EPI, BI>(P, u, cur, D, lds, red, wid, lane);
