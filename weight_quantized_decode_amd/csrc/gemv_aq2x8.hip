@@ -414,6 +414,7 @@ __device__ __forceinline__ void add_splits_n(const PieceRec &r) {
     const int r0 = 16 * r.rb0, nrows = min(16 * r.rb1, r.N) - r0;
     float v[NI][NL];
     int rowv[NI], mv[NI];
+    uint32_t scb[NI];  // the row scales, loaded with the partials (not after the sums)
     bool live[NI];
 #pragma unroll
     for (int it = 0; it < NI; it++) {
@@ -422,6 +423,7 @@ __device__ __forceinline__ void add_splits_n(const PieceRec &r) {
         live[it] = m < M && rr < nrows;
         rowv[it] = live[it] ? r0 + rr : 0;
         mv[it] = live[it] ? m : 0;
+        scb[it] = gld<uint16_t>(r.rscale + rowv[it]);
 #pragma unroll
         for (int j = 0; j < NL; j++)
             v[it][j] = __hip_atomic_load(as_global(r.part + (int64_t(mv[it]) * r.b + min(j, r.b - 1)) * r.Npad + rowv[it]),
@@ -433,10 +435,7 @@ __device__ __forceinline__ void add_splits_n(const PieceRec &r) {
 #pragma unroll
         for (int j = 0; j < NL; j++)
             if (j < r.b) sum += v[it][j];
-        if (live[it]) {
-            const float sc = half_bits_to_float(gld<uint16_t>(r.rscale + rowv[it]));
-            gst(r.y + int64_t(mv[it]) * r.ldy + rowv[it], sum * sc);
-        }
+        if (live[it]) gst(r.y + int64_t(mv[it]) * r.ldy + rowv[it], sum * half_bits_to_float(scb[it]));
     }
     if (threadIdx.x == 0) __hip_atomic_store(as_global(r.cnt), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -461,7 +460,7 @@ __device__ __forceinline__ void add_splits_g(const PieceRec *recs, const int *fl
     for (int base = 0; base < total; base += G * W * 64) {
         float v[G][NL];
         float *yp[G];
-        const uint16_t *sp[G];
+        uint32_t scb[G];  // the row scales, loaded with the partials (not after the sums)
         int bb[G];
         bool live[G];
 #pragma unroll
@@ -474,12 +473,12 @@ __device__ __forceinline__ void add_splits_g(const PieceRec *recs, const int *fl
             live[g] = item < total && rr < nrows;
             const int row = r0 + (live[g] ? rr : 0), mm = live[g] ? m : 0;
             const float *part = rp->part + int64_t(mm) * b * rp->Npad + row;
+            scb[g] = gld<uint16_t>(rp->rscale + row);
 #pragma unroll
             for (int j = 0; j < NL; j++)  // (unconditional: indices past b - 1 repeat the last split)
                 v[g][j] = __hip_atomic_load(as_global(part + int64_t(min(j, b - 1)) * rp->Npad), __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
             yp[g] = rp->y + int64_t(mm) * rp->ldy + row;
-            sp[g] = rp->rscale + row;
             bb[g] = b;
         }
 #pragma unroll
@@ -489,7 +488,7 @@ __device__ __forceinline__ void add_splits_g(const PieceRec *recs, const int *fl
 #pragma unroll
             for (int j = 0; j < NL; j++)
                 if (j < bb[g]) sum += v[g][j];
-            gst(yp[g], sum * half_bits_to_float(gld<uint16_t>(sp[g])));
+            gst(yp[g], sum * half_bits_to_float(scb[g]));
         }
     }
     if (int(threadIdx.x) < nc) __hip_atomic_store(as_global(recs[fl[threadIdx.x]].cnt), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
