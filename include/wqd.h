@@ -2,10 +2,11 @@
  *
  * The library computes the projection of batch-1 and small-batch LLM decode,
  *
- *     y[m][n] = sum_k x[m][k] * dequant(Wq)[n][k]       (0 <= m < M <= 8, 0 <= n < N, 0 <= k < K)
+ *     y[m][n] = sum_k x[m][k] * dequant(Wq)[n][k]       (0 <= m < M, 0 <= n < N, 0 <= k < K)
  *
- * with packed low-bit weights streamed from HBM once, decoded in registers and multiplied by a
- * short fp16 activation row, accumulating in fp32.  The operation and the formats are those of:
+ * with M <= 8 activation rows per call (16 in a batch-invariant list, WQD_MAX_M_VERIFY), packed
+ * low-bit weights streamed from HBM once, decoded in registers and multiplied by a short fp16
+ * activation row, accumulating in fp32.  The operation and the formats are those of:
  *   - trapetum "Benchmarks" (trapetum.neuralboot.com), "Kernel microbenchmarks" (4-bit and 8-bit
  *     codebook GEMV), "Additive vector-quantization GEMV (AQLM-style, 2-bit)", and the November
  *     update's fused, graphed decode step;
@@ -17,7 +18,7 @@
  * Conventions
  *   - Every pointer is a device pointer unless its name ends in _host.  The caller owns every
  *     buffer; the library allocates no device memory and never synchronizes the stream except in
- *     wqd_stack_setup and wqd_stream_check.
+ *     wqd_stream_check.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Kernels are enqueued
  *     on it asynchronously; calls are stream-ordered and reentrant.
  *   - Functions return a wqd_status.  Argument errors are detected before any HIP call.  A launch

@@ -211,7 +211,8 @@ AqFn aq_fn(int M, bool lut, bool rec);
 
 // Kernel instances for M = 1..8 of one format, or of the CB4+CB8 pair (the layer stack with its
 // 8-bit head), each defined in its own translation unit; `epi` selects the instance that applies
-// epilogues (residual add, SiLU pair), `bi` the batch-invariant one (single formats only).
+// epilogues (residual add, SiLU pair), `bi` the batch-invariant one (single formats only; these
+// also exist for M = 9..16, a verify of up to 16 rows in one pass).
 GemvFn gemv_fn_q4_0(int M, bool epi, bool bi);
 GemvFn gemv_fn_cb4(int M, bool epi, bool bi);
 GemvFn gemv_fn_cb8(int M, bool epi, bool bi);

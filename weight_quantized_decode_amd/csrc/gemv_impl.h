@@ -1,6 +1,7 @@
 // HIP kernels (gfx950) and the C entry points of libwqd that launch them.
 //
-// Design (one projection y = x W^T, M <= 8 activation rows):
+// Design (one projection y = x W^T, M <= 8 activation rows per call, up to 16 in a batch-invariant
+// verify):
 //   * One wavefront lane per weight row: a wave covers a group of 64 rows, and every load
 //     instruction reads chunk c of those 64 rows, 1 KiB of contiguous prepared code bytes
 //     (layout.h).  Each row's dot product stays inside its lane, so no cross-lane reduction.
