@@ -245,9 +245,11 @@ enum { WQD_BATCH_INVARIANT = 0x10 };
 /* Flag OR-ed into a mode: the TQ2 entries of the list multiply int8-quantized activations, as
  * wqd_gemm_i8 does ("Making a ternary reasoning model fast in vLLM": "Why small integers are a
  * good fit", and "prepare each input once" of its checklist).  Each distinct activation (x, ldx,
- * K) of the list's TQ2 entries is quantized once per call, by a launch placed before the first
- * launch that reads it (after the launches before it, which may have written x); entries that
- * share x share its int8 copy.  Other formats are unaffected. */
+ * K) of the list's TQ2 entries is quantized once per call, before the first launch that reads it
+ * (after the launches before it, which may have written x): the activations a segment of the list
+ * is the first to read are quantized together by one launch placed before the segment's launches
+ * (in WQD_PERSISTENT mode, one quantizer launch for the whole list; up to 8 activations per
+ * launch).  Entries that share x share its int8 copy.  Other formats are unaffected. */
 enum { WQD_INT8_ACTIVATIONS = 0x20 };
 
 /* Device workspace bytes for wqd_run_projections over this list in any mode (descriptor
@@ -279,9 +281,9 @@ WQD_API int wqd_run_projections(const wqd_proj *projs_host, int32_t count, int64
 
 /* Profiling variant: the same work as wqd_run_projections, with hipEvent_t events[2i] recorded
  * on the stream just before the i-th kernel launch of the call and events[2i+1] just after it.
- * Launch order in WQD_PERSISTENT mode: the int8 quantizers (WQD_INT8_ACTIVATIONS), the CB4+CB8
+ * Launch order in WQD_PERSISTENT mode: the int8 quantizer (WQD_INT8_ACTIVATIONS), the CB4+CB8
  * launch if both formats are present, then one launch per remaining format (ascending format
- * id); in the other modes, list order (a segment's quantizers first).
+ * id); in the other modes, list order (a segment's quantizer first).
  * n_events must be 2 * wqd_stack_launches(); the events are created and owned by the caller. */
 WQD_API int wqd_run_projections_timed(const wqd_proj *projs_host, int32_t count, int64_t M,
                                       int32_t mode, void *workspace, int64_t workspace_bytes,

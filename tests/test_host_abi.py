@@ -373,10 +373,12 @@ def test_int8_list_launch_counts():
     X = [FAKE + (1 << 40) + (j << 20) for j in range(3)]
     mlp = _fake_list([(I.TQ2, 17408, 5120, E0, X[0]), (I.TQ2, 17408, 5120, E0, X[0]),
                       (I.TQ2, 5120, 17408, E0, X[1])])
-    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_PERSISTENT | I8) == 3  # 2 quantizers + 1 product
+    assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_PERSISTENT | I8) == 2  # 1 quantizer (both x) + 1 product
     assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_FUSED | I8) == 4       # q(x0) [gate, up] q(x1) [down]
     assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_ORDERED | I8) == 5
     assert L.wqd_stack_launches(mlp, 3, 1, W.WQD_PERSISTENT) == 1
+    nine = _fake_list([(I.TQ2, 256, 1024, E0, FAKE + (1 << 40) + (j << 20)) for j in range(9)])
+    assert L.wqd_stack_launches(nine, 9, 1, W.WQD_PERSISTENT | I8) == 3  # 8 + 1 activations, then the product
     cb = _fake_list([(I.CB4, 64, 64, E0, X[2])])
     assert L.wqd_stack_launches(cb, 1, 1, W.WQD_PERSISTENT | I8) == 1    # no TQ2 entry: no quantizer
     assert L.wqd_stack_workspace_bytes(mlp, 3, 1) > 0

@@ -102,12 +102,9 @@ __global__ __launch_bounds__(256) void dequant_aq2x8_kernel(const uint8_t *w, co
 // the field order of the TQ2 chunk words (layout.h): within each 16-weight word, dword j holds the
 // activations of weights 2j, 2j+8, 2j+1, 2j+9.  Also writes a and the block's sum of q.
 template <bool PERM>
-__global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t *x, int64_t ldx, int M, int nb, int8_t *q,
-                                                          int64_t ldq, float *a, int32_t *qs) {
-    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wv >= M * nb) return;
+__device__ __forceinline__ void quantize_block(const uint16_t *x, int64_t ldx, int m, int b, int nb, int8_t *q,
+                                               int64_t ldq, float *a, int32_t *qs) {
     const int lane = threadIdx.x & 63;
-    const int m = wv / nb, b = wv - m * nb;
     const uint32_t pair = *reinterpret_cast<const uint32_t *>(x + (int64_t)m * ldx + (int64_t)b * 128 + 2 * lane);
     const float x0 = half_bits_to_float(pair & 0xFFFFu), x1 = half_bits_to_float(pair >> 16);
     float amax = fmaxf(fabsf(x0), fabsf(x1));
@@ -136,6 +133,47 @@ __global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t *x, int
         a[(int64_t)m * nb + b] = sc;
         qs[(int64_t)m * nb + b] = sum;
     }
+}
+
+template <bool PERM>
+__global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t *x, int64_t ldx, int M, int nb, int8_t *q,
+                                                          int64_t ldq, float *a, int32_t *qs) {
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= M * nb) return;
+    const int m = wv / nb, b = wv - m * nb;
+    quantize_block<PERM>(x, ldx, m, b, nb, q, ldq, a, qs);
+}
+
+// Several activations quantized by one launch (the int8 activations a list segment is the first
+// to read): job j takes waves [wave0, wave0 + M * nb) of the grid.
+constexpr int kMaxQuantJobs = 8;
+struct QuantJob {
+    const uint16_t *x;
+    int64_t ldx;
+    int8_t *q;
+    int64_t ldq;
+    float *a;
+    int32_t *qs;
+    int32_t M, nb, wave0, pad_;
+};
+struct QuantJobs {
+    QuantJob j[kMaxQuantJobs];
+    int32_t n, waves;
+};
+__global__ __launch_bounds__(256) void quantize_i8_jobs_kernel(QuantJobs J) {
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= J.waves) return;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxQuantJobs; i++) k += (i < J.n && J.j[i].wave0 <= wv) ? 1 : 0;
+    // (the job's fields by a switch on k: indexing the argument array with a variable would copy
+    // it to scratch memory)
+    QuantJob jb = J.j[0];
+#pragma unroll
+    for (int i = 1; i < kMaxQuantJobs; i++)
+        if (k == i) jb = J.j[i];
+    const int local = wv - jb.wave0, m = local / jb.nb, b = local - m * jb.nb;
+    quantize_block<true>(jb.x, jb.ldx, m, b, jb.nb, jb.q, jb.ldq, jb.a, jb.qs);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -595,7 +633,8 @@ struct LaunchGroup {
     bool lut = false;          // AQ2X8: the lookup-table kernel (else the matrix-core one)
     int64_t nwg = 0;           // AQ2X8: workgroups
     int am = 0;                // AQ2X8: activation rows of the launch when not all (rows 8.. at M > 8)
-    int xq = -1;               // >= 0: the int8 quantizer launch of StackPlan::xqs[xq]
+    int xq = -1;               // >= 0: one int8 quantizer launch for StackPlan::xq_order[xq, xq + nxq)
+    int nxq = 0;
 };
 
 // An activation quantized to int8 for the TQ2 entries of a list (WQD_INT8_ACTIVATIONS): q, the
@@ -612,6 +651,7 @@ struct StackPlan {
     std::vector<AqDesc> aqdescs;
     std::vector<LaunchGroup> groups;
     std::vector<XQ> xqs;
+    std::vector<int> xq_order;  // indices into xqs, in the order their quantizer launches take them
     int64_t off_stamp = 0;     // the table's stamp: fingerprint of the list setup wrote it for
     int64_t off_descs = 0, off_aqdescs = 0, off_ctr = 0, off_cnt = 0, cnt_bytes = 0, off_xq = 0, off_part = 0;
     int64_t part_bytes = 0;    // partial bytes this mode uses
@@ -713,15 +753,21 @@ static void plan_segment(const Proj *p, int b, int e, int64_t M, int mode, bool 
     // kernel format of entry i: TQ2 entries of an int8 list run the int8 product
     auto kfmt = [&](int i) { return (i8 && p[i].fmt == TQ2) ? TQ2I8 : p[i].fmt; };
     // quantize the activations this segment is the first to use (after the launches before it,
-    // which may have produced them)
+    // which may have produced them), all in one launch (up to kMaxQuantJobs per launch)
     for (int i = b; i < e; i++) {
         if (kfmt(i) != TQ2I8) continue;
-        XQ &xq = SP.xqs[xq_of(SP, p[i])];
+        const int k = xq_of(SP, p[i]);
+        XQ &xq = SP.xqs[k];
         if (xq.issued) continue;
         xq.issued = true;
-        LaunchGroup Q;
-        Q.xq = xq_of(SP, p[i]);
-        SP.groups.push_back(Q);
+        if (SP.groups.empty() || SP.groups.back().xq < 0 || SP.groups.back().nxq == kMaxQuantJobs ||
+            SP.groups.back().xq + SP.groups.back().nxq != int(SP.xq_order.size())) {
+            LaunchGroup Q;
+            Q.xq = int(SP.xq_order.size());
+            SP.groups.push_back(Q);
+        }
+        SP.xq_order.push_back(k);
+        SP.groups.back().nxq++;
     }
     int present = 0;
     for (int i = b; i < e; i++) present |= fmt_bit(kfmt(i));
@@ -1304,13 +1350,25 @@ static int run_projections_impl(const wqd_proj *projs, int32_t count, int64_t M,
     for (size_t gi = 0; gi < SP.groups.size(); gi++) {
         const LaunchGroup &G = SP.groups[gi];
         if (G.xq >= 0) {
-            const XQ &xq = SP.xqs[G.xq];
-            const int nb = int(xq.K / 128);
+            QuantJobs J;
+            memset(&J, 0, sizeof(J));
+            for (int t = 0; t < G.nxq; t++) {
+                const XQ &xq = SP.xqs[SP.xq_order[size_t(G.xq + t)]];
+                QuantJob &jb = J.j[t];
+                jb.x = static_cast<const uint16_t *>(xq.x);
+                jb.ldx = xq.ldx;
+                jb.q = reinterpret_cast<int8_t *>(base + xq.off_q);
+                jb.ldq = xq.K;
+                jb.a = reinterpret_cast<float *>(base + xq.off_a);
+                jb.qs = reinterpret_cast<int32_t *>(base + xq.off_s);
+                jb.M = int32_t(M);
+                jb.nb = int32_t(xq.K / 128);
+                jb.wave0 = J.waves;
+                J.waves += jb.M * jb.nb;
+            }
+            J.n = G.nxq;
             if ((rc = mark(0)) != WQD_OK) return rc;
-            hipLaunchKernelGGL(quantize_i8_kernel<true>, dim3(unsigned((M * nb + 3) / 4)), dim3(256), 0, st,
-                               static_cast<const uint16_t *>(xq.x), xq.ldx, int(M), nb,
-                               reinterpret_cast<int8_t *>(base + xq.off_q), xq.K,
-                               reinterpret_cast<float *>(base + xq.off_a), reinterpret_cast<int32_t *>(base + xq.off_s));
+            hipLaunchKernelGGL(quantize_i8_jobs_kernel, dim3(unsigned((J.waves + 3) / 4)), dim3(256), 0, st, J);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return hip_fail(e);
             if ((rc = mark(1)) != WQD_OK) return rc;
