@@ -427,24 +427,33 @@ static AqPlan plan_aq(int64_t N, int64_t K, int64_t M, int64_t nw, bool lut) {
     const int64_t setup = lut ? WQD_AQ_BUILD_CHARGE : 2;  // table build / activation staging
     if (nw < 1) nw = 1;
     double best = 1e300;
+    // The matrix-core kernel's waves take the row blocks of a slice in turn and meet at a barrier
+    // after each slice, so a slice costs its busiest wave: nrb rounded up to whole passes of the
+    // kAqWaves waves.  It also tries row chunks of exactly one or two such passes.
+    const int64_t gran = lut ? 1 : kAqWaves;
     for (int64_t b = 1; b <= KS && b <= bmax; b++) {
         const int64_t ns = (KS + b - 1) / b;
         if ((KS + ns - 1) / ns != b) continue;  // same split as a smaller b
-        int64_t a = nw / b;
-        if (a < (RB + per - 1) / per) a = (RB + per - 1) / per;
-        if (a > RB) a = RB;
-        if (a < 1) a = 1;
-        const int64_t nrb = (RB + a - 1) / a;
-        a = (RB + nrb - 1) / nrb;
-        if (b > 1 && a * kAqCntStride * 4 > kCntRegion) continue;  // the counters fit their region
-        const int64_t rounds = (a * b + nw - 1) / nw;
-        const double cost = double(rounds) * double(ns * (nrb + setup) + (b > 1 ? WQD_AQ_SPLIT_CHARGE : 0));
-        if (cost < best) {
-            best = cost;
-            A.a = a;
-            A.b = b;
-            A.nrb = nrb;
-            A.ns = ns;
+        const int64_t cand[3] = {nw / b, (RB + kAqWaves - 1) / kAqWaves, (RB + 2 * kAqWaves - 1) / (2 * kAqWaves)};
+        for (int ci = 0; ci < (lut ? 1 : 3); ci++) {
+            int64_t a = cand[ci];
+            if (a < (RB + per - 1) / per) a = (RB + per - 1) / per;
+            if (a > RB) a = RB;
+            if (a < 1) a = 1;
+            const int64_t nrb = (RB + a - 1) / a;
+            a = (RB + nrb - 1) / nrb;
+            if (b > 1 && a * kAqCntStride * 4 > kCntRegion) continue;  // the counters fit their region
+            const int64_t rounds = (a * b + nw - 1) / nw;
+            const int64_t nrb_cost = (nrb + gran - 1) / gran * gran;
+            const double cost =
+                double(rounds) * double(ns * (nrb_cost + setup) + (b > 1 ? WQD_AQ_SPLIT_CHARGE : 0));
+            if (cost < best) {
+                best = cost;
+                A.a = a;
+                A.b = b;
+                A.nrb = nrb;
+                A.ns = ns;
+            }
         }
     }
     A.RB = RB;

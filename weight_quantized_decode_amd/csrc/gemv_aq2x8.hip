@@ -35,6 +35,10 @@
 //   * A tile goes through the wave's LDS staging area, from which each lane reads the 8 code pairs
 //     it needs (row n, groups 4t + q), 2 bytes each.  The activations of a slice are staged in
 //     LDS (double-buffered, one barrier per slice).
+//   * A wave's one or two tiles of a slice share each step: the lookups of step t + 1 (both
+//     tiles, both codebooks) are issued before the products of step t.  A slice lasts as long as
+//     its busiest wave, so the planner charges a piece whole passes of the 16 waves over its row
+//     blocks (api.hip, plan_aq).
 //
 // Work (AqDesc): a workgroup walks its pieces in order, slice by slice; the tile loads of the next
 // two slices are in flight while a slice is processed.  When a workgroup serves few pieces (the
@@ -912,22 +916,47 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     uint8_t *stage = lds + L::off_stage + wid * kStageBytes;
     const uint8_t *code_src = stage + (n >> 3) * 544 + q4 * 16 + 2 * (n & 7);
     const uint32_t lkc = (1u << 16) | (uint32_t(n) << 4);
-    // One tile into accumulators D: transpose the codes through the staging area, then 8 steps of
-    // 4 groups, each two products (codebook 0, codebook 1).
-    auto mma_tile = [&](const u32x4 &v, const u32x4 (&A)[8], f32x4 (&D)[2]) __attribute__((always_inline)) {
-        *reinterpret_cast<u32x4 *>(stage + th * 544 + tg * 16) = v;
-        uint32_t cp[8];
+    // The wave's tiles of one slice into accumulators D[i]: each tile's codes transposed through
+    // the staging area (lane 16q + n: the code pairs of row n, groups 4t + q), then 8 steps of 4
+    // groups, each two products per tile (codebook 0, codebook 1).  The tiles' lookups and
+    // products alternate within a step; every accumulator still takes its products in the order
+    // t = 0..7, codebook 0 before 1.
+    // (NT: the wave's first NT tiles of the slice, all in the piece; no branch inside)
+    auto mma_tiles = [&](auto nt, const u32x4 (&v)[RW], const uint8_t *xs, f32x4 (&D)[RW][2])
+                         __attribute__((always_inline)) {
+        constexpr int NT = decltype(nt)::value;
+        uint32_t cp[NT][8];
 #pragma unroll
-        for (int t = 0; t < 8; t++) cp[t] = *reinterpret_cast<const uint16_t *>(code_src + t * 64);
+        for (int i = 0; i < NT; i++) {  // (the staging area is reused: the reads of tile i come first)
+            *reinterpret_cast<u32x4 *>(stage + th * 544 + tg * 16) = v[i];
+#pragma unroll
+            for (int t = 0; t < 8; t++) cp[i][t] = *reinterpret_cast<const uint16_t *>(code_src + t * 64);
+        }
+        // step t's lookups are issued before step t-1's products (two register sets), so each
+        // product waits for lookups issued one step earlier
+        u32x4 Bg[2][NT][2], Ax[2];
+        auto lookups = [&](int t, u32x4 (&B)[NT][2], u32x4 &A) __attribute__((always_inline)) {
+            A = *reinterpret_cast<const u32x4 *>(xs + t * 64);
+#pragma unroll
+            for (int i = 0; i < NT; i++) {
+                const uint32_t a0 = __builtin_amdgcn_perm(cp[i][t], lkc, 0x0c0c0400u);  // (c0 << 8) | (n << 4)
+                const uint32_t a1 = __builtin_amdgcn_perm(cp[i][t], lkc, 0x0c020500u);  // 64 KiB + (c1 << 8) | (n << 4)
+                B[i][0] = *reinterpret_cast<const u32x4 *>(lds + a0);
+                B[i][1] = *reinterpret_cast<const u32x4 *>(lds + a1);
+            }
+        };
+        lookups(0, Bg[0], Ax[0]);
 #pragma unroll
         for (int t = 0; t < 8; t++) {
-            const uint32_t a0 = __builtin_amdgcn_perm(cp[t], lkc, 0x0c0c0400u);  // (c0 << 8) | (n << 4)
-            const uint32_t a1 = __builtin_amdgcn_perm(cp[t], lkc, 0x0c020500u);  // 64 KiB + (c1 << 8) | (n << 4)
-            const u32x4 B0 = *reinterpret_cast<const u32x4 *>(lds + a0);
-            const u32x4 B1 = *reinterpret_cast<const u32x4 *>(lds + a1);
-            const h8 Ah = __builtin_bit_cast(h8, A[t]);
-            D[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, B0), D[t & 1], 0, 0, 0);
-            D[t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, B1), D[t & 1], 0, 0, 0);
+            if (t + 1 < 8) lookups(t + 1, Bg[(t + 1) & 1], Ax[(t + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            const h8 Ah = __builtin_bit_cast(h8, Ax[t & 1]);
+#pragma unroll
+            for (int i = 0; i < NT; i++) {
+                D[i][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, Bg[t & 1][i][0]), D[i][t & 1], 0, 0, 0);
+                D[i][t & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, __builtin_bit_cast(h8, Bg[t & 1][i][1]), D[i][t & 1], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -968,15 +997,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         settle_ops(on);
         if (fin) return;
         stage_x(on, xb ^ 1);
-        u32x4 A[8];  // lane 16q + m: activation row min(m, M-1), groups 4t + q of the slice
+        // step t's A operand, lane 16q + m: activation row min(m, M-1), groups 4t + q of the slice
         const uint8_t *xs = lds + L::off_x + xb * L::xbuf + min(n, M - 1) * kXRow + q4 * 16;
-#pragma unroll
-        for (int t = 0; t < 8; t++) A[t] = *reinterpret_cast<const u32x4 *>(xs + t * 64);
-#pragma unroll
-        for (int i = 0; i < RW; i++) {
-            if (W * i < rows_w) mma_tile(cur[i], A, Dacc[i]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        static_assert(RW == 2, "one or two tiles per wave and slice");
+        if (W < rows_w)
+            mma_tiles(std::integral_constant<int, 2>(), cur, xs, Dacc);
+        else if (0 < rows_w)
+            mma_tiles(std::integral_constant<int, 1>(), cur, xs, Dacc);
         lds_barrier();
         xb ^= 1;
         if (++ps < ps_end) return;
