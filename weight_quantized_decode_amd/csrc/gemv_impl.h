@@ -211,7 +211,11 @@ __device__ __forceinline__ void aq16_chunks(const Desc &D, int g, int cb, int ce
                                             const uint16_t *const (&xrow)[M], float (&acc)[M], Hook &&hook) {
     constexpr int P = 4;
     const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
-    const uint8_t *cbk = reinterpret_cast<const uint8_t *>(D.cbk);
+    // The gathers are buffer loads on a resource over the 1 MiB codebook: each takes the entry's
+    // 32-bit byte offset as it is (no 64-bit address arithmetic per gather).  Word 3 of the
+    // resource (0x00020000) is the raw 32-bit buffer format of gfx950.
+    const __amdgpu_buffer_rsrc_t cbr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(D.cbk), (short)0, 65536 * 16, 0x00020000);
     uint4 q[P];
     if (cb < ce) {
 #pragma unroll
@@ -228,7 +232,7 @@ __device__ __forceinline__ void aq16_chunks(const Desc &D, int g, int cb, int ce
 #pragma unroll
                 for (int i = 0; i < 8; i++) {
                     const uint32_t code = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                    e[i] = gld<u32x4>(cbk + (size_t)code * 16);
+                    e[i] = __builtin_amdgcn_raw_buffer_load_b128(cbr, code * 16, 0, 0);
                 }
                 q[j] = ld16_stream(cptr + (int64_t)min(cc + P, ce - 1) * 1024);
                 const int ng = min(8, (D.K - cc * 64) >> 3);  // groups inside K (8 but in a tail)
