@@ -353,6 +353,11 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
         cb = s * D.CS;
         ce = min(D.C, cb + D.CS);
     }
+    // (wave-uniform, but the compiler cannot tell: said so, the chunk loop's counters and the
+    // activation addresses stay in SGPRs instead of costing vector instructions per chunk)
+    cb = __builtin_amdgcn_readfirstlane(cb);
+    ce = __builtin_amdgcn_readfirstlane(ce);
+    g = __builtin_amdgcn_readfirstlane(g);
     const int row = g * 64 + lane;
     const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
     const uint16_t *xrow[M];
