@@ -679,15 +679,20 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
         }
     };
 
-    auto proc_group = [&](const uint4 (&buf)[U], const u32x2 (&X)[NWIN][H], int c, uint2 sq) {
+    // (full: every chunk of the group is below cfe, so no chunk needs its guard.  The batch-
+    // invariant instances keep it: they also run the shortest M = 1 launches, where a second,
+    // unguarded copy of the matrix-core body cost more than the guards: the fused decode step
+    // took 1.2% longer)
+    auto proc_group = [&](auto full, const uint4 (&buf)[U], const u32x2 (&X)[NWIN][H], int c, uint2 sq) {
+        constexpr bool kFull = decltype(full)::value;
         if constexpr (MF) {
             static_for<U>([&](auto jc) {
-                if (c + decltype(jc)::value < cfe) process_mf(jc, buf[decltype(jc)::value], X, c, sq);
+                if ((kFull && !BI) || c + decltype(jc)::value < cfe) process_mf(jc, buf[decltype(jc)::value], X, c, sq);
             });
         } else {
 #pragma unroll
             for (int j = 0; j < U; j++)
-                if (c + j < cfe) process(FullTag<true>{}, buf[j], c + j, sq);
+                if (kFull || c + j < cfe) process(FullTag<true>{}, buf[j], c + j, sq);
         }
     };
 
@@ -697,23 +702,24 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     if (cb < cfe) {
         const int ng = (cfe - cb + U - 1) / U;
         int gi = 0;
+        // (a group with a successor is full)
         while (true) {
             const int c = cb + gi * U;
             if (gi + 1 >= ng) {
-                proc_group(A, XA, c, sqA);
+                proc_group(FullTag<false>{}, A, XA, c, sqA);
                 break;
             }
             sqB = load_sq(c + U);
             load_group(B, XB, c + U);
-            proc_group(A, XA, c, sqA);
+            proc_group(FullTag<true>{}, A, XA, c, sqA);
             gi++;
             if (gi + 1 >= ng) {
-                proc_group(B, XB, c + U, sqB);
+                proc_group(FullTag<false>{}, B, XB, c + U, sqB);
                 break;
             }
             sqA = load_sq(c + 2 * U);
             load_group(A, XA, c + 2 * U);
-            proc_group(B, XB, c + U, sqB);
+            proc_group(FullTag<true>{}, B, XB, c + U, sqB);
             gi++;
         }
     }
