@@ -358,6 +358,10 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     cb = __builtin_amdgcn_readfirstlane(cb);
     ce = __builtin_amdgcn_readfirstlane(ce);
     g = __builtin_amdgcn_readfirstlane(g);
+    // TQ2 slices start at a multiple of 8 chunks (the planners align them to scale quads, which
+    // the scale loads rely on too), so a load group starts on an even chunk and the compiler knows
+    // which chunk of a group opens a 128-weight block (no branches or register copies for it)
+    if constexpr (FMT == TQ2) __builtin_assume((cb & 7) == 0);
     const int row = g * 64 + lane;
     const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
     const uint16_t *xrow[M];
