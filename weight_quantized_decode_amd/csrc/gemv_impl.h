@@ -360,8 +360,13 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
     g = __builtin_amdgcn_readfirstlane(g);
     // TQ2 slices start at a multiple of 8 chunks (the planners align them to scale quads, which
     // the scale loads rely on too), so a load group starts on an even chunk and the compiler knows
-    // which chunk of a group opens a 128-weight block (no branches or register copies for it)
-    if constexpr (FMT == TQ2) __builtin_assume((cb & 7) == 0);
+    // which chunk of a group opens a 128-weight block (no branches or register copies for it).
+    // Only an empty range can start elsewhere (a workgroup-split piece past the end of a row whose
+    // chunk count is not a multiple of 8): it is moved to a quad boundary, still empty.
+    if constexpr (FMT == TQ2) {
+        if (cb >= ce) cb = ce = cb & ~7;
+        __builtin_assume((cb & 7) == 0);
+    }
     const int row = g * 64 + lane;
     const uint8_t *cptr = D.codes + ((int64_t)g * D.C * 64 + lane) * 16;
     const uint16_t *xrow[M];
