@@ -353,8 +353,9 @@ __device__ __forceinline__ void run_unit(const Desc &D, int wu, int lane, uint32
         cb = s * D.CS;
         ce = min(D.C, cb + D.CS);
     }
-    // (wave-uniform, but the compiler cannot tell: said so, the chunk loop's counters and the
-    // activation addresses stay in SGPRs instead of costing vector instructions per chunk)
+    // These are wave-uniform, which the compiler cannot prove by itself; marked as such, the
+    // chunk loop's counters and the activation addresses stay in SGPRs instead of costing vector
+    // instructions per chunk.
     cb = __builtin_amdgcn_readfirstlane(cb);
     ce = __builtin_amdgcn_readfirstlane(ce);
     g = __builtin_amdgcn_readfirstlane(g);
